@@ -1,0 +1,183 @@
+"""DeepSeek-sparse-attention prefill hot path on MI355X (gfx950).
+
+Thin Python binding over libdsa.so (include/dsa.h).  This module only marshals
+arguments: every step of the path runs in the HIP kernels of the library, and
+PyTorch supplies device memory and the current stream.  There is no CPU or
+PyTorch fallback; calling any op without the built library raises.
+
+    idx = indexer_topk(q_idx, k_idx, w, q_pos0, top_k)       # int32 [L, top_k]
+    out = sparse_prefill(q, kv, idx, q_pos0, scale)          # bf16  [L, H, 512]
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libdsa.so"
+
+DSA_OK = 0
+STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
+                3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
+INDEX_HEADS = 32
+INDEX_DIM = 128
+MAX_TOPK = 4096
+D_LATENT = 512
+D_ROPE = 64
+DEFAULT_Q_BLOCK = 1024
+
+EXPORTED = ["dsa_indexer_topk_workspace_bytes", "dsa_indexer_topk", "dsa_causal_mask_topk",
+            "dsa_sparse_prefill", "dsa_sparse_prefill_gate", "dsa_status_string",
+            "dsa_last_error", "dsa_version"]
+
+_lib = None
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+
+
+def load_library(path: str | None = None):
+    """Load libdsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(f"{p} is missing: build it with `python -m dsa_sparse_attention_indexer_amd.build`")
+    lib = ctypes.CDLL(str(p))
+    P, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.dsa_indexer_topk_workspace_bytes.restype = sz
+    lib.dsa_indexer_topk_workspace_bytes.argtypes = [i64, i64, i32, i32]
+    lib.dsa_indexer_topk.restype = ctypes.c_int
+    lib.dsa_indexer_topk.argtypes = [P, P, P, i64, i64, i32, i32, i64, i32, i32, P, P, sz, P]
+    lib.dsa_causal_mask_topk.restype = ctypes.c_int
+    lib.dsa_causal_mask_topk.argtypes = [P, i64, i32, i64, P]
+    lib.dsa_sparse_prefill.restype = ctypes.c_int
+    lib.dsa_sparse_prefill.argtypes = [P, P, i64, P, i64, i64, i32, i32, i32, i32, i64, f32, i32, P, P, P]
+    lib.dsa_sparse_prefill_gate.restype = ctypes.c_int
+    lib.dsa_sparse_prefill_gate.argtypes = [i64, i64, i64, i64]
+    lib.dsa_status_string.restype = ctypes.c_char_p
+    lib.dsa_status_string.argtypes = [ctypes.c_int]
+    lib.dsa_last_error.restype = ctypes.c_char_p
+    lib.dsa_last_error.argtypes = []
+    lib.dsa_version.restype = ctypes.c_char_p
+    lib.dsa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != DSA_OK:
+        raise DSAError(status, _lib.dsa_last_error().decode())
+
+
+def _stream_ptr(tensor, stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(tensor.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _req(t, name, dtype, ndim):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got shape {tuple(t.shape)})")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def version() -> str:
+    return load_library().dsa_version().decode()
+
+
+def workspace_bytes(L: int, N: int, top_k: int, q_block: int = DEFAULT_Q_BLOCK) -> int:
+    return int(load_library().dsa_indexer_topk_workspace_bytes(L, N, top_k, q_block))
+
+
+def sparse_prefill_gate(B: int, L: int, N: int, min_context: int = 16384) -> bool:
+    return bool(load_library().dsa_sparse_prefill_gate(B, L, N, min_context))
+
+
+def indexer_topk(q_idx, k_idx, w, q_pos0: int, top_k: int, q_block: int = DEFAULT_Q_BLOCK,
+                 out=None, workspace=None, stream=None):
+    """Exact top-k key indices per query (ascending, -1 padded) -> int32 [L, top_k].
+
+    q_idx bf16 [L, 32, 128]; k_idx bf16 [N, 128]; w fp32 [L, 32]; query t sits at
+    position q_pos0 + t and may select keys 0..q_pos0+t.
+    """
+    import torch
+
+    lib = load_library()
+    _req(q_idx, "q_idx", torch.bfloat16, 3)
+    _req(k_idx, "k_idx", torch.bfloat16, 2)
+    _req(w, "w", torch.float32, 2)
+    L, nh, hd = q_idx.shape
+    N = k_idx.shape[0]
+    dev = q_idx.device
+    if out is None:
+        out = torch.empty((L, top_k), dtype=torch.int32, device=dev)
+    else:
+        _req(out, "out", torch.int32, 2)
+    need = lib.dsa_indexer_topk_workspace_bytes(L, N, top_k, q_block)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    _check(lib.dsa_indexer_topk(q_idx.data_ptr(), k_idx.data_ptr(), w.data_ptr(), L, N, nh, hd,
+                                q_pos0, top_k, q_block, out.data_ptr(), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream_ptr(q_idx, stream)))
+    return out
+
+
+def causal_mask_topk(idx, q_pos0: int, stream=None):
+    """In place: idx[t, j] > q_pos0 + t becomes -1.  Returns idx."""
+    import torch
+
+    lib = load_library()
+    _req(idx, "idx", torch.int32, 2)
+    L, k = idx.shape
+    _check(lib.dsa_causal_mask_topk(idx.data_ptr(), L, k, q_pos0, _stream_ptr(idx, stream)))
+    return idx
+
+
+def sparse_prefill(q, kv, idx, q_pos0: int, scale: float, q_block: int = DEFAULT_Q_BLOCK,
+                   return_lse: bool = False, out=None, lse=None, stream=None):
+    """Sparse absorbed-MLA attention -> bf16 [L, H, 512] (and fp32 lse [L, H]).
+
+    q bf16 [L, H, 576]; kv bf16 [N, >=576] (latent 0..511 | rope 512..575, the
+    latent is also the value); idx int32 [L, top_k] (-1 and future keys skipped).
+    """
+    import torch
+
+    lib = load_library()
+    _req(q, "q", torch.bfloat16, 3)
+    _req(idx, "idx", torch.int32, 2)
+    if not (isinstance(kv, torch.Tensor) and kv.dtype == torch.bfloat16 and kv.dim() == 2 and kv.is_cuda
+            and kv.stride(1) == 1):
+        raise ValueError("kv must be a bf16 GPU tensor [N, stride>=576] with unit column stride")
+    L, H, dqk = q.shape
+    N = kv.shape[0]
+    top_k = idx.shape[1]
+    if dqk != D_LATENT + D_ROPE:
+        raise ValueError(f"q must be [L, H, {D_LATENT + D_ROPE}]")
+    if idx.shape[0] != L:
+        raise ValueError("idx must have L rows")
+    if out is None:
+        out = torch.empty((L, H, D_LATENT), dtype=torch.bfloat16, device=q.device)
+    else:
+        _req(out, "out", torch.bfloat16, 3)
+    if return_lse and lse is None:
+        lse = torch.empty((L, H), dtype=torch.float32, device=q.device)
+    _check(lib.dsa_sparse_prefill(q.data_ptr(), kv.data_ptr(), kv.stride(0), idx.data_ptr(), L, N, H,
+                                  D_LATENT, D_ROPE, top_k, q_pos0, float(scale), q_block, out.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None, _stream_ptr(q, stream)))
+    return (out, lse) if return_lse else out

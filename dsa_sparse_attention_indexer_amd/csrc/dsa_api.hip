@@ -1,0 +1,222 @@
+// dsa_api.hip -- the C ABI (include/dsa.h): argument checks, workspace carving and
+// the query-block loop.  Host code only; every step of the path runs in the kernels
+// of indexer.hip and attention.hip.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+dsa_status_t fail(dsa_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+dsa_status_t hip_fail(hipError_t e, const char* what) {
+    return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int resolve_q_block(int32_t q_block) { return q_block <= 0 ? DSA_DEFAULT_Q_BLOCK : q_block; }
+
+bool debug_force_fallback() {
+    const char* v = getenv("DSA_DEBUG_FORCE_FALLBACK");
+    return v && v[0] == '1';
+}
+
+dsa_status_t check_indexer_args(const uint16_t* q_idx, const uint16_t* k_idx, const float* w,
+                                int64_t L, int64_t N, int32_t n_heads, int32_t head_dim,
+                                int64_t q_pos0, int32_t top_k, int32_t q_block,
+                                const int32_t* out_idx) {
+    if (L < 0) return fail(DSA_ERR_INVALID_ARG, "L must be >= 0 (got %lld)", (long long)L);
+    if (N <= 0) return fail(DSA_ERR_INVALID_ARG, "N must be > 0 (got %lld)", (long long)N);
+    if (N > (int64_t)INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "N above 2^31-1 is not supported");
+    if (q_pos0 < 0 || q_pos0 + L > N)
+        return fail(DSA_ERR_INVALID_ARG, "need 0 <= q_pos0 and q_pos0 + L <= N (q_pos0=%lld L=%lld N=%lld)",
+                    (long long)q_pos0, (long long)L, (long long)N);
+    if (top_k < 1 || top_k > DSA_MAX_TOPK)
+        return fail(DSA_ERR_INVALID_ARG, "top_k must be in 1..%d (got %d)", DSA_MAX_TOPK, top_k);
+    if (q_block < 0) return fail(DSA_ERR_INVALID_ARG, "q_block must be >= 0 (got %d)", q_block);
+    if (n_heads != DSA_INDEX_HEADS || head_dim != DSA_INDEX_DIM)
+        return fail(DSA_ERR_UNSUPPORTED, "indexer needs %d heads x %d dims (got %d x %d)", DSA_INDEX_HEADS,
+                    DSA_INDEX_DIM, n_heads, head_dim);
+    if (L > 0 && (!q_idx || !k_idx || !w || !out_idx))
+        return fail(DSA_ERR_INVALID_ARG, "null tensor pointer");
+    if (L > 0 && (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(w, 4) || !aligned(out_idx, 4)))
+        return fail(DSA_ERR_INVALID_ARG, "q_idx/k_idx must be 16-byte aligned, w/out_idx 4-byte aligned");
+    return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_version(void) { return "dsa-mi355x 0.1 (gfx950)"; }
+
+const char* dsa_last_error(void) { return g_last_error; }
+
+const char* dsa_status_string(dsa_status_t s) {
+    switch (s) {
+        case DSA_OK: return "ok";
+        case DSA_ERR_INVALID_ARG: return "invalid argument";
+        case DSA_ERR_UNSUPPORTED: return "unsupported shape";
+        case DSA_ERR_WORKSPACE: return "workspace too small";
+        case DSA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int dsa_sparse_prefill_gate(int64_t B, int64_t L, int64_t N, int64_t min_context) {
+    if (min_context <= 0) min_context = 16384;
+    return (B == 1 && L > 1 && N >= min_context) ? 1 : 0;
+}
+
+size_t dsa_indexer_topk_workspace_bytes(int64_t L, int64_t N, int32_t top_k, int32_t q_block) {
+    if (L < 0 || N <= 0 || N > (int64_t)INT32_MAX || top_k < 1 || top_k > DSA_MAX_TOPK || q_block < 0)
+        return 0;
+    int64_t qb = resolve_q_block(q_block);
+    int64_t rows = L < qb ? L : qb;
+    if (rows < 1) rows = 1;
+    return dsa::IndexerLayout::make(rows, N, top_k).total;
+}
+
+dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, const float* w, int64_t L,
+                              int64_t N, int32_t n_heads, int32_t head_dim, int64_t q_pos0, int32_t top_k,
+                              int32_t q_block, int32_t* out_idx, void* workspace, size_t workspace_bytes,
+                              dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    dsa_status_t st = check_indexer_args(q_idx, k_idx, w, L, N, n_heads, head_dim, q_pos0, top_k, q_block, out_idx);
+    if (st != DSA_OK) return st;
+    if (L == 0) return DSA_OK;
+    const size_t need = dsa_indexer_topk_workspace_bytes(L, N, top_k, q_block);
+    if (!workspace || workspace_bytes < need)
+        return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                    workspace ? "" : ", null");
+    if (!aligned(workspace, 256)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int qb = resolve_q_block(q_block);
+    const int64_t rows = L < qb ? L : qb;
+    const dsa::IndexerLayout lay = dsa::IndexerLayout::make(rows, N, top_k);
+    char* ws = static_cast<char*>(workspace);
+
+    dsa::IndexerArgs a{};
+    a.k_idx = k_idx;
+    a.N = N;
+    a.top_k = top_k;
+    a.cap = lay.cap;
+    a.sample_stride = lay.sample_stride;
+    a.fold_cap = lay.fold_cap;
+    a.force_fallback = debug_force_fallback() ? 1 : 0;
+    a.kstats = reinterpret_cast<dsa::KeyStats*>(ws + lay.off_kstats);
+    a.tau = reinterpret_cast<float*>(ws + lay.off_tau);
+    a.delta = reinterpret_cast<float*>(ws + lay.off_delta);
+    a.mode = reinterpret_cast<int*>(ws + lay.off_mode);
+    a.count = reinterpret_cast<int*>(ws + lay.off_count);
+    a.fb_ctrl = reinterpret_cast<int*>(ws + lay.off_fbctrl);
+    a.fb_list = reinterpret_cast<int*>(ws + lay.off_fblist);
+    a.sample = reinterpret_cast<float*>(ws + lay.off_sample);
+    a.cand_s = reinterpret_cast<float*>(ws + lay.off_cand_s);
+    a.cand_i = reinterpret_cast<int*>(ws + lay.off_cand_i);
+    a.fold_s = reinterpret_cast<float*>(ws + lay.off_fold_s);
+    a.fold_i = reinterpret_cast<int*>(ws + lay.off_fold_i);
+    a.fold_bi = reinterpret_cast<int*>(ws + lay.off_fold_bi);
+    a.fold_bs = reinterpret_cast<double*>(ws + lay.off_fold_bs);
+    a.fold_bf = reinterpret_cast<float*>(ws + lay.off_fold_bf);
+
+    // Key statistics over every key any query of the chunk may see.
+    const int64_t last = q_pos0 + L - 1;
+    const int64_t n_keys = (last < N - 1 ? last : N - 1) + 1;
+    hipError_t e = dsa::launch_key_stats(k_idx, n_keys, a.kstats, s);
+    if (e != hipSuccess) return hip_fail(e, "key statistics launch");
+
+    for (int64_t b0 = 0; b0 < L; b0 += qb) {
+        const int64_t Lb = (L - b0) < qb ? (L - b0) : qb;
+        a.q_idx = q_idx + (size_t)b0 * DSA_INDEX_HEADS * DSA_INDEX_DIM;
+        a.w = w + (size_t)b0 * DSA_INDEX_HEADS;
+        a.out = out_idx + (size_t)b0 * top_k;
+        a.pos0 = q_pos0 + b0;
+        a.Lb = (int)Lb;
+        const int64_t last_pos = a.pos0 + Lb - 1;
+        const int64_t n_last = (last_pos < N - 1 ? last_pos : N - 1) + 1;
+        const bool need_sample = n_last > lay.cap;
+        e = dsa::launch_indexer_block(a, need_sample, s);
+        if (e != hipSuccess) return hip_fail(e, "indexer launch");
+    }
+    return DSA_OK;
+}
+
+dsa_status_t dsa_causal_mask_topk(int32_t* idx, int64_t L, int32_t top_k, int64_t q_pos0, dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    if (L < 0) return fail(DSA_ERR_INVALID_ARG, "L must be >= 0");
+    if (top_k < 1) return fail(DSA_ERR_INVALID_ARG, "top_k must be >= 1");
+    if (q_pos0 < 0) return fail(DSA_ERR_INVALID_ARG, "q_pos0 must be >= 0");
+    if (L == 0) return DSA_OK;
+    if (!idx) return fail(DSA_ERR_INVALID_ARG, "null index pointer");
+    if (!aligned(idx, 4)) return fail(DSA_ERR_INVALID_ARG, "idx must be 4-byte aligned");
+    hipError_t e = dsa::launch_causal_mask(idx, L, top_k, q_pos0, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "causal mask launch");
+    return DSA_OK;
+}
+
+dsa_status_t dsa_sparse_prefill(const uint16_t* q, const uint16_t* kv, int64_t kv_stride, const int32_t* idx,
+                                int64_t L, int64_t N, int32_t H, int32_t d_latent, int32_t d_rope, int32_t top_k,
+                                int64_t q_pos0, float scale, int32_t q_block, uint16_t* out, float* lse,
+                                dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    if (L < 0) return fail(DSA_ERR_INVALID_ARG, "L must be >= 0 (got %lld)", (long long)L);
+    if (N <= 0) return fail(DSA_ERR_INVALID_ARG, "N must be > 0 (got %lld)", (long long)N);
+    if (N > (int64_t)INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "N above 2^31-1 is not supported");
+    if (q_pos0 < 0 || q_pos0 + L > N)
+        return fail(DSA_ERR_INVALID_ARG, "need 0 <= q_pos0 and q_pos0 + L <= N");
+    if (top_k < 1) return fail(DSA_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", top_k);
+    if (q_block < 0) return fail(DSA_ERR_INVALID_ARG, "q_block must be >= 0");
+    if (d_latent != DSA_D_LATENT || d_rope != DSA_D_ROPE)
+        return fail(DSA_ERR_UNSUPPORTED, "need d_latent=%d and d_rope=%d (got %d, %d)", DSA_D_LATENT, DSA_D_ROPE,
+                    d_latent, d_rope);
+    if (H <= 0 || H % 16 != 0 || H > DSA_MAX_HEADS)
+        return fail(DSA_ERR_UNSUPPORTED, "H must be a positive multiple of 16 up to %d (got %d)", DSA_MAX_HEADS, H);
+    if (kv_stride < d_latent + d_rope || kv_stride % 8 != 0)
+        return fail(DSA_ERR_INVALID_ARG, "kv_stride must be >= %d and a multiple of 8 (got %lld)",
+                    d_latent + d_rope, (long long)kv_stride);
+    if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+        return fail(DSA_ERR_INVALID_ARG, "scale must be finite");
+    if (L == 0) return DSA_OK;
+    if (!q || !kv || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(idx, 4) || !aligned(out, 8) || (lse && !aligned(lse, 4)))
+        return fail(DSA_ERR_INVALID_ARG, "q/kv must be 16-byte aligned, out 8-byte, idx/lse 4-byte");
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int qb = resolve_q_block(q_block);
+    for (int64_t b0 = 0; b0 < L; b0 += qb) {
+        dsa::AttentionArgs a{};
+        const int64_t Lb = (L - b0) < qb ? (L - b0) : qb;
+        a.q = q + (size_t)b0 * H * (d_latent + d_rope);
+        a.kv = kv;
+        a.idx = idx + (size_t)b0 * top_k;
+        a.out = out + (size_t)b0 * H * d_latent;
+        a.lse = lse ? lse + (size_t)b0 * H : nullptr;
+        a.kv_stride = kv_stride;
+        a.N = N;
+        a.pos0 = q_pos0 + b0;
+        a.Lb = (int)Lb;
+        a.H = H;
+        a.top_k = top_k;
+        a.scale = scale;
+        hipError_t e = dsa::launch_sparse_attention(a, s);
+        if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+    }
+    return DSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// dsa_internal.h -- host/device interface between the C ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+enum : int { kModeNormal = 0, kModeAll = 1 };
+
+struct KeyStats {
+    unsigned knorm_bits;  // max ||k_s||_2 (fp32 bits, rounded up)
+    unsigned kinf_bits;   // max |k_s,i|
+    int kexp_min;         // min exponent of the lowest set bit over nonzero k elements
+    int pad;
+};
+
+// Candidate capacity per query row: expected candidates are 2.5 * top_k.
+__host__ __device__ inline int cand_capacity(int top_k) {
+    int c = 4 * top_k;
+    if (c < 8192) c = 8192;
+    return (c + 1023) & ~1023;
+}
+
+// Keys scored in the threshold sample of a row group whose first row sees n_t keys.
+__host__ __device__ inline int sample_size(int64_t n_t, int top_k, int cap) {
+    if (n_t <= cap) return 0;
+    int64_t s = (int64_t)((n_t * 128 + (int64_t)(2.5 * top_k) - 1) / (int64_t)(2.5 * top_k));
+    if (s < 1024) s = 1024;
+    if (s > 16384) s = 16384;
+    if (s > n_t) s = n_t;
+    return (int)s;
+}
+
+// Rank (1 = largest) of the sample score used as the row's threshold estimate.
+__host__ __device__ inline int sample_rank(int64_t n_t, int s, int top_k) {
+    double r = 2.5 * (double)top_k * (double)s / (double)n_t;
+    int ri = (int)r;
+    if ((double)ri < r) ++ri;
+    if (ri < 1) ri = 1;
+    if (ri > s) ri = s;
+    return ri;
+}
+
+constexpr int kFallbackSlots = 32;
+constexpr int kFoldKeys = 4096;
+
+struct IndexerLayout {
+    int rows, cap, sample_stride, fold_cap;
+    size_t off_kstats, off_tau, off_delta, off_mode, off_count, off_fbctrl, off_fblist;
+    size_t off_sample, off_cand_s, off_cand_i;
+    size_t off_fold_s, off_fold_i, off_fold_bi, off_fold_bs, off_fold_bf;
+    size_t total;
+
+    static IndexerLayout make(int64_t rows, int64_t N, int top_k) {
+        IndexerLayout l{};
+        auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+        l.rows = (int)((rows + 3) & ~3LL);
+        l.cap = cand_capacity(top_k);
+        l.sample_stride = sample_size(N, top_k, l.cap);
+        l.fold_cap = top_k + kFoldKeys;
+        size_t o = 0;
+        l.off_kstats = o; o = al(o + sizeof(KeyStats));
+        l.off_tau = o; o = al(o + 4 * (size_t)l.rows);
+        l.off_delta = o; o = al(o + 4 * (size_t)l.rows);
+        l.off_mode = o; o = al(o + 4 * (size_t)l.rows);
+        l.off_count = o; o = al(o + 4 * (size_t)l.rows);
+        l.off_fbctrl = o; o = al(o + 16);
+        l.off_fblist = o; o = al(o + 4 * (size_t)l.rows);
+        l.off_sample = o; o = al(o + 4 * (size_t)l.rows * (size_t)l.sample_stride);
+        l.off_cand_s = o; o = al(o + 4 * (size_t)l.rows * (size_t)l.cap);
+        l.off_cand_i = o; o = al(o + 4 * (size_t)l.rows * (size_t)l.cap);
+        l.off_fold_s = o; o = al(o + 4 * (size_t)kFallbackSlots * 2 * l.fold_cap);
+        l.off_fold_i = o; o = al(o + 4 * (size_t)kFallbackSlots * 2 * l.fold_cap);
+        l.off_fold_bi = o; o = al(o + 4 * (size_t)kFallbackSlots * l.fold_cap);
+        l.off_fold_bs = o; o = al(o + 8 * (size_t)kFallbackSlots * l.fold_cap);
+        l.off_fold_bf = o; o = al(o + 4 * (size_t)kFallbackSlots * l.fold_cap);
+        l.total = o;
+        return l;
+    }
+};
+
+struct IndexerArgs {
+    const uint16_t* q_idx;  // rows of this block: [Lb][32][128]
+    const uint16_t* k_idx;  // [N][128]
+    const float* w;         // [Lb][32]
+    int32_t* out;           // [Lb][top_k]
+    int64_t N;
+    int64_t pos0;           // position of the block's first query
+    int Lb;
+    int top_k;
+    int cap;
+    int sample_stride;
+    int fold_cap;
+    int force_fallback;     // debug: send every scored row through the fallback fold
+    KeyStats* kstats;
+    float* tau;
+    float* delta;
+    int* mode;
+    int* count;
+    int* fb_ctrl;           // [0] flagged rows, [1] next row to take
+    int* fb_list;
+    float* sample;
+    float* cand_s;
+    int* cand_i;
+    float* fold_s;          // [slots][2][fold_cap]
+    int* fold_i;            // [slots][2][fold_cap]
+    int* fold_bi;           // [slots][fold_cap]
+    double* fold_bs;        // [slots][fold_cap]
+    float* fold_bf;         // [slots][fold_cap]
+};
+
+// Kernel launchers (indexer.hip).  Each returns the launch status.
+hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, hipStream_t s);
+hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s);
+hipError_t launch_causal_mask(int32_t* idx, int64_t L, int top_k, int64_t q_pos0, hipStream_t s);
+
+struct AttentionArgs {
+    const uint16_t* q;    // [Lb][H][576]
+    const uint16_t* kv;   // [N][kv_stride]
+    const int32_t* idx;   // [Lb][top_k]
+    uint16_t* out;        // [Lb][H][512]
+    float* lse;           // [Lb][H] or null
+    int64_t kv_stride;
+    int64_t N;
+    int64_t pos0;
+    int Lb, H, top_k;
+    float scale;
+};
+hipError_t launch_sparse_attention(const AttentionArgs& a, hipStream_t s);
+
+}  // namespace dsa

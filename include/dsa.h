@@ -1,0 +1,161 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek-sparse-attention prefill path.
+ *
+ * Three operations, one sequence per call (batch 1):
+ *   dsa_indexer_topk     indexer scores + exact top-k with causal masking
+ *   dsa_causal_mask_topk causal masking of an externally supplied index tensor
+ *   dsa_sparse_prefill   sparse absorbed-MLA attention over the selected keys
+ *
+ * Conventions shared by every entry point
+ *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense,
+ *     row-major, and live in device memory owned by the caller.  Inputs are
+ *     never written.
+ *   - Key index = sequence position.  Query t of the chunk sits at position
+ *     q_pos0 + t; it may only use keys 0 .. q_pos0 + t.
+ *   - Work is enqueued on `stream` (0 = the null stream) and returns without
+ *     waiting for the device.  The library keeps no pointer after return
+ *     beyond stream-ordered use, and allocates nothing on these paths.
+ *   - Arguments are validated before anything is enqueued; on a non-OK
+ *     status no output byte has been written.  Asynchronous device faults show
+ *     up at the caller's next synchronisation.  No exception crosses the ABI
+ *     and the library never aborts.
+ *   - Results are deterministic and identical run to run and for every
+ *     q_block value.  Calls may run concurrently on different streams when
+ *     each has its own workspace.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* dsa_stream_t; /* a hipStream_t */
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size or position          */
+    DSA_ERR_UNSUPPORTED = 2, /* a shape this build has no kernel for        */
+    DSA_ERR_WORKSPACE = 3,   /* workspace null or smaller than required     */
+    DSA_ERR_HIP = 4          /* a HIP runtime call failed (see last_error)  */
+} dsa_status_t;
+
+#define DSA_INDEX_HEADS 32   /* indexer heads                                 */
+#define DSA_INDEX_DIM 128    /* indexer head dimension                        */
+#define DSA_MAX_TOPK 4096    /* largest supported top_k                       */
+#define DSA_D_LATENT 512     /* latent width = value width                    */
+#define DSA_D_ROPE 64        /* rope width; key/query width is 576            */
+#define DSA_MAX_HEADS 128    /* attention heads: a multiple of 16, <= 128     */
+#define DSA_DEFAULT_Q_BLOCK 1024
+
+/*
+ * Bytes of device workspace dsa_indexer_topk needs for these sizes.  The
+ * figure depends on N, top_k and min(L, q_block), never on L*N.  Returns 0 for
+ * arguments dsa_indexer_topk would reject.
+ */
+size_t dsa_indexer_topk_workspace_bytes(int64_t L, int64_t N, int32_t top_k, int32_t q_block);
+
+/*
+ * Indexer + top-k ("GLM prefill now attends only to the keys its indexer
+ * picks", How it works: the indexer scores every cached key with 32 heads and
+ * keeps the top-k per query; the blocked form folds 4,096-key blocks into a
+ * running list and never builds the B x 32 x L x N score tensor.  The
+ * LiteTopK abstract supplies the threshold scheme: sample the score range,
+ * keep a tight threshold, write back only promising candidates, stay exact).
+ *
+ *   score(t, s) = sum_h w[t,h] * max(0, q_idx[t,h,:] . k_idx[s,:])
+ *
+ * Selection is over the causal keys s <= q_pos0 + t, highest score first,
+ * lower key index first among equal scores.  Scores are ranked exactly as
+ * the fp64 evaluation  d_h = sum_i q*k (i ascending), r_h = max(d_h, +0),
+ * s = sum_h fl64(w_h * r_h) (h ascending)  ranks them: fp32 matrix-core
+ * scores select, and every key whose fp32 score lies within a proven error
+ * bound of the k-th is re-scored in that fp64 order.
+ *
+ *   q_idx   bf16 [L][n_heads][head_dim]
+ *   k_idx   bf16 [N][head_dim]
+ *   w       fp32 [L][n_heads]
+ *   n_heads must be 32, head_dim must be 128 (else DSA_ERR_UNSUPPORTED)
+ *   q_pos0  0 <= q_pos0 and q_pos0 + L <= N
+ *   top_k   1 .. DSA_MAX_TOPK
+ *   q_block queries per internal block; 0 selects 1024
+ *   out_idx int32 [L][top_k]: selected keys in ascending order; a row with
+ *           fewer than top_k causal keys is padded with -1
+ *   workspace / workspace_bytes: device scratch of at least
+ *           dsa_indexer_topk_workspace_bytes(L, N, top_k, q_block) bytes,
+ *           256-byte aligned; contents need not be initialised
+ * L == 0 is a no-op returning DSA_OK.
+ */
+dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, const float* w,
+                              int64_t L, int64_t N, int32_t n_heads, int32_t head_dim,
+                              int64_t q_pos0, int32_t top_k, int32_t q_block, int32_t* out_idx,
+                              void* workspace, size_t workspace_bytes, dsa_stream_t stream);
+
+/*
+ * Causal masking of an index tensor ("cuda : support for sparse KV indices in
+ * MMA flash attention kernel", review thread: apply causality to the top-k
+ * indices with a separate op, masked entries becoming -1, assuming key index =
+ * sequence position).  In place: idx[t][j] > q_pos0 + t becomes -1; every
+ * other entry (including -1) is left as is.  Idempotent.
+ *   idx int32 [L][top_k] (device); L >= 0, top_k >= 1, q_pos0 >= 0
+ */
+dsa_status_t dsa_causal_mask_topk(int32_t* idx, int64_t L, int32_t top_k, int64_t q_pos0,
+                                  dsa_stream_t stream);
+
+/*
+ * Sparse prefill attention in the absorbed latent space ("GLM prefill now
+ * attends only to the keys its indexer picks", How it works: join the 512-wide
+ * latent and 64-wide rope caches into one 576-wide key, gather the top-k rows
+ * each query picked, all heads share that block, the latent is also the
+ * value; chunks above 1,024 queries run as query blocks).
+ *
+ *   for each query t and head h, over J = { idx[t][j] : idx != -1, idx <= q_pos0+t }:
+ *     l_j = scale * q[t,h,:] . kv[j, 0:576]
+ *     out[t,h,:] = sum_j softmax(l)_j * kv[j, 0:512]      (fp32 accumulate, bf16 out)
+ *     lse[t,h]   = log(sum_j exp(l_j))                    (natural log)
+ *   an empty J gives out = 0 and lse = -inf.
+ *
+ *   q        bf16 [L][H][d_latent + d_rope]
+ *   kv       bf16 [N][kv_stride]: latent in 0..d_latent-1, rope after it
+ *   kv_stride elements per kv row, >= d_latent + d_rope, a multiple of 8
+ *   idx      int32 [L][top_k]; indices must be < N (or -1); repeats are out of contract
+ *   H        a multiple of 16, <= DSA_MAX_HEADS (else DSA_ERR_UNSUPPORTED)
+ *   d_latent must be 512 and d_rope 64 (else DSA_ERR_UNSUPPORTED)
+ *   q_pos0   0 <= q_pos0, q_pos0 + L <= N
+ *   scale    logit scale (1/sqrt(192) for the GLM/DeepSeek shapes)
+ *   q_block  queries per launch; 0 selects 1024
+ *   out      bf16 [L][H][d_latent]
+ *   lse      fp32 [L][H] or NULL
+ * L == 0 is a no-op returning DSA_OK.
+ */
+dsa_status_t dsa_sparse_prefill(const uint16_t* q, const uint16_t* kv, int64_t kv_stride,
+                                const int32_t* idx, int64_t L, int64_t N, int32_t H,
+                                int32_t d_latent, int32_t d_rope, int32_t top_k, int64_t q_pos0,
+                                float scale, int32_t q_block, uint16_t* out, float* lse,
+                                dsa_stream_t stream);
+
+/*
+ * The sparse-prefill gate of the GLM page ("How it works": sparse only for a
+ * single sequence, only in prefill, and only once the cache holds at least
+ * min_context tokens; 16,384 by default).  Returns 1 when the sparse path
+ * applies to (B, L, N), else 0.  min_context <= 0 selects 16384.  Host only.
+ */
+int dsa_sparse_prefill_gate(int64_t B, int64_t L, int64_t N, int64_t min_context);
+
+/* Static description of a status code. */
+const char* dsa_status_string(dsa_status_t s);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* dsa_last_error(void);
+
+/* Library version string. */
+const char* dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

@@ -1,0 +1,133 @@
+"""Host-only checks of the C ABI: the library loads, exports what include/dsa.h
+declares, and rejects bad arguments before touching the GPU (validation runs
+before any HIP call, so these need no device)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import dsa_sparse_attention_indexer_amd as dsa
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "dsa.h"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not dsa.LIB_PATH.exists():
+        from dsa_sparse_attention_indexer_amd import build
+
+        build.build()
+    return dsa.load_library()
+
+
+def header_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(dsa.EXPORTED)
+
+
+def test_version_and_status_strings(lib):
+    assert b"gfx950" in lib.dsa_version()
+    assert lib.dsa_status_string(0) == b"ok"
+    assert lib.dsa_status_string(3) == b"workspace too small"
+    assert lib.dsa_status_string(99) == b"unknown status"
+
+
+def test_gate_matches_the_glm_rule(lib):
+    assert lib.dsa_sparse_prefill_gate(1, 512, 16384, 0) == 1
+    assert lib.dsa_sparse_prefill_gate(1, 512, 16383, 0) == 0  # below the minimum context
+    assert lib.dsa_sparse_prefill_gate(2, 512, 131072, 0) == 0  # batches stay dense
+    assert lib.dsa_sparse_prefill_gate(1, 1, 131072, 0) == 0  # decode untouched
+    assert lib.dsa_sparse_prefill_gate(1, 2, 4096, 4096) == 1
+
+
+def test_workspace_is_bounded_by_the_query_block(lib):
+    ws = lib.dsa_indexer_topk_workspace_bytes
+    a = ws(2048, 131072, 2048, 1024)
+    b = ws(8192, 131072, 2048, 1024)
+    assert a == b > 0  # independent of L beyond one block
+    assert ws(1024, 131072, 2048, 1024) == a
+    assert ws(512, 131072, 2048, 1024) < a
+    assert ws(1024, 131072, 2048, 256) < a
+    # grows with N only through the threshold sample, never as L*N
+    big = ws(8192, 786432, 2048, 1024)
+    assert big < 8192 * 786432 * 4 / 50
+    assert ws(-1, 100, 1, 0) == 0 and ws(1, 0, 1, 0) == 0 and ws(1, 100, 0, 0) == 0
+    assert ws(1, 100, dsa.MAX_TOPK + 1, 0) == 0
+
+
+NULL = None
+
+
+def call_indexer(lib, L=4, N=64, nh=32, hd=128, q_pos0=60, k=8, qb=0, ptr=1 << 20, ws=1 << 30,
+                 ws_bytes=1 << 40):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.dsa_indexer_topk(p, p, p, L, N, nh, hd, q_pos0, k, qb, p,
+                                ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=-1), 1), (dict(N=0), 1), (dict(q_pos0=-1), 1), (dict(q_pos0=61), 1),
+    (dict(k=0), 1), (dict(k=4097), 1), (dict(qb=-2), 1),
+    (dict(nh=16), 2), (dict(hd=64), 2), (dict(ptr=0), 1),
+    (dict(ws=0), 3), (dict(ws_bytes=10), 3), (dict(ptr=(1 << 20) + 2), 1),
+])
+def test_indexer_rejects_bad_arguments(lib, kw, status):
+    assert call_indexer(lib, **kw) == status
+    assert lib.dsa_last_error() != b""
+
+
+def test_indexer_zero_rows_is_a_no_op(lib):
+    assert call_indexer(lib, L=0, ptr=0, ws=0, ws_bytes=0) == 0
+
+
+def call_attn(lib, L=4, N=64, H=64, dl=512, dr=64, k=8, q_pos0=60, stride=576, scale=0.07, qb=0,
+              ptr=1 << 20):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.dsa_sparse_prefill(p, p, stride, p, L, N, H, dl, dr, k, q_pos0, scale, qb, p, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=-1), 1), (dict(N=0), 1), (dict(q_pos0=61), 1), (dict(k=0), 1), (dict(qb=-1), 1),
+    (dict(H=24), 2), (dict(H=0), 2), (dict(H=144), 2), (dict(dl=256), 2), (dict(dr=32), 2),
+    (dict(stride=575), 1), (dict(stride=580), 1), (dict(scale=float("nan")), 1),
+    (dict(scale=float("inf")), 1), (dict(ptr=0), 1),
+])
+def test_attention_rejects_bad_arguments(lib, kw, status):
+    assert call_attn(lib, **kw) == status
+    assert lib.dsa_last_error() != b""
+
+
+def test_attention_zero_rows_is_a_no_op(lib):
+    assert call_attn(lib, L=0, ptr=0) == 0
+
+
+def test_causal_mask_rejects_bad_arguments(lib):
+    f = lib.dsa_causal_mask_topk
+    assert f(ctypes.c_void_p(1 << 20), -1, 4, 0, None) == 1
+    assert f(ctypes.c_void_p(1 << 20), 4, 0, 0, None) == 1
+    assert f(ctypes.c_void_p(1 << 20), 4, 4, -1, None) == 1
+    assert f(None, 4, 4, 0, None) == 1
+    assert f(None, 0, 4, 0, None) == 0
+
+
+def test_python_binding_raises_without_library(monkeypatch, tmp_path):
+    import importlib
+
+    mod = importlib.reload(dsa)
+    try:
+        monkeypatch.setattr(mod, "LIB_PATH", tmp_path / "missing.so")
+        with pytest.raises(RuntimeError, match="missing"):
+            mod.load_library()
+    finally:
+        importlib.reload(dsa)
