@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Prefill throughput of the DSA hot path on one MI355X.
+
+One step = dsa_indexer_topk followed by dsa_sparse_prefill over one prefill
+chunk (indexer scores + exact top-k + causal masking + sparse absorbed-MLA
+attention), inputs resident in HBM.  Default workload: N = 131,072 cached keys,
+L = 2,048 queries (the newest positions, run as two 1,024-query blocks),
+top_k = 2,048, indexer 32 heads x 128, attention 64 heads x 576/512, bf16.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C3]
+
+Prints one JSON line (see the "roofline" and "cpu_baseline" objects).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "prefill tokens/sec (indexer+topk+sparse attn) at N=128K, top-k=2048; % roofline"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def workload_sizes(wl):
+    """Algorithmic work of one step, per query row: (indexer flops, attention flops, attention bytes)."""
+    rows = []
+    for t in range(wl.L):
+        p = wl.pos0 + t
+        n_t = min(p, wl.N - 1) + 1
+        k_valid = min(wl.top_k, n_t)
+        f_idx = 2 * 32 * 128 * n_t
+        f_attn = 2 * wl.H * (576 + 512) * k_valid
+        b_attn = k_valid * 576 * 2 + 4 * wl.top_k + wl.H * 576 * 2 + wl.H * 512 * 2
+        rows.append((f_idx, f_attn, b_attn))
+    return rows
+
+
+def cpu_baseline(wl, inp, target_s: float):
+    """Time the fp64 oracle (indexer + top-k + attention) on a bounded row sample."""
+    import numpy as np
+
+    import dsa_inputs as di
+    import oracle
+
+    oracle.build(force=False)
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    threads = max(1, min(16, threads))
+
+    def run(rows, n_threads):
+        t0 = time.perf_counter()
+        sel = oracle.topk(inp["q_idx"], inp["k_idx"], inp["w"], wl.pos0, wl.top_k, rows=rows,
+                          n_threads=n_threads)
+        idx = np.full((wl.L, wl.top_k), -1, np.int32)
+        idx[rows] = sel
+        oracle.attention(inp["q"], inp["kv"], idx, wl.pos0, di.SOFTMAX_SCALE, rows=rows, n_threads=n_threads)
+        return time.perf_counter() - t0
+
+    one = run(np.array([wl.L - 1], np.int64), 1)
+    n_rows = int(max(threads, min(wl.L, round(target_s * threads / max(one, 1e-3)))))
+    rows = np.unique(np.linspace(0, wl.L - 1, n_rows).round().astype(np.int64))
+    secs = run(rows, threads)
+    return {
+        "value": round(len(rows) / secs, 3),
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(rows)} of {wl.L} query rows evenly spaced over the chunk (full causal key "
+                  f"range each), fp64 C oracle: full-sort top-k + sparse attention; {secs:.1f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="C3", help="C0..C4 (default C3, the headline workload)")
+    ap.add_argument("--q-block", type=int, default=1024)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="do not bracket kernels with events (the roofline object is then omitted)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build is single-GPU; the path shards by query with no exchange "
+              "(see DESIGN.md) but multi-GPU runs are not part of it. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dsa_inputs as di
+    import dsa_sparse_attention_indexer_amd as dsa
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dsa.load_library()
+    wl = di.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    inp = di.make_inputs(wl)
+    log(f"[bench] {wl.name}: inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q_idx, k_idx, q, kv = bf(inp["q_idx"]), bf(inp["k_idx"]), bf(inp["q"]), bf(inp["kv"])
+    w = torch.from_numpy(inp["w"]).to(dev)
+    idx = torch.empty((wl.L, wl.top_k), dtype=torch.int32, device=dev)
+    out = torch.empty((wl.L, wl.H, 512), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(dsa.workspace_bytes(wl.L, wl.N, wl.top_k, args.q_block), dtype=torch.uint8, device=dev)
+    scale = float(np.float32(di.SOFTMAX_SCALE))
+
+    def step():
+        dsa.indexer_topk(q_idx, k_idx, w, wl.pos0, wl.top_k, q_block=args.q_block, out=idx, workspace=ws)
+        dsa.sparse_prefill(q, kv, idx, wl.pos0, scale, q_block=args.q_block, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    timing = not args.no_kernel_timing
+    if timing:
+        dsa.profile_enable(True)
+        for k in dsa.PROFILE_KERNELS:
+            dsa.profile_read(k)
+    torch.cuda.synchronize()  # barrier: one rank
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1000.0 / args.steps
+    kernels = {}
+    if timing:
+        for k in dsa.PROFILE_KERNELS:
+            ms, n = dsa.profile_read(k)
+            if n:
+                kernels[k] = {"launches_per_step": n / args.steps, "ms_per_launch": ms / n,
+                              "ms_per_step": ms / args.steps}
+        dsa.profile_enable(False)
+
+    value = wl.L / (ms_per_step / 1000.0)
+    sizes = workload_sizes(wl)
+    f_idx = sum(r[0] for r in sizes)
+    f_attn = sum(r[1] for r in sizes)
+    b_attn = sum(r[2] for r in sizes)
+    b_topk = 20 * wl.L * wl.top_k
+    t_roof_ms = (f_idx / (PEAK_BF16_TFLOPS * 1e12) + b_topk / (PEAK_HBM_GBS * 1e9)
+                 + max(f_attn / (PEAK_BF16_TFLOPS * 1e12), b_attn / (PEAK_HBM_GBS * 1e9))) * 1e3
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: N={wl.N} cached keys, L={wl.L} newest queries, top_k={wl.top_k}, "
+                        f"indexer 32x128 bf16 ({wl.indexer} keys), attention {wl.H} heads x 576/512 bf16, "
+                        f"q_block={args.q_block}",
+            "N": wl.N, "L": wl.L, "top_k": wl.top_k, "attn_heads": wl.H, "q_block": args.q_block,
+            "parallelism": "single GPU",
+        },
+        "step_roofline_frac": round(t_roof_ms / ms_per_step, 4),
+    }
+    if kernels:
+        per = {}
+        sf = kernels.get("score_filter")
+        at = kernels.get("sparse_attention")
+        if sf:
+            n = sf["launches_per_step"]
+            ach = f_idx / n / (sf["ms_per_launch"] * 1e-3) / 1e12
+            per["score_filter"] = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                                   "traffic": None, "ms_per_launch": round(sf["ms_per_launch"], 4)}
+        if at:
+            n = at["launches_per_step"]
+            ach = b_attn / n / (at["ms_per_launch"] * 1e-3) / 1e9
+            per["sparse_attention"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                                       "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                                       "traffic": None, "ms_per_launch": round(at["ms_per_launch"], 4)}
+        dom = max(per, key=lambda k: kernels[k]["ms_per_step"]) if per else None
+        if dom:
+            r = dict(per[dom])
+            r["kernel"] = dom
+            result["roofline"] = r
+        result["kernels"] = {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()}
+        result["kernel_rooflines"] = per
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        log(f"[bench] cpu baseline took {time.perf_counter() - t0:.1f} s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

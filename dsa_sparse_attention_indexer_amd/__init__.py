@@ -27,8 +27,10 @@ D_ROPE = 64
 DEFAULT_Q_BLOCK = 1024
 
 EXPORTED = ["dsa_indexer_topk_workspace_bytes", "dsa_indexer_topk", "dsa_causal_mask_topk",
-            "dsa_sparse_prefill", "dsa_sparse_prefill_gate", "dsa_status_string",
-            "dsa_last_error", "dsa_version"]
+            "dsa_sparse_prefill", "dsa_sparse_prefill_gate", "dsa_profile_enable",
+            "dsa_profile_read", "dsa_status_string", "dsa_last_error", "dsa_version"]
+PROFILE_KERNELS = ["key_stats", "score_sample", "row_prep", "score_filter", "select", "fold",
+                   "sparse_attention", "causal_mask"]
 
 _lib = None
 
@@ -65,6 +67,11 @@ def load_library(path: str | None = None):
     lib.dsa_last_error.argtypes = []
     lib.dsa_version.restype = ctypes.c_char_p
     lib.dsa_version.argtypes = []
+    lib.dsa_profile_enable.restype = ctypes.c_int
+    lib.dsa_profile_enable.argtypes = [ctypes.c_int]
+    lib.dsa_profile_read.restype = ctypes.c_int
+    lib.dsa_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int64)]
     _lib = lib
     return lib
 
@@ -99,6 +106,19 @@ def _req(t, name, dtype, ndim):
 
 def version() -> str:
     return load_library().dsa_version().decode()
+
+
+def profile_enable(on: bool = True):
+    """Bracket every library kernel launch with HIP events on its stream."""
+    _check(load_library().dsa_profile_enable(1 if on else 0))
+
+
+def profile_read(kernel: str):
+    """(total_ms, launches) of one kernel class since its last read; waits for its events."""
+    lib = load_library()
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(lib.dsa_profile_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def workspace_bytes(L: int, N: int, top_k: int, q_block: int = DEFAULT_Q_BLOCK) -> int:

@@ -53,7 +53,9 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     f32x4 o[kDv / 16];
 #pragma unroll
     for (int dt = 0; dt < kDv / 16; ++dt) o[dt] = f32x4{};
-    float m = -INFINITY, lsum = 0.f;
+    // lsum: sum of the bf16 weights actually multiplied into V (normalises the output);
+    // lexp: sum of the unrounded fp32 weights (gives the log-sum-exp).
+    float m = -INFINITY, lsum = 0.f, lexp = 0.f;
     const float sl2 = A.scale * 1.4426950408889634f;
     const int32_t* irow = A.idx + (size_t)t * A.top_k;
     const int n_tiles = (A.top_k + kAttnTile - 1) / kAttnTile;
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
         const float mnew = fmaxf(m, tmax);
         float alpha = 1.f;
         u16x8 pb;
-        float ps = 0.f;
+        float ps = 0.f, pe = 0.f;
         if (mnew == -INFINITY) {
 #pragma unroll
             for (int r = 0; r < 8; ++r) pb[r] = 0;
@@ -124,14 +126,19 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
             alpha = exp2f(m - mnew);
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const uint16_t b = float_to_bf16_rne(exp2f(lg[r] - mnew));
+                const float e = exp2f(lg[r] - mnew);
+                const uint16_t b = float_to_bf16_rne(e);
                 pb[r] = b;
-                ps += bf16_bits_to_float(b);  // normalise with the weights actually used
+                ps += bf16_bits_to_float(b);
+                pe += e;
             }
         }
         ps += __shfl_xor(ps, 16);
         ps += __shfl_xor(ps, 32);
+        pe += __shfl_xor(pe, 16);
+        pe += __shfl_xor(pe, 32);
         lsum = lsum * alpha + ps;
+        lexp = lexp * alpha + pe;
         m = mnew;
         const bf16x8 pbf = __builtin_bit_cast(bf16x8, pb);
 #pragma unroll
@@ -155,11 +162,12 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
         *reinterpret_cast<u16x4*>(orow + dt * 16) = pk;
     }
     if (A.lse && g == 0)
-        A.lse[(size_t)t * A.H + h] = lsum > 0.f ? (m + log2f(lsum)) * 0.6931471805599453f : -INFINITY;
+        A.lse[(size_t)t * A.H + h] = lexp > 0.f ? (m + log2f(lexp)) * 0.6931471805599453f : -INFINITY;
 }
 
 hipError_t launch_sparse_attention(const AttentionArgs& a, hipStream_t s) {
     const int threads = 64 * (a.H / 16);
+    ProfScope ps(s, kProfAttention);
     sparse_attn_kernel<<<a.Lb, threads, 0, s>>>(a);
     return hipGetLastError();
 }

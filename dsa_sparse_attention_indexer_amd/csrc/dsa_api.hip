@@ -6,8 +6,52 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+#include <vector>
+
 #include "../../include/dsa.h"
 #include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+std::atomic<bool> g_prof_on{false};
+std::mutex g_prof_mu;
+struct ProfRecord {
+    int kernel;
+    hipEvent_t start, stop;
+};
+std::vector<ProfRecord> g_prof;
+const char* const kProfNames[kProfCount] = {"key_stats", "score_sample", "row_prep", "score_filter",
+                                            "select", "fold", "sparse_attention", "causal_mask"};
+}  // namespace
+
+ProfScope::ProfScope(hipStream_t s, int k) : stream(s), kernel(k), start(nullptr), on(false) {
+    if (!g_prof_on.load(std::memory_order_relaxed)) return;
+    if (hipEventCreate(&start) != hipSuccess) return;
+    if (hipEventRecord(start, s) != hipSuccess) {
+        (void)hipEventDestroy(start);
+        return;
+    }
+    on = true;
+}
+
+ProfScope::~ProfScope() {
+    if (!on) return;
+    hipEvent_t stop;
+    if (hipEventCreate(&stop) != hipSuccess) {
+        (void)hipEventDestroy(start);
+        return;
+    }
+    if (hipEventRecord(stop, stream) != hipSuccess) {
+        (void)hipEventDestroy(start);
+        (void)hipEventDestroy(stop);
+        return;
+    }
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    g_prof.push_back({kernel, start, stop});
+}
+}  // namespace dsa
 
 namespace {
 
@@ -62,6 +106,42 @@ dsa_status_t check_indexer_args(const uint16_t* q_idx, const uint16_t* k_idx, co
 extern "C" {
 
 const char* dsa_version(void) { return "dsa-mi355x 0.1 (gfx950)"; }
+
+dsa_status_t dsa_profile_enable(int on) {
+    g_last_error[0] = 0;
+    dsa::g_prof_on.store(on != 0);
+    return DSA_OK;
+}
+
+dsa_status_t dsa_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
+    g_last_error[0] = 0;
+    if (!kernel || !total_ms || !launches) return fail(DSA_ERR_INVALID_ARG, "null argument");
+    int k = -1;
+    for (int i = 0; i < dsa::kProfCount; ++i)
+        if (strcmp(kernel, dsa::kProfNames[i]) == 0) k = i;
+    if (k < 0) return fail(DSA_ERR_INVALID_ARG, "unknown kernel class '%s'", kernel);
+    std::vector<dsa::ProfRecord> mine;
+    {
+        std::lock_guard<std::mutex> g(dsa::g_prof_mu);
+        std::vector<dsa::ProfRecord> rest;
+        for (auto& r : dsa::g_prof) (r.kernel == k ? mine : rest).push_back(r);
+        dsa::g_prof.swap(rest);
+    }
+    double sum = 0.0;
+    dsa_status_t st = DSA_OK;
+    for (auto& r : mine) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess && st == DSA_OK) st = hip_fail(e, "profile event");
+        sum += ms;
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    *total_ms = sum;
+    *launches = (int64_t)mine.size();
+    return st;
+}
 
 const char* dsa_last_error(void) { return g_last_error; }
 
@@ -149,7 +229,7 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
         a.Lb = (int)Lb;
         const int64_t last_pos = a.pos0 + Lb - 1;
         const int64_t n_last = (last_pos < N - 1 ? last_pos : N - 1) + 1;
-        const bool need_sample = n_last > lay.cap;
+        const bool need_sample = dsa::sample_size(n_last, top_k, lay.cap) > 0;
         e = dsa::launch_indexer_block(a, need_sample, s);
         if (e != hipSuccess) return hip_fail(e, "indexer launch");
     }

@@ -22,9 +22,11 @@ __host__ __device__ inline int cand_capacity(int top_k) {
     return (c + 1023) & ~1023;
 }
 
-// Keys scored in the threshold sample of a row group whose first row sees n_t keys.
+// Keys scored in the threshold sample of a 4-row group whose first row sees n_t keys.
+// Groups whose first row sees at most cap - 4 keys are not sampled: every row of such
+// a group sees at most cap keys, so all its causal keys fit the candidate buffer.
 __host__ __device__ inline int sample_size(int64_t n_t, int top_k, int cap) {
-    if (n_t <= cap) return 0;
+    if (n_t <= cap - 4) return 0;
     int64_t s = (int64_t)((n_t * 128 + (int64_t)(2.5 * top_k) - 1) / (int64_t)(2.5 * top_k));
     if (s < 1024) s = 1024;
     if (s > 16384) s = 16384;
@@ -108,6 +110,21 @@ struct IndexerArgs {
     int* fold_bi;           // [slots][fold_cap]
     double* fold_bs;        // [slots][fold_cap]
     float* fold_bf;         // [slots][fold_cap]
+};
+
+// Optional per-launch event timing (dsa_profile_enable).  A ProfScope records an
+// event before its launch and another after it on the same stream.
+enum ProfKernel : int {
+    kProfKeyStats = 0, kProfScoreSample, kProfRowPrep, kProfScoreFilter, kProfSelect, kProfFold,
+    kProfAttention, kProfCausalMask, kProfCount
+};
+struct ProfScope {
+    ProfScope(hipStream_t s, int kernel);
+    ~ProfScope();
+    hipStream_t stream;
+    int kernel;
+    hipEvent_t start;
+    bool on;
 };
 
 // Kernel launchers (indexer.hip).  Each returns the launch status.

@@ -350,8 +350,10 @@ __device__ bool select_core(const float* cs, const int* ci, int c, int k, float 
         const double sd = (double)s;
         if (sd > hi) {
             int o = atomicAdd(&S.sh[2], 1);
-            sel_i[o] = ci[i];
-            if (sel_s) sel_s[o] = s;
+            if (o < k) {  // at most k - 1 keys lie above kth + 2 delta
+                sel_i[o] = ci[i];
+                if (sel_s) sel_s[o] = s;
+            }
         } else if (sd >= lo) {
             int b = atomicAdd(&S.sh[3], 1);
             if (b < band_cap) {
@@ -399,12 +401,14 @@ __device__ bool select_core(const float* cs, const int* ci, int c, int k, float 
         }
         if (beat < need) {
             int o = atomicAdd(&S.sh[2], 1);
-            sel_i[o] = ix;
-            if (sel_s) sel_s[o] = band_f[x];
+            if (o < k) {
+                sel_i[o] = ix;
+                if (sel_s) sel_s[o] = band_f[x];
+            }
         }
     }
     __syncthreads();
-    return true;
+    return S.sh[2] == k;  // always true; guards the LDS writes above
 }
 
 // ------------------------------------------------------------------ 3. row prep
@@ -497,14 +501,14 @@ __global__ __launch_bounds__(256) void row_prep_kernel(IndexerArgs P) {
         P.mode[r] = kModeNormal;
     }
     __syncthreads();
-    if (nt <= P.cap) {
-        if (threadIdx.x == 0) P.tau[r] = -INFINITY;
-        return;
-    }
     const int g0 = r & ~(kRowsPerGroup - 1);
     const int64_t pg = P.pos0 + g0;
     const int64_t n0 = (pg < P.N - 1 ? pg : P.N - 1) + 1;
     const int S = sample_size(n0, P.top_k, P.cap);
+    if (S == 0) {  // the whole group keeps every causal key (at most cap per row)
+        if (threadIdx.x == 0) P.tau[r] = -INFINITY;
+        return;
+    }
     const int rk = sample_rank(n0, S, P.top_k);
     const float that = block_kth_largest(P.sample + (size_t)r * P.sample_stride, S, rk, s_hist, s_sh);
     if (threadIdx.x == 0) {
@@ -663,10 +667,10 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
             }
         }
         int32_t* out_row = P.out + (size_t)r * k;
-        // n >= k here (nt > k for every scored row); the list is the exact top-k.
-        for (int j = threadIdx.x; j < n; j += blockDim.x) s_sel[j] = Ri[cur][j];
+        // n == k here (nt > k for every scored row): the list is the exact top-k.
+        for (int j = threadIdx.x; j < k; j += blockDim.x) s_sel[j] = j < n ? Ri[cur][j] : -1;
         __syncthreads();
-        write_sorted_output(s_sel, n, out_row);
+        write_sorted_output(s_sel, k, out_row);
         __syncthreads();
     }
 }
@@ -685,6 +689,7 @@ __global__ void causal_mask_kernel(int32_t* idx, int64_t L, int top_k, int64_t q
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, hipStream_t s) {
+    ProfScope ps(s, kProfKeyStats);
     init_stats_kernel<<<1, 64, 0, s>>>(ks);
     int blocks = (int)((n_keys + 255) / 256);
     if (blocks > 2048) blocks = 2048;
@@ -695,11 +700,26 @@ hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks,
 
 hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s) {
     const int groups = (a.Lb + kRowsPerGroup - 1) / kRowsPerGroup;
-    if (need_sample) score_kernel<true><<<groups, kScoreThreads, 0, s>>>(a);
-    row_prep_kernel<<<a.Lb, 256, 0, s>>>(a);
-    score_kernel<false><<<groups, kScoreThreads, 0, s>>>(a);
-    select_kernel<<<a.Lb, kSelectThreads, 0, s>>>(a);
-    fold_kernel<<<kFallbackSlots, kSelectThreads, 0, s>>>(a);
+    if (need_sample) {
+        ProfScope ps(s, kProfScoreSample);
+        score_kernel<true><<<groups, kScoreThreads, 0, s>>>(a);
+    }
+    {
+        ProfScope ps(s, kProfRowPrep);
+        row_prep_kernel<<<a.Lb, 256, 0, s>>>(a);
+    }
+    {
+        ProfScope ps(s, kProfScoreFilter);
+        score_kernel<false><<<groups, kScoreThreads, 0, s>>>(a);
+    }
+    {
+        ProfScope ps(s, kProfSelect);
+        select_kernel<<<a.Lb, kSelectThreads, 0, s>>>(a);
+    }
+    {
+        ProfScope ps(s, kProfFold);
+        fold_kernel<<<kFallbackSlots, kSelectThreads, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
@@ -708,6 +728,7 @@ hipError_t launch_causal_mask(int32_t* idx, int64_t L, int top_k, int64_t q_pos0
     int blocks = (int)((total + 255) / 256);
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
+    ProfScope ps(s, kProfCausalMask);
     causal_mask_kernel<<<blocks, 256, 0, s>>>(idx, L, top_k, q_pos0);
     return hipGetLastError();
 }

@@ -145,6 +145,19 @@ dsa_status_t dsa_sparse_prefill(const uint16_t* q, const uint16_t* kv, int64_t k
  */
 int dsa_sparse_prefill_gate(int64_t B, int64_t L, int64_t N, int64_t min_context);
 
+/*
+ * Kernel timing diagnostics.  While enabled (on != 0), every kernel the library
+ * launches is bracketed by a pair of HIP events recorded on the caller's stream;
+ * the events add no synchronisation.  dsa_profile_read waits for the recorded
+ * events of one kernel class, returns the summed duration in milliseconds and
+ * the number of launches since the last read of that class, and forgets them.
+ * Kernel classes: "key_stats", "score_sample", "row_prep", "score_filter",
+ * "select", "fold", "sparse_attention", "causal_mask".  Unknown names give
+ * DSA_ERR_INVALID_ARG.  Host only; safe to call from one thread at a time.
+ */
+dsa_status_t dsa_profile_enable(int on);
+dsa_status_t dsa_profile_read(const char* kernel, double* total_ms, int64_t* launches);
+
 /* Static description of a status code. */
 const char* dsa_status_string(dsa_status_t s);
 
