@@ -24,11 +24,7 @@ constexpr int kKeyTile = 32;          // keys per MFMA tile (32x32x16 output col
 
 // Selector constants.
 constexpr int kSelectThreads = 512;
-constexpr int kBandMax = 4096;        // largest near-threshold band resolved in one pass
-constexpr int kFoldBlock = 4096;      // key block of the fallback fold
-constexpr int kSampleMax = 16384;     // largest score sample per row
-constexpr int kSampleRank = 128;      // target rank of the threshold inside the sample
-constexpr float kCandFactor = 2.5f;   // expected candidates per row = kCandFactor * top_k
+constexpr int kMaxTopK = 4096;        // largest top_k (DSA_MAX_TOPK)
 
 // Bound on |fp32 score - canonical fp64 score| in units of
 // 2^-24 * max_s ||k_s||_2 * sum_h |w_h| ||q_h||_2 (see the indexer source).

@@ -46,6 +46,7 @@ __host__ __device__ inline int sample_rank(int64_t n_t, int s, int top_k) {
 
 constexpr int kFallbackSlots = 32;
 constexpr int kFoldKeys = 4096;
+constexpr int kCandSegs = 4;  // candidate segments per row (one per scoring wave)
 
 struct IndexerLayout {
     int rows, cap, sample_stride, fold_cap;
@@ -66,7 +67,7 @@ struct IndexerLayout {
         l.off_tau = o; o = al(o + 4 * (size_t)l.rows);
         l.off_delta = o; o = al(o + 4 * (size_t)l.rows);
         l.off_mode = o; o = al(o + 4 * (size_t)l.rows);
-        l.off_count = o; o = al(o + 4 * (size_t)l.rows);
+        l.off_count = o; o = al(o + 4 * (size_t)l.rows * kCandSegs);
         l.off_fbctrl = o; o = al(o + 16);
         l.off_fblist = o; o = al(o + 4 * (size_t)l.rows);
         l.off_sample = o; o = al(o + 4 * (size_t)l.rows * (size_t)l.sample_stride);
@@ -99,7 +100,7 @@ struct IndexerArgs {
     float* tau;
     float* delta;
     int* mode;
-    int* count;
+    int* count;             // [Lb][kCandSegs] survivors per (row, scoring wave)
     int* fb_ctrl;           // [0] flagged rows, [1] next row to take
     int* fb_list;
     float* sample;

@@ -15,8 +15,8 @@
 //   4. score<filter>    bf16 MFMA scores of every causal key; keys with score >= tau_t
 //                       are written back as (score, key) candidates (only promising
 //                       candidates leave the chip)
-//   5. select           exact top-k of the candidates: radix select of the fp32 k-th
-//                       score, fp64 re-score of the keys within 2 delta of it, rank
+//   5. select           exact top-k of the candidates: value-binned selection of the fp32
+//                       k-th score, fp64 re-score of the keys within 2 delta of it, rank
 //                       count with the lower-index tie rule, ascending output
 //   6. fold (fallback)  rows whose candidate set could be incomplete or overflowed run
 //                       the pages' blocked fold: 4,096-key blocks merged into a running
@@ -39,6 +39,9 @@
 
 namespace dsa {
 
+constexpr int kSegs = kScoreThreads / kWave;  // candidate segments per row = score waves
+static_assert(kSegs == kCandSegs, "workspace layout assumes one candidate segment per scoring wave");
+
 // ------------------------------------------------------------------ helpers
 
 __device__ __forceinline__ int bf16_lsb_exp(uint16_t b) {
@@ -60,6 +63,10 @@ __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
 }
+__device__ __forceinline__ float wave_min(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+    return v;
+}
 __device__ __forceinline__ int wave_min_i(int v) {
     for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
     return v;
@@ -69,7 +76,21 @@ __device__ __forceinline__ int mbcnt64(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
-// Canonical fp64 term fl(w_h * max(0, sum_i q_h[i] k[i])) with i ascending.
+// Wave-aggregated append: lanes with pred get consecutive slots from *counter (one LDS
+// atomic per wave).  Returns the lane's slot, or -1.  Call with every lane of the wave
+// that reached this point.
+__device__ __forceinline__ int wave_append(bool pred, int* counter) {
+    const uint64_t m = __ballot(pred);
+    if (m == 0) return -1;
+    const int leader = __builtin_ctzll(m);
+    int base = 0;
+    if ((int)(threadIdx.x & 63) == leader) base = atomicAdd(counter, __builtin_popcountll(m));
+    base = __shfl(base, leader);
+    return pred ? base + mbcnt64(m) : -1;
+}
+
+// Canonical fp64 term fl(w_h * max(0, sum_i q_h[i] k[i])) with i ascending.  A product of
+// two bf16 values is exact in fp64, so fma(q, k, d) rounds exactly as d + fl(q*k) does.
 __device__ double canonical_head_term(const uint16_t* __restrict__ q_h,
                                       const uint16_t* __restrict__ k_row, float w_h) {
 #pragma clang fp contract(off)
@@ -77,13 +98,11 @@ __device__ double canonical_head_term(const uint16_t* __restrict__ q_h,
     const u16x8* qa = reinterpret_cast<const u16x8*>(q_h);
     const u16x8* ka = reinterpret_cast<const u16x8*>(k_row);
     for (int c = 0; c < kIdxDim / 8; ++c) {
-        u16x8 qv = qa[c], kv = ka[c];
-        for (int j = 0; j < 8; ++j) {
-            double prod = (double)bf16_bits_to_float(qv[j]) * (double)bf16_bits_to_float(kv[j]);
-            d = d + prod;
-        }
+        const u16x8 qv = qa[c], kv = ka[c];
+        for (int j = 0; j < 8; ++j)
+            d = __builtin_fma((double)bf16_bits_to_float(qv[j]), (double)bf16_bits_to_float(kv[j]), d);
     }
-    double r = d > 0.0 ? d : 0.0;
+    const double r = d > 0.0 ? d : 0.0;
     return (double)w_h * r;
 }
 
@@ -98,31 +117,46 @@ __global__ void init_stats_kernel(KeyStats* ks) {
     }
 }
 
+// 16 lanes per key row (16 bytes each, so a wave reads 4 whole rows per load).
 __global__ __launch_bounds__(256) void key_stats_kernel(const uint16_t* __restrict__ k_idx,
                                                         int64_t n_keys, KeyStats* ks) {
+    const int sub = threadIdx.x & 15;
     float nmax = 0.f, amax = 0.f;
     int emin = INT_MAX;
-    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < n_keys;
-         s += (int64_t)gridDim.x * blockDim.x) {
-        const u16x8* kr = reinterpret_cast<const u16x8*>(k_idx + s * kIdxDim);
+    const int64_t rows_per_step = (int64_t)gridDim.x * (blockDim.x >> 4);
+    for (int64_t s = (int64_t)blockIdx.x * (blockDim.x >> 4) + (threadIdx.x >> 4); s < n_keys;
+         s += rows_per_step) {
+        const u16x8 v = reinterpret_cast<const u16x8*>(k_idx + s * kIdxDim)[sub];
         float ss = 0.f;
-        for (int c = 0; c < kIdxDim / 8; ++c) {
-            u16x8 v = kr[c];
-            for (int j = 0; j < 8; ++j) {
-                float x = bf16_bits_to_float(v[j]);
-                ss = fmaf(x, x, ss);
-                amax = fmaxf(amax, fabsf(x));
-                if ((v[j] & 0x7fff) != 0) emin = min(emin, bf16_lsb_exp(v[j]));
-            }
+        for (int j = 0; j < 8; ++j) {
+            const float x = bf16_bits_to_float(v[j]);
+            ss = fmaf(x, x, ss);
+            amax = fmaxf(amax, fabsf(x));
+            if ((v[j] & 0x7fff) != 0) emin = min(emin, bf16_lsb_exp(v[j]));
         }
+        for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
         nmax = fmaxf(nmax, sqrtf(ss));
     }
     nmax = wave_max(nmax);
     amax = wave_max(amax);
     emin = wave_min_i(emin);
+    __shared__ float s_n[4], s_a[4];
+    __shared__ int s_e[4];
+    const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
+        s_n[w] = nmax;
+        s_a[w] = amax;
+        s_e[w] = emin;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int i = 1; i < (int)(blockDim.x >> 6); ++i) {
+            nmax = fmaxf(nmax, s_n[i]);
+            amax = fmaxf(amax, s_a[i]);
+            emin = min(emin, s_e[i]);
+        }
         // 128 fp32 squares+adds and the sqrt: relative error < 2^-16; pad by 2^-14.
-        float up = nmax * (1.0f + 1.0f / 16384.0f);
+        const float up = nmax * (1.0f + 1.0f / 16384.0f);
         atomicMax(&ks->knorm_bits, __float_as_uint(up));
         atomicMax(&ks->kinf_bits, __float_as_uint(amax));
         atomicMin(&ks->kexp_min, emin);
@@ -131,10 +165,99 @@ __global__ __launch_bounds__(256) void key_stats_kernel(const uint16_t* __restri
 
 // ------------------------------------------------------------------ 2/4. MFMA scoring
 
-// One workgroup = 4 consecutive query rows; each of its 4 waves takes every 4th
-// 32-key tile.  Lane l owns head (l & 31) of the A operand and key (l & 31) of the B
+// One workgroup = 4 consecutive query rows; its 4 waves split the 32-key tiles
+// round-robin, each wave scoring all 4 rows of a tile (a key tile is loaded once per
+// 4 rows).  Lane l owns head (l & 31) of the A operand and key (l & 31) of the B
 // operand; its half (l >> 5) holds dimensions [64*half, 64*half+64) split into eight
-// MFMA K-steps of 8, the same permutation on both operands.
+// MFMA K-steps of 8, the same permutation on both operands.  The key tile two steps
+// ahead is in flight while the MFMAs of the next tile run under the epilogue of the
+// current one.  Survivors go to a per-(row, wave) segment with a wave-uniform counter,
+// so candidate write-back needs no atomics.
+template <bool kSample>
+struct ScoreTile {
+    const IndexerArgs& P;
+    const bf16x8 (&a)[kRowsPerGroup][8];
+    const float (*s_w)[2][16];
+    const int64_t (&pr)[kRowsPerGroup];
+    const float (&tau_r)[kRowsPerGroup];
+    const int (&row_of)[kRowsPerGroup];
+    const bool (&live)[kRowsPerGroup];
+    int64_t n0;
+    int S;
+    int wave, lane, hf, col;
+    int seg;
+    int (&cnt)[kRowsPerGroup];
+
+    int64_t tile0;  // first tile of this wave's contiguous range
+
+    __device__ __forceinline__ int64_t tile_of(int it) const { return tile0 + it; }
+
+    __device__ __forceinline__ void load(bf16x8 (&b)[8], int it) const {
+        const int64_t pos = tile_of(it) * kKeyTile + col;
+        int64_t key;
+        if (kSample) key = pos < S ? (pos * n0) / S : 0;
+        else key = pos < P.N ? pos : P.N - 1;
+        const u16x8* kp = reinterpret_cast<const u16x8*>(P.k_idx + key * kIdxDim + hf * 64);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) b[kk] = __builtin_bit_cast(bf16x8, kp[kk]);
+    }
+
+    __device__ __forceinline__ void mfma(f32x16 (&acc)[kRowsPerGroup], const bf16x8 (&b)[8]) const {
+#pragma unroll
+        for (int j = 0; j < kRowsPerGroup; ++j) acc[j] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+            for (int j = 0; j < kRowsPerGroup; ++j) acc[j] = mfma_32x32x16(a[j][kk], b[kk], acc[j]);
+    }
+
+    __device__ __forceinline__ void epilogue(const f32x16 (&acc)[kRowsPerGroup], int it) {
+        const int64_t pos = tile_of(it) * kKeyTile + col;
+        float sc[kRowsPerGroup];
+#pragma unroll
+        for (int j = 0; j < kRowsPerGroup; ++j) {
+            const f32x4* wv = reinterpret_cast<const f32x4*>(&s_w[j][hf][0]);
+            float part = 0.f;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 w4 = wv[q4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)  // ReLU on the bit pattern: negatives and -0 -> +0
+                    part += w4[e] * __int_as_float(max(__float_as_int(acc[j][q4 * 4 + e]), 0));
+            }
+            auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+            sc[j] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + 0.0f;
+        }
+        if (kSample) {
+#pragma unroll
+            for (int j = 0; j < kRowsPerGroup; ++j)
+                if (hf == 0 && pos < S && live[j]) P.sample[(size_t)row_of[j] * P.sample_stride + pos] = sc[j];
+        } else {
+            bool keep[kRowsPerGroup];
+            uint64_t m[kRowsPerGroup];
+            uint64_t any = 0;
+#pragma unroll
+            for (int j = 0; j < kRowsPerGroup; ++j) {
+                keep[j] = live[j] && hf == 0 && pos <= pr[j] && sc[j] >= tau_r[j];
+                m[j] = __ballot(keep[j]);
+                any |= m[j];
+            }
+            if (any) {
+#pragma unroll
+                for (int j = 0; j < kRowsPerGroup; ++j) {
+                    const int o = cnt[j] + mbcnt64(m[j]);
+                    if (keep[j] && o < seg) {
+                        const size_t off = (size_t)row_of[j] * P.cap + (size_t)wave * seg + o;
+                        P.cand_s[off] = sc[j];
+                        P.cand_i[off] = (int)pos;
+                    }
+                    cnt[j] += __builtin_popcountll(m[j]);
+                }
+            }
+        }
+    }
+};
+
 template <bool kSample>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P) {
     const int g = blockIdx.x;
@@ -142,7 +265,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P) {
     const int lane = threadIdx.x & 63;
     const int hf = lane >> 5;
     const int col = lane & 31;
-    __shared__ int s_count[kRowsPerGroup];
+    __shared__ __attribute__((aligned(16))) float s_w[kRowsPerGroup][2][16];
 
     int64_t pr[kRowsPerGroup];
     float tau_r[kRowsPerGroup];
@@ -154,261 +277,425 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P) {
     int64_t n0 = 0;
 #pragma unroll
     for (int j = 0; j < kRowsPerGroup; ++j) {
-        int r = r0 + j;
-        bool valid = r < P.Lb;
+        const int r = r0 + j;
+        const bool valid = r < P.Lb;
         row_of[j] = valid ? r : r0;
-        int64_t p = P.pos0 + r;
+        const int64_t p = P.pos0 + r;
         pr[j] = valid ? p : -1;
-        int64_t nt = valid ? (p < P.N - 1 ? p : P.N - 1) + 1 : 0;
+        const int64_t nt = valid ? (p < P.N - 1 ? p : P.N - 1) + 1 : 0;
         if (kSample) {
             live[j] = valid;
             tau_r[j] = 0.f;
         } else {
-            bool use = valid && P.mode[r] == kModeNormal;
+            const bool use = valid && P.mode[r] == kModeNormal;
             live[j] = use;
             tau_r[j] = use ? P.tau[r] : INFINITY;
             if (use && nt > n_keys) n_keys = nt;
         }
     }
     if (kSample) {
-        int64_t p = P.pos0 + r0;
+        const int64_t p = P.pos0 + r0;
         n0 = (p < P.N - 1 ? p : P.N - 1) + 1;
         S = sample_size(n0, P.top_k, P.cap);
         n_keys = S;
     }
-    if (threadIdx.x < kRowsPerGroup) s_count[threadIdx.x] = 0;
+    if (threadIdx.x < kRowsPerGroup * 32) {
+        // Weights in the order each lane half reads them: head 8*(i/4) + 4*half + i%4.
+        const int j = threadIdx.x >> 5, h2 = (threadIdx.x >> 4) & 1, i = threadIdx.x & 15;
+        s_w[j][h2][i] = P.w[(size_t)row_of[j] * kIdxHeads + 8 * (i >> 2) + 4 * h2 + (i & 3)];
+    }
     __syncthreads();
 
+    int cnt[kRowsPerGroup] = {0, 0, 0, 0};
     if (n_keys > 0) {
         bf16x8 a[kRowsPerGroup][8];
-        float wf[kRowsPerGroup][16];
 #pragma unroll
         for (int j = 0; j < kRowsPerGroup; ++j) {
             const u16x8* qp = reinterpret_cast<const u16x8*>(
                 P.q_idx + ((size_t)row_of[j] * kIdxHeads + col) * kIdxDim + hf * 64);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) a[j][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                int h = 8 * (i >> 2) + 4 * hf + (i & 3);
-                wf[j][i] = P.w[(size_t)row_of[j] * kIdxHeads + h];
-            }
         }
+        // Wave w scores the contiguous tile range [w*tpw, (w+1)*tpw): its candidate segment
+        // is then in ascending key order and the segments concatenate in order.
         const int64_t n_tiles = (n_keys + kKeyTile - 1) / kKeyTile;
-        for (int64_t ti = wave; ti < n_tiles; ti += kScoreThreads / kWave) {
-            const int64_t pos = ti * kKeyTile + col;
-            int64_t key;
-            if (kSample) key = pos < S ? (pos * n0) / S : 0;
-            else key = pos < P.N ? pos : P.N - 1;
-            const u16x8* kp = reinterpret_cast<const u16x8*>(P.k_idx + key * kIdxDim + hf * 64);
-            bf16x8 b[8];
+        const int64_t tpw = (n_tiles + kSegs - 1) / kSegs;
+        const int64_t t0 = (int64_t)wave * tpw;
+        const int n_my = n_tiles > t0 ? (int)((n_tiles - t0) < tpw ? (n_tiles - t0) : tpw) : 0;
+        ScoreTile<kSample> T{P, a, s_w, pr, tau_r, row_of, live, n0, S, wave, lane, hf, col, P.cap / kSegs, cnt, t0};
+        bf16x8 b0[8], b1[8];
+        f32x16 acc0[kRowsPerGroup], acc1[kRowsPerGroup];
+        if (n_my > 0) T.load(b0, 0);
+        if (n_my > 1) T.load(b1, 1);
+        if (n_my > 0) T.mfma(acc0, b0);
+        int it = 0;
+        // Steady state: tiles it (in acc0), it+1 (b1 loaded), it+2, it+3 all exist.
+        for (; it + 3 < n_my; it += 2) {
+            T.load(b0, it + 2);
+            T.mfma(acc1, b1);
+            T.epilogue(acc0, it);
+            T.load(b1, it + 3);
+            T.mfma(acc0, b0);
+            T.epilogue(acc1, it + 1);
+        }
+        // Tail (fewer than four tiles left, acc0 holds tile it, b1 holds tile it+1).
+        for (; it < n_my; ++it) {
+            if (it + 1 < n_my) T.mfma(acc1, b1);
+            T.epilogue(acc0, it);
+            if (it + 1 < n_my) {
+                if (it + 2 < n_my) T.load(b1, it + 2);
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) b[kk] = __builtin_bit_cast(bf16x8, kp[kk]);
-            f32x16 acc[kRowsPerGroup];
-#pragma unroll
-            for (int j = 0; j < kRowsPerGroup; ++j) acc[j] = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-                for (int j = 0; j < kRowsPerGroup; ++j) acc[j] = mfma_32x32x16(a[j][kk], b[kk], acc[j]);
-#pragma unroll
-            for (int j = 0; j < kRowsPerGroup; ++j) {
-                float part = 0.f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) part += wf[j][i] * fmaxf(acc[j][i], 0.f);
-                auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
-                                                           false, false);
-                float s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                s = s + 0.0f;
-                if (kSample) {
-                    if (hf == 0 && pos < S && live[j]) P.sample[(size_t)row_of[j] * P.sample_stride + pos] = s;
-                } else {
-                    bool keep = live[j] && hf == 0 && pos <= pr[j] && s >= tau_r[j];
-                    uint64_t m = __ballot(keep);
-                    if (m) {
-                        int base = 0;
-                        if (lane == 0) base = atomicAdd(&s_count[j], __builtin_popcountll(m));
-                        base = __shfl(base, 0);
-                        if (keep) {
-                            int o = base + mbcnt64(m);
-                            if (o < P.cap) {
-                                size_t off = (size_t)row_of[j] * P.cap + o;
-                                P.cand_s[off] = s;
-                                P.cand_i[off] = (int)pos;
-                            }
-                        }
-                    }
-                }
+                for (int j = 0; j < kRowsPerGroup; ++j) acc0[j] = acc1[j];
             }
         }
     }
-    if (!kSample) {
-        __syncthreads();
-        if (threadIdx.x < kRowsPerGroup && r0 + (int)threadIdx.x < P.Lb)
-            P.count[r0 + threadIdx.x] = s_count[threadIdx.x];
+    if (!kSample && lane == 0) {
+#pragma unroll
+        for (int j = 0; j < kRowsPerGroup; ++j)
+            if (r0 + j < P.Lb) P.count[(size_t)(r0 + j) * kSegs + wave] = cnt[j];
     }
 }
 
-// ------------------------------------------------------------------ block-wide radix select
+// ------------------------------------------------------------------ block-wide selection
 
-// k-th largest (1-based) of v[0..n) under the float order (-0 == +0); 1 <= k <= n.
-// All threads of the block must call it.  hist: 256 ints of LDS, sh: 4 ints of LDS.
-__device__ float block_kth_largest(const float* v, int n, int k, int* hist, int* sh) {
-    uint32_t prefix = 0, pmask = 0;
-    int remaining = k;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
-        __syncthreads();
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
-            uint32_t key = float_order_key(v[i]);
-            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
-        }
-        __syncthreads();
-        if (threadIdx.x < 64) {
-            const int l = threadIdx.x;
-            int c[4], lsum = 0;
-            for (int j = 0; j < 4; ++j) {
-                c[j] = hist[255 - 4 * l - j];
-                lsum += c[j];
-            }
-            int incl = lsum;
-            for (int o = 1; o < 64; o <<= 1) {
-                int t = __shfl_up(incl, o);
-                if (l >= o) incl += t;
-            }
-            int excl = incl - lsum;
-            if (excl < remaining && remaining <= incl) {
-                int acc = excl;
-                for (int j = 0; j < 4; ++j) {
-                    if (acc + c[j] >= remaining) {
-                        sh[0] = 255 - 4 * l - j;
-                        sh[1] = acc;
-                        break;
-                    }
-                    acc += c[j];
-                }
-            }
-        }
-        __syncthreads();
-        const int d = sh[0];
-        remaining -= sh[1];
-        prefix |= (uint32_t)d << shift;
-        pmask |= 255u << shift;
-        __syncthreads();
-    }
-    return order_key_float(prefix);
-}
-
-// Bitonic sort (ascending) of n = power of two ints in LDS.
-__device__ void block_bitonic_sort(int* a, int n) {
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < (n >> 1); i += blockDim.x) {
-                int lo = 2 * i - (i & (stride - 1));
-                int hi = lo + stride;
-                bool asc = (lo & size) == 0;
-                int x = a[lo], y = a[hi];
-                if ((x > y) == asc) {
-                    a[lo] = y;
-                    a[hi] = x;
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-struct SelectScratch {
-    int hist[256];
-    int sh[8];
-    double term[32][kIdxHeads];  // fp64 re-score staging: 32 keys x 32 heads
+// Up to kSegs (score, key) lists, read as one.
+struct CandList {
+    const float* s[kSegs];
+    const int* i[kSegs];
+    int n[kSegs];
+    int nseg;
 };
 
-// Exact top-k of a candidate list (cs, ci, c) under (canonical score desc, key asc).
-// Writes the k selected keys (unordered) to sel_i and, if sel_s is not null, their
-// fp32 scores to sel_s.  band_i / band_s / band_f: caller storage for up to band_cap
-// near-threshold entries (key, canonical score, fp32 score).
-// Returns false (uniformly) when the candidate set cannot be proven complete
-// (k-th fp32 score within 2 delta of the filter threshold) or the band overflows.
-__device__ bool select_core(const float* cs, const int* ci, int c, int k, float delta,
-                            float tau_f, const uint16_t* __restrict__ q_row,
-                            const float* __restrict__ w_row, const uint16_t* __restrict__ k_idx,
-                            int* band_i, double* band_s, float* band_f, int band_cap, int* sel_i,
-                            float* sel_s, SelectScratch& S) {
-    const float kth = block_kth_largest(cs, c, k, S.hist, S.sh);
-    const double lo = (double)kth - 2.0 * (double)delta;
-    const double hi = (double)kth + 2.0 * (double)delta;
-    if (tau_f != -INFINITY && lo < (double)tau_f) return false;
-    if (threadIdx.x == 0) {
-        S.sh[2] = 0;  // selected count
-        S.sh[3] = 0;  // band count
+constexpr int kBins = 2048;
+constexpr int kDirect = 512;
+constexpr int kRescoreKeys = 16;  // band keys re-scored per pass (x 32 heads = 512 items)
+
+// One row's selection scratch.  The phases use the union in turn: binned k-th search
+// (sel), fp64 re-score staging (rs), then the selected keys (out, fold path only).
+struct SelectScratch {
+    union {
+        struct {
+            int hist[kBins];
+            float direct[kDirect];
+        } sel;
+        struct {
+            uint16_t q[kIdxHeads * kIdxDim];      // the query row's indexer q (8 KB)
+            uint16_t k[kRescoreKeys][kIdxDim];    // band key rows of this pass (4 KB)
+        } rs;
+        int out[kMaxTopK];
+    };
+    double term[kRescoreKeys][kIdxHeads];
+    float red_f[32];
+    int red_i[32];
+    int sh[16];
+};
+
+__device__ __forceinline__ void block_minmax(float& mn, float& mx, SelectScratch& S) {
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) {
+        S.red_f[w] = mn;
+        S.red_f[16 + w] = mx;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < c; i += blockDim.x) {
-        const float s = cs[i];
-        const double sd = (double)s;
-        if (sd > hi) {
-            int o = atomicAdd(&S.sh[2], 1);
-            if (o < k) {  // at most k - 1 keys lie above kth + 2 delta
-                sel_i[o] = ci[i];
-                if (sel_s) sel_s[o] = s;
-            }
-        } else if (sd >= lo) {
-            int b = atomicAdd(&S.sh[3], 1);
-            if (b < band_cap) {
-                band_i[b] = ci[i];
-                band_s[b] = sd;
-                band_f[b] = s;
+    mn = S.red_f[0];
+    mx = S.red_f[16];
+    for (int i = 1; i < nw; ++i) {
+        mn = fminf(mn, S.red_f[i]);
+        mx = fmaxf(mx, S.red_f[16 + i]);
+    }
+    __syncthreads();
+}
+
+// Inclusive scan of one int per thread in thread order (block of at most 16 waves).
+__device__ __forceinline__ int block_incl_scan(int v, SelectScratch& S) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(x, o);
+        if (lane >= o) x += t;
+    }
+    __syncthreads();
+    if (lane == 63) S.red_i[w] = x;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < w; ++i) base += S.red_i[i];
+    __syncthreads();
+    return x + base;
+}
+
+__device__ __forceinline__ int bin_of(float s, float vmin, double scale) {
+    const double d = ((double)s - (double)vmin) * scale;
+    const int b = (int)d;
+    return b < kBins - 1 ? b : kBins - 1;
+}
+
+// Values owned by this thread: a block-strided walk over a CandList ...
+struct ListSrc {
+    const CandList& L;
+    template <class F>
+    __device__ __forceinline__ void for_each(F&& f) const {
+#pragma unroll
+        for (int g = 0; g < kSegs; ++g)
+            if (g < L.nseg)
+                for (int i = threadIdx.x; i < L.n[g]; i += blockDim.x) f(L.s[g][i] + 0.0f);
+    }
+};
+// ... or this thread's register-resident chunk.
+template <int CH>
+struct RegSrc {
+    const float (&v)[CH];
+    int nv;
+    template <class F>
+    __device__ __forceinline__ void for_each(F&& f) const {
+#pragma unroll
+        for (int e = 0; e < CH; ++e)
+            if (e < nv) f(v[e]);
+    }
+};
+
+// k-th largest value (1-based) under the float order (-0 == +0), by value-linear binning
+// (LiteTopK's bins: cheap even when every score shares an exponent) refined up to three
+// times, then a rank count over the crossing bin.  Requires 1 <= k <= total.  Returns
+// false (uniformly) if a bin still holds more than kDirect distinct values after that.
+template <class Src>
+__device__ bool block_kth_binned(const Src& src, int k, float* out, SelectScratch& S) {
+    constexpr int kLevels = 3;
+    float vmin = INFINITY, vmax = -INFINITY;
+    src.for_each([&](float v) {
+        vmin = fminf(vmin, v);
+        vmax = fmaxf(vmax, v);
+    });
+    block_minmax(vmin, vmax, S);
+    float lv_min[kLevels];
+    double lv_scale[kLevels];
+    int lv_bin[kLevels];
+    int nlv = 0, above = 0;
+    auto active = [&](float v) {
+        bool in = true;
+#pragma unroll
+        for (int l = 0; l < kLevels; ++l)
+            if (l < nlv) in = in && bin_of(v, lv_min[l], lv_scale[l]) == lv_bin[l];
+        return in;
+    };
+    for (;;) {
+        if (vmin == vmax) {
+            *out = vmin;
+            return true;
+        }
+        const double scale = (double)kBins / ((double)vmax - (double)vmin);
+        for (int i = threadIdx.x; i < kBins; i += blockDim.x) S.sel.hist[i] = 0;
+        __syncthreads();
+        src.for_each([&](float v) {
+            if (active(v)) atomicAdd(&S.sel.hist[bin_of(v, vmin, scale)], 1);
+        });
+        __syncthreads();
+        // Descending bin order: thread t owns bins kBins-1-t*per down to kBins-per-t*per.
+        const int per = kBins / blockDim.x;
+        int c = 0;
+        for (int j = 0; j < per; ++j) c += S.sel.hist[kBins - 1 - threadIdx.x * per - j];
+        const int incl = block_incl_scan(c, S) + above;
+        const int excl = incl - c;
+        if (threadIdx.x == 0) S.sh[0] = -1;
+        __syncthreads();
+        if (excl < k && k <= incl) {
+            int acc = excl;
+            for (int j = 0; j < per; ++j) {
+                const int b = kBins - 1 - threadIdx.x * per - j;
+                if (acc + S.sel.hist[b] >= k) {
+                    S.sh[0] = b;
+                    S.sh[1] = acc;
+                    S.sh[2] = S.sel.hist[b];
+                    break;
+                }
+                acc += S.sel.hist[b];
             }
         }
+        __syncthreads();
+        const int b = S.sh[0];
+        above = S.sh[1];
+        const int nb = S.sh[2];
+        __syncthreads();
+        if (b < 0) return false;  // unreachable for 1 <= k <= total
+#pragma unroll
+        for (int l = 0; l < kLevels; ++l)
+            if (l == nlv) {
+                lv_min[l] = vmin;
+                lv_scale[l] = scale;
+                lv_bin[l] = b;
+            }
+        ++nlv;
+        if (nb <= kDirect) {
+            if (threadIdx.x == 0) S.sh[3] = 0;
+            __syncthreads();
+            src.for_each([&](float v) {
+                const int o = wave_append(active(v), &S.sh[3]);
+                if (o >= 0 && o < kDirect) S.sel.direct[o] = v;
+            });
+            __syncthreads();
+            const int n = S.sh[3] < kDirect ? S.sh[3] : kDirect;
+            const int r = k - above;  // rank inside the bin, 1-based
+            for (int x = threadIdx.x; x < n; x += blockDim.x) {
+                const float vx = S.sel.direct[x];
+                int gt = 0, ge = 0;
+                for (int y = 0; y < n; ++y) {
+                    const float vy = S.sel.direct[y];
+                    gt += vy > vx;
+                    ge += vy >= vx;
+                }
+                if (gt < r && r <= ge) S.red_f[31] = vx;  // every writer holds the same value
+            }
+            __syncthreads();
+            *out = S.red_f[31];
+            __syncthreads();
+            return true;
+        }
+        if (nlv == kLevels) return false;
+        vmin = INFINITY;
+        vmax = -INFINITY;
+        src.for_each([&](float v) {
+            if (active(v)) {
+                vmin = fminf(vmin, v);
+                vmax = fmaxf(vmax, v);
+            }
+        });
+        block_minmax(vmin, vmax, S);
     }
-    __syncthreads();
-    const int n_in = S.sh[2];
-    const int nb = S.sh[3];
-    if (nb > band_cap) return false;
-    const int need = k - n_in;
-    if (delta > 0.f) {
-        // Re-score the band in the canonical fp64 order: 32 keys x 32 heads per pass.
-        for (int b0 = 0; b0 < nb; b0 += 32) {
-            for (int it = threadIdx.x; it < 32 * kIdxHeads; it += blockDim.x) {
-                const int bl = it >> 5, h = it & 31;
-                if (b0 + bl < nb) {
-                    const int key = band_i[b0 + bl];
-                    S.term[bl][h] = canonical_head_term(q_row + h * kIdxDim,
-                                                        k_idx + (size_t)key * kIdxDim, w_row[h]);
+}
+
+// Bitonic sort (ascending) of n = power of two ints in LDS.  Wave w owns the pairs
+// [w*pw, (w+1)*pw); stages whose stride is at most pw stay inside that wave's chunk and
+// need no block barrier (LDS accesses of one wave complete in order).
+__device__ void block_bitonic_sort(int* a, int n) {
+    const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int pairs = n >> 1;
+    int pw = 1;
+    while (pw * nw < pairs) pw <<= 1;
+    for (int size = 2; size <= n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int j = lane; j < pw; j += 64) {
+                const int i = w * pw + j;
+                if (i < pairs) {
+                    const int lo = 2 * i - (i & (stride - 1));
+                    const int hi = lo + stride;
+                    const bool asc = (lo & size) == 0;
+                    const int x = a[lo], y = a[hi];
+                    if ((x > y) == asc) {
+                        a[lo] = y;
+                        a[hi] = x;
+                    }
                 }
             }
-            __syncthreads();
-            if (threadIdx.x < 32 && b0 + (int)threadIdx.x < nb) {
-#pragma clang fp contract(off)
-                double s = 0.0;
-                for (int h = 0; h < kIdxHeads; ++h) s = s + S.term[threadIdx.x][h];
-                if (s == 0.0) s = 0.0;
-                band_s[b0 + threadIdx.x] = s;
-            }
-            __syncthreads();
+            const int next = stride > 1 ? stride >> 1 : size;  // stride of the following stage
+            if (stride > pw || (next > pw && size < n) || (stride == 1 && size == n)) __syncthreads();
+            else __builtin_amdgcn_wave_barrier();
         }
     }
-    // Rank count: a band key is selected iff fewer than `need` band keys beat it.
-    for (int x = threadIdx.x; x < nb; x += blockDim.x) {
-        const double sx = band_s[x];
-        const int ix = band_i[x];
-        int beat = 0;
-        for (int y = 0; y < nb && beat < need; ++y) {
-            const double sy = band_s[y];
-            beat += (sy > sx) || (sy == sx && band_i[y] < ix);
+}
+
+// fp64 canonical scores of band entries [0, nb) (keys in band_key), in place into band_s.
+__device__ void band_rescore(int nb, const int* band_key, double* band_s, const uint16_t* __restrict__ q_row,
+                             const float* __restrict__ w_row, const uint16_t* __restrict__ k_idx,
+                             SelectScratch& S) {
+    // The query row and each pass's key rows are staged in LDS so the 128-step fp64
+    // chains never wait on global memory.
+    for (int i = threadIdx.x; i < kIdxHeads * kIdxDim / 8; i += blockDim.x)
+        reinterpret_cast<u16x8*>(S.rs.q)[i] = reinterpret_cast<const u16x8*>(q_row)[i];
+    for (int b0 = 0; b0 < nb; b0 += kRescoreKeys) {
+        for (int i = threadIdx.x; i < kRescoreKeys * kIdxDim / 8; i += blockDim.x) {
+            const int bl = i / (kIdxDim / 8), c = i % (kIdxDim / 8);
+            const int key = b0 + bl < nb ? band_key[b0 + bl] : band_key[b0];
+            reinterpret_cast<u16x8*>(S.rs.k[bl])[c] = reinterpret_cast<const u16x8*>(k_idx + (size_t)key * kIdxDim)[c];
         }
-        if (beat < need) {
-            int o = atomicAdd(&S.sh[2], 1);
-            if (o < k) {
-                sel_i[o] = ix;
-                if (sel_s) sel_s[o] = band_f[x];
+        __syncthreads();
+        for (int it = threadIdx.x; it < kRescoreKeys * kIdxHeads; it += blockDim.x) {
+            const int bl = it >> 5, h = it & 31;
+            if (b0 + bl < nb) S.term[bl][h] = canonical_head_term(S.rs.q + h * kIdxDim, S.rs.k[bl], w_row[h]);
+        }
+        __syncthreads();
+        if (threadIdx.x < kRescoreKeys && b0 + (int)threadIdx.x < nb) {
+#pragma clang fp contract(off)
+            double sum = 0.0;
+            for (int h = 0; h < kIdxHeads; ++h) sum = sum + S.term[threadIdx.x][h];
+            if (sum == 0.0) sum = 0.0;
+            band_s[b0 + threadIdx.x] = sum;
+        }
+        __syncthreads();
+    }
+}
+
+// Is band entry x among the `need` best of the band under (score desc, key asc)?
+__device__ __forceinline__ bool band_wins(int x, int nb, int need, const int* band_key, const double* band_s) {
+    const double sx = band_s[x];
+    const int ix = band_key[x];
+    int beat = 0;
+#pragma unroll 4
+    for (int y = 0; y < nb; ++y) {
+        const double sy = band_s[y];
+        beat += (sy > sx) || (sy == sx && band_key[y] < ix);
+    }
+    return beat < need;
+}
+
+// Exact top-k of an unordered candidate list under (canonical score desc, key asc), used
+// by the blocked fold.  Writes the k selected keys (unordered) to sel_i and their fp32
+// scores to sel_s.  band_i / band_s / band_f: storage for up to band_cap near-threshold
+// entries.  Returns false (uniformly) if a buffer would overflow.
+__device__ bool select_core(const CandList& L, int k, float delta, const uint16_t* __restrict__ q_row,
+                            const float* __restrict__ w_row, const uint16_t* __restrict__ k_idx, int* band_i,
+                            double* band_s, float* band_f, int band_cap, int* sel_i, float* sel_s,
+                            SelectScratch& S) {
+    float kth;
+    if (!block_kth_binned(ListSrc{L}, k, &kth, S)) return false;
+    const double lo = (double)kth - 2.0 * (double)delta;
+    const double hi = (double)kth + 2.0 * (double)delta;
+    if (threadIdx.x == 0) {
+        S.sh[4] = 0;  // keys above the band
+        S.sh[5] = 0;  // band size
+        S.sh[6] = 0;  // selected keys written
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < kSegs; ++g)
+        if (g < L.nseg)
+            for (int i = threadIdx.x; i < L.n[g]; i += blockDim.x) {
+                const float sv = L.s[g][i] + 0.0f;
+                const double sd = (double)sv;
+                const int o = wave_append(sd > hi, &S.sh[4]);
+                if (o >= 0 && o < k) {
+                    sel_i[o] = L.i[g][i];
+                    sel_s[o] = sv;
+                }
+                const int b = wave_append(sd <= hi && sd >= lo, &S.sh[5]);
+                if (b >= 0 && b < band_cap) {
+                    band_i[b] = L.i[g][i];
+                    band_s[b] = sd;
+                    band_f[b] = sv;
+                }
             }
+    __syncthreads();
+    const int n_in = S.sh[4];
+    const int nb = S.sh[5];
+    __syncthreads();
+    if (nb > band_cap || n_in >= k || n_in + nb < k) return false;
+    if (delta > 0.f && nb > 0) band_rescore(nb, band_i, band_s, q_row, w_row, k_idx, S);
+    if (threadIdx.x == 0) S.sh[6] = n_in;
+    __syncthreads();
+    for (int x0 = 0; x0 < nb; x0 += blockDim.x) {
+        const int x = x0 + threadIdx.x;
+        const bool win = x < nb && band_wins(x, nb, k - n_in, band_i, band_s);
+        const int o = wave_append(win, &S.sh[6]);
+        if (o >= 0 && o < k) {
+            sel_i[o] = band_i[x];
+            sel_s[o] = band_f[x];
         }
     }
     __syncthreads();
-    return S.sh[2] == k;  // always true; guards the LDS writes above
+    const bool ok = S.sh[6] == k;  // always true; guards the writes above
+    __syncthreads();
+    return ok;
 }
 
 // ------------------------------------------------------------------ 3. row prep
@@ -420,8 +707,7 @@ __global__ __launch_bounds__(256) void row_prep_kernel(IndexerArgs P) {
     __shared__ double s_l1[kIdxHeads], s_l2[kIdxHeads];
     __shared__ int s_eq[kIdxHeads];
     __shared__ float s_delta;
-    __shared__ int s_hist[256];
-    __shared__ int s_sh[8];
+    __shared__ SelectScratch S;
     if (r == 0 && threadIdx.x == 0) {
         P.fb_ctrl[0] = 0;
         P.fb_ctrl[1] = 0;
@@ -441,9 +727,9 @@ __global__ __launch_bounds__(256) void row_prep_kernel(IndexerArgs P) {
         double l1 = 0.0, l2 = 0.0;
         int em = INT_MAX;
         for (int c = 0; c < 2; ++c) {
-            u16x8 v = qp[c];
+            const u16x8 v = qp[c];
             for (int j = 0; j < 8; ++j) {
-                double x = (double)bf16_bits_to_float(v[j]);
+                const double x = (double)bf16_bits_to_float(v[j]);
                 l1 += fabs(x);
                 l2 += x * x;
                 if ((v[j] & 0x7fff) != 0) em = min(em, bf16_lsb_exp(v[j]));
@@ -467,7 +753,7 @@ __global__ __launch_bounds__(256) void row_prep_kernel(IndexerArgs P) {
         const double kinf = (double)__uint_as_float(ks.kinf_bits);
         const float* wr = P.w + (size_t)r * kIdxHeads;
         // Exactness: every product and partial sum of the fp32 evaluation is a multiple
-        // of 2^emin and below 2^(24+emin) in magnitude -> fp32 scores are exact.
+        // of 2^e and below 2^(24+e) in magnitude -> fp32 scores are exact.
         double lhs = 0.0, dsum = 0.0;
         int emin = INT_MAX;
         bool any = false;
@@ -492,7 +778,7 @@ __global__ __launch_bounds__(256) void row_prep_kernel(IndexerArgs P) {
         }
         float d = 0.f;
         if (!exact) {
-            double dd = kDeltaCoef * ldexp(1.0, -24) * knorm * dsum;
+            const double dd = kDeltaCoef * ldexp(1.0, -24) * knorm * dsum;
             d = (float)(dd * (1.0 + 1.0 / 1048576.0));
             if (!(d > 0.f)) d = FLT_MIN;
         }
@@ -504,17 +790,25 @@ __global__ __launch_bounds__(256) void row_prep_kernel(IndexerArgs P) {
     const int g0 = r & ~(kRowsPerGroup - 1);
     const int64_t pg = P.pos0 + g0;
     const int64_t n0 = (pg < P.N - 1 ? pg : P.N - 1) + 1;
-    const int S = sample_size(n0, P.top_k, P.cap);
-    if (S == 0) {  // the whole group keeps every causal key (at most cap per row)
+    const int Sn = sample_size(n0, P.top_k, P.cap);
+    if (Sn == 0) {  // the whole group keeps every causal key (at most cap per row)
         if (threadIdx.x == 0) P.tau[r] = -INFINITY;
         return;
     }
-    const int rk = sample_rank(n0, S, P.top_k);
-    const float that = block_kth_largest(P.sample + (size_t)r * P.sample_stride, S, rk, s_hist, s_sh);
+    const int rk = sample_rank(n0, Sn, P.top_k);
+    CandList L{};
+    L.s[0] = P.sample + (size_t)r * P.sample_stride;
+    L.n[0] = Sn;
+    L.nseg = 1;
+    float that = 0.f;
+    const bool ok = block_kth_binned(ListSrc{L}, rk, &that, S);
     if (threadIdx.x == 0) {
-        double t = (double)that - 2.0 * (double)s_delta;
-        float tf = (float)t;
-        if ((double)tf > t) tf = nextafterf(tf, -INFINITY);
+        float tf = -INFINITY;  // an unresolved sample keeps every key (and falls back later)
+        if (ok) {
+            const double t = (double)that - 2.0 * (double)s_delta;
+            tf = (float)t;
+            if ((double)tf > t) tf = nextafterf(tf, -INFINITY);
+        }
         P.tau[r] = tf;
     }
 }
@@ -530,44 +824,135 @@ __device__ void write_sorted_output(int* sel, int k, int32_t* out_row) {
     for (int i = threadIdx.x; i < k; i += blockDim.x) out_row[i] = sel[i];
 }
 
-constexpr int kSelBand = 2048;
+constexpr int kSelBand = 1024;
+constexpr int kSelChunk = 16;  // candidates per thread: the block has cap / 16 threads
 
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(IndexerArgs P) {
+// Exact top-k of one row's candidates.  The four segments written by the scoring waves
+// are each in ascending key order and cover ascending key ranges, so their concatenation
+// is sorted by key: thread t holds positions [16t, 16t+16) of it in registers, and the
+// ascending output is a stable compaction (one block scan) of the selected positions.
+__global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
     const int r = blockIdx.x;
     const int64_t p = P.pos0 + r;
     const int64_t nt = (p < P.N - 1 ? p : P.N - 1) + 1;
-    int32_t* out_row = P.out + (size_t)r * P.top_k;
+    const int k = P.top_k;
+    int32_t* out_row = P.out + (size_t)r * k;
     if (P.mode[r] == kModeAll) {
-        for (int j = threadIdx.x; j < P.top_k; j += blockDim.x) out_row[j] = j < nt ? j : -1;
+        for (int j = threadIdx.x; j < k; j += blockDim.x) out_row[j] = j < nt ? j : -1;
         return;
     }
     __shared__ SelectScratch S;
-    __shared__ int s_band_i[kSelBand];
+    __shared__ int s_band_key[kSelBand];
+    __shared__ int s_band_pos[kSelBand];
     __shared__ double s_band_s[kSelBand];
-    __shared__ float s_band_f[kSelBand];
-    __shared__ int s_sel[4096];
-    const int c = P.count[r];
-    bool ok = !P.force_fallback && c <= P.cap && c >= P.top_k;
+    __shared__ uint32_t s_win[kSelChunk * 1024 / 32];
+    const int seg = P.cap / kSegs;
+    int cnt[kSegs], start[kSegs];
+    int total = 0;
+    bool ok = !P.force_fallback;
+#pragma unroll
+    for (int w = 0; w < kSegs; ++w) {
+        cnt[w] = P.count[(size_t)r * kSegs + w];
+        ok = ok && cnt[w] <= seg;
+        start[w] = total;
+        total += cnt[w];
+    }
+    ok = ok && total >= k;
+    const float tau_f = P.tau[r];
+    const float delta = P.delta[r];
+    float v[kSelChunk];
+    int key[kSelChunk];
+    int nv = 0;
+    const int base = threadIdx.x * kSelChunk;
     if (ok) {
-        ok = select_core(P.cand_s + (size_t)r * P.cap, P.cand_i + (size_t)r * P.cap, c, P.top_k,
-                         P.delta[r], P.tau[r], P.q_idx + (size_t)r * kIdxHeads * kIdxDim,
-                         P.w + (size_t)r * kIdxHeads, P.k_idx, s_band_i, s_band_s, s_band_f,
-                         kSelBand, s_sel, nullptr, S);
-    }
-    if (!ok) {
-        if (threadIdx.x == 0) {
-            int slot = atomicAdd(&P.fb_ctrl[0], 1);
-            P.fb_list[slot] = r;
+#pragma unroll
+        for (int e = 0; e < kSelChunk; ++e) {
+            const int j = base + e;
+            v[e] = -INFINITY;
+            key[e] = 0;
+            if (j < total) {
+                int w = 0, s0 = 0;
+#pragma unroll
+                for (int x = 1; x < kSegs; ++x)
+                    if (j >= start[x]) {
+                        w = x;
+                        s0 = start[x];
+                    }
+                const size_t off = (size_t)r * P.cap + (size_t)w * seg + (j - s0);
+                v[e] = P.cand_s[off] + 0.0f;
+                key[e] = P.cand_i[off];
+            }
         }
-        return;
+        nv = total > base ? (total - base < kSelChunk ? total - base : kSelChunk) : 0;
     }
-    write_sorted_output(s_sel, P.top_k, out_row);
+    float kth = 0.f;
+    if (ok) ok = block_kth_binned(RegSrc<kSelChunk>{v, nv}, k, &kth, S);
+    const double lo = (double)kth - 2.0 * (double)delta;
+    const double hi = (double)kth + 2.0 * (double)delta;
+    if (ok && tau_f != -INFINITY && lo < (double)tau_f) ok = false;  // candidate set not provably complete
+    if (ok) {
+        if (threadIdx.x == 0) {
+            S.sh[4] = 0;
+            S.sh[5] = 0;
+        }
+        for (int i = threadIdx.x; i < kSelChunk * 1024 / 32; i += blockDim.x) s_win[i] = 0u;
+        __syncthreads();
+        int n_above = 0;
+#pragma unroll
+        for (int e = 0; e < kSelChunk; ++e) {
+            const double sd = (double)v[e];
+            n_above += e < nv && sd > hi;
+            const bool in_band = e < nv && sd <= hi && sd >= lo;
+            const int b = wave_append(in_band, &S.sh[5]);
+            if (b >= 0 && b < kSelBand) {
+                s_band_key[b] = key[e];
+                s_band_pos[b] = base + e;
+                s_band_s[b] = sd;
+            }
+        }
+        for (int o = 32; o > 0; o >>= 1) n_above += __shfl_xor(n_above, o);
+        if ((threadIdx.x & 63) == 0) atomicAdd(&S.sh[4], n_above);
+        __syncthreads();
+        const int n_in = S.sh[4];
+        const int nb = S.sh[5];
+        __syncthreads();
+        ok = nb <= kSelBand && n_in < k && n_in + nb >= k;
+        if (ok) {
+            if (delta > 0.f && nb > 0)
+                band_rescore(nb, s_band_key, s_band_s, P.q_idx + (size_t)r * kIdxHeads * kIdxDim,
+                             P.w + (size_t)r * kIdxHeads, P.k_idx, S);
+            for (int x = threadIdx.x; x < nb; x += blockDim.x)
+                if (band_wins(x, nb, k - n_in, s_band_key, s_band_s))
+                    atomicOr(&s_win[s_band_pos[x] >> 5], 1u << (s_band_pos[x] & 31));
+            __syncthreads();
+            // Stable compaction: selected = above the band, or a band winner.
+            int c = 0;
+#pragma unroll
+            for (int e = 0; e < kSelChunk; ++e) {
+                const int j = base + e;
+                c += e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u));
+            }
+            int o = block_incl_scan(c, S) - c;
+#pragma unroll
+            for (int e = 0; e < kSelChunk; ++e) {
+                const int j = base + e;
+                if (e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u))) {
+                    if (o < k) out_row[o] = key[e];
+                    ++o;
+                }
+            }
+        }
+    }
+    if (!ok && threadIdx.x == 0) {
+        const int slot = atomicAdd(&P.fb_ctrl[0], 1);
+        P.fb_list[slot] = r;
+    }
 }
 
 // ------------------------------------------------------------------ 6. fallback fold
 
-// Scores keys [k0, k1) of one row with MFMA (8 waves, one 32-key tile per wave per step)
-// and appends those with score > lo to (dst_s, dst_i) at *cnt (LDS counter).
+// Scores keys [k0, k1) of one row with MFMA (one 32-key tile per wave per step) and
+// appends those with score > lo to (dst_s, dst_i) at *cnt (LDS counter).
 __device__ void fold_score_block(const IndexerArgs& P, int r, int64_t k0, int64_t k1, float lo,
                                  float* dst_s, int* dst_i, int* cnt, int cap) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -595,14 +980,14 @@ __device__ void fold_score_block(const IndexerArgs& P, int r, int64_t k0, int64_
         float s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         s = s + 0.0f;
         // Later keys lose ties, so only a score strictly above kth - 2 delta can enter.
-        bool keep = hf == 0 && pos < k1 && s > lo;
-        uint64_t m = __ballot(keep);
+        const bool keep = hf == 0 && pos < k1 && s > lo;
+        const uint64_t m = __ballot(keep);
         if (m) {
             int base = 0;
             if (lane == 0) base = atomicAdd(cnt, __builtin_popcountll(m));
             base = __shfl(base, 0);
             if (keep) {
-                int o = base + mbcnt64(m);
+                const int o = base + mbcnt64(m);
                 if (o < cap) {
                     dst_s[o] = s;
                     dst_i[o] = (int)pos;
@@ -618,7 +1003,6 @@ __device__ void fold_score_block(const IndexerArgs& P, int r, int64_t k0, int64_
 __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
     __shared__ SelectScratch S;
     __shared__ int s_row, s_cnt;
-    __shared__ int s_sel[4096];
     const int slot = blockIdx.x;
     float* Rs[2] = {P.fold_s + (size_t)slot * 2 * P.fold_cap, P.fold_s + (size_t)slot * 2 * P.fold_cap + P.fold_cap};
     int* Ri[2] = {P.fold_i + (size_t)slot * 2 * P.fold_cap, P.fold_i + (size_t)slot * 2 * P.fold_cap + P.fold_cap};
@@ -628,7 +1012,7 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
     const int k = P.top_k;
     for (;;) {
         if (threadIdx.x == 0) {
-            int i = atomicAdd(&P.fb_ctrl[1], 1);
+            const int i = atomicAdd(&P.fb_ctrl[1], 1);
             s_row = i < P.fb_ctrl[0] ? P.fb_list[i] : -1;
         }
         __syncthreads();
@@ -648,19 +1032,30 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
             __syncthreads();
             fold_score_block(P, r, b0, b1, lo, Rs[cur], Ri[cur], &s_cnt, P.fold_cap);
             __syncthreads();
-            n = s_cnt;
+            n = s_cnt < P.fold_cap ? s_cnt : P.fold_cap;
             __syncthreads();
             if (n > k) {
                 // Keep exactly the top-k of the list; their fp32 scores go to the other buffer.
                 const int nxt = cur ^ 1;
-                bool ok = select_core(Rs[cur], Ri[cur], n, k, delta, -INFINITY, q_row, w_row, P.k_idx,
-                                      band_i, band_s, band_f, P.fold_cap, Ri[nxt], Rs[nxt], S);
-                (void)ok;  // band capacity == list capacity: cannot overflow
+                CandList L{};
+                L.s[0] = Rs[cur];
+                L.i[0] = Ri[cur];
+                L.n[0] = n;
+                L.nseg = 1;
+                const bool ok = select_core(L, k, delta, q_row, w_row, P.k_idx, band_i, band_s, band_f,
+                                            P.fold_cap, Ri[nxt], Rs[nxt], S);
+                (void)ok;  // band capacity == list capacity
                 __syncthreads();
                 cur = nxt;
                 n = k;
-                const float kth = block_kth_largest(Rs[cur], n, k, S.hist, S.sh);
-                double l = (double)kth - 2.0 * (double)delta;
+                CandList R{};
+                R.s[0] = Rs[cur];
+                R.i[0] = Ri[cur];
+                R.n[0] = n;
+                R.nseg = 1;
+                float kth = -INFINITY;
+                block_kth_binned(ListSrc{R}, k, &kth, S);
+                const double l = (double)kth - 2.0 * (double)delta;
                 float lf = (float)l;
                 if ((double)lf > l) lf = nextafterf(lf, -INFINITY);
                 lo = lf;
@@ -668,9 +1063,9 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
         }
         int32_t* out_row = P.out + (size_t)r * k;
         // n == k here (nt > k for every scored row): the list is the exact top-k.
-        for (int j = threadIdx.x; j < k; j += blockDim.x) s_sel[j] = j < n ? Ri[cur][j] : -1;
+        for (int j = threadIdx.x; j < k; j += blockDim.x) S.out[j] = j < n ? Ri[cur][j] : -1;
         __syncthreads();
-        write_sorted_output(s_sel, k, out_row);
+        write_sorted_output(S.out, k, out_row);
         __syncthreads();
     }
 }
@@ -691,8 +1086,8 @@ __global__ void causal_mask_kernel(int32_t* idx, int64_t L, int top_k, int64_t q
 hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, hipStream_t s) {
     ProfScope ps(s, kProfKeyStats);
     init_stats_kernel<<<1, 64, 0, s>>>(ks);
-    int blocks = (int)((n_keys + 255) / 256);
-    if (blocks > 2048) blocks = 2048;
+    int blocks = (int)((n_keys + 15) / 16);
+    if (blocks > 1024) blocks = 1024;
     if (blocks < 1) blocks = 1;
     key_stats_kernel<<<blocks, 256, 0, s>>>(k_idx, n_keys, ks);
     return hipGetLastError();
@@ -714,7 +1109,7 @@ hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStrea
     }
     {
         ProfScope ps(s, kProfSelect);
-        select_kernel<<<a.Lb, kSelectThreads, 0, s>>>(a);
+        select_kernel<<<a.Lb, a.cap / kSelChunk, 0, s>>>(a);
     }
     {
         ProfScope ps(s, kProfFold);
