@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="do not bracket kernels with events (the roofline object is then omitted)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise copy of MIB MiB (read MIB, write MIB) three "
+                         "times, to scale the FETCH_SIZE / WRITE_SIZE counters, and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -112,9 +115,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
+        return
     dsa.load_library()
     wl = di.CONFIGS[args.config]
-    dev = torch.device("cuda:0")
     t0 = time.perf_counter()
     inp = di.make_inputs(wl)
     log(f"[bench] {wl.name}: inputs generated in {time.perf_counter() - t0:.1f} s")

@@ -35,9 +35,16 @@ def hipcc() -> str:
     return p
 
 
+# Per-source extras.  The indexer's scoring loop keeps its MFMA accumulators in VGPRs,
+# where the ReLU/weight epilogue reads them without AGPR-to-VGPR copies.
+SOURCE_FLAGS = {
+    "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, obj_dir: Path) -> Path:
     obj = obj_dir / (Path(src).stem + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", "-c", str(CSRC / src), "-o", str(obj)]
+    cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), f"-I{INCLUDE}", "-c", str(CSRC / src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

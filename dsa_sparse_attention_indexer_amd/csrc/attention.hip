@@ -5,17 +5,24 @@
 // query gathers only its top-k rows; every head shares that gathered block; the
 // latent is also the value, so the output is 512 wide per head.
 //
-// One workgroup per query, one wave per 16 heads.  Per 32-key tile:
-//   gather   the 32 selected rows into LDS twice: row-major (keys x 576) for the
-//            logits and transposed (512 x keys) for the value product; the
-//            [top_k x 576] block never exists in HBM
+// One workgroup per query, one wave per 16 heads (at least 4 waves: the extra waves of
+// a small head count only gather).  Per 32-key tile:
+//   gather   the 32 selected rows (row-major, 1152 bytes each) into one of two LDS
+//            buffers by DMA (global_load_lds, 16 bytes per lane, consecutive lanes on
+//            consecutive pieces of a row).  The next tile's rows and the keys of the
+//            tile after it are requested before the current tile is computed, so the
+//            gather latency hides behind the MFMAs without staging registers; the
+//            [top_k x 576] block never exists in HBM.  The compiler does not track LDS
+//            DMA, so each wave waits on vmcnt itself before the tile barrier
 //   logits   S^T[key][head] = K . Q^T on 16x16x32 bf16 MFMA (M = keys, N = heads,
-//            18 K-steps over 576); Q stays in VGPRs for the whole row
+//            18 K-steps over 576); Q stays in registers for the whole row
 //   softmax  online, fp32, base-2 with log2(e) folded into the scale; invalid keys
 //            (-1, > position, padding) contribute nothing
-//   values   O^T[d][head] += V^T . P^T on 16x16x32 MFMA: the logits' output layout
-//            is already the B operand (lane = head, 8 keys per lane) once the K order
-//            of the product is permuted to match, so P never leaves registers
+//   values   O^T[d][head] += V^T . P^T on 16x16x32 MFMA.  V^T comes straight from the
+//            row-major tile through the LDS transpose read (ds_read_b64_tr_b16), and the
+//            logits' output layout is already the B operand (lane = head, 8 keys per
+//            lane) once the K order of the product is permuted to match, so P never
+//            leaves registers
 #include <math.h>
 
 #include "dsa_common.h"
@@ -26,8 +33,21 @@ namespace dsa {
 constexpr int kAttnTile = 32;
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
+constexpr int kRowChunks = kDqk * 2 / 16;             // 72 16-byte pieces per key row
+constexpr int kTileChunks = kAttnTile * kRowChunks;   // 2304
 constexpr int kKrowStride = kDqk + 8;   // 1168 B: conflict-free 16-lane column reads
-constexpr int kVtStride = kAttnTile + 4;  // 72 B
+constexpr int kAttnMinThreads = 256;
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+// Four bf16 of column block [d0, d0+4) from four consecutive tile rows, transposed
+// across each 16-lane group (lane i receives column d0 + i of rows r..r+3 when source
+// lane s addresses row r + s/4, columns 4*(s%4)..+4).
+__device__ __forceinline__ u16x4 lds_read_tr(const uint16_t* p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(u16x4, v);
+}
 
 __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     const int t = blockIdx.x;
@@ -36,122 +56,137 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     const int g = lane >> 4;
     const int c16 = lane & 15;
     const int nthreads = blockDim.x;
-    const int h = wave * 16 + c16;
     const int64_t p = A.pos0 + t;
+    const bool compute = wave < A.H / 16;
+    const int h = wave * 16 + c16;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Krow[kAttnTile][kKrowStride];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[kDv][kVtStride];
-    __shared__ int s_key[kAttnTile];
+    __shared__ __attribute__((aligned(16))) uint16_t Kbuf[2][kAttnTile][kKrowStride];
+    __shared__ int s_idx[3][kAttnTile];  // raw top-k entries of three consecutive tiles
+
+    const int32_t* irow = A.idx + (size_t)t * A.top_k;
+    const int n_tiles = (A.top_k + kAttnTile - 1) / kAttnTile;
+    const int nwaves = nthreads >> 6;
+    // Entry j of the row as a key this query may use, or -1.
+    auto key_of = [&](int slot, int r, int tile_j) -> int {
+        const int key = s_idx[slot][r];
+        return (tile_j + r < A.top_k && key >= 0 && key <= p && key < A.N) ? key : -1;
+    };
+    // DMA of the raw entries of tile j into slot (lanes past top_k fetch nothing).
+    auto fetch_idx = [&](int j, int slot) {
+        if (wave == 0 && lane < kAttnTile && j * kAttnTile + lane < A.top_k)
+            __builtin_amdgcn_global_load_lds(irow + j * kAttnTile + lane, &s_idx[slot][0], 4, 0, 0);
+    };
+    // DMA of the rows of tile j (entries in slot) into buffer buf: wave w takes rows
+    // w, w + nwaves, ...; a row is 72 pieces, one 64-lane request and one of 8 lanes.
+    auto fetch_rows = [&](int j, int slot, int buf) {
+        for (int r = wave; r < kAttnTile; r += nwaves) {
+            int key = __builtin_amdgcn_readfirstlane(key_of(slot, r, j * kAttnTile));
+            key = key < 0 ? 0 : key;  // masked later; any valid row will do
+            const char* src = reinterpret_cast<const char*>(A.kv + (size_t)key * A.kv_stride);
+            char* dst = reinterpret_cast<char*>(&Kbuf[buf][r][0]);
+            __builtin_amdgcn_global_load_lds(src + lane * 16, dst, 16, 0, 0);
+            if (lane < kRowChunks - 64)
+                __builtin_amdgcn_global_load_lds(src + 1024 + lane * 16, dst + 1024, 16, 0, 0);
+        }
+    };
+    // This wave's DMAs have landed; the barrier then publishes every wave's.
+    auto dma_wait = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+    fetch_idx(0, 0);
+    fetch_idx(1, 1);
+    dma_wait();
+    __syncthreads();
+    fetch_rows(0, 0, 0);
+    dma_wait();
 
     bf16x8 qf[kDqk / 32];
-    {
+    f32x4 o[kDv / 16];
+    if (compute) {
         const uint16_t* qrow = A.q + ((size_t)t * A.H + h) * kDqk + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < kDqk / 32; ++ks)
             qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qrow + ks * 32));
-    }
-    f32x4 o[kDv / 16];
 #pragma unroll
-    for (int dt = 0; dt < kDv / 16; ++dt) o[dt] = f32x4{};
+        for (int dt = 0; dt < kDv / 16; ++dt) o[dt] = f32x4{};
+    }
     // lsum: sum of the bf16 weights actually multiplied into V (normalises the output);
     // lexp: sum of the unrounded fp32 weights (gives the log-sum-exp).
     float m = -INFINITY, lsum = 0.f, lexp = 0.f;
     const float sl2 = A.scale * 1.4426950408889634f;
-    const int32_t* irow = A.idx + (size_t)t * A.top_k;
-    const int n_tiles = (A.top_k + kAttnTile - 1) / kAttnTile;
+    __syncthreads();
 
     for (int tile = 0; tile < n_tiles; ++tile) {
-        __syncthreads();
-        if (threadIdx.x < kAttnTile) {
-            const int j = tile * kAttnTile + threadIdx.x;
-            const int key = j < A.top_k ? irow[j] : -1;
-            s_key[threadIdx.x] = (key >= 0 && key <= p && key < A.N) ? key : -1;
-        }
-        __syncthreads();
-        // Latent columns: 4 keys x 8 columns per item -> row-major and transposed copies.
-        for (int it = threadIdx.x; it < (kAttnTile / 4) * (kDv / 8); it += nthreads) {
-            const int kq = it >> 6, c = it & 63;
-            u16x8 v[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                int key = s_key[kq * 4 + x];
-                key = key < 0 ? 0 : key;
-                v[x] = *reinterpret_cast<const u16x8*>(A.kv + (size_t)key * A.kv_stride + c * 8);
-            }
-#pragma unroll
-            for (int x = 0; x < 4; ++x) *reinterpret_cast<u16x8*>(&Krow[kq * 4 + x][c * 8]) = v[x];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                u16x4 pk = {v[0][e], v[1][e], v[2][e], v[3][e]};
-                *reinterpret_cast<u16x4*>(&Vt[c * 8 + e][kq * 4]) = pk;
-            }
-        }
-        // Rope columns: row-major only.
-        for (int it = threadIdx.x; it < kAttnTile * ((kDqk - kDv) / 8); it += nthreads) {
-            const int j = it >> 3, c = kDv / 8 + (it & 7);
-            int key = s_key[j];
-            key = key < 0 ? 0 : key;
-            *reinterpret_cast<u16x8*>(&Krow[j][c * 8]) =
-                *reinterpret_cast<const u16x8*>(A.kv + (size_t)key * A.kv_stride + c * 8);
-        }
-        __syncthreads();
+        const int cur = tile & 1;
+        const int slot = tile % 3;
+        // Rows of the next tile and the entries of the tile after it are in flight while
+        // this one is computed.
+        if (tile + 1 < n_tiles) fetch_rows(tile + 1, (tile + 1) % 3, cur ^ 1);
+        if (tile + 2 < n_tiles) fetch_idx(tile + 2, (tile + 2) % 3);
 
-        f32x4 s0 = f32x4{}, s1 = f32x4{};
+        if (compute) {
+            f32x4 s0 = f32x4{}, s1 = f32x4{};
 #pragma unroll
-        for (int ks = 0; ks < kDqk / 32; ++ks) {
-            const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&Krow[c16][ks * 32 + 8 * g]));
-            const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&Krow[16 + c16][ks * 32 + 8 * g]));
-            s0 = mfma_16x16x32(a0, qf[ks], s0);
-            s1 = mfma_16x16x32(a1, qf[ks], s1);
-        }
-        float lg[8];
-        float tmax = -INFINITY;
+            for (int ks = 0; ks < kDqk / 32; ++ks) {
+                const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&Kbuf[cur][c16][ks * 32 + 8 * g]));
+                const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&Kbuf[cur][16 + c16][ks * 32 + 8 * g]));
+                s0 = mfma_16x16x32(a0, qf[ks], s0);
+                s1 = mfma_16x16x32(a1, qf[ks], s1);
+            }
+            float lg[8];
+            float tmax = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            lg[r] = s_key[4 * g + r] >= 0 ? s0[r] * sl2 : -INFINITY;
-            lg[4 + r] = s_key[16 + 4 * g + r] >= 0 ? s1[r] * sl2 : -INFINITY;
-        }
+            for (int r = 0; r < 4; ++r) {
+                lg[r] = key_of(slot, 4 * g + r, tile * kAttnTile) >= 0 ? s0[r] * sl2 : -INFINITY;
+                lg[4 + r] = key_of(slot, 16 + 4 * g + r, tile * kAttnTile) >= 0 ? s1[r] * sl2 : -INFINITY;
+            }
 #pragma unroll
-        for (int r = 0; r < 8; ++r) tmax = fmaxf(tmax, lg[r]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mnew = fmaxf(m, tmax);
-        float alpha = 1.f;
-        u16x8 pb;
-        float ps = 0.f, pe = 0.f;
-        if (mnew == -INFINITY) {
+            for (int r = 0; r < 8; ++r) tmax = fmaxf(tmax, lg[r]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float mnew = fmaxf(m, tmax);
+            float alpha = 1.f;
+            u16x8 pb;
+            float ps = 0.f, pe = 0.f;
+            if (mnew == -INFINITY) {
 #pragma unroll
-            for (int r = 0; r < 8; ++r) pb[r] = 0;
-        } else {
-            alpha = exp2f(m - mnew);
+                for (int r = 0; r < 8; ++r) pb[r] = 0;
+            } else {
+                alpha = exp2f(m - mnew);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const float e = exp2f(lg[r] - mnew);
-                const uint16_t b = float_to_bf16_rne(e);
-                pb[r] = b;
-                ps += bf16_bits_to_float(b);
-                pe += e;
+                for (int r = 0; r < 8; ++r) {
+                    const float e = exp2f(lg[r] - mnew);
+                    const uint16_t b = float_to_bf16_rne(e);
+                    pb[r] = b;
+                    ps += bf16_bits_to_float(b);
+                    pe += e;
+                }
+            }
+            ps += __shfl_xor(ps, 16);
+            ps += __shfl_xor(ps, 32);
+            pe += __shfl_xor(pe, 16);
+            pe += __shfl_xor(pe, 32);
+            lsum = lsum * alpha + ps;
+            lexp = lexp * alpha + pe;
+            m = mnew;
+            const bf16x8 pbf = __builtin_bit_cast(bf16x8, pb);
+            // Source lane (g, c16) addresses row kb + c16/4, columns 4*(c16%4)..+4 of each
+            // 16-column block, kb = 4g (K slots 0-3 of its group) or 16 + 4g (slots 4-7).
+            const uint16_t* vlo = &Kbuf[cur][4 * g + (c16 >> 2)][4 * (c16 & 3)];
+            const uint16_t* vhi = vlo + 16 * kKrowStride;
+#pragma unroll
+            for (int dt = 0; dt < kDv / 16; ++dt) {
+                const u16x4 lo = lds_read_tr(vlo + dt * 16);
+                const u16x4 hi = lds_read_tr(vhi + dt * 16);
+                const u16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[dt] *= alpha;
+                o[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, av), pbf, o[dt]);
             }
         }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        pe += __shfl_xor(pe, 16);
-        pe += __shfl_xor(pe, 32);
-        lsum = lsum * alpha + ps;
-        lexp = lexp * alpha + pe;
-        m = mnew;
-        const bf16x8 pbf = __builtin_bit_cast(bf16x8, pb);
-#pragma unroll
-        for (int dt = 0; dt < kDv / 16; ++dt) {
-            const uint16_t* vp = &Vt[dt * 16 + c16][0];
-            const u16x4 lo = *reinterpret_cast<const u16x4*>(vp + 4 * g);
-            const u16x4 hi = *reinterpret_cast<const u16x4*>(vp + 16 + 4 * g);
-            const u16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            o[dt] *= alpha;
-            o[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, av), pbf, o[dt]);
-        }
+        dma_wait();
+        __syncthreads();
     }
 
+    if (!compute) return;
     const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
     uint16_t* orow = A.out + ((size_t)t * A.H + h) * kDv + 4 * g;
 #pragma unroll
@@ -166,7 +201,8 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
 }
 
 hipError_t launch_sparse_attention(const AttentionArgs& a, hipStream_t s) {
-    const int threads = 64 * (a.H / 16);
+    int threads = 64 * (a.H / 16);
+    if (threads < kAttnMinThreads) threads = kAttnMinThreads;
     ProfScope ps(s, kProfAttention);
     sparse_attn_kernel<<<a.Lb, threads, 0, s>>>(a);
     return hipGetLastError();

@@ -206,8 +206,7 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
     a.fb_ctrl = reinterpret_cast<int*>(ws + lay.off_fbctrl);
     a.fb_list = reinterpret_cast<int*>(ws + lay.off_fblist);
     a.sample = reinterpret_cast<float*>(ws + lay.off_sample);
-    a.cand_s = reinterpret_cast<float*>(ws + lay.off_cand_s);
-    a.cand_i = reinterpret_cast<int*>(ws + lay.off_cand_i);
+    a.cand = reinterpret_cast<uint2*>(ws + lay.off_cand);
     a.fold_s = reinterpret_cast<float*>(ws + lay.off_fold_s);
     a.fold_i = reinterpret_cast<int*>(ws + lay.off_fold_i);
     a.fold_bi = reinterpret_cast<int*>(ws + lay.off_fold_bi);

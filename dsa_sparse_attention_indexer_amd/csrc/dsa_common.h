@@ -18,7 +18,6 @@ constexpr int kWave = 64;
 // Indexer constants.
 constexpr int kIdxHeads = 32;
 constexpr int kIdxDim = 128;
-constexpr int kRowsPerGroup = 4;      // indexer query rows per workgroup
 constexpr int kScoreThreads = 256;    // 4 waves
 constexpr int kKeyTile = 32;          // keys per MFMA tile (32x32x16 output columns)
 

@@ -22,11 +22,13 @@ __host__ __device__ inline int cand_capacity(int top_k) {
     return (c + 1023) & ~1023;
 }
 
-// Keys scored in the threshold sample of a 4-row group whose first row sees n_t keys.
-// Groups whose first row sees at most cap - 4 keys are not sampled: every row of such
-// a group sees at most cap keys, so all its causal keys fit the candidate buffer.
+constexpr int kRowsPerGroup = 4;  // indexer query rows scored together (one sample each)
+
+// Keys scored in the threshold sample of a row group whose first row sees n_t keys.
+// Groups whose first row sees at most cap - kRowsPerGroup keys are not sampled: every row
+// of such a group sees at most cap keys, so all its causal keys fit the candidate buffer.
 __host__ __device__ inline int sample_size(int64_t n_t, int top_k, int cap) {
-    if (n_t <= cap - 4) return 0;
+    if (n_t <= cap - kRowsPerGroup) return 0;
     int64_t s = (int64_t)((n_t * 128 + (int64_t)(2.5 * top_k) - 1) / (int64_t)(2.5 * top_k));
     if (s < 1024) s = 1024;
     if (s > 16384) s = 16384;
@@ -51,14 +53,14 @@ constexpr int kCandSegs = 4;  // candidate segments per row (one per scoring wav
 struct IndexerLayout {
     int rows, cap, sample_stride, fold_cap;
     size_t off_kstats, off_tau, off_delta, off_mode, off_count, off_fbctrl, off_fblist;
-    size_t off_sample, off_cand_s, off_cand_i;
+    size_t off_sample, off_cand;
     size_t off_fold_s, off_fold_i, off_fold_bi, off_fold_bs, off_fold_bf;
     size_t total;
 
     static IndexerLayout make(int64_t rows, int64_t N, int top_k) {
         IndexerLayout l{};
         auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-        l.rows = (int)((rows + 3) & ~3LL);
+        l.rows = (int)((rows + kRowsPerGroup - 1) & ~(int64_t)(kRowsPerGroup - 1));
         l.cap = cand_capacity(top_k);
         l.sample_stride = sample_size(N, top_k, l.cap);
         l.fold_cap = top_k + kFoldKeys;
@@ -71,8 +73,7 @@ struct IndexerLayout {
         l.off_fbctrl = o; o = al(o + 16);
         l.off_fblist = o; o = al(o + 4 * (size_t)l.rows);
         l.off_sample = o; o = al(o + 4 * (size_t)l.rows * (size_t)l.sample_stride);
-        l.off_cand_s = o; o = al(o + 4 * (size_t)l.rows * (size_t)l.cap);
-        l.off_cand_i = o; o = al(o + 4 * (size_t)l.rows * (size_t)l.cap);
+        l.off_cand = o; o = al(o + 8 * (size_t)l.rows * (size_t)l.cap);
         l.off_fold_s = o; o = al(o + 4 * (size_t)kFallbackSlots * 2 * l.fold_cap);
         l.off_fold_i = o; o = al(o + 4 * (size_t)kFallbackSlots * 2 * l.fold_cap);
         l.off_fold_bi = o; o = al(o + 4 * (size_t)kFallbackSlots * l.fold_cap);
@@ -104,8 +105,7 @@ struct IndexerArgs {
     int* fb_ctrl;           // [0] flagged rows, [1] next row to take
     int* fb_list;
     float* sample;
-    float* cand_s;
-    int* cand_i;
+    uint2* cand;            // [Lb][cap] (fp32 score bits, key) in kCandSegs segments
     float* fold_s;          // [slots][2][fold_cap]
     int* fold_i;            // [slots][2][fold_cap]
     int* fold_bi;           // [slots][fold_cap]

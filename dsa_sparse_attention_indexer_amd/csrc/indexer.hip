@@ -165,57 +165,81 @@ __global__ __launch_bounds__(256) void key_stats_kernel(const uint16_t* __restri
 
 // ------------------------------------------------------------------ 2/4. MFMA scoring
 
-// One workgroup = 4 consecutive query rows; its 4 waves split the 32-key tiles
-// round-robin, each wave scoring all 4 rows of a tile (a key tile is loaded once per
-// 4 rows).  Lane l owns head (l & 31) of the A operand and key (l & 31) of the B
-// operand; its half (l >> 5) holds dimensions [64*half, 64*half+64) split into eight
-// MFMA K-steps of 8, the same permutation on both operands.  The key tile two steps
-// ahead is in flight while the MFMAs of the next tile run under the epilogue of the
-// current one.  Survivors go to a per-(row, wave) segment with a wave-uniform counter,
-// so candidate write-back needs no atomics.
+// One workgroup = 4 consecutive query rows; each of its 4 waves scores all 4 rows over
+// its own contiguous quarter of the causal key tiles (a key tile is loaded once per 4
+// rows, and no wave waits for another).  Lane l owns head (l & 31) of the A operand and
+// key (l & 31) of the B operand; its half (l >> 5) holds dimensions [64*half, 64*half+64)
+// of both, eight MFMA K-steps of 8.  Key tiles are loaded straight into the B layout into
+// three register buffers, so two tiles are in flight while one is consumed.  The query fragments sit in AGPRs, read by the MFMAs directly, which leaves
+// the VGPRs to the accumulators, the key tiles and the head weights.
+//
+// A wave's rows run as two pairs: the MFMA chains of one pair execute under the epilogue
+// (ReLU, weighted head sum, filter) of the other, so one set of accumulators suffices
+// and it stays in VGPRs.  After the cross-half add both lane halves hold the scores of
+// both rows of a pair, so the low half files survivors of the first row and the high
+// half those of the second.  Survivors are staged in LDS per (wave, row) and flushed to
+// the row's per-wave segment as coalesced (score, key) runs, with wave-uniform counters
+// (no atomics).
+constexpr int kStageSlots = 64;  // LDS staging entries per (wave, row) for filter survivors
+
 template <bool kSample>
 struct ScoreTile {
     const IndexerArgs& P;
     const bf16x8 (&a)[kRowsPerGroup][8];
     const float (*s_w)[2][16];
-    const int64_t (&pr)[kRowsPerGroup];
-    const float (&tau_r)[kRowsPerGroup];
-    const int (&row_of)[kRowsPerGroup];
-    const bool (&live)[kRowsPerGroup];
-    int64_t n0;
-    int S;
-    int wave, lane, hf, col;
+    // Per lane half: parameters of row 2q + hf of row pair q.
+    uint32_t pr_m[2];   // last causal key
+    float tau_m[2];     // candidate threshold
+    bool live_m[2];
+    float* sample0;     // sample: row 0's sample list (rows are sample_stride apart)
+    uint2* cand0;       // filter: row 0's segment of this wave (rows are cap apart)
+    uint32_t n0;        // sample: keys of the group's first row
+    uint32_t S;         // sample: sample size
+    float s_ratio;      // sample: key stride n0 / S (any in-range keys would do)
+    int lane, hf, col;
     int seg;
-    int (&cnt)[kRowsPerGroup];
+    int (&cnt)[kRowsPerGroup];  // survivors so far per row (including any past seg)
+    uint2* lbuf;        // filter: this wave's LDS staging lists, kStageSlots per row
+    int lcnt[kRowsPerGroup];    // entries staged per row (wave-uniform)
+    int gcnt[kRowsPerGroup];    // entries already flushed to the segment per row
+    uint32_t tile0;     // first tile of this wave's contiguous range (wave-uniform)
 
-    int64_t tile0;  // first tile of this wave's contiguous range
+    __device__ __forceinline__ uint32_t pos_of(int it) const { return (tile0 + (uint32_t)it) * kKeyTile + col; }
 
-    __device__ __forceinline__ int64_t tile_of(int it) const { return tile0 + it; }
-
+    // Tile indices past the wave's range still address valid keys (clamped), so callers
+    // need no guard.
     __device__ __forceinline__ void load(bf16x8 (&b)[8], int it) const {
-        const int64_t pos = tile_of(it) * kKeyTile + col;
-        int64_t key;
-        if (kSample) key = pos < S ? (pos * n0) / S : 0;
-        else key = pos < P.N ? pos : P.N - 1;
-        const u16x8* kp = reinterpret_cast<const u16x8*>(P.k_idx + key * kIdxDim + hf * 64);
+        const uint32_t pos = pos_of(it);
+        uint32_t key;
+        if (kSample) key = min((uint32_t)((float)pos * s_ratio), n0 - 1u);  // strided sample
+        else key = pos < (uint32_t)P.N ? pos : (uint32_t)P.N - 1u;
+        const u16x8* kp = reinterpret_cast<const u16x8*>(P.k_idx + (size_t)key * kIdxDim + hf * 64);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) b[kk] = __builtin_bit_cast(bf16x8, kp[kk]);
     }
 
-    __device__ __forceinline__ void mfma(f32x16 (&acc)[kRowsPerGroup], const bf16x8 (&b)[8]) const {
+    // MFMA chains of rows J0 and J0+1 over one key tile, interleaved.
+    template <int J0>
+    __device__ __forceinline__ void mfma2(f32x16 (&acc)[kRowsPerGroup], const bf16x8 (&b)[8]) const {
+        f32x16 c0 = {}, c1 = {};
 #pragma unroll
-        for (int j = 0; j < kRowsPerGroup; ++j) acc[j] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-            for (int j = 0; j < kRowsPerGroup; ++j) acc[j] = mfma_32x32x16(a[j][kk], b[kk], acc[j]);
+        for (int kk = 0; kk < 8; ++kk) {
+            c0 = mfma_32x32x16(a[J0][kk], b[kk], c0);
+            c1 = mfma_32x32x16(a[J0 + 1][kk], b[kk], c1);
+        }
+        acc[J0] = c0;
+        acc[J0 + 1] = c1;
     }
 
-    __device__ __forceinline__ void epilogue(const f32x16 (&acc)[kRowsPerGroup], int it) {
-        const int64_t pos = tile_of(it) * kKeyTile + col;
-        float sc[kRowsPerGroup];
+    // Scores of rows J0, J0+1 for tile it: ReLU, weighted head sum, then the sample store
+    // or the threshold filter.
+    template <int J0>
+    __device__ __forceinline__ void epilogue2(const f32x16 (&acc)[kRowsPerGroup], int it) {
+        const uint32_t pos = pos_of(it);
+        float sc[2];
 #pragma unroll
-        for (int j = 0; j < kRowsPerGroup; ++j) {
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = J0 + jj;
             const f32x4* wv = reinterpret_cast<const f32x4*>(&s_w[j][hf][0]);
             float part = 0.f;
 #pragma unroll
@@ -226,63 +250,96 @@ struct ScoreTile {
                     part += w4[e] * __int_as_float(max(__float_as_int(acc[j][q4 * 4 + e]), 0));
             }
             auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-            sc[j] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + 0.0f;
+            sc[jj] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + 0.0f;
         }
+        // Lane half hf handles row J0 + hf from here on (selects, not branches).
+        const float s_mine = hf ? sc[1] : sc[0];
+        const uint32_t j_mine = J0 + hf;
         if (kSample) {
-#pragma unroll
-            for (int j = 0; j < kRowsPerGroup; ++j)
-                if (hf == 0 && pos < S && live[j]) P.sample[(size_t)row_of[j] * P.sample_stride + pos] = sc[j];
+            if (pos < S && live_m[J0 / 2]) sample0[j_mine * (uint32_t)P.sample_stride + pos] = s_mine;
         } else {
-            bool keep[kRowsPerGroup];
-            uint64_t m[kRowsPerGroup];
-            uint64_t any = 0;
-#pragma unroll
-            for (int j = 0; j < kRowsPerGroup; ++j) {
-                keep[j] = live[j] && hf == 0 && pos <= pr[j] && sc[j] >= tau_r[j];
-                m[j] = __ballot(keep[j]);
-                any |= m[j];
-            }
-            if (any) {
-#pragma unroll
-                for (int j = 0; j < kRowsPerGroup; ++j) {
-                    const int o = cnt[j] + mbcnt64(m[j]);
-                    if (keep[j] && o < seg) {
-                        const size_t off = (size_t)row_of[j] * P.cap + (size_t)wave * seg + o;
-                        P.cand_s[off] = sc[j];
-                        P.cand_i[off] = (int)pos;
-                    }
-                    cnt[j] += __builtin_popcountll(m[j]);
-                }
+            const bool keep = live_m[J0 / 2] && pos <= pr_m[J0 / 2] && s_mine >= tau_m[J0 / 2];
+            const uint64_t m = __ballot(keep);
+            if (m) {
+                const uint32_t m0 = (uint32_t)m, m1 = (uint32_t)(m >> 32);
+                // Slot within the row's segment: earlier survivors of the row plus the
+                // survivors among the lower lanes of this half.
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi(m1, __builtin_amdgcn_mbcnt_lo(hf ? 0u : m0, 0u));
+                const uint32_t o = (uint32_t)(hf ? lcnt[J0 + 1] : lcnt[J0]) + below;  // < kStageSlots
+                if (keep) lbuf[j_mine * kStageSlots + o] = uint2{__float_as_uint(s_mine), pos};
+                const int c0 = __builtin_popcount(m0), c1 = __builtin_popcount(m1);
+                lcnt[J0] += c0;
+                lcnt[J0 + 1] += c1;
+                cnt[J0] += c0;
+                cnt[J0 + 1] += c1;
             }
         }
+    }
+
+    // Staged survivors of row j -> its global segment: one coalesced 8-byte store per lane.
+    // Entries past the segment's capacity are dropped (the row is then re-done by the
+    // fold, which the count past seg signals).
+    __device__ __forceinline__ void flush_row(int j) {
+        if (lane < lcnt[j]) {
+            const uint2 e = lbuf[j * kStageSlots + lane];
+            const uint32_t o = (uint32_t)gcnt[j] + (uint32_t)lane;
+            if (o < (uint32_t)seg) cand0[(uint32_t)j * (uint32_t)P.cap + o] = e;
+        }
+        gcnt[j] += lcnt[j];
+        lcnt[j] = 0;
+    }
+    // A tile adds at most 32 survivors per row, so rows holding kStageSlots/2 or more are
+    // flushed before each tile: a staging list never overflows, and global stores (which
+    // the in-order memory counter would make the key-tile loads wait for) stay rare.
+    __device__ __forceinline__ void flush_full() {
+        if (kSample) return;
+#pragma unroll
+        for (int j = 0; j < kRowsPerGroup; ++j)
+            if (lcnt[j] >= kStageSlots / 2) flush_row(j);
+    }
+    __device__ __forceinline__ void flush_all() {
+        if (kSample) return;
+#pragma unroll
+        for (int j = 0; j < kRowsPerGroup; ++j)
+            if (lcnt[j] > 0) flush_row(j);
+    }
+
+    // One tile: rows 0,1 of tile it run on the MFMA pipe under the epilogue of rows 2,3 of
+    // tile it-1, then rows 2,3 of tile it under the epilogue of rows 0,1 of tile it.
+    __device__ __forceinline__ void step(f32x16 (&acc)[kRowsPerGroup], const bf16x8 (&b)[8], int it) {
+        flush_full();
+        mfma2<0>(acc, b);
+        epilogue2<2>(acc, it - 1);
+        mfma2<2>(acc, b);
+        epilogue2<0>(acc, it);
     }
 };
 
 template <bool kSample>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P) {
     const int g = blockIdx.x;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int hf = lane >> 5;
     const int col = lane & 31;
     __shared__ __attribute__((aligned(16))) float s_w[kRowsPerGroup][2][16];
+    __shared__ uint2 s_stage[kSegs][kRowsPerGroup * kStageSlots];
 
-    int64_t pr[kRowsPerGroup];
+    const int seg = P.cap / kSegs;
+    uint32_t pr[kRowsPerGroup];
     float tau_r[kRowsPerGroup];
     int row_of[kRowsPerGroup];
     bool live[kRowsPerGroup];
     int64_t n_keys = 0;
     const int r0 = g * kRowsPerGroup;
-    int S = 0;
-    int64_t n0 = 0;
+    uint32_t S = 0, n0 = 0;
 #pragma unroll
     for (int j = 0; j < kRowsPerGroup; ++j) {
         const int r = r0 + j;
         const bool valid = r < P.Lb;
         row_of[j] = valid ? r : r0;
-        const int64_t p = P.pos0 + r;
-        pr[j] = valid ? p : -1;
-        const int64_t nt = valid ? (p < P.N - 1 ? p : P.N - 1) + 1 : 0;
+        const int64_t p = P.pos0 + r;  // <= N - 1
+        pr[j] = valid ? (uint32_t)p : 0u;
         if (kSample) {
             live[j] = valid;
             tau_r[j] = 0.f;
@@ -290,13 +347,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P) {
             const bool use = valid && P.mode[r] == kModeNormal;
             live[j] = use;
             tau_r[j] = use ? P.tau[r] : INFINITY;
-            if (use && nt > n_keys) n_keys = nt;
+            if (use && p + 1 > n_keys) n_keys = p + 1;
         }
     }
     if (kSample) {
         const int64_t p = P.pos0 + r0;
-        n0 = (p < P.N - 1 ? p : P.N - 1) + 1;
-        S = sample_size(n0, P.top_k, P.cap);
+        n0 = (uint32_t)(p + 1);
+        S = (uint32_t)sample_size(n0, P.top_k, P.cap);
         n_keys = S;
     }
     if (threadIdx.x < kRowsPerGroup * 32) {
@@ -314,39 +371,52 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P) {
             const u16x8* qp = reinterpret_cast<const u16x8*>(
                 P.q_idx + ((size_t)row_of[j] * kIdxHeads + col) * kIdxDim + hf * 64);
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) a[j][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+            for (int kk = 0; kk < 8; ++kk) {
+                a[j][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+                asm volatile("" : "+a"(a[j][kk]));  // keep the query fragments in AGPRs
+            }
         }
         // Wave w scores the contiguous tile range [w*tpw, (w+1)*tpw): its candidate segment
         // is then in ascending key order and the segments concatenate in order.
-        const int64_t n_tiles = (n_keys + kKeyTile - 1) / kKeyTile;
-        const int64_t tpw = (n_tiles + kSegs - 1) / kSegs;
-        const int64_t t0 = (int64_t)wave * tpw;
-        const int n_my = n_tiles > t0 ? (int)((n_tiles - t0) < tpw ? (n_tiles - t0) : tpw) : 0;
-        ScoreTile<kSample> T{P, a, s_w, pr, tau_r, row_of, live, n0, S, wave, lane, hf, col, P.cap / kSegs, cnt, t0};
-        bf16x8 b0[8], b1[8];
-        f32x16 acc0[kRowsPerGroup], acc1[kRowsPerGroup];
-        if (n_my > 0) T.load(b0, 0);
-        if (n_my > 1) T.load(b1, 1);
-        if (n_my > 0) T.mfma(acc0, b0);
-        int it = 0;
-        // Steady state: tiles it (in acc0), it+1 (b1 loaded), it+2, it+3 all exist.
-        for (; it + 3 < n_my; it += 2) {
-            T.load(b0, it + 2);
-            T.mfma(acc1, b1);
-            T.epilogue(acc0, it);
-            T.load(b1, it + 3);
-            T.mfma(acc0, b0);
-            T.epilogue(acc1, it + 1);
-        }
-        // Tail (fewer than four tiles left, acc0 holds tile it, b1 holds tile it+1).
-        for (; it < n_my; ++it) {
-            if (it + 1 < n_my) T.mfma(acc1, b1);
-            T.epilogue(acc0, it);
-            if (it + 1 < n_my) {
-                if (it + 2 < n_my) T.load(b1, it + 2);
-#pragma unroll
-                for (int j = 0; j < kRowsPerGroup; ++j) acc0[j] = acc1[j];
+        const int n_tiles = (int)((n_keys + kKeyTile - 1) / kKeyTile);
+        const int tpw = (n_tiles + kSegs - 1) / kSegs;
+        const int t0 = wave * tpw;
+        const int n_my = n_tiles > t0 ? min(n_tiles - t0, tpw) : 0;
+        // Rows of a group are consecutive (invalid rows never store), so every row's
+        // list is addressed from row 0's.
+        ScoreTile<kSample> T{P, a, s_w,
+                             {hf ? pr[1] : pr[0], hf ? pr[3] : pr[2]},
+                             {hf ? tau_r[1] : tau_r[0], hf ? tau_r[3] : tau_r[2]},
+                             {hf ? live[1] : live[0], hf ? live[3] : live[2]},
+                             kSample ? P.sample + (size_t)r0 * P.sample_stride : nullptr,
+                             kSample ? nullptr : P.cand + (size_t)r0 * P.cap + (size_t)wave * seg,
+                             n0, S, kSample && S > 0 ? (float)n0 / (float)S : 0.f, lane, hf, col, seg, cnt,
+                             s_stage[wave], {0, 0, 0, 0}, {0, 0, 0, 0}, (uint32_t)t0};
+        // Tile it sits in buffer it % 3; tile it+3 is loaded once tile it's MFMAs are issued.
+        bf16x8 b0[8], b1[8], b2[8];
+        f32x16 acc[kRowsPerGroup];
+        if (n_my > 0) {
+            T.load(b0, 0);
+            T.load(b1, 1);
+            T.load(b2, 2);
+            T.template mfma2<0>(acc, b0);
+            T.template mfma2<2>(acc, b0);
+            T.load(b0, 3);
+            T.template epilogue2<0>(acc, 0);
+            int it = 1;
+            for (; it + 2 < n_my; it += 3) {
+                T.step(acc, b1, it);
+                T.load(b1, it + 3);
+                T.step(acc, b2, it + 1);
+                T.load(b2, it + 4);
+                T.step(acc, b0, it + 2);
+                T.load(b0, it + 5);
             }
+            if (it < n_my) T.step(acc, b1, it);
+            if (it + 1 < n_my) T.step(acc, b2, it + 1);
+            T.flush_full();
+            T.template epilogue2<2>(acc, n_my - 1);
+            T.flush_all();
         }
     }
     if (!kSample && lane == 0) {
@@ -878,9 +948,9 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
                         w = x;
                         s0 = start[x];
                     }
-                const size_t off = (size_t)r * P.cap + (size_t)w * seg + (j - s0);
-                v[e] = P.cand_s[off] + 0.0f;
-                key[e] = P.cand_i[off];
+                const uint2 c = P.cand[(size_t)r * P.cap + (size_t)w * seg + (j - s0)];
+                v[e] = __uint_as_float(c.x) + 0.0f;
+                key[e] = (int)c.y;
             }
         }
         nv = total > base ? (total - base < kSelChunk ? total - base : kSelChunk) : 0;
@@ -958,10 +1028,10 @@ __device__ void fold_score_block(const IndexerArgs& P, int r, int64_t k0, int64_
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int hf = lane >> 5, col = lane & 31;
     const int n_waves = blockDim.x >> 6;
-    const u16x8* qp = reinterpret_cast<const u16x8*>(P.q_idx + ((size_t)r * kIdxHeads + col) * kIdxDim + hf * 64);
+    const u16x8* qp = reinterpret_cast<const u16x8*>(P.q_idx + ((size_t)r * kIdxHeads + col) * kIdxDim + hf * 8);
     bf16x8 a[8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) a[kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+    for (int kk = 0; kk < 8; ++kk) a[kk] = __builtin_bit_cast(bf16x8, qp[2 * kk]);
     float wf[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) wf[i] = P.w[(size_t)r * kIdxHeads + 8 * (i >> 2) + 4 * hf + (i & 3)];
@@ -969,10 +1039,10 @@ __device__ void fold_score_block(const IndexerArgs& P, int r, int64_t k0, int64_
     for (int64_t ti = wave; ti < n_tiles; ti += n_waves) {
         const int64_t pos = k0 + ti * kKeyTile + col;
         const int64_t key = pos < k1 ? pos : k1 - 1;
-        const u16x8* kp = reinterpret_cast<const u16x8*>(P.k_idx + key * kIdxDim + hf * 64);
+        const u16x8* kp = reinterpret_cast<const u16x8*>(P.k_idx + key * kIdxDim + hf * 8);
         f32x16 acc = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) acc = mfma_32x32x16(a[kk], __builtin_bit_cast(bf16x8, kp[kk]), acc);
+        for (int kk = 0; kk < 8; ++kk) acc = mfma_32x32x16(a[kk], __builtin_bit_cast(bf16x8, kp[2 * kk]), acc);
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) part += wf[i] * fmaxf(acc[i], 0.f);
