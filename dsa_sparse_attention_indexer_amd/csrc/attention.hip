@@ -67,9 +67,10 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     const int n_tiles = (A.top_k + kAttnTile - 1) / kAttnTile;
     const int nwaves = nthreads >> 6;
     // Entry j of the row as a key this query may use, or -1.
+    const int p32 = (int)p;  // <= N - 1 <= INT32_MAX - 1
     auto key_of = [&](int slot, int r, int tile_j) -> int {
         const int key = s_idx[slot][r];
-        return (tile_j + r < A.top_k && key >= 0 && key <= p && key < A.N) ? key : -1;
+        return (tile_j + r < A.top_k && key >= 0 && key <= p32) ? key : -1;
     };
     // DMA of the raw entries of tile j into slot (lanes past top_k fetch nothing).
     auto fetch_idx = [&](int j, int slot) {
@@ -132,42 +133,56 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
                 s0 = mfma_16x16x32(a0, qf[ks], s0);
                 s1 = mfma_16x16x32(a1, qf[ks], s1);
             }
+            // Usable entries of the tile as a bit mask (bit r: entry r), one ballot per wave.
+            const uint32_t vmask = (uint32_t)__ballot(lane < kAttnTile && key_of(slot, lane & 31, tile * kAttnTile) >= 0);
+            const uint32_t mlo = vmask >> (4 * g), mhi = vmask >> (16 + 4 * g);
             float lg[8];
             float tmax = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                lg[r] = key_of(slot, 4 * g + r, tile * kAttnTile) >= 0 ? s0[r] * sl2 : -INFINITY;
-                lg[4 + r] = key_of(slot, 16 + 4 * g + r, tile * kAttnTile) >= 0 ? s1[r] * sl2 : -INFINITY;
+                lg[r] = (mlo >> r) & 1u ? s0[r] * sl2 : -INFINITY;
+                lg[4 + r] = (mhi >> r) & 1u ? s1[r] * sl2 : -INFINITY;
             }
 #pragma unroll
             for (int r = 0; r < 8; ++r) tmax = fmaxf(tmax, lg[r]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            const float mnew = fmaxf(m, tmax);
-            float alpha = 1.f;
+            // The exponentials are taken against a reference m that moves only when a tile's
+            // maximum exceeds it by more than 2^8 (weights then stay below 256, well inside
+            // bf16 and fp32), so the accumulator rescale is skipped on most tiles.
+            const bool bump = tmax > m + 8.0f;
+            if (__ballot(bump)) {
+                const float alpha = bump ? __builtin_amdgcn_exp2f(m - tmax) : 1.0f;
+#pragma unroll
+                for (int dt = 0; dt < kDv / 16; ++dt) o[dt] *= alpha;
+                lsum *= alpha;
+                lexp *= alpha;
+                m = bump ? tmax : m;
+            }
             u16x8 pb;
             float ps = 0.f, pe = 0.f;
-            if (mnew == -INFINITY) {
+            if (m == -INFINITY) {  // nothing usable yet (the same for every head)
 #pragma unroll
                 for (int r = 0; r < 8; ++r) pb[r] = 0;
             } else {
-                alpha = exp2f(m - mnew);
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float e = exp2f(lg[r] - mnew);
-                    const uint16_t b = float_to_bf16_rne(e);
-                    pb[r] = b;
-                    ps += bf16_bits_to_float(b);
-                    pe += e;
+                for (int r = 0; r < 8; r += 2) {
+                    const float e0 = __builtin_amdgcn_exp2f(lg[r] - m);
+                    const float e1 = __builtin_amdgcn_exp2f(lg[r + 1] - m);
+                    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+                    const uint32_t b2 = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)e0, (__bf16)e1});
+                    pb[r] = (uint16_t)b2;
+                    pb[r + 1] = (uint16_t)(b2 >> 16);
+                    ps += __uint_as_float(b2 << 16) + __uint_as_float(b2 & 0xffff0000u);
+                    pe += e0 + e1;
                 }
             }
             ps += __shfl_xor(ps, 16);
             ps += __shfl_xor(ps, 32);
             pe += __shfl_xor(pe, 16);
             pe += __shfl_xor(pe, 32);
-            lsum = lsum * alpha + ps;
-            lexp = lexp * alpha + pe;
-            m = mnew;
+            lsum += ps;
+            lexp += pe;
             const bf16x8 pbf = __builtin_bit_cast(bf16x8, pb);
             // Source lane (g, c16) addresses row kb + c16/4, columns 4*(c16%4)..+4 of each
             // 16-column block, kb = 4g (K slots 0-3 of its group) or 16 + 4g (slots 4-7).
@@ -178,7 +193,6 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
                 const u16x4 lo = lds_read_tr(vlo + dt * 16);
                 const u16x4 hi = lds_read_tr(vhi + dt * 16);
                 const u16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                o[dt] *= alpha;
                 o[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, av), pbf, o[dt]);
             }
         }

@@ -10,7 +10,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 #include "dsa_internal.h"
 
 namespace dsa {
