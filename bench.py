@@ -33,6 +33,43 @@ def log(msg: str):
     print(msg, file=sys.stderr, flush=True)
 
 
+# Source files that define each timed kernel; a traffic figure measured with hardware
+# counters is reported only while these files are unchanged since the measurement.
+KERNEL_SOURCES = {
+    "score_filter": ["indexer.hip", "dsa_common.h", "dsa_internal.h", "../build.py"],
+    "sparse_attention": ["attention.hip", "dsa_common.h", "dsa_internal.h", "../build.py"],
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = ROOT / "dsa_sparse_attention_indexer_amd" / "csrc"
+    for name in KERNEL_SOURCES[kernel]:
+        h.update((csrc / name).resolve().read_bytes())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.txt (FETCH_SIZE and
+    WRITE_SIZE counter runs, scaled by a plain copy of known size), or None when the file
+    is missing or the kernel's sources changed since it was measured."""
+    f = ROOT / "profiles" / f"traffic_{kernel}_{workload}.txt"
+    if not f.exists():
+        return None
+    fields = {}
+    for line in f.read_text().splitlines():
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        if fields.get("source_sha256") != kernel_source_hash(kernel):
+            return None
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError, OSError):
+        return None
+
+
 def workload_sizes(wl):
     """Algorithmic work of one step, per query row: (indexer flops, attention flops, attention bytes)."""
     rows = []
@@ -98,12 +135,17 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (read MIB, write MIB) three "
                          "times, to scale the FETCH_SIZE / WRITE_SIZE counters, and exit")
+    ap.add_argument("--print-source-hash", metavar="KERNEL", choices=sorted(KERNEL_SOURCES),
+                    help="print the source hash a traffic summary for KERNEL must carry, and exit")
     args = ap.parse_args()
+    if args.print_source_hash:
+        print(kernel_source_hash(args.print_source_hash))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build is single-GPU; the path shards by query with no exchange "
-              "(see DESIGN.md) but multi-GPU runs are not part of it. Use --gpus 1.", file=sys.stderr)
+        print("bench.py: this path runs on one GPU (it would shard by query with no exchange); "
+              "runs on several GPUs are not part of it. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -210,13 +252,15 @@ def main():
             ach = f_idx / n / (sf["ms_per_launch"] * 1e-3) / 1e12
             per["score_filter"] = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                                   "traffic": None, "ms_per_launch": round(sf["ms_per_launch"], 4)}
+                                   "traffic": measured_traffic("score_filter", wl.name),
+                                   "ms_per_launch": round(sf["ms_per_launch"], 4)}
         if at:
             n = at["launches_per_step"]
             ach = b_attn / n / (at["ms_per_launch"] * 1e-3) / 1e9
             per["sparse_attention"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                                        "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                                       "traffic": None, "ms_per_launch": round(at["ms_per_launch"], 4)}
+                                       "traffic": measured_traffic("sparse_attention", wl.name),
+                                       "ms_per_launch": round(at["ms_per_launch"], 4)}
         dom = max(per, key=lambda k: kernels[k]["ms_per_step"]) if per else None
         if dom:
             r = dict(per[dom])

@@ -438,7 +438,8 @@ struct CandList {
 
 constexpr int kBins = 2048;
 constexpr int kDirect = 512;
-constexpr int kRescoreKeys = 16;  // band keys re-scored per pass (x 32 heads = 512 items)
+constexpr int kRescoreKeys = 16;   // band keys per fp64 MFMA block
+constexpr int kRescoreRound = 64;  // band keys re-scored per round (four blocks, eight waves)
 
 // One row's selection scratch.  The phases use the union in turn: binned k-th search
 // (sel), fp64 re-score staging (rs), then the selected keys (out, fold path only).
@@ -448,13 +449,12 @@ struct SelectScratch {
             int hist[kBins];
             float direct[kDirect];
         } sel;
-        struct {
-            uint16_t q[kIdxHeads * kIdxDim];      // the query row's indexer q (8 KB)
-            uint16_t k[kRescoreKeys][kIdxDim];    // band key rows of this pass (4 KB)
-        } rs;
         int out[kMaxTopK];
+        double term[kRescoreRound][kIdxHeads];  // head terms of one re-score round
     };
-    double term[kRescoreKeys][kIdxHeads];
+    double q1[kIdxHeads];    // per head: sum_i |q_h,i| (rounded up)
+    int qe[kIdxHeads];       // per head: lowest set-bit exponent over nonzero q_h,i (INT_MAX: none)
+    int bad[kRescoreRound];  // band keys of the round whose dot products need the sequential order
     float red_f[32];
     int red_i[32];
     int sh[16];
@@ -666,31 +666,120 @@ __device__ void block_bitonic_sort(int* a, int n) {
 }
 
 // fp64 canonical scores of band entries [0, nb) (keys in band_key), in place into band_s.
+//
+// The canonical head dot product d_h = sum_i q_i k_i is a sequential fp64 sum of exact
+// bf16 x bf16 products.  When every product is a multiple of 2^e (e = lowest set-bit
+// exponent of q_h plus that of k) and sum_i |q_i k_i| <= |q_h|_1 |k|_inf < 2^(53+e),
+// every partial sum in any order is exactly representable, so the sequential sum equals
+// the exact one and any summation order gives it.  Those dot products run on fp64 MFMA
+// (16 band keys x 16 heads x 4 dims per instruction); keys failing the test take the
+// sequential path.  The head terms fl(w_h max(d_h, +0)) and their ascending-h sum are
+// always evaluated in the canonical order.
 __device__ void band_rescore(int nb, const int* band_key, double* band_s, const uint16_t* __restrict__ q_row,
                              const float* __restrict__ w_row, const uint16_t* __restrict__ k_idx,
                              SelectScratch& S) {
-    // The query row and each pass's key rows are staged in LDS so the 128-step fp64
-    // chains never wait on global memory.
-    for (int i = threadIdx.x; i < kIdxHeads * kIdxDim / 8; i += blockDim.x)
-        reinterpret_cast<u16x8*>(S.rs.q)[i] = reinterpret_cast<const u16x8*>(q_row)[i];
-    for (int b0 = 0; b0 < nb; b0 += kRescoreKeys) {
-        for (int i = threadIdx.x; i < kRescoreKeys * kIdxDim / 8; i += blockDim.x) {
-            const int bl = i / (kIdxDim / 8), c = i % (kIdxDim / 8);
-            const int key = b0 + bl < nb ? band_key[b0 + bl] : band_key[b0];
-            reinterpret_cast<u16x8*>(S.rs.k[bl])[c] = reinterpret_cast<const u16x8*>(k_idx + (size_t)key * kIdxDim)[c];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nwaves = blockDim.x >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    // Per-head statistics of the query: 16 lanes per head, 8 dimensions per lane.
+    for (int h = wave * 4 + g; h < kIdxHeads; h += nwaves * 4) {
+        const u16x8 v = reinterpret_cast<const u16x8*>(q_row + h * kIdxDim)[c];
+        double l1 = 0.0;
+        int e = INT_MAX;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            l1 += fabs((double)bf16_bits_to_float(v[j]));
+            if ((v[j] & 0x7fff) != 0) e = min(e, bf16_lsb_exp(v[j]));
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            l1 += __shfl_xor(l1, o);
+            e = min(e, __shfl_xor(e, o));
+        }
+        if (c == 0) {
+            S.q1[h] = l1 * (1.0 + 1.0 / 1048576.0);  // covers the rounding of the sums above
+            S.qe[h] = e;
+        }
+    }
+    __syncthreads();
+    for (int m0 = 0; m0 < nb; m0 += kRescoreRound) {
+        if (threadIdx.x < kRescoreRound) S.bad[threadIdx.x] = 0;
+        __syncthreads();
+        // Wave w: block w/2 of the round (band keys m0 + 16*(w/2) ..), heads 16*(w%2) ..
+        // Lane (g, c) feeds key 16*(w/2) + c (A) and head 16*(w%2) + c (B), dimensions
+        // 32g .. 32g+31, one per K-step.
+        for (int wb = wave; wb < 2 * (kRescoreRound / kRescoreKeys); wb += nwaves) {
+            const int mb = m0 + kRescoreKeys * (wb >> 1);
+            if (mb >= nb) continue;
+            const int head = 16 * (wb & 1) + c;
+            const int key = band_key[mb + c < nb ? mb + c : mb];
+            const u16x8* kp = reinterpret_cast<const u16x8*>(k_idx + (size_t)key * kIdxDim + 32 * g);
+            const u16x8* qp = reinterpret_cast<const u16x8*>(q_row + head * kIdxDim + 32 * g);
+            u16x8 kv[4], qv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                kv[j] = kp[j];
+                qv[j] = qp[j];
+            }
+            // Exactness statistics of key mb + c over all 128 dimensions.
+            float kinf = 0.f;
+            int ke = INT_MAX;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    kinf = fmaxf(kinf, fabsf(bf16_bits_to_float(kv[j][e])));
+                    if ((kv[j][e] & 0x7fff) != 0) ke = min(ke, bf16_lsb_exp(kv[j][e]));
+                }
+            kinf = fmaxf(kinf, __shfl_xor(kinf, 16));
+            kinf = fmaxf(kinf, __shfl_xor(kinf, 32));
+            ke = min(ke, __shfl_xor(ke, 16));
+            ke = min(ke, __shfl_xor(ke, 32));
+            f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int ks = 0; ks < 32; ks += 2) {
+                const double a0 = (double)bf16_bits_to_float(kv[ks >> 3][ks & 7]);
+                const double b0 = (double)bf16_bits_to_float(qv[ks >> 3][ks & 7]);
+                const double a1 = (double)bf16_bits_to_float(kv[(ks + 1) >> 3][(ks + 1) & 7]);
+                const double b1 = (double)bf16_bits_to_float(qv[(ks + 1) >> 3][(ks + 1) & 7]);
+                acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc1, 0, 0, 0);
+            }
+            // Lane (g, c) holds d for keys mb + g + 4i (i = 0..3) and its head.
+            const double wh = (double)w_row[head];
+            const double qh1 = S.q1[head];
+            const int qhe = S.qe[head];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = g + 4 * i;
+                const float kinf_m = __shfl(kinf, m);
+                const int ke_m = __shfl(ke, m);
+                if (mb + m < nb) {
+                    const double d = acc0[i] + acc1[i];
+                    const bool exact = kinf_m == 0.f || qhe == INT_MAX ||
+                                       qh1 * (double)kinf_m < ldexp(1.0, 53 + qhe + ke_m);
+                    const int slot = mb - m0 + m;
+                    if (!exact) S.bad[slot] = 1;
+                    const double r = d > 0.0 ? d : 0.0;
+                    S.term[slot][head] = wh * r;  // a lone product: nothing to contract
+                }
+            }
         }
         __syncthreads();
-        for (int it = threadIdx.x; it < kRescoreKeys * kIdxHeads; it += blockDim.x) {
+        // Keys whose dot products could round: the canonical sequential evaluation.
+        for (int it = threadIdx.x; it < kRescoreRound * kIdxHeads; it += blockDim.x) {
             const int bl = it >> 5, h = it & 31;
-            if (b0 + bl < nb) S.term[bl][h] = canonical_head_term(S.rs.q + h * kIdxDim, S.rs.k[bl], w_row[h]);
+            if (m0 + bl < nb && S.bad[bl])
+                S.term[bl][h] = canonical_head_term(q_row + h * kIdxDim,
+                                                    k_idx + (size_t)band_key[m0 + bl] * kIdxDim, w_row[h]);
         }
         __syncthreads();
-        if (threadIdx.x < kRescoreKeys && b0 + (int)threadIdx.x < nb) {
+        if (threadIdx.x < kRescoreRound && m0 + (int)threadIdx.x < nb) {
 #pragma clang fp contract(off)
             double sum = 0.0;
             for (int h = 0; h < kIdxHeads; ++h) sum = sum + S.term[threadIdx.x][h];
             if (sum == 0.0) sum = 0.0;
-            band_s[b0 + threadIdx.x] = sum;
+            band_s[m0 + threadIdx.x] = sum;
         }
         __syncthreads();
     }
