@@ -48,7 +48,7 @@ class Workload:
     top_k: int
     H: int
     seed: int
-    indexer: str  # "int" | "gauss" | "sink" | "concentrated" | "zero"
+    indexer: str  # "int" | "gauss" | "sink" | "concentrated" | "zero" | "wide"
     attention: str = "small"  # "small" = N(0,1)/24, "sharp" = q 2*N(0,1), kv N(0,1), "zero_q"
     int_twin: bool = False
     q_pos0: int | None = None  # default N - L
@@ -162,6 +162,12 @@ def make_indexer_inputs(wl: Workload, rng: np.random.Generator | None = None):
         k = _normal_f32(rng, N * IDX_HEAD_DIM).reshape(kshape)
         if wl.indexer == "sink":
             k[:64] *= np.float32(3.0)
+    elif wl.indexer == "wide":
+        # every element scaled by its own power of two in [2^-24, 2^24]: dot products whose
+        # exact value needs far more than 53 bits
+        k = _normal_f32(rng, N * IDX_HEAD_DIM).reshape(kshape)
+        k *= np.exp2(rng.integers(-24, 25, size=kshape)).astype(np.float32)
+        q *= np.exp2(rng.integers(-24, 25, size=qshape)).astype(np.float32)
     elif wl.indexer == "concentrated":
         c = rng.standard_normal(IDX_HEAD_DIM, dtype=np.float32)
         k = _normal_f32(rng, N * IDX_HEAD_DIM).reshape(kshape)

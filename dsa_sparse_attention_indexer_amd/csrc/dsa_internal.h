@@ -22,7 +22,7 @@ __host__ __device__ inline int cand_capacity(int top_k) {
     return (c + 1023) & ~1023;
 }
 
-constexpr int kRowsPerGroup = 4;  // indexer query rows scored together (one sample each)
+constexpr int kRowsPerGroup = 8;  // indexer query rows scored together (one sample each)
 
 // Keys scored in the threshold sample of a row group whose first row sees n_t keys.
 // Groups whose first row sees at most cap - kRowsPerGroup keys are not sampled: every row
@@ -48,7 +48,7 @@ __host__ __device__ inline int sample_rank(int64_t n_t, int s, int top_k) {
 
 constexpr int kFallbackSlots = 32;
 constexpr int kFoldKeys = 4096;
-constexpr int kCandSegs = 4;  // candidate segments per row (one per scoring wave)
+constexpr int kCandSegs = 8;  // candidate segments per row: 2 key halves x 4 scoring waves
 
 struct IndexerLayout {
     int rows, cap, sample_stride, fold_cap;
@@ -101,7 +101,7 @@ struct IndexerArgs {
     float* tau;
     float* delta;
     int* mode;
-    int* count;             // [Lb][kCandSegs] survivors per (row, scoring wave)
+    int* count;             // [Lb][kCandSegs] survivors per (row, segment)
     int* fb_ctrl;           // [0] flagged rows, [1] next row to take
     int* fb_list;
     float* sample;

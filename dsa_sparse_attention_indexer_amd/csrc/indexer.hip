@@ -39,8 +39,7 @@
 
 namespace dsa {
 
-constexpr int kSegs = kScoreThreads / kWave;  // candidate segments per row = score waves
-static_assert(kSegs == kCandSegs, "workspace layout assumes one candidate segment per scoring wave");
+constexpr int kSegs = kCandSegs;  // candidate segments per row: (key half, scoring wave)
 
 // ------------------------------------------------------------------ helpers
 
@@ -165,43 +164,53 @@ __global__ __launch_bounds__(256) void key_stats_kernel(const uint16_t* __restri
 
 // ------------------------------------------------------------------ 2/4. MFMA scoring
 
-// One workgroup = 4 consecutive query rows; each of its 4 waves scores all 4 rows over
-// its own contiguous quarter of the causal key tiles (a key tile is loaded once per 4
-// rows, and no wave waits for another).  Lane l owns head (l & 31) of the A operand and
-// key (l & 31) of the B operand; its half (l >> 5) holds dimensions [64*half, 64*half+64)
-// of both, eight MFMA K-steps of 8.  Key tiles are loaded straight into the B layout into
-// three register buffers, so two tiles are in flight while one is consumed.  The query fragments sit in AGPRs, read by the MFMAs directly, which leaves
-// the VGPRs to the accumulators, the key tiles and the head weights.
+// One workgroup = 8 consecutive query rows over one half of their causal keys (two
+// workgroups per row group; the half follows the XCD the workgroup lands on, so each
+// XCD's L2 streams only its half of the key cache).  Each of the 4 waves scores all 8
+// rows over its own contiguous quarter of that half: candidate segment 4*half + wave, so
+// a row's 8 segments cover ascending key ranges.  Eight rows per wave means every key
+// byte brought into the CU feeds 8 x 32 heads of MFMA work, which halves the per-CU key
+// stream that the vector L1 has to sustain compared with four rows.
 //
-// A wave's rows run as two pairs: the MFMA chains of one pair execute under the epilogue
-// (ReLU, weighted head sum, filter) of the other, so one set of accumulators suffices
-// and it stays in VGPRs.  After the cross-half add both lane halves hold the scores of
-// both rows of a pair, so the low half files survivors of the first row and the high
-// half those of the second.  Survivors are staged in LDS per (wave, row) and flushed to
-// the row's per-wave segment as coalesced (score, key) runs, with wave-uniform counters
-// (no atomics).
+// Lane l owns head (l & 31) of the A operand and key (l & 31) of the B operand; its half
+// (l >> 5) holds dimensions [64*half, 64*half+64) of both, eight MFMA K-steps of 8.  Key
+// tiles are loaded straight into the B layout, three tiles ahead.  The 8 rows' query
+// fragments fill the AGPRs (the MFMAs read A operands from there directly), leaving the
+// VGPRs to the accumulators and the key tiles; the head weights are read from LDS in
+// the epilogue.
+//
+// The rows run as four pairs: the MFMA chains of one pair execute under the epilogue
+// (ReLU, weighted head sum, filter) of the previous pair.  After the cross-half add both
+// lane halves hold the scores of both rows of a pair, so the low half files survivors
+// of the first row and the high half those of the second.  Survivors are staged in LDS
+// per (wave, row) and flushed to the row's segment as coalesced (score, key) runs, with
+// wave-uniform counters (no atomics).
+constexpr int kRowsPerWave = kRowsPerGroup;   // 8
+constexpr int kPairs = kRowsPerWave / 2;
+constexpr int kKeyHalves = 2;
 constexpr int kStageSlots = 64;  // LDS staging entries per (wave, row) for filter survivors
+static_assert(kKeyHalves * (kScoreThreads / kWave) == kSegs, "one candidate segment per (half, wave)");
 
 template <bool kSample>
 struct ScoreTile {
     const IndexerArgs& P;
-    const bf16x8 (&a)[kRowsPerGroup][8];
+    const bf16x8 (&a)[kRowsPerWave][8];
     const float (*s_w)[2][16];
     // Per lane half: parameters of row 2q + hf of row pair q.
-    uint32_t pr_m[2];   // last causal key
-    float tau_m[2];     // candidate threshold
-    bool live_m[2];
+    uint32_t pr_m[kPairs];   // last causal key
+    float tau_m[kPairs];     // candidate threshold
+    bool live_m[kPairs];
     float* sample0;     // sample: row 0's sample list (rows are sample_stride apart)
-    uint2* cand0;       // filter: row 0's segment of this wave (rows are cap apart)
+    uint2* cand0;       // filter: row 0's segment (rows are cap apart)
     uint32_t n0;        // sample: keys of the group's first row
     uint32_t S;         // sample: sample size
     float s_ratio;      // sample: key stride n0 / S (any in-range keys would do)
     int lane, hf, col;
     int seg;
-    int (&cnt)[kRowsPerGroup];  // survivors so far per row (including any past seg)
-    uint2* lbuf;        // filter: this wave's LDS staging lists, kStageSlots per row
-    int lcnt[kRowsPerGroup];    // entries staged per row (wave-uniform)
-    int gcnt[kRowsPerGroup];    // entries already flushed to the segment per row
+    int (&cnt)[kRowsPerWave];   // survivors so far per row (including any past seg)
+    uint2* lbuf;                // filter: this wave's LDS staging lists, kStageSlots per row
+    int lcnt[kRowsPerWave];     // entries staged per row (wave-uniform)
+    int gcnt[kRowsPerWave];     // entries already flushed to the segment per row
     uint32_t tile0;     // first tile of this wave's contiguous range (wave-uniform)
 
     __device__ __forceinline__ uint32_t pos_of(int it) const { return (tile0 + (uint32_t)it) * kKeyTile + col; }
@@ -220,7 +229,7 @@ struct ScoreTile {
 
     // MFMA chains of rows J0 and J0+1 over one key tile, interleaved.
     template <int J0>
-    __device__ __forceinline__ void mfma2(f32x16 (&acc)[kRowsPerGroup], const bf16x8 (&b)[8]) const {
+    __device__ __forceinline__ void mfma2(f32x16 (&acc)[kRowsPerWave], const bf16x8 (&b)[8]) const {
         f32x16 c0 = {}, c1 = {};
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
@@ -234,8 +243,11 @@ struct ScoreTile {
     // Scores of rows J0, J0+1 for tile it: ReLU, weighted head sum, then the sample store
     // or the threshold filter.
     template <int J0>
-    __device__ __forceinline__ void epilogue2(const f32x16 (&acc)[kRowsPerGroup], int it) {
+    __device__ __forceinline__ void epilogue2(const f32x16 (&acc)[kRowsPerWave], int it) {
         const uint32_t pos = pos_of(it);
+        // The weights are re-read from LDS here; held across the loop they would take
+        // 128 VGPRs.
+        asm volatile("" ::: "memory");
         float sc[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
@@ -255,14 +267,15 @@ struct ScoreTile {
         // Lane half hf handles row J0 + hf from here on (selects, not branches).
         const float s_mine = hf ? sc[1] : sc[0];
         const uint32_t j_mine = J0 + hf;
+        constexpr int q = J0 / 2;
         if (kSample) {
-            if (pos < S && live_m[J0 / 2]) sample0[j_mine * (uint32_t)P.sample_stride + pos] = s_mine;
+            if (pos < S && live_m[q]) sample0[j_mine * (uint32_t)P.sample_stride + pos] = s_mine;
         } else {
-            const bool keep = live_m[J0 / 2] && pos <= pr_m[J0 / 2] && s_mine >= tau_m[J0 / 2];
+            const bool keep = live_m[q] && pos <= pr_m[q] && s_mine >= tau_m[q];
             const uint64_t m = __ballot(keep);
             if (m) {
                 const uint32_t m0 = (uint32_t)m, m1 = (uint32_t)(m >> 32);
-                // Slot within the row's segment: earlier survivors of the row plus the
+                // Slot within the row's staging list: entries already staged plus the
                 // survivors among the lower lanes of this half.
                 const uint32_t below = __builtin_amdgcn_mbcnt_hi(m1, __builtin_amdgcn_mbcnt_lo(hf ? 0u : m0, 0u));
                 const uint32_t o = (uint32_t)(hf ? lcnt[J0 + 1] : lcnt[J0]) + below;  // < kStageSlots
@@ -294,47 +307,56 @@ struct ScoreTile {
     __device__ __forceinline__ void flush_full() {
         if (kSample) return;
 #pragma unroll
-        for (int j = 0; j < kRowsPerGroup; ++j)
+        for (int j = 0; j < kRowsPerWave; ++j)
             if (lcnt[j] >= kStageSlots / 2) flush_row(j);
     }
     __device__ __forceinline__ void flush_all() {
         if (kSample) return;
 #pragma unroll
-        for (int j = 0; j < kRowsPerGroup; ++j)
+        for (int j = 0; j < kRowsPerWave; ++j)
             if (lcnt[j] > 0) flush_row(j);
     }
 
-    // One tile: rows 0,1 of tile it run on the MFMA pipe under the epilogue of rows 2,3 of
-    // tile it-1, then rows 2,3 of tile it under the epilogue of rows 0,1 of tile it.
-    __device__ __forceinline__ void step(f32x16 (&acc)[kRowsPerGroup], const bf16x8 (&b)[8], int it) {
+    // One tile: each pair's MFMA chains run under the epilogue of the pair before (pair 3
+    // of tile it-1 for pair 0).
+    __device__ __forceinline__ void step(f32x16 (&acc)[kRowsPerWave], const bf16x8 (&b)[8], int it) {
         flush_full();
         mfma2<0>(acc, b);
-        epilogue2<2>(acc, it - 1);
+        epilogue2<6>(acc, it - 1);
         mfma2<2>(acc, b);
         epilogue2<0>(acc, it);
+        mfma2<4>(acc, b);
+        epilogue2<2>(acc, it);
+        mfma2<6>(acc, b);
+        epilogue2<4>(acc, it);
     }
 };
 
 template <bool kSample>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P) {
-    const int g = blockIdx.x;
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int n_groups) {
+    // Workgroups go round-robin over the 8 XCDs: XCDs 0-3 take key half 0, 4-7 half 1.
+    const int xcd = blockIdx.x & 7;
+    const int half = xcd >> 2;
+    const int g = (int)(blockIdx.x >> 3) * 4 + (xcd & 3);
+    if (g >= n_groups) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int hf = lane >> 5;
     const int col = lane & 31;
-    __shared__ __attribute__((aligned(16))) float s_w[kRowsPerGroup][2][16];
-    __shared__ uint2 s_stage[kSegs][kRowsPerGroup * kStageSlots];
+    const int segment = half * (kScoreThreads / kWave) + wave;
+    __shared__ __attribute__((aligned(16))) float s_w[kRowsPerWave][2][16];
+    __shared__ uint2 s_stage[kScoreThreads / kWave][kRowsPerWave * kStageSlots];
 
     const int seg = P.cap / kSegs;
-    uint32_t pr[kRowsPerGroup];
-    float tau_r[kRowsPerGroup];
-    int row_of[kRowsPerGroup];
-    bool live[kRowsPerGroup];
+    uint32_t pr[kRowsPerWave];
+    float tau_r[kRowsPerWave];
+    int row_of[kRowsPerWave];
+    bool live[kRowsPerWave];
     int64_t n_keys = 0;
-    const int r0 = g * kRowsPerGroup;
+    const int r0 = g * kRowsPerWave;
     uint32_t S = 0, n0 = 0;
 #pragma unroll
-    for (int j = 0; j < kRowsPerGroup; ++j) {
+    for (int j = 0; j < kRowsPerWave; ++j) {
         const int r = r0 + j;
         const bool valid = r < P.Lb;
         row_of[j] = valid ? r : r0;
@@ -356,18 +378,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P) {
         S = (uint32_t)sample_size(n0, P.top_k, P.cap);
         n_keys = S;
     }
-    if (threadIdx.x < kRowsPerGroup * 32) {
-        // Weights in the order each lane half reads them: head 8*(i/4) + 4*half + i%4.
+    // Weights in the order each lane half reads them: head 8*(i/4) + 4*half + i%4.
+    {
         const int j = threadIdx.x >> 5, h2 = (threadIdx.x >> 4) & 1, i = threadIdx.x & 15;
         s_w[j][h2][i] = P.w[(size_t)row_of[j] * kIdxHeads + 8 * (i >> 2) + 4 * h2 + (i & 3)];
     }
     __syncthreads();
 
-    int cnt[kRowsPerGroup] = {0, 0, 0, 0};
+    int cnt[kRowsPerWave] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (n_keys > 0) {
-        bf16x8 a[kRowsPerGroup][8];
+        bf16x8 a[kRowsPerWave][8];
 #pragma unroll
-        for (int j = 0; j < kRowsPerGroup; ++j) {
+        for (int j = 0; j < kRowsPerWave; ++j) {
             const u16x8* qp = reinterpret_cast<const u16x8*>(
                 P.q_idx + ((size_t)row_of[j] * kIdxHeads + col) * kIdxDim + hf * 64);
 #pragma unroll
@@ -376,33 +398,38 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P) {
                 asm volatile("" : "+a"(a[j][kk]));  // keep the query fragments in AGPRs
             }
         }
-        // Wave w scores the contiguous tile range [w*tpw, (w+1)*tpw): its candidate segment
-        // is then in ascending key order and the segments concatenate in order.
+        // Segment s covers the contiguous tile range [s*tps, (s+1)*tps).
         const int n_tiles = (int)((n_keys + kKeyTile - 1) / kKeyTile);
-        const int tpw = (n_tiles + kSegs - 1) / kSegs;
-        const int t0 = wave * tpw;
-        const int n_my = n_tiles > t0 ? min(n_tiles - t0, tpw) : 0;
+        const int tps = (n_tiles + kSegs - 1) / kSegs;
+        const int t0 = segment * tps;
+        const int n_my = n_tiles > t0 ? min(n_tiles - t0, tps) : 0;
         // Rows of a group are consecutive (invalid rows never store), so every row's
         // list is addressed from row 0's.
         ScoreTile<kSample> T{P, a, s_w,
-                             {hf ? pr[1] : pr[0], hf ? pr[3] : pr[2]},
-                             {hf ? tau_r[1] : tau_r[0], hf ? tau_r[3] : tau_r[2]},
-                             {hf ? live[1] : live[0], hf ? live[3] : live[2]},
+                             {hf ? pr[1] : pr[0], hf ? pr[3] : pr[2], hf ? pr[5] : pr[4], hf ? pr[7] : pr[6]},
+                             {hf ? tau_r[1] : tau_r[0], hf ? tau_r[3] : tau_r[2], hf ? tau_r[5] : tau_r[4],
+                              hf ? tau_r[7] : tau_r[6]},
+                             {hf ? live[1] : live[0], hf ? live[3] : live[2], hf ? live[5] : live[4],
+                              hf ? live[7] : live[6]},
                              kSample ? P.sample + (size_t)r0 * P.sample_stride : nullptr,
-                             kSample ? nullptr : P.cand + (size_t)r0 * P.cap + (size_t)wave * seg,
+                             kSample ? nullptr : P.cand + (size_t)r0 * P.cap + (size_t)segment * seg,
                              n0, S, kSample && S > 0 ? (float)n0 / (float)S : 0.f, lane, hf, col, seg, cnt,
-                             s_stage[wave], {0, 0, 0, 0}, {0, 0, 0, 0}, (uint32_t)t0};
+                             s_stage[wave], {0, 0, 0, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0, 0}, (uint32_t)t0};
         // Tile it sits in buffer it % 3; tile it+3 is loaded once tile it's MFMAs are issued.
         bf16x8 b0[8], b1[8], b2[8];
-        f32x16 acc[kRowsPerGroup];
+        f32x16 acc[kRowsPerWave];
         if (n_my > 0) {
             T.load(b0, 0);
             T.load(b1, 1);
             T.load(b2, 2);
             T.template mfma2<0>(acc, b0);
             T.template mfma2<2>(acc, b0);
-            T.load(b0, 3);
             T.template epilogue2<0>(acc, 0);
+            T.template mfma2<4>(acc, b0);
+            T.template epilogue2<2>(acc, 0);
+            T.template mfma2<6>(acc, b0);
+            T.load(b0, 3);
+            T.template epilogue2<4>(acc, 0);
             int it = 1;
             for (; it + 2 < n_my; it += 3) {
                 T.step(acc, b1, it);
@@ -414,15 +441,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P) {
             }
             if (it < n_my) T.step(acc, b1, it);
             if (it + 1 < n_my) T.step(acc, b2, it + 1);
-            T.flush_full();
-            T.template epilogue2<2>(acc, n_my - 1);
+            T.flush_full();  // the last epilogue adds up to 32 more entries to rows 6, 7
+            T.template epilogue2<6>(acc, n_my - 1);
             T.flush_all();
         }
     }
     if (!kSample && lane == 0) {
 #pragma unroll
-        for (int j = 0; j < kRowsPerGroup; ++j)
-            if (r0 + j < P.Lb) P.count[(size_t)(r0 + j) * kSegs + wave] = cnt[j];
+        for (int j = 0; j < kRowsPerWave; ++j)
+            if (r0 + j < P.Lb) P.count[(size_t)(r0 + j) * kSegs + segment] = cnt[j];
     }
 }
 
@@ -986,7 +1013,7 @@ __device__ void write_sorted_output(int* sel, int k, int32_t* out_row) {
 constexpr int kSelBand = 1024;
 constexpr int kSelChunk = 16;  // candidates per thread: the block has cap / 16 threads
 
-// Exact top-k of one row's candidates.  The four segments written by the scoring waves
+// Exact top-k of one row's candidates.  The eight segments written by the scoring waves
 // are each in ascending key order and cover ascending key ranges, so their concatenation
 // is sorted by key: thread t holds positions [16t, 16t+16) of it in registers, and the
 // ascending output is a stable compaction (one block scan) of the selected positions.
@@ -1254,9 +1281,10 @@ hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks,
 
 hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s) {
     const int groups = (a.Lb + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int score_wgs = 8 * ((groups + 3) / 4);  // two key halves per group, XCD-mapped
     if (need_sample) {
         ProfScope ps(s, kProfScoreSample);
-        score_kernel<true><<<groups, kScoreThreads, 0, s>>>(a);
+        score_kernel<true><<<score_wgs, kScoreThreads, 0, s>>>(a, groups);
     }
     {
         ProfScope ps(s, kProfRowPrep);
@@ -1264,7 +1292,7 @@ hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStrea
     }
     {
         ProfScope ps(s, kProfScoreFilter);
-        score_kernel<false><<<groups, kScoreThreads, 0, s>>>(a);
+        score_kernel<false><<<score_wgs, kScoreThreads, 0, s>>>(a, groups);
     }
     {
         ProfScope ps(s, kProfSelect);

@@ -114,6 +114,11 @@ def test_c4_sampled_rows(dsa_gpu, oracle_mod):
     dict(N=20000, L=13, top_k=100, kind="int"),                # integer ties, small k
     dict(N=1, L=1, top_k=5, kind="gauss"),                     # single key
     dict(N=40000, L=6, top_k=2048, kind="concentrated"),
+    # elements scaled by 2^-24..2^24: the dot products need more than 53 bits, so the band
+    # re-score takes the sequential fp64 evaluation (in select, and in the fold when the
+    # band outgrows select's buffer)
+    dict(N=1000, L=8, top_k=64, kind="wide"),
+    dict(N=3000, L=8, top_k=64, kind="wide"),
 ])
 def test_edge_cases(dsa_gpu, oracle_mod, case):
     q_pos0 = case.get("q_pos0", case["N"] - case["L"])
