@@ -176,8 +176,7 @@ __global__ __launch_bounds__(256) void key_stats_kernel(const uint16_t* __restri
 // (l >> 5) holds dimensions [64*half, 64*half+64) of both, eight MFMA K-steps of 8.  Key
 // tiles are loaded straight into the B layout, three tiles ahead.  The 8 rows' query
 // fragments fill the AGPRs (the MFMAs read A operands from there directly), leaving the
-// VGPRs to the accumulators and the key tiles; the head weights are read from LDS in
-// the epilogue.
+// VGPRs to the accumulators and the key tiles; the head weights are read from LDS.
 //
 // The rows run as four pairs: the MFMA chains of one pair execute under the epilogue
 // (ReLU, weighted head sum, filter) of the previous pair.  After the cross-half add both
@@ -245,9 +244,6 @@ struct ScoreTile {
     template <int J0>
     __device__ __forceinline__ void epilogue2(const f32x16 (&acc)[kRowsPerWave], int it) {
         const uint32_t pos = pos_of(it);
-        // The weights are re-read from LDS here; held across the loop they would take
-        // 128 VGPRs.
-        asm volatile("" ::: "memory");
         float sc[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
@@ -318,13 +314,17 @@ struct ScoreTile {
     }
 
     // One tile: each pair's MFMA chains run under the epilogue of the pair before (pair 3
-    // of tile it-1 for pair 0).
+    // of tile it-1 for pair 0).  The head weights are read from LDS; the two compiler
+    // memory barriers let each half-step's weight reads start early without hoisting all
+    // of them out of the loop (held across it they would take 128 VGPRs).
     __device__ __forceinline__ void step(f32x16 (&acc)[kRowsPerWave], const bf16x8 (&b)[8], int it) {
         flush_full();
+        asm volatile("" ::: "memory");
         mfma2<0>(acc, b);
         epilogue2<6>(acc, it - 1);
         mfma2<2>(acc, b);
         epilogue2<0>(acc, it);
+        asm volatile("" ::: "memory");
         mfma2<4>(acc, b);
         epilogue2<2>(acc, it);
         mfma2<6>(acc, b);
