@@ -59,6 +59,12 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     const int64_t p = A.pos0 + t;
     const bool compute = wave < A.H / 16;
     const int h = wave * 16 + c16;
+    // The K order of the value product (and, to match, the row order of the logits):
+    // lane group g takes tile rows slot_row(g, 0..3) and 16 + those.  Groups 0, 1 get the
+    // even rows 0..14 and groups 2, 3 the odd ones, so the transpose reads of each lane
+    // pair of groups land on disjoint LDS banks with the 1168-byte row stride.
+    auto slot_row = [](int grp, int j) { return 8 * (grp & 1) + 2 * j + (grp >> 1); };
+    const int pi_c = slot_row(c16 >> 2, c16 & 3);  // A-operand row of lane c16 in the logits
 
     __shared__ __attribute__((aligned(16))) uint16_t Kbuf[2][kAttnTile][kKrowStride];
     __shared__ int s_idx[3][kAttnTile];  // raw top-k entries of three consecutive tiles
@@ -128,20 +134,21 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
             f32x4 s0 = f32x4{}, s1 = f32x4{};
 #pragma unroll
             for (int ks = 0; ks < kDqk / 32; ++ks) {
-                const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&Kbuf[cur][c16][ks * 32 + 8 * g]));
-                const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&Kbuf[cur][16 + c16][ks * 32 + 8 * g]));
+                const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&Kbuf[cur][pi_c][ks * 32 + 8 * g]));
+                const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&Kbuf[cur][16 + pi_c][ks * 32 + 8 * g]));
                 s0 = mfma_16x16x32(a0, qf[ks], s0);
                 s1 = mfma_16x16x32(a1, qf[ks], s1);
             }
             // Usable entries of the tile as a bit mask (bit r: entry r), one ballot per wave.
             const uint32_t vmask = (uint32_t)__ballot(lane < kAttnTile && key_of(slot, lane & 31, tile * kAttnTile) >= 0);
-            const uint32_t mlo = vmask >> (4 * g), mhi = vmask >> (16 + 4 * g);
+            // Element r of this lane's logits is tile row slot_row(g, r) (s0) or 16 + that (s1).
+            const uint32_t mlo = vmask >> slot_row(g, 0), mhi = vmask >> (16 + slot_row(g, 0));
             float lg[8];
             float tmax = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                lg[r] = (mlo >> r) & 1u ? s0[r] * sl2 : -INFINITY;
-                lg[4 + r] = (mhi >> r) & 1u ? s1[r] * sl2 : -INFINITY;
+                lg[r] = (mlo >> (2 * r)) & 1u ? s0[r] * sl2 : -INFINITY;
+                lg[4 + r] = (mhi >> (2 * r)) & 1u ? s1[r] * sl2 : -INFINITY;
             }
 #pragma unroll
             for (int r = 0; r < 8; ++r) tmax = fmaxf(tmax, lg[r]);
@@ -184,9 +191,9 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
             lsum += ps;
             lexp += pe;
             const bf16x8 pbf = __builtin_bit_cast(bf16x8, pb);
-            // Source lane (g, c16) addresses row kb + c16/4, columns 4*(c16%4)..+4 of each
-            // 16-column block, kb = 4g (K slots 0-3 of its group) or 16 + 4g (slots 4-7).
-            const uint16_t* vlo = &Kbuf[cur][4 * g + (c16 >> 2)][4 * (c16 & 3)];
+            // Source lane (g, c16) addresses row slot_row(g, c16/4) (K slots 0-3 of its group)
+            // or 16 + that (slots 4-7), columns 4*(c16%4)..+4 of each 16-column block.
+            const uint16_t* vlo = &Kbuf[cur][slot_row(g, c16 >> 2)][4 * (c16 & 3)];
             const uint16_t* vhi = vlo + 16 * kKrowStride;
 #pragma unroll
             for (int dt = 0; dt < kDv / 16; ++dt) {
