@@ -123,18 +123,30 @@ __global__ __launch_bounds__(256) void key_stats_kernel(const uint16_t* __restri
     float nmax = 0.f, amax = 0.f;
     int emin = INT_MAX;
     const int64_t rows_per_step = (int64_t)gridDim.x * (blockDim.x >> 4);
+    // Four rows per pass, loads issued together (rows past the end re-read the last row,
+    // which changes no maximum or minimum).
+    constexpr int kU = 4;
     for (int64_t s = (int64_t)blockIdx.x * (blockDim.x >> 4) + (threadIdx.x >> 4); s < n_keys;
-         s += rows_per_step) {
-        const u16x8 v = reinterpret_cast<const u16x8*>(k_idx + s * kIdxDim)[sub];
-        float ss = 0.f;
-        for (int j = 0; j < 8; ++j) {
-            const float x = bf16_bits_to_float(v[j]);
-            ss = fmaf(x, x, ss);
-            amax = fmaxf(amax, fabsf(x));
-            if ((v[j] & 0x7fff) != 0) emin = min(emin, bf16_lsb_exp(v[j]));
+         s += kU * rows_per_step) {
+        u16x8 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t row = min(s + u * rows_per_step, n_keys - 1);
+            v[u] = reinterpret_cast<const u16x8*>(k_idx + row * kIdxDim)[sub];
         }
-        for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
-        nmax = fmaxf(nmax, sqrtf(ss));
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = bf16_bits_to_float(v[u][j]);
+                ss = fmaf(x, x, ss);
+                amax = fmaxf(amax, fabsf(x));
+                if ((v[u][j] & 0x7fff) != 0) emin = min(emin, bf16_lsb_exp(v[u][j]));
+            }
+            for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
+            nmax = fmaxf(nmax, sqrtf(ss));
+        }
     }
     nmax = wave_max(nmax);
     amax = wave_max(amax);
