@@ -24,12 +24,20 @@ __host__ __device__ inline int cand_capacity(int top_k) {
 
 constexpr int kRowsPerGroup = 8;  // indexer query rows scored together (one sample each)
 
+// Sample keys expected above the threshold: the threshold is the sample's rank-r score
+// with r about kSampleRank, estimating the 2.5 k-th score of the row.  The true k-th score
+// sits near sample rank kSampleRank / 2.5 (~51, std ~7), so the threshold falls below it
+// with overwhelming probability.  The candidate count (2.5 k, relative std ~1/11) is
+// spread over 8 segments of cap/8 = 1.6 x their mean; a smaller sample (r = 64) was
+// measured to overflow segments and send rows to the fold.
+constexpr int kSampleRank = 128;
+
 // Keys scored in the threshold sample of a row group whose first row sees n_t keys.
 // Groups whose first row sees at most cap - kRowsPerGroup keys are not sampled: every row
 // of such a group sees at most cap keys, so all its causal keys fit the candidate buffer.
 __host__ __device__ inline int sample_size(int64_t n_t, int top_k, int cap) {
     if (n_t <= cap - kRowsPerGroup) return 0;
-    int64_t s = (int64_t)((n_t * 128 + (int64_t)(2.5 * top_k) - 1) / (int64_t)(2.5 * top_k));
+    int64_t s = (int64_t)((n_t * kSampleRank + (int64_t)(2.5 * top_k) - 1) / (int64_t)(2.5 * top_k));
     if (s < 1024) s = 1024;
     if (s > 16384) s = 16384;
     if (s > n_t) s = n_t;
