@@ -213,10 +213,13 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
     a.fold_bs = reinterpret_cast<double*>(ws + lay.off_fold_bs);
     a.fold_bf = reinterpret_cast<float*>(ws + lay.off_fold_bf);
 
-    // Key statistics over every key any query of the chunk may see.
+    // Key statistics and the tiled key copy, over every key any query of the chunk may see.
     const int64_t last = q_pos0 + L - 1;
     const int64_t n_keys = (last < N - 1 ? last : N - 1) + 1;
-    hipError_t e = dsa::launch_key_stats(k_idx, n_keys, a.kstats, s);
+    uint16_t* k_tile = reinterpret_cast<uint16_t*>(ws + lay.off_ktile);
+    a.k_tile = k_tile;
+    a.n_ktiles = (n_keys + dsa::kKeyTileKeys - 1) / dsa::kKeyTileKeys;
+    hipError_t e = dsa::launch_key_stats(k_idx, n_keys, a.kstats, k_tile, s);
     if (e != hipSuccess) return hip_fail(e, "key statistics launch");
 
     for (int64_t b0 = 0; b0 < L; b0 += qb) {

@@ -58,10 +58,20 @@ constexpr int kFallbackSlots = 32;
 constexpr int kFoldKeys = 4096;
 constexpr int kCandSegs = 8;  // candidate segments per row: 2 key halves x 4 scoring waves
 
+// Indexer keys are re-laid out once per call as 32-key tiles of 8 KB in the order the
+// scoring MFMA's B operand is loaded: [tile][k-step 0..7][lane 0..63][8 bf16], where lane
+// l = 32*hf + c holds key 32*tile + c, dims 64*hf + 8*kstep .. +7.  Every scoring load
+// instruction then reads 1 KB of consecutive bytes.
+constexpr int kKeyTileKeys = 32;
+constexpr size_t kKeyTileBytes = (size_t)kKeyTileKeys * 128 * 2;
+__host__ __device__ inline size_t key_tile_bytes(int64_t n_keys) {
+    return (size_t)((n_keys + kKeyTileKeys - 1) / kKeyTileKeys) * kKeyTileBytes;
+}
+
 struct IndexerLayout {
     int rows, cap, sample_stride, fold_cap;
     size_t off_kstats, off_tau, off_delta, off_mode, off_count, off_fbctrl, off_fblist;
-    size_t off_sample, off_cand;
+    size_t off_sample, off_cand, off_ktile;
     size_t off_fold_s, off_fold_i, off_fold_bi, off_fold_bs, off_fold_bf;
     size_t total;
 
@@ -82,6 +92,7 @@ struct IndexerLayout {
         l.off_fblist = o; o = al(o + 4 * (size_t)l.rows);
         l.off_sample = o; o = al(o + 4 * (size_t)l.rows * (size_t)l.sample_stride);
         l.off_cand = o; o = al(o + 8 * (size_t)l.rows * (size_t)l.cap);
+        l.off_ktile = o; o = al(o + key_tile_bytes(N));
         l.off_fold_s = o; o = al(o + 4 * (size_t)kFallbackSlots * 2 * l.fold_cap);
         l.off_fold_i = o; o = al(o + 4 * (size_t)kFallbackSlots * 2 * l.fold_cap);
         l.off_fold_bi = o; o = al(o + 4 * (size_t)kFallbackSlots * l.fold_cap);
@@ -95,6 +106,8 @@ struct IndexerLayout {
 struct IndexerArgs {
     const uint16_t* q_idx;  // rows of this block: [Lb][32][128]
     const uint16_t* k_idx;  // [N][128]
+    const uint16_t* k_tile; // keys 0..n_ktiles*32-1 in scoring tile order (pad keys zero)
+    int64_t n_ktiles;
     const float* w;         // [Lb][32]
     int32_t* out;           // [Lb][top_k]
     int64_t N;
@@ -137,7 +150,7 @@ struct ProfScope {
 };
 
 // Kernel launchers (indexer.hip).  Each returns the launch status.
-hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, hipStream_t s);
+hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, uint16_t* k_tile, hipStream_t s);
 hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s);
 hipError_t launch_causal_mask(int32_t* idx, int64_t L, int top_k, int64_t q_pos0, hipStream_t s);
 

@@ -107,18 +107,33 @@ __device__ double canonical_head_term(const uint16_t* __restrict__ q_h,
 
 // ------------------------------------------------------------------ 1. key stats
 
-__global__ void init_stats_kernel(KeyStats* ks) {
+static_assert(kKeyTileKeys == kKeyTile, "scoring tiles and the tiled key copy disagree");
+
+// Chunk c (dims 8c..8c+7) of key `key` in the scoring tile order.
+__device__ __forceinline__ void store_key_tile_chunk(uint16_t* k_tile, int64_t key, int c, u16x8 v) {
+    const int64_t t = key / kKeyTileKeys;
+    const int lane = (c >> 3) * 32 + (int)(key % kKeyTileKeys);
+    reinterpret_cast<u16x8*>(k_tile)[t * (kKeyTileBytes / 16) + (c & 7) * 64 + lane] = v;
+}
+
+__global__ void init_stats_kernel(KeyStats* ks, uint16_t* k_tile, int64_t n_keys) {
     if (threadIdx.x == 0) {
         ks->knorm_bits = 0u;
         ks->kinf_bits = 0u;
         ks->kexp_min = INT_MAX;
         ks->pad = 0;
     }
+    // Zero the pad keys of the last tile (16 chunks of 16 bytes per key).
+    const int64_t n_pad = (kKeyTileKeys - n_keys % kKeyTileKeys) % kKeyTileKeys;
+    for (int i = threadIdx.x; i < (int)n_pad * 16; i += blockDim.x)
+        store_key_tile_chunk(k_tile, n_keys + i / 16, i % 16, u16x8{});
 }
 
-// 16 lanes per key row (16 bytes each, so a wave reads 4 whole rows per load).
+// 16 lanes per key row (16 bytes each, so a wave reads 4 whole rows per load).  Each
+// row is also written to its place in the scoring tiles.
 __global__ __launch_bounds__(256) void key_stats_kernel(const uint16_t* __restrict__ k_idx,
-                                                        int64_t n_keys, KeyStats* ks) {
+                                                        int64_t n_keys, KeyStats* ks,
+                                                        uint16_t* __restrict__ k_tile) {
     const int sub = threadIdx.x & 15;
     float nmax = 0.f, amax = 0.f;
     int emin = INT_MAX;
@@ -134,6 +149,9 @@ __global__ __launch_bounds__(256) void key_stats_kernel(const uint16_t* __restri
             const int64_t row = min(s + u * rows_per_step, n_keys - 1);
             v[u] = reinterpret_cast<const u16x8*>(k_idx + row * kIdxDim)[sub];
         }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            if (s + u * rows_per_step < n_keys) store_key_tile_chunk(k_tile, s + u * rows_per_step, sub, v[u]);
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             float ss = 0.f;
@@ -202,11 +220,41 @@ constexpr int kKeyHalves = 2;
 constexpr int kStageSlots = 64;  // LDS staging entries per (wave, row) for filter survivors
 static_assert(kKeyHalves * (kScoreThreads / kWave) == kSegs, "one candidate segment per (half, wave)");
 
+// sum_e w_e * r[e] with e ascending (fused multiply-adds), where lane 16g + e of W holds w_e
+// for the lanes of its 16-lane row g: DPP row_newbcast:e hands that lane's value to every
+// lane of the row, so the weights take one register per query row instead of 16.  A DPP
+// source needs two wait states after a VALU write of it; W is written once, before the
+// scoring loop, and the build checks the generated code for any closer write.
+__device__ __forceinline__ float weighted_head_sum(float W, const float (&r)[16]) {
+    float p;
+    asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %4 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %6 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %7 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %8 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %9 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+        : "=&v"(p)
+        : "v"(W), "v"(r[0]), "v"(r[1]), "v"(r[2]), "v"(r[3]), "v"(r[4]), "v"(r[5]), "v"(r[6]), "v"(r[7]));
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %3 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %4 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %7 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %8 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %9 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+        : "+v"(p)
+        : "v"(W), "v"(r[8]), "v"(r[9]), "v"(r[10]), "v"(r[11]), "v"(r[12]), "v"(r[13]), "v"(r[14]), "v"(r[15]));
+    return p;
+}
+
 template <bool kSample>
 struct ScoreTile {
     const IndexerArgs& P;
     const bf16x8 (&a)[kRowsPerWave][8];
-    const float (*s_w)[2][16];
+    const float (&wl)[kRowsPerWave];  // per row: lane 16g + e holds the weight of its half's head e
     // Per lane half: parameters of row 2q + hf of row pair q.
     uint32_t pr_m[kPairs];   // last causal key
     float tau_m[kPairs];     // candidate threshold
@@ -227,15 +275,20 @@ struct ScoreTile {
     __device__ __forceinline__ uint32_t pos_of(int it) const { return (tile0 + (uint32_t)it) * kKeyTile + col; }
 
     // Tile indices past the wave's range still address valid keys (clamped), so callers
-    // need no guard.
+    // need no guard.  The filter reads the tiled key copy (1 KB per load instruction); the
+    // sample's strided keys come from the row-major keys.
     __device__ __forceinline__ void load(bf16x8 (&b)[8], int it) const {
-        const uint32_t pos = pos_of(it);
-        uint32_t key;
-        if (kSample) key = min((uint32_t)((float)pos * s_ratio), n0 - 1u);  // strided sample
-        else key = pos < (uint32_t)P.N ? pos : (uint32_t)P.N - 1u;
-        const u16x8* kp = reinterpret_cast<const u16x8*>(P.k_idx + (size_t)key * kIdxDim + hf * 64);
+        if (kSample) {
+            const uint32_t key = min((uint32_t)((float)pos_of(it) * s_ratio), n0 - 1u);
+            const u16x8* kp = reinterpret_cast<const u16x8*>(P.k_idx + (size_t)key * kIdxDim + hf * 64);
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) b[kk] = __builtin_bit_cast(bf16x8, kp[kk]);
+            for (int kk = 0; kk < 8; ++kk) b[kk] = __builtin_bit_cast(bf16x8, kp[kk]);
+        } else {
+            const uint32_t t = min(tile0 + (uint32_t)it, (uint32_t)P.n_ktiles - 1u);
+            const u16x8* kp = reinterpret_cast<const u16x8*>(P.k_tile) + (size_t)t * (kKeyTileBytes / 16) + lane;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) b[kk] = __builtin_bit_cast(bf16x8, kp[kk * 64]);
+        }
     }
 
     // MFMA chains of rows J0 and J0+1 over one key tile, interleaved.
@@ -260,15 +313,11 @@ struct ScoreTile {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int j = J0 + jj;
-            const f32x4* wv = reinterpret_cast<const f32x4*>(&s_w[j][hf][0]);
-            float part = 0.f;
+            float r[16];
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 w4 = wv[q4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)  // ReLU on the bit pattern: negatives and -0 -> +0
-                    part += w4[e] * __int_as_float(max(__float_as_int(acc[j][q4 * 4 + e]), 0));
-            }
+            for (int e = 0; e < 16; ++e)  // ReLU on the bit pattern: negatives and -0 -> +0
+                r[e] = __int_as_float(max(__float_as_int(acc[j][e]), 0));
+            const float part = weighted_head_sum(wl[j], r);
             auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
             sc[jj] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + 0.0f;
         }
@@ -326,9 +375,8 @@ struct ScoreTile {
     }
 
     // One tile: each pair's MFMA chains run under the epilogue of the pair before (pair 3
-    // of tile it-1 for pair 0).  The head weights are read from LDS; the two compiler
-    // memory barriers let each half-step's weight reads start early without hoisting all
-    // of them out of the loop (held across it they would take 128 VGPRs).
+    // of tile it-1 for pair 0).  The two compiler memory barriers keep each half-step's
+    // staging-list accesses in their half-step (measured slightly faster than without).
     __device__ __forceinline__ void step(f32x16 (&acc)[kRowsPerWave], const bf16x8 (&b)[8], int it) {
         flush_full();
         asm volatile("" ::: "memory");
@@ -396,6 +444,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
         s_w[j][h2][i] = P.w[(size_t)row_of[j] * kIdxHeads + 8 * (i >> 2) + 4 * h2 + (i & 3)];
     }
     __syncthreads();
+    float wl[kRowsPerWave];
+#pragma unroll
+    for (int j = 0; j < kRowsPerWave; ++j) wl[j] = s_w[j][hf][lane & 15];
 
     int cnt[kRowsPerWave] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (n_keys > 0) {
@@ -417,7 +468,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
         const int n_my = n_tiles > t0 ? min(n_tiles - t0, tps) : 0;
         // Rows of a group are consecutive (invalid rows never store), so every row's
         // list is addressed from row 0's.
-        ScoreTile<kSample> T{P, a, s_w,
+        ScoreTile<kSample> T{P, a, wl,
                              {hf ? pr[1] : pr[0], hf ? pr[3] : pr[2], hf ? pr[5] : pr[4], hf ? pr[7] : pr[6]},
                              {hf ? tau_r[1] : tau_r[0], hf ? tau_r[3] : tau_r[2], hf ? tau_r[5] : tau_r[4],
                               hf ? tau_r[7] : tau_r[6]},
@@ -1281,13 +1332,14 @@ __global__ void causal_mask_kernel(int32_t* idx, int64_t L, int top_k, int64_t q
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, hipStream_t s) {
+hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, uint16_t* k_tile,
+                             hipStream_t s) {
     ProfScope ps(s, kProfKeyStats);
-    init_stats_kernel<<<1, 64, 0, s>>>(ks);
+    init_stats_kernel<<<1, 64, 0, s>>>(ks, k_tile, n_keys);
     int blocks = (int)((n_keys + 15) / 16);
     if (blocks > 1024) blocks = 1024;
     if (blocks < 1) blocks = 1;
-    key_stats_kernel<<<blocks, 256, 0, s>>>(k_idx, n_keys, ks);
+    key_stats_kernel<<<blocks, 256, 0, s>>>(k_idx, n_keys, ks, k_tile);
     return hipGetLastError();
 }
 
