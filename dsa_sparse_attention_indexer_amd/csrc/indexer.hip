@@ -256,8 +256,7 @@ struct ScoreTile {
     const bf16x8 (&a)[kRowsPerWave][8];
     const float (&wl)[kRowsPerWave];  // per row: lane 16g + e holds the weight of its half's head e
     // Per lane half: parameters of row 2q + hf of row pair q.
-    uint32_t pr_m[kPairs];   // last causal key
-    float tau_m[kPairs];     // candidate threshold
+    float tau_m[kPairs];     // candidate threshold (+inf for rows the filter skips)
     bool live_m[kPairs];
     float* sample0;     // sample: row 0's sample list (rows are sample_stride apart)
     uint2* cand0;       // filter: row 0's segment (rows are cap apart)
@@ -265,6 +264,8 @@ struct ScoreTile {
     uint32_t S;         // sample: sample size
     float s_ratio;      // sample: key stride n0 / S (any in-range keys would do)
     int lane, hf, col;
+    int colm;           // col - hf
+    int first_pos;      // position of the group's first row
     int seg;
     int (&cnt)[kRowsPerWave];   // survivors so far per row (including any past seg)
     uint2* lbuf;                // filter: this wave's LDS staging lists, kStageSlots per row
@@ -309,27 +310,34 @@ struct ScoreTile {
     template <int J0>
     __device__ __forceinline__ void epilogue2(const f32x16 (&acc)[kRowsPerWave], int it) {
         const uint32_t pos = pos_of(it);
-        float sc[2];
+        float part[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const int j = J0 + jj;
             float r[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e)  // ReLU on the bit pattern: negatives and -0 -> +0
-                r[e] = __int_as_float(max(__float_as_int(acc[j][e]), 0));
-            const float part = weighted_head_sum(wl[j], r);
-            auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-            sc[jj] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + 0.0f;
+                r[e] = __int_as_float(max(__float_as_int(acc[J0 + jj][e]), 0));
+            part[jj] = weighted_head_sum(wl[J0 + jj], r);
         }
-        // Lane half hf handles row J0 + hf from here on (selects, not branches).
-        const float s_mine = hf ? sc[1] : sc[0];
+        // Each lane half holds its 16 heads' partial sum of both rows.  One swap of the
+        // upper half of row J0 with the lower half of row J0+1 leaves lane half hf with
+        // both partial sums of row J0 + hf, which handles that row from here on.
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]),
+                                                         false, false);
+        const float s_mine = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + 0.0f;
         const uint32_t j_mine = J0 + hf;
         constexpr int q = J0 / 2;
         if (kSample) {
             if (pos < S && live_m[q]) sample0[j_mine * (uint32_t)P.sample_stride + pos] = s_mine;
         } else {
-            const bool keep = live_m[q] && pos <= pr_m[q] && s_mine >= tau_m[q];
-            const uint64_t m = __ballot(keep);
+            // Rows not scored here have an infinite threshold.  Causality, pos <= p_row
+            // with p_row = first_pos + J0 + hf, is tested as col - hf <= first_pos + J0 -
+            // 32 * tile: one compare against a wave-uniform bound.
+            const int lim = first_pos + J0 - (int)((tile0 + (uint32_t)it) * kKeyTile);
+            // (Two ballots of single compares: each is the compare's own lane mask.)
+            const bool above = s_mine >= tau_m[q], causal = colm <= lim;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(above) & __builtin_amdgcn_ballot_w64(causal);
+            const bool keep = above && causal;
             if (m) {
                 const uint32_t m0 = (uint32_t)m, m1 = (uint32_t)(m >> 32);
                 // Slot within the row's staging list: entries already staged plus the
@@ -408,7 +416,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
     __shared__ uint2 s_stage[kScoreThreads / kWave][kRowsPerWave * kStageSlots];
 
     const int seg = P.cap / kSegs;
-    uint32_t pr[kRowsPerWave];
     float tau_r[kRowsPerWave];
     int row_of[kRowsPerWave];
     bool live[kRowsPerWave];
@@ -421,7 +428,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
         const bool valid = r < P.Lb;
         row_of[j] = valid ? r : r0;
         const int64_t p = P.pos0 + r;  // <= N - 1
-        pr[j] = valid ? (uint32_t)p : 0u;
         if (kSample) {
             live[j] = valid;
             tau_r[j] = 0.f;
@@ -469,14 +475,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
         // Rows of a group are consecutive (invalid rows never store), so every row's
         // list is addressed from row 0's.
         ScoreTile<kSample> T{P, a, wl,
-                             {hf ? pr[1] : pr[0], hf ? pr[3] : pr[2], hf ? pr[5] : pr[4], hf ? pr[7] : pr[6]},
                              {hf ? tau_r[1] : tau_r[0], hf ? tau_r[3] : tau_r[2], hf ? tau_r[5] : tau_r[4],
                               hf ? tau_r[7] : tau_r[6]},
                              {hf ? live[1] : live[0], hf ? live[3] : live[2], hf ? live[5] : live[4],
                               hf ? live[7] : live[6]},
                              kSample ? P.sample + (size_t)r0 * P.sample_stride : nullptr,
                              kSample ? nullptr : P.cand + (size_t)r0 * P.cap + (size_t)segment * seg,
-                             n0, S, kSample && S > 0 ? (float)n0 / (float)S : 0.f, lane, hf, col, seg, cnt,
+                             n0, S, kSample && S > 0 ? (float)n0 / (float)S : 0.f, lane, hf, col, col - hf,
+                             (int)(P.pos0 + r0), seg, cnt,
                              s_stage[wave], {0, 0, 0, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0, 0}, (uint32_t)t0};
         // Tile it sits in buffer it % 3; tile it+3 is loaded once tile it's MFMAs are issued.
         bf16x8 b0[8], b1[8], b2[8];
