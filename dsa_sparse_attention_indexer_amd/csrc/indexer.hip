@@ -250,6 +250,18 @@ __device__ __forceinline__ float weighted_head_sum(float W, const float (&r)[16]
     return p;
 }
 
+// Scheduling pattern for the region ending here (the next pair's 16 MFMAs and this
+// pair's epilogue): one MFMA, then two VALU instructions, repeated.  Spreading the
+// epilogue thinly keeps the matrix pipe fed (the default schedule bunches the VALU work
+// and leaves the last MFMAs back to back).
+__device__ __forceinline__ void interleave_with_mfma() {
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x2, 2, 0);  // VALU
+    }
+}
+
 template <bool kSample>
 struct ScoreTile {
     const IndexerArgs& P;
@@ -327,6 +339,7 @@ struct ScoreTile {
         const float s_mine = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + 0.0f;
         const uint32_t j_mine = J0 + hf;
         constexpr int q = J0 / 2;
+        interleave_with_mfma();
         if (kSample) {
             if (pos < S && live_m[q]) sample0[j_mine * (uint32_t)P.sample_stride + pos] = s_mine;
         } else {
