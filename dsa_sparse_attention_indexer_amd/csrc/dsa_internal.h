@@ -15,6 +15,14 @@ struct KeyStats {
     int pad;
 };
 
+// The key-statistics blocks fold their results into kStatSlots partial slots (block b into
+// slot b % kStatSlots), each on its own 128-byte line, so no address takes more than a few
+// dozen atomics; the consumer reduces the slots.
+constexpr int kStatSlots = 64;
+struct alignas(128) KeyStatsSlot {
+    KeyStats s;
+};
+
 // Candidate capacity per query row: expected candidates are 2.5 * top_k.
 __host__ __device__ inline int cand_capacity(int top_k) {
     int c = 4 * top_k;
@@ -83,7 +91,7 @@ struct IndexerLayout {
         l.sample_stride = sample_size(N, top_k, l.cap);
         l.fold_cap = top_k + kFoldKeys;
         size_t o = 0;
-        l.off_kstats = o; o = al(o + sizeof(KeyStats));
+        l.off_kstats = o; o = al(o + sizeof(KeyStatsSlot) * kStatSlots);
         l.off_tau = o; o = al(o + 4 * (size_t)l.rows);
         l.off_delta = o; o = al(o + 4 * (size_t)l.rows);
         l.off_mode = o; o = al(o + 4 * (size_t)l.rows);
@@ -118,7 +126,7 @@ struct IndexerArgs {
     int sample_stride;
     int fold_cap;
     int force_fallback;     // debug: send every scored row through the fallback fold
-    KeyStats* kstats;
+    KeyStatsSlot* kstats;   // [kStatSlots] partial key statistics
     float* tau;
     float* delta;
     int* mode;
@@ -150,7 +158,7 @@ struct ProfScope {
 };
 
 // Kernel launchers (indexer.hip).  Each returns the launch status.
-hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, uint16_t* k_tile, hipStream_t s);
+hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStatsSlot* ks, uint16_t* k_tile, hipStream_t s);
 hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s);
 hipError_t launch_causal_mask(int32_t* idx, int64_t L, int top_k, int64_t q_pos0, hipStream_t s);
 

@@ -116,12 +116,12 @@ __device__ __forceinline__ void store_key_tile_chunk(uint16_t* k_tile, int64_t k
     reinterpret_cast<u16x8*>(k_tile)[t * (kKeyTileBytes / 16) + (c & 7) * 64 + lane] = v;
 }
 
-__global__ void init_stats_kernel(KeyStats* ks, uint16_t* k_tile, int64_t n_keys) {
-    if (threadIdx.x == 0) {
-        ks->knorm_bits = 0u;
-        ks->kinf_bits = 0u;
-        ks->kexp_min = INT_MAX;
-        ks->pad = 0;
+__global__ void init_stats_kernel(KeyStatsSlot* ks, uint16_t* k_tile, int64_t n_keys) {
+    for (int i = threadIdx.x; i < kStatSlots; i += blockDim.x) {
+        ks[i].s.knorm_bits = 0u;
+        ks[i].s.kinf_bits = 0u;
+        ks[i].s.kexp_min = INT_MAX;
+        ks[i].s.pad = 0;
     }
     // Zero the pad keys of the last tile (16 chunks of 16 bytes per key).
     const int64_t n_pad = (kKeyTileKeys - n_keys % kKeyTileKeys) % kKeyTileKeys;
@@ -132,7 +132,7 @@ __global__ void init_stats_kernel(KeyStats* ks, uint16_t* k_tile, int64_t n_keys
 // 16 lanes per key row (16 bytes each, so a wave reads 4 whole rows per load).  Each
 // row is also written to its place in the scoring tiles.
 __global__ __launch_bounds__(256) void key_stats_kernel(const uint16_t* __restrict__ k_idx,
-                                                        int64_t n_keys, KeyStats* ks,
+                                                        int64_t n_keys, KeyStatsSlot* slots,
                                                         uint16_t* __restrict__ k_tile) {
     const int sub = threadIdx.x & 15;
     float nmax = 0.f, amax = 0.f;
@@ -186,6 +186,7 @@ __global__ __launch_bounds__(256) void key_stats_kernel(const uint16_t* __restri
         }
         // 128 fp32 squares+adds and the sqrt: relative error < 2^-16; pad by 2^-14.
         const float up = nmax * (1.0f + 1.0f / 16384.0f);
+        KeyStats* ks = &slots[blockIdx.x % kStatSlots].s;
         atomicMax(&ks->knorm_bits, __float_as_uint(up));
         atomicMax(&ks->kinf_bits, __float_as_uint(amax));
         atomicMin(&ks->kexp_min, emin);
@@ -968,7 +969,60 @@ __device__ bool select_core(const CandList& L, int k, float delta, const uint16_
 
 // ------------------------------------------------------------------ 3. row prep
 
-__global__ __launch_bounds__(256) void row_prep_kernel(IndexerArgs P) {
+// Order-preserving unsigned key of a float (larger float, larger key) and its inverse.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// A value no larger than the rk-th largest of vals[0..n) (1 <= rk <= n <= 64 * 256), for
+// a block of 256 threads: three 8-bit radix passes over the order-preserving keys find the
+// bucket of 2^8 keys holding that value, and its lowest key is returned (at most 2^-15
+// relative below the value).  The candidate threshold only has to be a safe estimate.
+__device__ float rank_floor_256(const float* __restrict__ vals, int n, int rk, SelectScratch& S) {
+    constexpr int kPer = 64;
+    uint32_t key[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int j = (int)threadIdx.x + i * 256;
+        key[i] = j < n ? order_key(vals[j]) : 0u;
+    }
+    uint32_t prefix = 0u;
+    int remaining = rk;
+    int* hist = S.sel.hist;
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = 24 - 8 * pass;
+        hist[threadIdx.x] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int j = (int)threadIdx.x + i * 256;
+            const bool in = j < n && (pass == 0 || (key[i] >> (shift + 8)) == prefix);
+            if (in) atomicAdd(&hist[(key[i] >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        // Thread t owns bin 255 - t, so the scan counts keys from the largest bin down.
+        const int c = hist[255 - threadIdx.x];
+        const int incl = block_incl_scan(c, S);
+        if (incl - c < remaining && remaining <= incl) {
+            S.sh[0] = 255 - (int)threadIdx.x;
+            S.sh[1] = incl - c;
+        }
+        __syncthreads();
+        prefix = (prefix << 8) | (uint32_t)S.sh[0];
+        remaining -= S.sh[1];
+        __syncthreads();
+    }
+    return order_key_value(prefix << 8);
+}
+
+constexpr int kRowPrepThreads = 256;  // 8 threads per head; one radix bin per thread
+
+__global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P) {
     const int r = blockIdx.x;
     const int64_t p = P.pos0 + r;
     const int64_t nt = (p < P.N - 1 ? p : P.N - 1) + 1;
@@ -1014,45 +1068,73 @@ __global__ __launch_bounds__(256) void row_prep_kernel(IndexerArgs P) {
             s_eq[h] = em;
         }
     }
+    // Key statistics: wave 0 reduces the partial slots.
+    KeyStats ks{};
+    if (threadIdx.x < 64) {
+        unsigned kn = 0u, ki = 0u;
+        int ke = INT_MAX;
+        for (int i = threadIdx.x; i < kStatSlots; i += 64) {
+            const KeyStats e = P.kstats[i].s;
+            kn = max(kn, e.knorm_bits);
+            ki = max(ki, e.kinf_bits);
+            ke = min(ke, e.kexp_min);
+        }
+        for (int o = 32; o > 0; o >>= 1) {
+            kn = max(kn, (unsigned)__shfl_xor((int)kn, o));
+            ki = max(ki, (unsigned)__shfl_xor((int)ki, o));
+            ke = min(ke, __shfl_xor(ke, o));
+        }
+        ks.knorm_bits = kn;
+        ks.kinf_bits = ki;
+        ks.kexp_min = ke;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const KeyStats ks = *P.kstats;
+    if (threadIdx.x < 64) {
+        // Lane h < 32 takes head h; the per-head terms are then reduced across the wave
+        // (the fp64 sums feed bounds that carry their own rounding margins).
         const double knorm = (double)__uint_as_float(ks.knorm_bits);
         const double kinf = (double)__uint_as_float(ks.kinf_bits);
-        const float* wr = P.w + (size_t)r * kIdxHeads;
-        // Exactness: every product and partial sum of the fp32 evaluation is a multiple
-        // of 2^e and below 2^(24+e) in magnitude -> fp32 scores are exact.
-        double lhs = 0.0, dsum = 0.0;
+        const int h = threadIdx.x;
+        double dsum = 0.0, lhs = 0.0;
         int emin = INT_MAX;
-        bool any = false;
-        for (int h = 0; h < kIdxHeads; ++h) {
-            const float wh = wr[h];
-            dsum += fabs((double)wh) * sqrt(s_l2[h]);
+        bool used = false, subnormal = false;
+        if (h < kIdxHeads) {
+            const float wh = P.w[(size_t)r * kIdxHeads + h];
+            dsum = fabs((double)wh) * sqrt(s_l2[h]);
             if (wh != 0.f && s_l1[h] > 0.0) {
-                any = true;
-                lhs += fabs((double)wh) * s_l1[h] * kinf;
-                emin = min(emin, f32_lsb_exp(wh) + s_eq[h]);
+                used = true;
+                lhs = fabs((double)wh) * s_l1[h] * kinf;
+                emin = f32_lsb_exp(wh) + s_eq[h];
             }
-        }
-        bool exact;
-        if (!any || ks.kexp_min == INT_MAX) {
-            exact = true;  // every score is exactly zero
-        } else {
-            const int e = emin + ks.kexp_min;
-            exact = (e >= -100) && (lhs * (1.0 + 1e-12) < ldexp(1.0, 24 + e));
             // each head's dot product must also stay above the fp32 subnormal range
-            for (int h = 0; h < kIdxHeads && exact; ++h)
-                if (s_l1[h] > 0.0 && s_eq[h] + ks.kexp_min < -100) exact = false;
+            subnormal = s_l1[h] > 0.0 && s_eq[h] + ks.kexp_min < -100;
         }
-        float d = 0.f;
-        if (!exact) {
-            const double dd = kDeltaCoef * ldexp(1.0, -24) * knorm * dsum;
-            d = (float)(dd * (1.0 + 1.0 / 1048576.0));
-            if (!(d > 0.f)) d = FLT_MIN;
+        for (int o = 32; o > 0; o >>= 1) {
+            dsum += __shfl_xor(dsum, o);
+            lhs += __shfl_xor(lhs, o);
+            emin = min(emin, __shfl_xor(emin, o));
         }
-        s_delta = d;
-        P.delta[r] = d;
-        P.mode[r] = kModeNormal;
+        const bool any = __ballot(used) != 0, any_subnormal = __ballot(subnormal) != 0;
+        if (threadIdx.x == 0) {
+            // Exactness: every product and partial sum of the fp32 evaluation is a multiple
+            // of 2^e and below 2^(24+e) in magnitude -> fp32 scores are exact.
+            bool exact;
+            if (!any || ks.kexp_min == INT_MAX) {
+                exact = true;  // every score is exactly zero
+            } else {
+                const int e = emin + ks.kexp_min;
+                exact = (e >= -100) && (lhs * (1.0 + 1e-12) < ldexp(1.0, 24 + e)) && !any_subnormal;
+            }
+            float d = 0.f;
+            if (!exact) {
+                const double dd = kDeltaCoef * ldexp(1.0, -24) * knorm * dsum;
+                d = (float)(dd * (1.0 + 1.0 / 1048576.0));
+                if (!(d > 0.f)) d = FLT_MIN;
+            }
+            s_delta = d;
+            P.delta[r] = d;
+            P.mode[r] = kModeNormal;
+        }
     }
     __syncthreads();
     const int g0 = r & ~(kRowsPerGroup - 1);
@@ -1064,19 +1146,11 @@ __global__ __launch_bounds__(256) void row_prep_kernel(IndexerArgs P) {
         return;
     }
     const int rk = sample_rank(n0, Sn, P.top_k);
-    CandList L{};
-    L.s[0] = P.sample + (size_t)r * P.sample_stride;
-    L.n[0] = Sn;
-    L.nseg = 1;
-    float that = 0.f;
-    const bool ok = block_kth_binned(ListSrc{L}, rk, &that, S);
+    const float that = rank_floor_256(P.sample + (size_t)r * P.sample_stride, Sn, rk, S);
     if (threadIdx.x == 0) {
-        float tf = -INFINITY;  // an unresolved sample keeps every key (and falls back later)
-        if (ok) {
-            const double t = (double)that - 2.0 * (double)s_delta;
-            tf = (float)t;
-            if ((double)tf > t) tf = nextafterf(tf, -INFINITY);
-        }
+        const double t = (double)that - 2.0 * (double)s_delta;
+        float tf = (float)t;
+        if ((double)tf > t) tf = nextafterf(tf, -INFINITY);
         P.tau[r] = tf;
     }
 }
@@ -1351,7 +1425,7 @@ __global__ void causal_mask_kernel(int32_t* idx, int64_t L, int top_k, int64_t q
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, uint16_t* k_tile,
+hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStatsSlot* ks, uint16_t* k_tile,
                              hipStream_t s) {
     ProfScope ps(s, kProfKeyStats);
     init_stats_kernel<<<1, 64, 0, s>>>(ks, k_tile, n_keys);
@@ -1371,7 +1445,7 @@ hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStrea
     }
     {
         ProfScope ps(s, kProfRowPrep);
-        row_prep_kernel<<<a.Lb, 256, 0, s>>>(a);
+        row_prep_kernel<<<a.Lb, kRowPrepThreads, 0, s>>>(a);
     }
     {
         ProfScope ps(s, kProfScoreFilter);
