@@ -198,7 +198,7 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
     a.sample_stride = lay.sample_stride;
     a.fold_cap = lay.fold_cap;
     a.force_fallback = debug_force_fallback() ? 1 : 0;
-    a.kstats = reinterpret_cast<dsa::KeyStatsSlot*>(ws + lay.off_kstats);
+    a.kstats = reinterpret_cast<dsa::KeyStats*>(ws + lay.off_kstats);
     a.tau = reinterpret_cast<float*>(ws + lay.off_tau);
     a.delta = reinterpret_cast<float*>(ws + lay.off_delta);
     a.mode = reinterpret_cast<int*>(ws + lay.off_mode);
@@ -219,6 +219,7 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
     uint16_t* k_tile = reinterpret_cast<uint16_t*>(ws + lay.off_ktile);
     a.k_tile = k_tile;
     a.n_ktiles = (n_keys + dsa::kKeyTileKeys - 1) / dsa::kKeyTileKeys;
+    a.n_kstats = dsa::key_stats_blocks(n_keys);
     hipError_t e = dsa::launch_key_stats(k_idx, n_keys, a.kstats, k_tile, s);
     if (e != hipSuccess) return hip_fail(e, "key statistics launch");
 

@@ -15,13 +15,17 @@ struct KeyStats {
     int pad;
 };
 
-// The key-statistics blocks fold their results into kStatSlots partial slots (block b into
-// slot b % kStatSlots), each on its own 128-byte line, so no address takes more than a few
-// dozen atomics; the consumer reduces the slots.
-constexpr int kStatSlots = 64;
-struct alignas(128) KeyStatsSlot {
-    KeyStats s;
-};
+// Every key-statistics block writes its partial result to its own slot (no atomics, no
+// initialisation); the consumer reduces the slots.  One block per four 32-key tiles, at
+// most kStatSlots blocks.
+constexpr int kStatSlots = 1024;
+__host__ __device__ inline int key_stats_blocks(int64_t n_keys) {
+    const int64_t tiles = (n_keys + 31) / 32;
+    int64_t b = (tiles + 3) / 4;
+    if (b > kStatSlots) b = kStatSlots;
+    if (b < 1) b = 1;
+    return (int)b;
+}
 
 // Candidate capacity per query row: expected candidates are 2.5 * top_k.
 __host__ __device__ inline int cand_capacity(int top_k) {
@@ -91,7 +95,7 @@ struct IndexerLayout {
         l.sample_stride = sample_size(N, top_k, l.cap);
         l.fold_cap = top_k + kFoldKeys;
         size_t o = 0;
-        l.off_kstats = o; o = al(o + sizeof(KeyStatsSlot) * kStatSlots);
+        l.off_kstats = o; o = al(o + sizeof(KeyStats) * kStatSlots);
         l.off_tau = o; o = al(o + 4 * (size_t)l.rows);
         l.off_delta = o; o = al(o + 4 * (size_t)l.rows);
         l.off_mode = o; o = al(o + 4 * (size_t)l.rows);
@@ -126,7 +130,8 @@ struct IndexerArgs {
     int sample_stride;
     int fold_cap;
     int force_fallback;     // debug: send every scored row through the fallback fold
-    KeyStatsSlot* kstats;   // [kStatSlots] partial key statistics
+    KeyStats* kstats;       // [n_kstats] partial key statistics, one per key-statistics block
+    int n_kstats;
     float* tau;
     float* delta;
     int* mode;
@@ -158,7 +163,7 @@ struct ProfScope {
 };
 
 // Kernel launchers (indexer.hip).  Each returns the launch status.
-hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStatsSlot* ks, uint16_t* k_tile, hipStream_t s);
+hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, uint16_t* k_tile, hipStream_t s);
 hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s);
 hipError_t launch_causal_mask(int32_t* idx, int64_t L, int top_k, int64_t q_pos0, hipStream_t s);
 

@@ -109,61 +109,55 @@ __device__ double canonical_head_term(const uint16_t* __restrict__ q_h,
 
 static_assert(kKeyTileKeys == kKeyTile, "scoring tiles and the tiled key copy disagree");
 
-// Chunk c (dims 8c..8c+7) of key `key` in the scoring tile order.
-__device__ __forceinline__ void store_key_tile_chunk(uint16_t* k_tile, int64_t key, int c, u16x8 v) {
-    const int64_t t = key / kKeyTileKeys;
-    const int lane = (c >> 3) * 32 + (int)(key % kKeyTileKeys);
-    reinterpret_cast<u16x8*>(k_tile)[t * (kKeyTileBytes / 16) + (c & 7) * 64 + lane] = v;
-}
-
-__global__ void init_stats_kernel(KeyStatsSlot* ks, uint16_t* k_tile, int64_t n_keys) {
-    for (int i = threadIdx.x; i < kStatSlots; i += blockDim.x) {
-        ks[i].s.knorm_bits = 0u;
-        ks[i].s.kinf_bits = 0u;
-        ks[i].s.kexp_min = INT_MAX;
-        ks[i].s.pad = 0;
-    }
-    // Zero the pad keys of the last tile (16 chunks of 16 bytes per key).
-    const int64_t n_pad = (kKeyTileKeys - n_keys % kKeyTileKeys) % kKeyTileKeys;
-    for (int i = threadIdx.x; i < (int)n_pad * 16; i += blockDim.x)
-        store_key_tile_chunk(k_tile, n_keys + i / 16, i % 16, u16x8{});
-}
-
-// 16 lanes per key row (16 bytes each, so a wave reads 4 whole rows per load).  Each
-// row is also written to its place in the scoring tiles.
-__global__ __launch_bounds__(256) void key_stats_kernel(const uint16_t* __restrict__ k_idx,
-                                                        int64_t n_keys, KeyStatsSlot* slots,
-                                                        uint16_t* __restrict__ k_tile) {
-    const int sub = threadIdx.x & 15;
+// One wave per 32-key tile (tile = global wave index, then strided): eight 1-KB row-major
+// loads (16 lanes per key row), the statistics, then the tile is re-ordered through LDS
+// and written as eight 1-KB stores in the scoring order.  Keys past the end are zero.
+constexpr int kStatsThreads = 256;
+constexpr int kStatsRowPad = 17;  // LDS row stride in 16-byte chunks (16 + 1 against bank conflicts)
+__global__ __launch_bounds__(kStatsThreads) void key_stats_kernel(const uint16_t* __restrict__ k_idx,
+                                                                  int64_t n_keys, KeyStats* slots,
+                                                                  uint16_t* __restrict__ k_tile) {
+    __shared__ u16x8 s_t[kStatsThreads / kWave][kKeyTileKeys * kStatsRowPad];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    u16x8* st = s_t[wave];
     float nmax = 0.f, amax = 0.f;
     int emin = INT_MAX;
-    const int64_t rows_per_step = (int64_t)gridDim.x * (blockDim.x >> 4);
-    // Four rows per pass, loads issued together (rows past the end re-read the last row,
-    // which changes no maximum or minimum).
-    constexpr int kU = 4;
-    for (int64_t s = (int64_t)blockIdx.x * (blockDim.x >> 4) + (threadIdx.x >> 4); s < n_keys;
-         s += kU * rows_per_step) {
-        u16x8 v[kU];
+    const int64_t n_tiles = (n_keys + kKeyTileKeys - 1) / kKeyTileKeys;
+    const int64_t n_waves = (int64_t)gridDim.x * (kStatsThreads / kWave);
+    for (int64_t t = (int64_t)blockIdx.x * (kStatsThreads / kWave) + wave; t < n_tiles; t += n_waves) {
+        u16x8 v[8];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int64_t row = min(s + u * rows_per_step, n_keys - 1);
-            v[u] = reinterpret_cast<const u16x8*>(k_idx + row * kIdxDim)[sub];
+        for (int i = 0; i < 8; ++i) {  // chunk q = 64 i + lane: key q / 16 of the tile, dims 8 (q % 16) ..
+            const int q = i * 64 + lane;
+            const int64_t key = t * kKeyTileKeys + (q >> 4);
+            v[i] = key < n_keys ? reinterpret_cast<const u16x8*>(k_idx + key * kIdxDim)[q & 15] : u16x8{};
         }
 #pragma unroll
-        for (int u = 0; u < kU; ++u)
-            if (s + u * rows_per_step < n_keys) store_key_tile_chunk(k_tile, s + u * rows_per_step, sub, v[u]);
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
+        for (int i = 0; i < 8; ++i) {
             float ss = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float x = bf16_bits_to_float(v[u][j]);
+                const uint32_t b = v[i][j];
+                const float x = bf16_bits_to_float((uint16_t)b);
                 ss = fmaf(x, x, ss);
                 amax = fmaxf(amax, fabsf(x));
-                if ((v[u][j] & 0x7fff) != 0) emin = min(emin, bf16_lsb_exp(v[u][j]));
+                // exponent of the lowest set bit (branch-free form of bf16_lsb_exp)
+                const uint32_t mag = b & 0x7fffu, e = mag >> 7, m = mag & 0x7fu;
+                const int l = (int)(e ? e : 1u) - 134 + __builtin_ctz((e ? 0x80u : 0u) | m | (mag ? 0u : 1u));
+                emin = mag ? min(emin, l) : emin;
             }
             for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
             nmax = fmaxf(nmax, sqrtf(ss));
+            const int q = i * 64 + lane;
+            st[(q >> 4) * kStatsRowPad + (q & 15)] = v[i];
+        }
+        // Store i: lane l = 32 hf + c writes key c, dims 64 hf + 8 i .. (the scoring order).
+        // (LDS accesses of one wave complete in order, so the reads see this tile's writes
+        // and the next tile's writes come after them.)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const u16x8 w = st[(lane & 31) * kStatsRowPad + (lane >> 5) * 8 + i];
+            reinterpret_cast<u16x8*>(k_tile)[t * (int64_t)(kKeyTileBytes / 16) + i * 64 + lane] = w;
         }
     }
     nmax = wave_max(nmax);
@@ -186,10 +180,7 @@ __global__ __launch_bounds__(256) void key_stats_kernel(const uint16_t* __restri
         }
         // 128 fp32 squares+adds and the sqrt: relative error < 2^-16; pad by 2^-14.
         const float up = nmax * (1.0f + 1.0f / 16384.0f);
-        KeyStats* ks = &slots[blockIdx.x % kStatSlots].s;
-        atomicMax(&ks->knorm_bits, __float_as_uint(up));
-        atomicMax(&ks->kinf_bits, __float_as_uint(amax));
-        atomicMin(&ks->kexp_min, emin);
+        slots[blockIdx.x] = KeyStats{__float_as_uint(up), __float_as_uint(amax), emin, 0};
     }
 }
 
@@ -979,30 +970,61 @@ __device__ __forceinline__ float order_key_value(uint32_t k) {
 }
 
 // A value no larger than the rk-th largest of vals[0..n) (1 <= rk <= n <= 64 * 256), for
-// a block of 256 threads: three 8-bit radix passes over the order-preserving keys find the
-// bucket of 2^8 keys holding that value, and its lowest key is returned (at most 2^-15
-// relative below the value).  The candidate threshold only has to be a safe estimate.
+// a block of 256 threads.  The values become order-preserving keys; the bits above the
+// highest bit in which the smallest and largest key differ are common to all of them, and
+// up to three 8-bit radix passes over the bits below find the bucket holding the rk-th
+// largest key.  Its lowest key is returned (the candidate threshold only has to be a safe
+// estimate; the bucket spans at most 2^-24 of the key range).
 __device__ float rank_floor_256(const float* __restrict__ vals, int n, int rk, SelectScratch& S) {
     constexpr int kPer = 64;
     uint32_t key[kPer];
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int j = (int)threadIdx.x + i * 256;
         key[i] = j < n ? order_key(vals[j]) : 0u;
+        if (j < n) {
+            kmin = min(kmin, key[i]);
+            kmax = max(kmax, key[i]);
+        }
     }
-    uint32_t prefix = 0u;
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        S.red_i[w] = (int)kmin;
+        S.red_i[4 + w] = (int)kmax;
+    }
+    __syncthreads();
+    kmin = (uint32_t)S.red_i[0];
+    kmax = (uint32_t)S.red_i[4];
+    for (int i = 1; i < 4; ++i) {
+        kmin = min(kmin, (uint32_t)S.red_i[i]);
+        kmax = max(kmax, (uint32_t)S.red_i[4 + i]);
+    }
+    __syncthreads();
+    if (kmin == kmax) return order_key_value(kmin);
+    // Keys = common high bits | d, with d < 2^(top+1).  Pass p takes the 8 bits of d ending
+    // at bit top - 8p (bits under 0 read as zero); the passes stop once bit 0 is reached.
+    const int top = 31 - __builtin_clz(kmin ^ kmax);
+    const uint32_t common = top == 31 ? 0u : (kmax >> (top + 1)) << (top + 1);
+    uint32_t prefix = 0u;  // digits found so far, as a number
     int remaining = rk;
+    int sh = top - 7;      // d >> sh (or d << -sh) puts the current digit in bits 0..7
     int* hist = S.sel.hist;
-#pragma unroll
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = 24 - 8 * pass;
+    for (int pass = 0;; ++pass, sh -= 8) {
         hist[threadIdx.x] = 0;
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
+            if (i * 256 >= n) break;  // uniform
             const int j = (int)threadIdx.x + i * 256;
-            const bool in = j < n && (pass == 0 || (key[i] >> (shift + 8)) == prefix);
-            if (in) atomicAdd(&hist[(key[i] >> shift) & 255u], 1);
+            const uint32_t d = key[i] - common;
+            const bool in = j < n && (pass == 0 || (d >> (sh + 8)) == prefix);
+            const uint32_t digit = (sh >= 0 ? d >> sh : d << -sh) & 255u;
+            if (in) atomicAdd(&hist[digit], 1);
         }
         __syncthreads();
         // Thread t owns bin 255 - t, so the scan counts keys from the largest bin down.
@@ -1016,8 +1038,10 @@ __device__ float rank_floor_256(const float* __restrict__ vals, int n, int rk, S
         prefix = (prefix << 8) | (uint32_t)S.sh[0];
         remaining -= S.sh[1];
         __syncthreads();
+        if (sh <= 0 || pass == 2) break;  // every bit of d is decided, or 24 of them are
     }
-    return order_key_value(prefix << 8);
+    const uint32_t floor_d = sh >= 0 ? prefix << sh : prefix >> -sh;
+    return order_key_value(common + floor_d);
 }
 
 constexpr int kRowPrepThreads = 256;  // 8 threads per head; one radix bin per thread
@@ -1073,8 +1097,10 @@ __global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P
     if (threadIdx.x < 64) {
         unsigned kn = 0u, ki = 0u;
         int ke = INT_MAX;
-        for (int i = threadIdx.x; i < kStatSlots; i += 64) {
-            const KeyStats e = P.kstats[i].s;
+#pragma unroll
+        for (int u = 0; u < kStatSlots / 64; ++u) {  // loads issued together
+            const int i = (int)threadIdx.x + 64 * u;
+            const KeyStats e = i < P.n_kstats ? P.kstats[i] : KeyStats{0u, 0u, INT_MAX, 0};
             kn = max(kn, e.knorm_bits);
             ki = max(ki, e.kinf_bits);
             ke = min(ke, e.kexp_min);
@@ -1425,14 +1451,12 @@ __global__ void causal_mask_kernel(int32_t* idx, int64_t L, int top_k, int64_t q
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStatsSlot* ks, uint16_t* k_tile,
+hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, uint16_t* k_tile,
                              hipStream_t s) {
     ProfScope ps(s, kProfKeyStats);
-    init_stats_kernel<<<1, 64, 0, s>>>(ks, k_tile, n_keys);
-    int blocks = (int)((n_keys + 15) / 16);
-    if (blocks > 1024) blocks = 1024;
-    if (blocks < 1) blocks = 1;
-    key_stats_kernel<<<blocks, 256, 0, s>>>(k_idx, n_keys, ks, k_tile);
+    static_assert(kStatsThreads / kWave == 4 && kKeyTileKeys == 32, "key_stats_blocks assumes 4 waves of 32-key tiles");
+    const int blocks = key_stats_blocks(n_keys);
+    key_stats_kernel<<<blocks, kStatsThreads, 0, s>>>(k_idx, n_keys, ks, k_tile);
     return hipGetLastError();
 }
 
