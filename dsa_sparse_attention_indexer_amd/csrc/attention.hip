@@ -49,6 +49,24 @@ __device__ __forceinline__ u16x4 lds_read_tr(const uint16_t* p) {
     return __builtin_bit_cast(u16x4, v);
 }
 
+// Global -> LDS DMA of 16 (or 4) bytes per lane: lane i's bytes land at lds + 16 i (4 i).
+// Written as inline asm on purpose: the compiler, seeing an LDS DMA in flight, would wait
+// for it before every later LDS read it cannot prove disjoint, i.e. before the current
+// tile's reads, and serialise the next tile's gather with this tile's compute.  The waits
+// for these DMAs are therefore all explicit (vmcnt before the tile barrier); the compiler's
+// own vmcnt waits for other loads can only over-wait on them (the counter is in order).
+// M0 holds the LDS address; one wait state separates its write from the DMA.
+__device__ __forceinline__ void dma_lds16(const void* src, const void* lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_lds4(const void* src, const void* lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(src), "s"(m0) : "memory", "m0");
+}
+
 __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     const int t = blockIdx.x;
     const int wave = threadIdx.x >> 6;
@@ -81,7 +99,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     // DMA of the raw entries of tile j into slot (lanes past top_k fetch nothing).
     auto fetch_idx = [&](int j, int slot) {
         if (wave == 0 && lane < kAttnTile && j * kAttnTile + lane < A.top_k)
-            __builtin_amdgcn_global_load_lds(irow + j * kAttnTile + lane, &s_idx[slot][0], 4, 0, 0);
+            dma_lds4(irow + j * kAttnTile + lane, &s_idx[slot][0]);
     };
     // DMA of the rows of tile j (entries in slot) into buffer buf: wave w takes rows
     // w, w + nwaves, ...; a row is 72 pieces, one 64-lane request and one of 8 lanes.
@@ -91,9 +109,9 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
             key = key < 0 ? 0 : key;  // masked later; any valid row will do
             const char* src = reinterpret_cast<const char*>(A.kv + (size_t)key * A.kv_stride);
             char* dst = reinterpret_cast<char*>(&Kbuf[buf][r][0]);
-            __builtin_amdgcn_global_load_lds(src + lane * 16, dst, 16, 0, 0);
+            dma_lds16(src + lane * 16, dst);
             if (lane < kRowChunks - 64)
-                __builtin_amdgcn_global_load_lds(src + 1024 + lane * 16, dst + 1024, 16, 0, 0);
+                dma_lds16(src + 1024 + lane * 16, dst + 1024);
         }
     };
     // This wave's DMAs have landed; the barrier then publishes every wave's.
@@ -113,6 +131,10 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
 #pragma unroll
         for (int ks = 0; ks < kDqk / 32; ++ks)
             qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qrow + ks * 32));
+        // Take the query fragments' load waits here, once: left to first use, they would
+        // sit inside the tile loop and also wait for that tile's gather DMAs.
+#pragma unroll
+        for (int ks = 0; ks < kDqk / 32; ++ks) asm volatile("" :: "v"(qf[ks]));
 #pragma unroll
         for (int dt = 0; dt < kDv / 16; ++dt) o[dt] = f32x4{};
     }
