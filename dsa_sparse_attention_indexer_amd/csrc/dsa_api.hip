@@ -199,6 +199,7 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
     a.fold_cap = lay.fold_cap;
     a.force_fallback = debug_force_fallback() ? 1 : 0;
     a.kstats = reinterpret_cast<dsa::KeyStats*>(ws + lay.off_kstats);
+    a.qstat = reinterpret_cast<dsa::QHeadStat*>(ws + lay.off_qstat);
     a.tau = reinterpret_cast<float*>(ws + lay.off_tau);
     a.delta = reinterpret_cast<float*>(ws + lay.off_delta);
     a.mode = reinterpret_cast<int*>(ws + lay.off_mode);

@@ -80,10 +80,18 @@ __host__ __device__ inline size_t key_tile_bytes(int64_t n_keys) {
     return (size_t)((n_keys + kKeyTileKeys - 1) / kKeyTileKeys) * kKeyTileBytes;
 }
 
+// Per (query row, head) statistics of q_idx that the exact re-score needs: an upper bound
+// of sum_i |q_h,i| and the lowest set-bit exponent over the nonzero q_h,i (INT_MAX: none).
+struct QHeadStat {
+    double l1;
+    int e;
+    int pad;
+};
+
 struct IndexerLayout {
     int rows, cap, sample_stride, fold_cap;
     size_t off_kstats, off_tau, off_delta, off_mode, off_count, off_fbctrl, off_fblist;
-    size_t off_sample, off_cand, off_ktile;
+    size_t off_sample, off_cand, off_ktile, off_qstat;
     size_t off_fold_s, off_fold_i, off_fold_bi, off_fold_bs, off_fold_bf;
     size_t total;
 
@@ -105,6 +113,7 @@ struct IndexerLayout {
         l.off_sample = o; o = al(o + 4 * (size_t)l.rows * (size_t)l.sample_stride);
         l.off_cand = o; o = al(o + 8 * (size_t)l.rows * (size_t)l.cap);
         l.off_ktile = o; o = al(o + key_tile_bytes(N));
+        l.off_qstat = o; o = al(o + sizeof(QHeadStat) * 32 * (size_t)l.rows);
         l.off_fold_s = o; o = al(o + 4 * (size_t)kFallbackSlots * 2 * l.fold_cap);
         l.off_fold_i = o; o = al(o + 4 * (size_t)kFallbackSlots * 2 * l.fold_cap);
         l.off_fold_bi = o; o = al(o + 4 * (size_t)kFallbackSlots * l.fold_cap);
@@ -131,6 +140,7 @@ struct IndexerArgs {
     int fold_cap;
     int force_fallback;     // debug: send every scored row through the fallback fold
     KeyStats* kstats;       // [n_kstats] partial key statistics, one per key-statistics block
+    QHeadStat* qstat;       // [Lb][32] per-head q statistics (row prep)
     int n_kstats;
     float* tau;
     float* delta;

@@ -540,7 +540,7 @@ struct CandList {
 constexpr int kBins = 2048;
 constexpr int kDirect = 512;
 constexpr int kRescoreKeys = 16;   // band keys per fp64 MFMA block
-constexpr int kRescoreRound = 64;  // band keys re-scored per round (four blocks, eight waves)
+constexpr int kRescoreRound = 128;  // band keys re-scored per round (8 blocks x 2 head halves)
 
 // One row's selection scratch.  The phases use the union in turn: binned k-th search
 // (sel), fp64 re-score staging (rs), then the selected keys (out, fold path only).
@@ -553,8 +553,6 @@ struct SelectScratch {
         int out[kMaxTopK];
         double term[kRescoreRound][kIdxHeads];  // head terms of one re-score round
     };
-    double q1[kIdxHeads];    // per head: sum_i |q_h,i| (rounded up)
-    int qe[kIdxHeads];       // per head: lowest set-bit exponent over nonzero q_h,i (INT_MAX: none)
     int bad[kRescoreRound];  // band keys of the round whose dot products need the sequential order
     float red_f[32];
     int red_i[32];
@@ -777,32 +775,11 @@ __device__ void block_bitonic_sort(int* a, int n) {
 // sequential path.  The head terms fl(w_h max(d_h, +0)) and their ascending-h sum are
 // always evaluated in the canonical order.
 __device__ void band_rescore(int nb, const int* band_key, double* band_s, const uint16_t* __restrict__ q_row,
-                             const float* __restrict__ w_row, const uint16_t* __restrict__ k_idx,
-                             SelectScratch& S) {
+                             const float* __restrict__ w_row, const QHeadStat* __restrict__ qs_row,
+                             const uint16_t* __restrict__ k_idx, SelectScratch& S) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nwaves = blockDim.x >> 6;
     const int g = lane >> 4, c = lane & 15;
-    // Per-head statistics of the query: 16 lanes per head, 8 dimensions per lane.
-    for (int h = wave * 4 + g; h < kIdxHeads; h += nwaves * 4) {
-        const u16x8 v = reinterpret_cast<const u16x8*>(q_row + h * kIdxDim)[c];
-        double l1 = 0.0;
-        int e = INT_MAX;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            l1 += fabs((double)bf16_bits_to_float(v[j]));
-            if ((v[j] & 0x7fff) != 0) e = min(e, bf16_lsb_exp(v[j]));
-        }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            l1 += __shfl_xor(l1, o);
-            e = min(e, __shfl_xor(e, o));
-        }
-        if (c == 0) {
-            S.q1[h] = l1 * (1.0 + 1.0 / 1048576.0);  // covers the rounding of the sums above
-            S.qe[h] = e;
-        }
-    }
-    __syncthreads();
     for (int m0 = 0; m0 < nb; m0 += kRescoreRound) {
         if (threadIdx.x < kRescoreRound) S.bad[threadIdx.x] = 0;
         __syncthreads();
@@ -848,8 +825,8 @@ __device__ void band_rescore(int nb, const int* band_key, double* band_s, const 
             }
             // Lane (g, c) holds d for keys mb + g + 4i (i = 0..3) and its head.
             const double wh = (double)w_row[head];
-            const double qh1 = S.q1[head];
-            const int qhe = S.qe[head];
+            const double qh1 = qs_row[head].l1;
+            const int qhe = qs_row[head].e;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = g + 4 * i;
@@ -904,7 +881,8 @@ __device__ __forceinline__ bool band_wins(int x, int nb, int need, const int* ba
 // scores to sel_s.  band_i / band_s / band_f: storage for up to band_cap near-threshold
 // entries.  Returns false (uniformly) if a buffer would overflow.
 __device__ bool select_core(const CandList& L, int k, float delta, const uint16_t* __restrict__ q_row,
-                            const float* __restrict__ w_row, const uint16_t* __restrict__ k_idx, int* band_i,
+                            const float* __restrict__ w_row, const QHeadStat* __restrict__ qs_row,
+                            const uint16_t* __restrict__ k_idx, int* band_i,
                             double* band_s, float* band_f, int band_cap, int* sel_i, float* sel_s,
                             SelectScratch& S) {
     float kth;
@@ -940,7 +918,7 @@ __device__ bool select_core(const CandList& L, int k, float delta, const uint16_
     const int nb = S.sh[5];
     __syncthreads();
     if (nb > band_cap || n_in >= k || n_in + nb < k) return false;
-    if (delta > 0.f && nb > 0) band_rescore(nb, band_i, band_s, q_row, w_row, k_idx, S);
+    if (delta > 0.f && nb > 0) band_rescore(nb, band_i, band_s, q_row, w_row, qs_row, k_idx, S);
     if (threadIdx.x == 0) S.sh[6] = n_in;
     __syncthreads();
     for (int x0 = 0; x0 < nb; x0 += blockDim.x) {
@@ -1090,6 +1068,8 @@ __global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P
             s_l1[h] = l1;
             s_l2[h] = l2;
             s_eq[h] = em;
+            // for the exact re-score: the bound covers the rounding of the sums above
+            P.qstat[(size_t)r * kIdxHeads + h] = QHeadStat{l1 * (1.0 + 1.0 / 1048576.0), em, 0};
         }
     }
     // Key statistics: wave 0 reduces the partial slots.
@@ -1288,7 +1268,7 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
         if (ok) {
             if (delta > 0.f && nb > 0)
                 band_rescore(nb, s_band_key, s_band_s, P.q_idx + (size_t)r * kIdxHeads * kIdxDim,
-                             P.w + (size_t)r * kIdxHeads, P.k_idx, S);
+                             P.w + (size_t)r * kIdxHeads, P.qstat + (size_t)r * kIdxHeads, P.k_idx, S);
             for (int x = threadIdx.x; x < nb; x += blockDim.x)
                 if (band_wins(x, nb, k - n_in, s_band_key, s_band_s))
                     atomicOr(&s_win[s_band_pos[x] >> 5], 1u << (s_band_pos[x] & 31));
@@ -1410,7 +1390,8 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
                 L.i[0] = Ri[cur];
                 L.n[0] = n;
                 L.nseg = 1;
-                const bool ok = select_core(L, k, delta, q_row, w_row, P.k_idx, band_i, band_s, band_f,
+                const bool ok = select_core(L, k, delta, q_row, w_row, P.qstat + (size_t)r * kIdxHeads, P.k_idx,
+                                            band_i, band_s, band_f,
                                             P.fold_cap, Ri[nxt], Rs[nxt], S);
                 (void)ok;  // band capacity == list capacity
                 __syncthreads();
