@@ -10,6 +10,12 @@ top_k = 2,048, indexer 32 heads x 128, attention 64 heads x 576/512, bf16.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C3]
 
 Prints one JSON line (see the "roofline" and "cpu_baseline" objects).
+
+    python bench.py --decode [--config C3]
+
+times the decode step instead: the newest position's query (L = 1) selects its top-k
+of the N cached keys (dsa_indexer_topk) and attends over them with the split-key
+attention (dsa_sparse_decode); one JSON line of its own.
 """
 from __future__ import annotations
 
@@ -135,6 +141,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB (read MIB, write MIB) three "
                          "times, to scale the FETCH_SIZE / WRITE_SIZE counters, and exit")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the decode step (L = 1 indexer + split-key attention) instead")
     ap.add_argument("--print-source-hash", metavar="KERNEL", choices=sorted(KERNEL_SOURCES),
                     help="print the source hash a traffic summary for KERNEL must carry, and exit")
     args = ap.parse_args()
@@ -172,6 +180,9 @@ def main():
     t0 = time.perf_counter()
     inp = di.make_inputs(wl)
     log(f"[bench] {wl.name}: inputs generated in {time.perf_counter() - t0:.1f} s")
+    if args.decode:
+        bench_decode(args, wl, inp, dev)
+        return
 
     def bf(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -272,6 +283,93 @@ def main():
         t0 = time.perf_counter()
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
         log(f"[bench] cpu baseline took {time.perf_counter() - t0:.1f} s")
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(args, wl, inp, dev):
+    """Decode step at the configuration's cache: position N - 1 queries (L = 1)."""
+    import numpy as np
+    import torch
+
+    import dsa_inputs as di
+    import dsa_sparse_attention_indexer_amd as dsa
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t = wl.L - 1
+    pos = wl.pos0 + t
+    q_idx, w = bf(inp["q_idx"][t:t + 1]), torch.from_numpy(inp["w"][t:t + 1].copy()).to(dev)
+    q, k_idx, kv = bf(inp["q"][t:t + 1]), bf(inp["k_idx"]), bf(inp["kv"])
+    idx = torch.empty((1, wl.top_k), dtype=torch.int32, device=dev)
+    out = torch.empty((1, wl.H, 512), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(dsa.workspace_bytes(1, wl.N, wl.top_k, 0), dtype=torch.uint8, device=dev)
+    dws = torch.empty(max(dsa.decode_workspace_bytes(1, wl.H, wl.top_k, 0), 1), dtype=torch.uint8, device=dev)
+    scale = float(np.float32(di.SOFTMAX_SCALE))
+
+    def step():
+        dsa.indexer_topk(q_idx, k_idx, w, pos, wl.top_k, out=idx, workspace=ws)
+        dsa.sparse_decode(q, kv, idx, pos, scale, out=out, workspace=dws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    dsa.profile_enable(True)
+    for k in dsa.PROFILE_KERNELS:
+        dsa.profile_read(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1000.0 / args.steps
+    kernels = {}
+    for k in dsa.PROFILE_KERNELS:
+        ms, n = dsa.profile_read(k)
+        if n:
+            kernels[k] = {"launches_per_step": round(n / args.steps, 4), "ms_per_launch": round(ms / n, 5)}
+    dsa.profile_enable(False)
+    n_t = pos + 1
+    f_idx = 2 * 32 * 128 * n_t
+    b_attn = wl.top_k * 576 * 2 + 4 * wl.top_k + wl.H * 576 * 2 + wl.H * 512 * 2
+    result = {
+        "metric": f"decode steps/sec (L=1 indexer+topk+split sparse attn) at N={wl.N}, top-k={wl.top_k}",
+        "value": round(1000.0 / ms_per_step, 1),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} decode: query at position {pos} of N={wl.N} cached keys, "
+                               f"top_k={wl.top_k}, attention {wl.H} heads x 576/512 bf16, split keys",
+                   "N": wl.N, "L": 1, "top_k": wl.top_k, "attn_heads": wl.H},
+        "kernels": kernels,
+    }
+    sp = kernels.get("attn_split")
+    sf = kernels.get("score_filter")
+    if sp:
+        ach = b_attn / (sp["ms_per_launch"] * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "attn_split"}
+    if sf:
+        ach = f_idx / (sf["ms_per_launch"] * 1e-3) / 1e12
+        result["indexer_roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 5),
+                                      "kernel": "score_filter"}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=False)
+        t0 = time.perf_counter()
+        sel = oracle.topk(inp["q_idx"][t:t + 1], inp["k_idx"], inp["w"][t:t + 1], pos, wl.top_k)
+        oracle.attention(inp["q"][t:t + 1], inp["kv"], sel, pos, di.SOFTMAX_SCALE)
+        secs = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(1.0 / secs, 3), "unit": "steps/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"one decode step (1 query over {n_t} keys), fp64 C oracle: "
+                                            f"full-sort top-k + sparse attention; {secs:.2f} s"}
     print(json.dumps(result), flush=True)
 
 

@@ -27,10 +27,11 @@ D_ROPE = 64
 DEFAULT_Q_BLOCK = 1024
 
 EXPORTED = ["dsa_indexer_topk_workspace_bytes", "dsa_indexer_topk", "dsa_causal_mask_topk",
-            "dsa_sparse_prefill", "dsa_sparse_prefill_gate", "dsa_profile_enable",
+            "dsa_sparse_prefill", "dsa_sparse_decode_workspace_bytes", "dsa_sparse_decode",
+            "dsa_sparse_prefill_gate", "dsa_profile_enable",
             "dsa_profile_read", "dsa_status_string", "dsa_last_error", "dsa_version"]
 PROFILE_KERNELS = ["key_stats", "score_sample", "row_prep", "score_filter", "select", "fold",
-                   "sparse_attention", "causal_mask"]
+                   "sparse_attention", "causal_mask", "attn_split", "attn_merge"]
 
 _lib = None
 
@@ -59,6 +60,10 @@ def load_library(path: str | None = None):
     lib.dsa_causal_mask_topk.argtypes = [P, i64, i32, i64, P]
     lib.dsa_sparse_prefill.restype = ctypes.c_int
     lib.dsa_sparse_prefill.argtypes = [P, P, i64, P, i64, i64, i32, i32, i32, i32, i64, f32, i32, P, P, P]
+    lib.dsa_sparse_decode_workspace_bytes.restype = sz
+    lib.dsa_sparse_decode_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    lib.dsa_sparse_decode.restype = ctypes.c_int
+    lib.dsa_sparse_decode.argtypes = [P, P, i64, P, i64, i64, i32, i32, i32, i32, i64, f32, i32, P, P, P, sz, P]
     lib.dsa_sparse_prefill_gate.restype = ctypes.c_int
     lib.dsa_sparse_prefill_gate.argtypes = [i64, i64, i64, i64]
     lib.dsa_status_string.restype = ctypes.c_char_p
@@ -200,4 +205,47 @@ def sparse_prefill(q, kv, idx, q_pos0: int, scale: float, q_block: int = DEFAULT
     _check(lib.dsa_sparse_prefill(q.data_ptr(), kv.data_ptr(), kv.stride(0), idx.data_ptr(), L, N, H,
                                   D_LATENT, D_ROPE, top_k, q_pos0, float(scale), q_block, out.data_ptr(),
                                   lse.data_ptr() if lse is not None else None, _stream_ptr(q, stream)))
+    return (out, lse) if return_lse else out
+
+
+def decode_workspace_bytes(L: int, H: int, top_k: int, splits: int = 0) -> int:
+    return int(load_library().dsa_sparse_decode_workspace_bytes(L, H, top_k, splits))
+
+
+def sparse_decode(q, kv, idx, q_pos0: int, scale: float, splits: int = 0, return_lse: bool = False,
+                  out=None, lse=None, workspace=None, stream=None):
+    """Split-key sparse attention (decode and short chunks): the sparse_prefill result,
+    with each query's top-k list cut into `splits` parts merged by log-sum-exp.
+
+    Arguments as sparse_prefill; splits = 0 picks the count.  workspace: optional uint8
+    GPU tensor of at least decode_workspace_bytes(L, H, top_k, splits) bytes.
+    """
+    import torch
+
+    lib = load_library()
+    _req(q, "q", torch.bfloat16, 3)
+    _req(idx, "idx", torch.int32, 2)
+    if not (isinstance(kv, torch.Tensor) and kv.dtype == torch.bfloat16 and kv.dim() == 2 and kv.is_cuda
+            and kv.stride(1) == 1):
+        raise ValueError("kv must be a bf16 GPU tensor [N, stride>=576] with unit column stride")
+    L, H, dqk = q.shape
+    N = kv.shape[0]
+    top_k = idx.shape[1]
+    if dqk != D_LATENT + D_ROPE:
+        raise ValueError(f"q must be [L, H, {D_LATENT + D_ROPE}]")
+    if idx.shape[0] != L:
+        raise ValueError("idx must have L rows")
+    if out is None:
+        out = torch.empty((L, H, D_LATENT), dtype=torch.bfloat16, device=q.device)
+    else:
+        _req(out, "out", torch.bfloat16, 3)
+    if return_lse and lse is None:
+        lse = torch.empty((L, H), dtype=torch.float32, device=q.device)
+    need = max(decode_workspace_bytes(L, H, top_k, splits), 1)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.dsa_sparse_decode(q.data_ptr(), kv.data_ptr(), kv.stride(0), idx.data_ptr(), L, N, H,
+                                 D_LATENT, D_ROPE, top_k, q_pos0, float(scale), splits, out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
     return (out, lse) if return_lse else out

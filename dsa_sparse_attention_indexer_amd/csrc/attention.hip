@@ -67,6 +67,9 @@ __device__ __forceinline__ void dma_lds4(const void* src, const void* lds) {
                  :: "v"(src), "s"(m0) : "memory", "m0");
 }
 
+// kSplit: workgroup (t, s) takes the tiles [s*tps, (s+1)*tps) of query t (tps = tiles per
+// split) and writes an unnormalised partial instead of the output.
+template <bool kSplit>
 __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     const int t = blockIdx.x;
     const int wave = threadIdx.x >> 6;
@@ -88,7 +91,10 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     __shared__ int s_idx[3][kAttnTile];  // raw top-k entries of three consecutive tiles
 
     const int32_t* irow = A.idx + (size_t)t * A.top_k;
-    const int n_tiles = (A.top_k + kAttnTile - 1) / kAttnTile;
+    const int n_all = (A.top_k + kAttnTile - 1) / kAttnTile;
+    const int tps = kSplit ? (n_all + A.splits - 1) / A.splits : n_all;
+    const int t_lo = kSplit ? (int)blockIdx.y * tps : 0;
+    const int n_tiles = t_lo + tps < n_all ? t_lo + tps : n_all;  // one past this workgroup's last tile
     const int nwaves = nthreads >> 6;
     // Entry j of the row as a key this query may use, or -1.
     const int p32 = (int)p;  // <= N - 1 <= INT32_MAX - 1
@@ -117,11 +123,11 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     // This wave's DMAs have landed; the barrier then publishes every wave's.
     auto dma_wait = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-    fetch_idx(0, 0);
-    fetch_idx(1, 1);
+    if (t_lo < n_tiles) fetch_idx(t_lo, t_lo % 3);
+    if (t_lo + 1 < n_tiles) fetch_idx(t_lo + 1, (t_lo + 1) % 3);
     dma_wait();
     __syncthreads();
-    fetch_rows(0, 0, 0);
+    if (t_lo < n_tiles) fetch_rows(t_lo, t_lo % 3, t_lo & 1);
     dma_wait();
 
     bf16x8 qf[kDqk / 32];
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     const float sl2 = A.scale * 1.4426950408889634f;
     __syncthreads();
 
-    for (int tile = 0; tile < n_tiles; ++tile) {
+    for (int tile = t_lo; tile < n_tiles; ++tile) {
         const int cur = tile & 1;
         const int slot = tile % 3;
         // Rows of the next tile and the entries of the tile after it are in flight while
@@ -230,6 +236,14 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     }
 
     if (!compute) return;
+    if (kSplit) {
+        const size_t ph = ((size_t)t * A.splits + blockIdx.y) * A.H + h;
+        float* po = A.part_o + ph * kDv + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < kDv / 16; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+        if (g == 0) *reinterpret_cast<f32x4*>(A.part_ml + ph * 4) = f32x4{m, lsum, lexp, 0.f};
+        return;
+    }
     const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
     uint16_t* orow = A.out + ((size_t)t * A.H + h) * kDv + 4 * g;
 #pragma unroll
@@ -243,11 +257,77 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
         A.lse[(size_t)t * A.H + h] = lexp > 0.f ? (m + log2f(lexp)) * 0.6931471805599453f : -INFINITY;
 }
 
+// Merge of the split partials of query t, head h (one workgroup of 128 threads, four
+// output columns per thread): with M the largest reference max over the splits and
+// c_s = 2^(m_s - M), out = sum_s c_s O_s / sum_s c_s l_s and lse = M + log2(sum_s c_s e_s)
+// (natural log on output), exactly the normalisation of the unsplit kernel.
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttentionArgs A) {
+    const int t = blockIdx.x, h = blockIdx.y;
+    __shared__ float s_c[kMaxSplits];
+    __shared__ float s_norm[2];
+    const size_t base = (size_t)t * A.splits * A.H + h;  // partial (t, s, h) = base + s * H
+    if (threadIdx.x < 64) {
+        float mx = -INFINITY;
+        for (int sp = threadIdx.x; sp < A.splits; sp += 64)
+            mx = fmaxf(mx, A.part_ml[(base + (size_t)sp * A.H) * 4]);
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        float den = 0.f, dex = 0.f;
+        for (int sp = threadIdx.x; sp < A.splits; sp += 64) {
+            const f32x4 ml = *reinterpret_cast<const f32x4*>(A.part_ml + (base + (size_t)sp * A.H) * 4);
+            const float c = ml[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[0] - mx);
+            s_c[sp] = c;
+            den += c * ml[1];
+            dex += c * ml[2];
+        }
+        for (int o = 32; o > 0; o >>= 1) {
+            den += __shfl_xor(den, o);
+            dex += __shfl_xor(dex, o);
+        }
+        if (threadIdx.x == 0) {
+            s_norm[0] = den > 0.f ? 1.0f / den : 0.f;
+            if (A.lse) A.lse[(size_t)t * A.H + h] = dex > 0.f ? (mx + log2f(dex)) * 0.6931471805599453f : -INFINITY;
+        }
+    }
+    __syncthreads();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const float* po = A.part_o + base * kDv + 4 * threadIdx.x;
+    const size_t stride = (size_t)A.H * kDv;  // between consecutive splits
+    constexpr int kU = 8;                     // loads issued together
+    for (int s0 = 0; s0 < A.splits; s0 += kU) {
+        f32x4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            v[u] = s0 + u < A.splits ? *reinterpret_cast<const f32x4*>(po + (size_t)(s0 + u) * stride) : f32x4{};
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            if (s0 + u < A.splits) acc += s_c[s0 + u] * v[u];
+    }
+    const float inv = s_norm[0];
+    u16x4 pk;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pk[r] = float_to_bf16_rne(acc[r] * inv);
+    *reinterpret_cast<u16x4*>(A.out + ((size_t)t * A.H + h) * kDv + 4 * threadIdx.x) = pk;
+}
+
 hipError_t launch_sparse_attention(const AttentionArgs& a, hipStream_t s) {
     int threads = 64 * (a.H / 16);
     if (threads < kAttnMinThreads) threads = kAttnMinThreads;
     ProfScope ps(s, kProfAttention);
-    sparse_attn_kernel<<<a.Lb, threads, 0, s>>>(a);
+    sparse_attn_kernel<false><<<a.Lb, threads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_sparse_attention_split(const AttentionArgs& a, hipStream_t s) {
+    int threads = 64 * (a.H / 16);
+    if (threads < kAttnMinThreads) threads = kAttnMinThreads;
+    {
+        ProfScope ps(s, kProfAttnSplit);
+        sparse_attn_kernel<true><<<dim3(a.Lb, a.splits), threads, 0, s>>>(a);
+    }
+    {
+        ProfScope ps(s, kProfAttnMerge);
+        attn_merge_kernel<<<dim3(a.Lb, a.H), kDv / 4, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

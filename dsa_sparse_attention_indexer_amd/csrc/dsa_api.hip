@@ -23,7 +23,8 @@ struct ProfRecord {
 };
 std::vector<ProfRecord> g_prof;
 const char* const kProfNames[kProfCount] = {"key_stats", "score_sample", "row_prep", "score_filter",
-                                            "select", "fold", "sparse_attention", "causal_mask"};
+                                            "select", "fold", "sparse_attention", "causal_mask",
+                                            "attn_split", "attn_merge"};
 }  // namespace
 
 ProfScope::ProfScope(hipStream_t s, int k) : stream(s), kernel(k), start(nullptr), on(false) {
@@ -299,6 +300,86 @@ dsa_status_t dsa_sparse_prefill(const uint16_t* q, const uint16_t* kv, int64_t k
         a.scale = scale;
         hipError_t e = dsa::launch_sparse_attention(a, s);
         if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+    }
+    return DSA_OK;
+}
+
+static int resolve_splits(int64_t L, int32_t top_k, int32_t splits) {
+    const int n_tiles = (top_k + 31) / 32;
+    if (splits > 0) return splits < n_tiles ? splits : n_tiles;
+    const int64_t rows = L < dsa::kDecodeRows ? L : dsa::kDecodeRows;
+    int64_t s = (512 + rows - 1) / (rows > 0 ? rows : 1);  // about 512 workgroups
+    if (s > n_tiles) s = n_tiles;
+    if (s > dsa::kMaxSplits) s = dsa::kMaxSplits;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+size_t dsa_sparse_decode_workspace_bytes(int64_t L, int32_t H, int32_t top_k, int32_t splits) {
+    if (L < 0 || H <= 0 || H % 16 != 0 || H > DSA_MAX_HEADS || top_k < 1 || splits < 0 || splits > dsa::kMaxSplits)
+        return 0;
+    if (L == 0) return 0;
+    return dsa::decode_workspace_bytes(L, H, resolve_splits(L, top_k, splits));
+}
+
+dsa_status_t dsa_sparse_decode(const uint16_t* q, const uint16_t* kv, int64_t kv_stride, const int32_t* idx,
+                               int64_t L, int64_t N, int32_t H, int32_t d_latent, int32_t d_rope, int32_t top_k,
+                               int64_t q_pos0, float scale, int32_t splits, uint16_t* out, float* lse,
+                               void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    if (L < 0) return fail(DSA_ERR_INVALID_ARG, "L must be >= 0 (got %lld)", (long long)L);
+    if (N <= 0) return fail(DSA_ERR_INVALID_ARG, "N must be > 0 (got %lld)", (long long)N);
+    if (N > (int64_t)INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "N above 2^31-1 is not supported");
+    if (q_pos0 < 0 || q_pos0 + L > N)
+        return fail(DSA_ERR_INVALID_ARG, "need 0 <= q_pos0 and q_pos0 + L <= N");
+    if (top_k < 1) return fail(DSA_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", top_k);
+    if (splits < 0 || splits > dsa::kMaxSplits)
+        return fail(DSA_ERR_INVALID_ARG, "splits must be in 0..%d (got %d)", dsa::kMaxSplits, splits);
+    if (d_latent != DSA_D_LATENT || d_rope != DSA_D_ROPE)
+        return fail(DSA_ERR_UNSUPPORTED, "need d_latent=%d and d_rope=%d (got %d, %d)", DSA_D_LATENT, DSA_D_ROPE,
+                    d_latent, d_rope);
+    if (H <= 0 || H % 16 != 0 || H > DSA_MAX_HEADS)
+        return fail(DSA_ERR_UNSUPPORTED, "H must be a positive multiple of 16 up to %d (got %d)", DSA_MAX_HEADS, H);
+    if (kv_stride < d_latent + d_rope || kv_stride % 8 != 0)
+        return fail(DSA_ERR_INVALID_ARG, "kv_stride must be >= %d and a multiple of 8 (got %lld)",
+                    d_latent + d_rope, (long long)kv_stride);
+    if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+        return fail(DSA_ERR_INVALID_ARG, "scale must be finite");
+    if (L == 0) return DSA_OK;
+    if (!q || !kv || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(idx, 4) || !aligned(out, 8) || (lse && !aligned(lse, 4)))
+        return fail(DSA_ERR_INVALID_ARG, "q/kv must be 16-byte aligned, out 8-byte, idx/lse 4-byte");
+    const int S = resolve_splits(L, top_k, splits);
+    const size_t need = dsa::decode_workspace_bytes(L, H, S);
+    if (!workspace || workspace_bytes < need)
+        return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                    workspace ? "" : ", null");
+    if (!aligned(workspace, 256)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int64_t rows = L < dsa::kDecodeRows ? L : dsa::kDecodeRows;
+    float* part_o = static_cast<float*>(workspace);
+    float* part_ml = part_o + (size_t)rows * S * H * 512;
+    for (int64_t b0 = 0; b0 < L; b0 += dsa::kDecodeRows) {
+        dsa::AttentionArgs a{};
+        const int64_t Lb = (L - b0) < dsa::kDecodeRows ? (L - b0) : dsa::kDecodeRows;
+        a.q = q + (size_t)b0 * H * (d_latent + d_rope);
+        a.kv = kv;
+        a.idx = idx + (size_t)b0 * top_k;
+        a.out = out + (size_t)b0 * H * d_latent;
+        a.lse = lse ? lse + (size_t)b0 * H : nullptr;
+        a.kv_stride = kv_stride;
+        a.N = N;
+        a.pos0 = q_pos0 + b0;
+        a.Lb = (int)Lb;
+        a.H = H;
+        a.top_k = top_k;
+        a.scale = scale;
+        a.splits = S;
+        a.part_o = part_o;
+        a.part_ml = part_ml;
+        hipError_t e = dsa::launch_sparse_attention_split(a, s);
+        if (e != hipSuccess) return hip_fail(e, "split attention launch");
     }
     return DSA_OK;
 }

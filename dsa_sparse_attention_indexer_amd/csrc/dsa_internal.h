@@ -161,7 +161,7 @@ struct IndexerArgs {
 // event before its launch and another after it on the same stream.
 enum ProfKernel : int {
     kProfKeyStats = 0, kProfScoreSample, kProfRowPrep, kProfScoreFilter, kProfSelect, kProfFold,
-    kProfAttention, kProfCausalMask, kProfCount
+    kProfAttention, kProfCausalMask, kProfAttnSplit, kProfAttnMerge, kProfCount
 };
 struct ProfScope {
     ProfScope(hipStream_t s, int kernel);
@@ -188,7 +188,22 @@ struct AttentionArgs {
     int64_t pos0;
     int Lb, H, top_k;
     float scale;
+    // Split over the keys (decode): splits > 1 sends split s of query t to workgroup (t, s),
+    // which writes its unnormalised partial into part_o / part_ml for the merge.
+    int splits;
+    float* part_o;        // [Lb][splits][H][512] fp32
+    float* part_ml;       // [Lb][splits][H][4]: reference max (base 2), bf16-weight sum, fp32-weight sum
 };
 hipError_t launch_sparse_attention(const AttentionArgs& a, hipStream_t s);
+// Split-key attention and the log-sum-exp merge of its partials.
+hipError_t launch_sparse_attention_split(const AttentionArgs& a, hipStream_t s);
+
+// Workspace of the split-key attention: the partials of min(L, 1024) queries.
+constexpr int kDecodeRows = 1024;
+constexpr int kMaxSplits = 128;
+__host__ __device__ inline size_t decode_workspace_bytes(int64_t rows, int H, int splits) {
+    const size_t r = (size_t)(rows < kDecodeRows ? rows : kDecodeRows);
+    return r * (size_t)splits * (size_t)H * (512 + 4) * sizeof(float);
+}
 
 }  // namespace dsa

@@ -138,6 +138,33 @@ dsa_status_t dsa_sparse_prefill(const uint16_t* q, const uint16_t* kv, int64_t k
                                 dsa_stream_t stream);
 
 /*
+ * Sparse attention split over the selected keys, for decode (L = 1) and short
+ * chunks ("GLM prefill now attends only to the keys its indexer picks", How it
+ * works: the sparse path uses the same absorbed form decode already uses; and
+ * Evidence: decode continues after a sparse prefill).  Each query's top-k list
+ * is cut into `splits` contiguous parts attended by separate workgroups; each
+ * part's unnormalised output and softmax sums are merged by log-sum-exp.  The
+ * result is the dsa_sparse_prefill result (same definition, same arguments),
+ * up to the rounding order of the merge.
+ *
+ *   splits   1 .. 128 parts per query (clamped to ceil(top_k/32)); 0 picks a count
+ *            that gives about 512 workgroups
+ *   workspace / workspace_bytes: device scratch of at least
+ *            dsa_sparse_decode_workspace_bytes(L, H, top_k, splits) bytes, 256-byte
+ *            aligned, caller-owned; it holds the partials of up to 1,024 queries
+ *            (longer chunks run in blocks of 1,024 queries reusing it)
+ *   other arguments and the errors as dsa_sparse_prefill; a short or null
+ *   workspace gives DSA_ERR_WORKSPACE, splits outside 0..128 DSA_ERR_INVALID_ARG.
+ * L == 0 is a no-op returning DSA_OK.
+ */
+size_t dsa_sparse_decode_workspace_bytes(int64_t L, int32_t H, int32_t top_k, int32_t splits);
+dsa_status_t dsa_sparse_decode(const uint16_t* q, const uint16_t* kv, int64_t kv_stride,
+                               const int32_t* idx, int64_t L, int64_t N, int32_t H,
+                               int32_t d_latent, int32_t d_rope, int32_t top_k, int64_t q_pos0,
+                               float scale, int32_t splits, uint16_t* out, float* lse,
+                               void* workspace, size_t workspace_bytes, dsa_stream_t stream);
+
+/*
  * The sparse-prefill gate of the GLM page ("How it works": sparse only for a
  * single sequence, only in prefill, and only once the cache holds at least
  * min_context tokens; 16,384 by default).  Returns 1 when the sparse path
@@ -152,8 +179,9 @@ int dsa_sparse_prefill_gate(int64_t B, int64_t L, int64_t N, int64_t min_context
  * events of one kernel class, returns the summed duration in milliseconds and
  * the number of launches since the last read of that class, and forgets them.
  * Kernel classes: "key_stats", "score_sample", "row_prep", "score_filter",
- * "select", "fold", "sparse_attention", "causal_mask".  Unknown names give
- * DSA_ERR_INVALID_ARG.  Host only; safe to call from one thread at a time.
+ * "select", "fold", "sparse_attention", "causal_mask", "attn_split",
+ * "attn_merge".  Unknown names give DSA_ERR_INVALID_ARG.  Host only; safe to
+ * call from one thread at a time.
  */
 dsa_status_t dsa_profile_enable(int on);
 dsa_status_t dsa_profile_read(const char* kernel, double* total_ms, int64_t* launches);

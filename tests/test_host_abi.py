@@ -112,6 +112,48 @@ def test_attention_zero_rows_is_a_no_op(lib):
     assert call_attn(lib, L=0, ptr=0) == 0
 
 
+def call_decode(lib, L=1, N=64, H=64, dl=512, dr=64, k=64, q_pos0=63, stride=576, scale=0.07, splits=0,
+                ptr=1 << 20, ws=1 << 24, ws_bytes=1 << 30):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    w = ctypes.c_void_p(ws) if ws else None
+    return lib.dsa_sparse_decode(p, p, stride, p, L, N, H, dl, dr, k, q_pos0, scale, splits, p, None,
+                                 w, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=-1), 1), (dict(N=0), 1), (dict(q_pos0=64), 1), (dict(k=0), 1), (dict(splits=-1), 1),
+    (dict(splits=129), 1), (dict(H=24), 2), (dict(H=144), 2), (dict(dl=256), 2), (dict(dr=32), 2),
+    (dict(stride=575), 1), (dict(scale=float("nan")), 1), (dict(ptr=0), 1),
+    (dict(ws=0), 3), (dict(ws_bytes=1024), 3), (dict(ws=(1 << 24) + 16), 1),
+])
+def test_decode_rejects_bad_arguments(lib, kw, status):
+    assert call_decode(lib, **kw) == status
+    assert lib.dsa_last_error() != b""
+
+
+def test_decode_zero_rows_is_a_no_op(lib):
+    assert call_decode(lib, L=0, ptr=0, ws=0, ws_bytes=0) == 0
+
+
+def test_decode_workspace_size():
+    import dsa_sparse_attention_indexer_amd as d
+
+    lib = d.load_library()
+    f = lib.dsa_sparse_decode_workspace_bytes
+    # explicit splits: rows x splits x H x (512 + 4) fp32
+    assert f(1, 64, 2048, 8) == 1 * 8 * 64 * 516 * 4
+    # splits are clamped to the tile count of top_k (32 keys per tile)
+    assert f(1, 64, 64, 8) == 1 * 2 * 64 * 516 * 4
+    # automatic: about 512 workgroups, at most one tile each and at most 128 splits
+    assert f(1, 64, 2048, 0) == 1 * 64 * 64 * 516 * 4
+    assert f(4, 16, 8192, 0) == 4 * 128 * 16 * 516 * 4
+    assert f(1024, 64, 2048, 0) == 1024 * 1 * 64 * 516 * 4
+    # partials of at most 1,024 queries
+    assert f(5000, 64, 2048, 2) == 1024 * 2 * 64 * 516 * 4
+    assert f(0, 64, 2048, 0) == 0
+    assert f(1, 24, 2048, 0) == 0 and f(1, 64, 0, 0) == 0 and f(1, 64, 2048, 129) == 0
+
+
 def test_causal_mask_rejects_bad_arguments(lib):
     f = lib.dsa_causal_mask_topk
     assert f(ctypes.c_void_p(1 << 20), -1, 4, 0, None) == 1
