@@ -235,6 +235,7 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
         const int64_t last_pos = a.pos0 + Lb - 1;
         const int64_t n_last = (last_pos < N - 1 ? last_pos : N - 1) + 1;
         const bool need_sample = dsa::sample_size(n_last, top_k, lay.cap) > 0;
+        a.parts = dsa::key_parts((Lb + dsa::kRowsPerGroup - 1) / dsa::kRowsPerGroup);
         e = dsa::launch_indexer_block(a, need_sample, s);
         if (e != hipSuccess) return hip_fail(e, "indexer launch");
     }

@@ -66,6 +66,15 @@ __host__ __device__ inline int sample_rank(int64_t n_t, int s, int top_k) {
     return ri;
 }
 
+// Key parts per row group: the two halves while the groups fill 256 compute units (128 or
+// more groups), else a power of two giving about 256 workgroups (at most 256 parts).
+inline int key_parts(int groups) {
+    if (groups >= 128) return 2;
+    int p = 4;
+    while (p < 256 && p * groups < 256) p <<= 1;
+    return p;
+}
+
 constexpr int kFallbackSlots = 32;
 constexpr int kFoldKeys = 4096;
 constexpr int kCandSegs = 8;  // candidate segments per row: 2 key halves x 4 scoring waves
@@ -139,6 +148,11 @@ struct IndexerArgs {
     int sample_stride;
     int fold_cap;
     int force_fallback;     // debug: send every scored row through the fallback fold
+    // Key parts per row group.  2 (the key halves, XCD-mapped): the 8 candidate segments of
+    // a row are written in key order by the 2 x 4 scoring waves.  More parts (few row
+    // groups): every wave of every part appends to the row's single list through an atomic
+    // counter (count[r][0]), and the selection sorts its output.
+    int parts;
     KeyStats* kstats;       // [n_kstats] partial key statistics, one per key-statistics block
     QHeadStat* qstat;       // [Lb][32] per-head q statistics (row prep)
     int n_kstats;

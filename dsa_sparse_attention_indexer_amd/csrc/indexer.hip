@@ -270,6 +270,7 @@ struct ScoreTile {
     int lane, hf, col;
     int colm;           // col - hf
     int first_pos;      // position of the group's first row
+    int first_row;      // the group's first row in the block
     int seg;
     int (&cnt)[kRowsPerWave];   // survivors so far per row (including any past seg)
     uint2* lbuf;                // filter: this wave's LDS staging lists, kStageSlots per row
@@ -363,9 +364,16 @@ struct ScoreTile {
     // Entries past the segment's capacity are dropped (the row is then re-done by the
     // fold, which the count past seg signals).
     __device__ __forceinline__ void flush_row(int j) {
+        uint32_t base = (uint32_t)gcnt[j];
+        if (P.parts > 2) {  // shared list: reserve the slots (one atomic per flush)
+            uint32_t b = 0u;
+            if (lane == 0) b = atomicAdd(reinterpret_cast<unsigned*>(&P.count[(size_t)(first_row + j) * kSegs]),
+                                         (unsigned)lcnt[j]);
+            base = __builtin_amdgcn_readfirstlane(b);
+        }
         if (lane < lcnt[j]) {
             const uint2 e = lbuf[j * kStageSlots + lane];
-            const uint32_t o = (uint32_t)gcnt[j] + (uint32_t)lane;
+            const uint32_t o = base + (uint32_t)lane;
             if (o < (uint32_t)seg) cand0[(uint32_t)j * (uint32_t)P.cap + o] = e;
         }
         gcnt[j] += lcnt[j];
@@ -408,19 +416,29 @@ struct ScoreTile {
 template <bool kSample>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int n_groups) {
     // Workgroups go round-robin over the 8 XCDs: XCDs 0-3 take key half 0, 4-7 half 1.
-    const int xcd = blockIdx.x & 7;
-    const int half = xcd >> 2;
-    const int g = (int)(blockIdx.x >> 3) * 4 + (xcd & 3);
+    // Two parts: XCDs 0-3 take key half 0 and 4-7 half 1.  More parts: consecutive
+    // workgroups take consecutive parts of one group.
+    const bool appended = P.parts > 2;
+    int part, g;
+    if (!appended) {
+        const int xcd = blockIdx.x & 7;
+        part = xcd >> 2;
+        g = (int)(blockIdx.x >> 3) * 4 + (xcd & 3);
+    } else {
+        part = (int)blockIdx.x % P.parts;
+        g = (int)blockIdx.x / P.parts;
+    }
     if (g >= n_groups) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int hf = lane >> 5;
     const int col = lane & 31;
-    const int segment = half * (kScoreThreads / kWave) + wave;
+    const int segment = part * (kScoreThreads / kWave) + wave;
+    const int n_segs = P.parts * (kScoreThreads / kWave);
     __shared__ __attribute__((aligned(16))) float s_w[kRowsPerWave][2][16];
     __shared__ uint2 s_stage[kScoreThreads / kWave][kRowsPerWave * kStageSlots];
 
-    const int seg = P.cap / kSegs;
+    const int seg = appended ? P.cap : P.cap / kSegs;  // capacity of this wave's list per row
     float tau_r[kRowsPerWave];
     int row_of[kRowsPerWave];
     bool live[kRowsPerWave];
@@ -474,7 +492,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
         }
         // Segment s covers the contiguous tile range [s*tps, (s+1)*tps).
         const int n_tiles = (int)((n_keys + kKeyTile - 1) / kKeyTile);
-        const int tps = (n_tiles + kSegs - 1) / kSegs;
+        const int tps = (n_tiles + n_segs - 1) / n_segs;
         const int t0 = segment * tps;
         const int n_my = n_tiles > t0 ? min(n_tiles - t0, tps) : 0;
         // Rows of a group are consecutive (invalid rows never store), so every row's
@@ -485,9 +503,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
                              {hf ? live[1] : live[0], hf ? live[3] : live[2], hf ? live[5] : live[4],
                               hf ? live[7] : live[6]},
                              kSample ? P.sample + (size_t)r0 * P.sample_stride : nullptr,
-                             kSample ? nullptr : P.cand + (size_t)r0 * P.cap + (size_t)segment * seg,
+                             kSample ? nullptr : P.cand + (size_t)r0 * P.cap + (appended ? 0 : (size_t)segment * seg),
                              n0, S, kSample && S > 0 ? (float)n0 / (float)S : 0.f, lane, hf, col, col - hf,
-                             (int)(P.pos0 + r0), seg, cnt,
+                             (int)(P.pos0 + r0), r0, seg, cnt,
                              s_stage[wave], {0, 0, 0, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0, 0}, (uint32_t)t0};
         // Tile it sits in buffer it % 3; tile it+3 is loaded once tile it's MFMAs are issued.
         bf16x8 b0[8], b1[8], b2[8];
@@ -523,7 +541,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
     if (!kSample && lane == 0) {
 #pragma unroll
         for (int j = 0; j < kRowsPerWave; ++j)
-            if (r0 + j < P.Lb) P.count[(size_t)(r0 + j) * kSegs + segment] = cnt[j];
+            if (r0 + j < P.Lb && !appended) P.count[(size_t)(r0 + j) * kSegs + segment] = cnt[j];
     }
 }
 
@@ -1036,6 +1054,7 @@ __global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P
         P.fb_ctrl[0] = 0;
         P.fb_ctrl[1] = 0;
     }
+    if (P.parts > 2 && threadIdx.x == 0) P.count[(size_t)r * kSegs] = 0;  // appended list counter
     if (nt <= P.top_k) {
         if (threadIdx.x == 0) {
             P.mode[r] = kModeAll;
@@ -1173,6 +1192,9 @@ __device__ void write_sorted_output(int* sel, int k, int32_t* out_row) {
 }
 
 constexpr int kSelBand = 1024;
+// Appended candidate lists are put back in key order through a bitmap of the causal keys
+// held in the re-score's term array, when the keys fit it.
+constexpr int kSelBitmapKeys = kRescoreRound * kIdxHeads * 64;  // 32 KB of bits
 constexpr int kSelChunk = 16;  // candidates per thread: the block has cap / 16 threads
 
 // Exact top-k of one row's candidates.  The eight segments written by the scoring waves
@@ -1194,13 +1216,15 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
     __shared__ int s_band_pos[kSelBand];
     __shared__ double s_band_s[kSelBand];
     __shared__ uint32_t s_win[kSelChunk * 1024 / 32];
-    const int seg = P.cap / kSegs;
+    // Eight key-ordered segments, or (more key parts) one appended list in no key order.
+    const bool appended = P.parts > 2;
+    const int seg = appended ? P.cap : P.cap / kSegs;
     int cnt[kSegs], start[kSegs];
     int total = 0;
     bool ok = !P.force_fallback;
 #pragma unroll
     for (int w = 0; w < kSegs; ++w) {
-        cnt[w] = P.count[(size_t)r * kSegs + w];
+        cnt[w] = appended && w > 0 ? 0 : P.count[(size_t)r * kSegs + w];
         ok = ok && cnt[w] <= seg;
         start[w] = total;
         total += cnt[w];
@@ -1273,21 +1297,71 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
                 if (band_wins(x, nb, k - n_in, s_band_key, s_band_s))
                     atomicOr(&s_win[s_band_pos[x] >> 5], 1u << (s_band_pos[x] & 31));
             __syncthreads();
-            // Stable compaction: selected = above the band, or a band winner.
-            int c = 0;
+            // Selected = above the band, or a band winner.
+            if (!appended) {
+                // Stable compaction: the candidate list is in key order.
+                int c = 0;
 #pragma unroll
-            for (int e = 0; e < kSelChunk; ++e) {
-                const int j = base + e;
-                c += e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u));
-            }
-            int o = block_incl_scan(c, S) - c;
-#pragma unroll
-            for (int e = 0; e < kSelChunk; ++e) {
-                const int j = base + e;
-                if (e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u))) {
-                    if (o < k) out_row[o] = key[e];
-                    ++o;
+                for (int e = 0; e < kSelChunk; ++e) {
+                    const int j = base + e;
+                    c += e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u));
                 }
+                int o = block_incl_scan(c, S) - c;
+#pragma unroll
+                for (int e = 0; e < kSelChunk; ++e) {
+                    const int j = base + e;
+                    if (e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u))) {
+                        if (o < k) out_row[o] = key[e];
+                        ++o;
+                    }
+                }
+            } else if (nt <= kSelBitmapKeys) {
+                // Appended list (no key order), causal keys within the bitmap: mark the
+                // selected keys, then each thread emits its words' keys at its scanned offset.
+                uint32_t* bm = reinterpret_cast<uint32_t*>(&S.term[0][0]);
+                const int nw = (int)((nt + 31) >> 5);
+                for (int i = threadIdx.x; i < nw; i += blockDim.x) bm[i] = 0u;
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < kSelChunk; ++e) {
+                    const int j = base + e;
+                    if (e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u)))
+                        atomicOr(&bm[key[e] >> 5], 1u << (key[e] & 31));
+                }
+                __syncthreads();
+                const int per = (nw + (int)blockDim.x - 1) / (int)blockDim.x;
+                const int w0 = (int)threadIdx.x * per, w1 = min(nw, w0 + per);
+                int c = 0;
+                for (int i = w0; i < w1; ++i) c += __builtin_popcount(bm[i]);
+                int o = block_incl_scan(c, S) - c;
+                for (int i = w0; i < w1; ++i) {
+                    uint32_t b = bm[i];
+                    while (b) {
+                        const int bit = __builtin_ctz(b);
+                        b &= b - 1u;
+                        if (o < k) out_row[o] = i * 32 + bit;
+                        ++o;
+                    }
+                }
+            } else {
+                // Appended list over a larger key range: gather the selection, then sort it.
+                int c = 0;
+#pragma unroll
+                for (int e = 0; e < kSelChunk; ++e) {
+                    const int j = base + e;
+                    c += e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u));
+                }
+                int o = block_incl_scan(c, S) - c;
+#pragma unroll
+                for (int e = 0; e < kSelChunk; ++e) {
+                    const int j = base + e;
+                    if (e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u))) {
+                        if (o < k) S.out[o] = key[e];
+                        ++o;
+                    }
+                }
+                __syncthreads();
+                write_sorted_output(S.out, k, out_row);
             }
         }
     }
@@ -1443,7 +1517,8 @@ hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks,
 
 hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s) {
     const int groups = (a.Lb + kRowsPerGroup - 1) / kRowsPerGroup;
-    const int score_wgs = 8 * ((groups + 3) / 4);  // two key halves per group, XCD-mapped
+    // Two key halves per group (XCD-mapped) while that fills the GPU, else more key parts.
+    const int score_wgs = a.parts == 2 ? 8 * ((groups + 3) / 4) : groups * a.parts;
     if (need_sample) {
         ProfScope ps(s, kProfScoreSample);
         score_kernel<true><<<score_wgs, kScoreThreads, 0, s>>>(a, groups);

@@ -119,6 +119,13 @@ def test_c4_sampled_rows(dsa_gpu, oracle_mod):
     # band outgrows select's buffer)
     dict(N=1000, L=8, top_k=64, kind="wide"),
     dict(N=3000, L=8, top_k=64, kind="wide"),
+    # few row groups: more key parts per group, candidates appended to one list per row,
+    # the selection put back in key order through a bitmap of the causal keys ...
+    dict(N=131072, L=1, top_k=2048, kind="concentrated"),        # decode: 256 key parts
+    dict(N=50000, L=3, top_k=512, kind="sink"),
+    dict(N=20000, L=200, top_k=700, kind="gauss"),               # 25 groups: 16 key parts
+    # ... or, past 262,144 causal keys, by sorting the selection
+    dict(N=300000, L=2, top_k=2048, kind="gauss"),
 ])
 def test_edge_cases(dsa_gpu, oracle_mod, case):
     q_pos0 = case.get("q_pos0", case["N"] - case["L"])
