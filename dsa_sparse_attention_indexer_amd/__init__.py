@@ -7,6 +7,9 @@ PyTorch fallback; calling any op without the built library raises.
 
     idx = indexer_topk(q_idx, k_idx, w, q_pos0, top_k)       # int32 [L, top_k]
     out = sparse_prefill(q, kv, idx, q_pos0, scale)          # bf16  [L, H, 512]
+
+A batch of sequences of any lengths goes through the *_varlen calls, described by
+host-side cu_q / cu_k offsets and per-sequence start positions pos0.
 """
 from __future__ import annotations
 
@@ -25,9 +28,12 @@ MAX_TOPK = 4096
 D_LATENT = 512
 D_ROPE = 64
 DEFAULT_Q_BLOCK = 1024
+MAX_BATCH = 65536
 
 EXPORTED = ["dsa_indexer_topk_workspace_bytes", "dsa_indexer_topk", "dsa_causal_mask_topk",
             "dsa_sparse_prefill", "dsa_sparse_decode_workspace_bytes", "dsa_sparse_decode",
+            "dsa_indexer_topk_varlen_workspace_bytes", "dsa_indexer_topk_varlen",
+            "dsa_sparse_prefill_varlen_workspace_bytes", "dsa_sparse_prefill_varlen",
             "dsa_sparse_prefill_gate", "dsa_profile_enable",
             "dsa_profile_read", "dsa_status_string", "dsa_last_error", "dsa_version"]
 PROFILE_KERNELS = ["key_stats", "score_sample", "row_prep", "score_filter", "select", "fold",
@@ -64,6 +70,15 @@ def load_library(path: str | None = None):
     lib.dsa_sparse_decode_workspace_bytes.argtypes = [i64, i32, i32, i32]
     lib.dsa_sparse_decode.restype = ctypes.c_int
     lib.dsa_sparse_decode.argtypes = [P, P, i64, P, i64, i64, i32, i32, i32, i32, i64, f32, i32, P, P, P, sz, P]
+    lib.dsa_indexer_topk_varlen_workspace_bytes.restype = sz
+    lib.dsa_indexer_topk_varlen_workspace_bytes.argtypes = [i64, P, P, P, i32, i32]
+    lib.dsa_indexer_topk_varlen.restype = ctypes.c_int
+    lib.dsa_indexer_topk_varlen.argtypes = [P, P, P, i64, P, P, P, i32, i32, i32, i32, P, P, sz, P]
+    lib.dsa_sparse_prefill_varlen_workspace_bytes.restype = sz
+    lib.dsa_sparse_prefill_varlen_workspace_bytes.argtypes = [i64, P, P, P, i32, i32, i32]
+    lib.dsa_sparse_prefill_varlen.restype = ctypes.c_int
+    lib.dsa_sparse_prefill_varlen.argtypes = [P, P, i64, P, i64, P, P, P, i32, i32, i32, i32, f32, i32, P, P,
+                                              P, sz, P]
     lib.dsa_sparse_prefill_gate.restype = ctypes.c_int
     lib.dsa_sparse_prefill_gate.argtypes = [i64, i64, i64, i64]
     lib.dsa_status_string.restype = ctypes.c_char_p
@@ -248,4 +263,98 @@ def sparse_decode(q, kv, idx, q_pos0: int, scale: float, splits: int = 0, return
                                  D_LATENT, D_ROPE, top_k, q_pos0, float(scale), splits, out.data_ptr(),
                                  lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
+    return (out, lse) if return_lse else out
+
+
+def _host_i64(x, name, n):
+    """A host int64 array of n entries (list, tuple, numpy array or CPU tensor)."""
+    vals = [int(v) for v in (x.tolist() if hasattr(x, "tolist") else x)]
+    if len(vals) != n:
+        raise ValueError(f"{name} must have {n} entries (got {len(vals)})")
+    return (ctypes.c_int64 * max(n, 1))(*vals)
+
+
+def _batch(cu_q, cu_k, pos0):
+    B = len(pos0.tolist() if hasattr(pos0, "tolist") else pos0)
+    return B, _host_i64(cu_q, "cu_q", B + 1), _host_i64(cu_k, "cu_k", B + 1), _host_i64(pos0, "pos0", B)
+
+
+def varlen_workspace_bytes(cu_q, cu_k, pos0, top_k: int, q_block: int = DEFAULT_Q_BLOCK) -> int:
+    B, cq, ck, p0 = _batch(cu_q, cu_k, pos0)
+    return int(load_library().dsa_indexer_topk_varlen_workspace_bytes(B, cq, ck, p0, top_k, q_block))
+
+
+def indexer_topk_varlen(q_idx, k_idx, w, cu_q, cu_k, pos0, top_k: int, q_block: int = DEFAULT_Q_BLOCK,
+                        out=None, workspace=None, stream=None):
+    """indexer_topk for each sequence of a packed batch -> int32 [T, top_k].
+
+    Sequence b owns query rows cu_q[b]..cu_q[b+1]-1 of q_idx [T, 32, 128] and w [T, 32],
+    keys cu_k[b]..cu_k[b+1]-1 of k_idx, and its first query sits at position pos0[b].
+    Indices are positions within the sequence.  cu_q, cu_k, pos0 live on the host.
+    """
+    import torch
+
+    lib = load_library()
+    _req(q_idx, "q_idx", torch.bfloat16, 3)
+    _req(k_idx, "k_idx", torch.bfloat16, 2)
+    _req(w, "w", torch.float32, 2)
+    B, cq, ck, p0 = _batch(cu_q, cu_k, pos0)
+    T, nh, hd = q_idx.shape
+    if B > 0 and (cq[B] != T or ck[B] > k_idx.shape[0] or w.shape[0] != T):
+        raise ValueError("cu_q[B] must equal the query rows and cu_k[B] fit k_idx")
+    dev = q_idx.device
+    if out is None:
+        out = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    else:
+        _req(out, "out", torch.int32, 2)
+    need = lib.dsa_indexer_topk_varlen_workspace_bytes(B, cq, ck, p0, top_k, q_block)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    _check(lib.dsa_indexer_topk_varlen(q_idx.data_ptr(), k_idx.data_ptr(), w.data_ptr(), B, cq, ck, p0, nh, hd,
+                                       top_k, q_block, out.data_ptr(), workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), _stream_ptr(q_idx, stream)))
+    return out
+
+
+def prefill_varlen_workspace_bytes(cu_q, cu_k, pos0, H: int, top_k: int, splits: int = 1) -> int:
+    B, cq, ck, p0 = _batch(cu_q, cu_k, pos0)
+    return int(load_library().dsa_sparse_prefill_varlen_workspace_bytes(B, cq, ck, p0, H, top_k, splits))
+
+
+def sparse_prefill_varlen(q, kv, idx, cu_q, cu_k, pos0, scale: float, splits: int = 1, return_lse: bool = False,
+                          out=None, lse=None, workspace=None, stream=None):
+    """sparse_prefill for each sequence of a packed batch -> bf16 [T, H, 512] (and lse).
+
+    q [T, H, 576], idx [T, top_k] (positions within each sequence), kv rows
+    cu_k[b]..cu_k[b+1]-1 belong to sequence b.  splits as sparse_decode (1: one
+    workgroup per query; 0: picked from T).
+    """
+    import torch
+
+    lib = load_library()
+    _req(q, "q", torch.bfloat16, 3)
+    _req(idx, "idx", torch.int32, 2)
+    if not (isinstance(kv, torch.Tensor) and kv.dtype == torch.bfloat16 and kv.dim() == 2 and kv.is_cuda
+            and kv.stride(1) == 1):
+        raise ValueError("kv must be a bf16 GPU tensor [N, stride>=576] with unit column stride")
+    B, cq, ck, p0 = _batch(cu_q, cu_k, pos0)
+    T, H, dqk = q.shape
+    top_k = idx.shape[1]
+    if dqk != D_LATENT + D_ROPE:
+        raise ValueError(f"q must be [T, H, {D_LATENT + D_ROPE}]")
+    if idx.shape[0] != T or (B > 0 and (cq[B] != T or ck[B] > kv.shape[0])):
+        raise ValueError("idx must have T rows, cu_q[B] must equal T and cu_k[B] fit kv")
+    if out is None:
+        out = torch.empty((T, H, D_LATENT), dtype=torch.bfloat16, device=q.device)
+    else:
+        _req(out, "out", torch.bfloat16, 3)
+    if return_lse and lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    need = lib.dsa_sparse_prefill_varlen_workspace_bytes(B, cq, ck, p0, H, top_k, splits)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
+    _check(lib.dsa_sparse_prefill_varlen(q.data_ptr(), kv.data_ptr(), kv.stride(0), idx.data_ptr(), B, cq, ck, p0,
+                                         H, D_LATENT, D_ROPE, top_k, float(scale), splits, out.data_ptr(),
+                                         lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
     return (out, lse) if return_lse else out

@@ -77,7 +77,13 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     const int g = lane >> 4;
     const int c16 = lane & 15;
     const int nthreads = blockDim.x;
-    const int64_t p = A.pos0 + t;
+    int64_t p = A.pos0 + t;
+    const uint16_t* kv = A.kv;
+    if (A.qinfo) {  // a batch: the query's own sequence
+        const QueryInfo qi = A.qinfo[t];
+        p = qi.pos;
+        kv = A.kv + (size_t)qi.kbase * A.kv_stride;
+    }
     const bool compute = wave < A.H / 16;
     const int h = wave * 16 + c16;
     // The K order of the value product (and, to match, the row order of the logits):
@@ -113,7 +119,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
         for (int r = wave; r < kAttnTile; r += nwaves) {
             int key = __builtin_amdgcn_readfirstlane(key_of(slot, r, j * kAttnTile));
             key = key < 0 ? 0 : key;  // masked later; any valid row will do
-            const char* src = reinterpret_cast<const char*>(A.kv + (size_t)key * A.kv_stride);
+            const char* src = reinterpret_cast<const char*>(kv + (size_t)key * A.kv_stride);
             char* dst = reinterpret_cast<char*>(&Kbuf[buf][r][0]);
             dma_lds16(src + lane * 16, dst);
             if (lane < kRowChunks - 64)

@@ -102,6 +102,101 @@ dsa_status_t check_indexer_args(const uint16_t* q_idx, const uint16_t* k_idx, co
     return DSA_OK;
 }
 
+// A batch of sequences given by host arrays cu_q, cu_k [B+1] and pos0 [B]: sequence b has
+// query rows cu_q[b] .. cu_q[b+1]-1 at positions pos0[b] .., and keys (kv rows)
+// cu_k[b] .. cu_k[b+1]-1, indexed 0 .. N_b-1 within it.
+struct Batch {
+    int64_t B = 0, T = 0, NK = 0;  // sequences, query rows, key rows
+    int64_t P = 0;                 // indexer rows: each sequence's run padded to a multiple of 8
+    int64_t n_max = 0;             // most keys any query may see
+    int64_t tiles = 0;             // 32-key tiles over the keys each sequence's queries may see
+};
+
+int64_t round8(int64_t x) { return (x + dsa::kRowsPerGroup - 1) / dsa::kRowsPerGroup * dsa::kRowsPerGroup; }
+int64_t visible_keys(const int64_t* cu_q, const int64_t* pos0, int64_t b) {
+    const int64_t L = cu_q[b + 1] - cu_q[b];
+    return L > 0 ? pos0[b] + L : 0;
+}
+
+dsa_status_t check_batch(int64_t B, const int64_t* cu_q, const int64_t* cu_k, const int64_t* pos0, Batch* out) {
+    *out = Batch{};
+    if (B < 0 || B > DSA_MAX_BATCH)
+        return fail(DSA_ERR_INVALID_ARG, "B must be in 0..%d (got %lld)", DSA_MAX_BATCH, (long long)B);
+    if (B == 0) return DSA_OK;
+    if (!cu_q || !cu_k || !pos0) return fail(DSA_ERR_INVALID_ARG, "null cu_q/cu_k/pos0 host array");
+    if (cu_q[0] != 0 || cu_k[0] != 0) return fail(DSA_ERR_INVALID_ARG, "cu_q[0] and cu_k[0] must be 0");
+    Batch bt;
+    bt.B = B;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t L = cu_q[b + 1] - cu_q[b], N = cu_k[b + 1] - cu_k[b];
+        if (L < 0 || N < 0)
+            return fail(DSA_ERR_INVALID_ARG, "cu_q and cu_k must be non-decreasing (sequence %lld)", (long long)b);
+        if (N > (int64_t)INT32_MAX)
+            return fail(DSA_ERR_UNSUPPORTED, "sequence %lld: more than 2^31-1 keys", (long long)b);
+        if (pos0[b] < 0 || pos0[b] + L > N)
+            return fail(DSA_ERR_INVALID_ARG, "sequence %lld: need 0 <= pos0 and pos0 + L <= N (pos0=%lld L=%lld N=%lld)",
+                        (long long)b, (long long)pos0[b], (long long)L, (long long)N);
+        const int64_t nv = visible_keys(cu_q, pos0, b);
+        bt.P += round8(L);
+        bt.n_max = nv > bt.n_max ? nv : bt.n_max;
+        bt.tiles += (nv + dsa::kKeyTileKeys - 1) / dsa::kKeyTileKeys;
+    }
+    bt.T = cu_q[B];
+    bt.NK = cu_k[B];
+    *out = bt;
+    return DSA_OK;
+}
+
+// Writes the batch tables, kVarlenChunk sequences per launch.
+hipError_t write_batch_tables(int64_t B, const int64_t* cu_q, const int64_t* cu_k, const int64_t* pos0,
+                              dsa::RowInfo* rows, dsa::SeqKeys* seqs, dsa::QueryInfo* qinfo, hipStream_t s) {
+    int64_t row0 = 0, tbase = 0;
+    for (int64_t c0 = 0; c0 < B; c0 += dsa::kVarlenChunk) {
+        dsa::VarlenChunk c{};
+        c.n = (int)((B - c0) < dsa::kVarlenChunk ? (B - c0) : dsa::kVarlenChunk);
+        for (int i = 0; i < c.n; ++i) {
+            const int64_t b = c0 + i;
+            c.qrow0[i] = cu_q[b];
+            c.L[i] = cu_q[b + 1] - cu_q[b];
+            c.row0[i] = row0;
+            c.pos0[i] = pos0[b];
+            c.kbase[i] = cu_k[b];
+            c.nvis[i] = visible_keys(cu_q, pos0, b);
+            c.tbase[i] = tbase;
+            row0 += round8(c.L[i]);
+            tbase += (c.nvis[i] + dsa::kKeyTileKeys - 1) / dsa::kKeyTileKeys;
+        }
+        hipError_t e = dsa::launch_varlen_tables(c, c0, rows, seqs, qinfo, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+int resolve_q_block8(int32_t q_block) { return (int)round8(resolve_q_block(q_block)); }
+
+dsa::IndexerLayout batch_indexer_layout(const Batch& bt, int32_t top_k, int32_t q_block) {
+    const int64_t qb = resolve_q_block8(q_block);
+    const int64_t rows = bt.P < qb ? bt.P : qb;
+    return dsa::IndexerLayout::make(rows < 1 ? 1 : rows, bt.n_max < 1 ? 1 : bt.n_max, top_k, bt.tiles, bt.P, bt.B);
+}
+
+// Checks shared by the attention entry points (everything but positions and workspace).
+dsa_status_t check_attention_shape(int32_t H, int32_t d_latent, int32_t d_rope, int32_t top_k, int64_t kv_stride,
+                                   float scale) {
+    if (top_k < 1) return fail(DSA_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", top_k);
+    if (d_latent != DSA_D_LATENT || d_rope != DSA_D_ROPE)
+        return fail(DSA_ERR_UNSUPPORTED, "need d_latent=%d and d_rope=%d (got %d, %d)", DSA_D_LATENT, DSA_D_ROPE,
+                    d_latent, d_rope);
+    if (H <= 0 || H % 16 != 0 || H > DSA_MAX_HEADS)
+        return fail(DSA_ERR_UNSUPPORTED, "H must be a positive multiple of 16 up to %d (got %d)", DSA_MAX_HEADS, H);
+    if (kv_stride < d_latent + d_rope || kv_stride % 8 != 0)
+        return fail(DSA_ERR_INVALID_ARG, "kv_stride must be >= %d and a multiple of 8 (got %lld)",
+                    d_latent + d_rope, (long long)kv_stride);
+    if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+        return fail(DSA_ERR_INVALID_ARG, "scale must be finite");
+    return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -381,6 +476,185 @@ dsa_status_t dsa_sparse_decode(const uint16_t* q, const uint16_t* kv, int64_t kv
         a.part_ml = part_ml;
         hipError_t e = dsa::launch_sparse_attention_split(a, s);
         if (e != hipSuccess) return hip_fail(e, "split attention launch");
+    }
+    return DSA_OK;
+}
+
+
+size_t dsa_indexer_topk_varlen_workspace_bytes(int64_t B, const int64_t* cu_q, const int64_t* cu_k,
+                                               const int64_t* pos0, int32_t top_k, int32_t q_block) {
+    if (top_k < 1 || top_k > DSA_MAX_TOPK || q_block < 0) return 0;
+    Batch bt;
+    if (check_batch(B, cu_q, cu_k, pos0, &bt) != DSA_OK) {
+        g_last_error[0] = 0;
+        return 0;
+    }
+    if (bt.T == 0) return 0;
+    return batch_indexer_layout(bt, top_k, q_block).total;
+}
+
+dsa_status_t dsa_indexer_topk_varlen(const uint16_t* q_idx, const uint16_t* k_idx, const float* w, int64_t B,
+                                     const int64_t* cu_q, const int64_t* cu_k, const int64_t* pos0,
+                                     int32_t n_heads, int32_t head_dim, int32_t top_k, int32_t q_block,
+                                     int32_t* out_idx, void* workspace, size_t workspace_bytes,
+                                     dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    Batch bt;
+    dsa_status_t st = check_batch(B, cu_q, cu_k, pos0, &bt);
+    if (st != DSA_OK) return st;
+    if (top_k < 1 || top_k > DSA_MAX_TOPK)
+        return fail(DSA_ERR_INVALID_ARG, "top_k must be in 1..%d (got %d)", DSA_MAX_TOPK, top_k);
+    if (q_block < 0) return fail(DSA_ERR_INVALID_ARG, "q_block must be >= 0 (got %d)", q_block);
+    if (n_heads != DSA_INDEX_HEADS || head_dim != DSA_INDEX_DIM)
+        return fail(DSA_ERR_UNSUPPORTED, "indexer needs %d heads x %d dims (got %d x %d)", DSA_INDEX_HEADS,
+                    DSA_INDEX_DIM, n_heads, head_dim);
+    if (bt.T == 0) return DSA_OK;
+    if (!q_idx || !k_idx || !w || !out_idx) return fail(DSA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(w, 4) || !aligned(out_idx, 4))
+        return fail(DSA_ERR_INVALID_ARG, "q_idx/k_idx must be 16-byte aligned, w/out_idx 4-byte aligned");
+    const dsa::IndexerLayout lay = batch_indexer_layout(bt, top_k, q_block);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", lay.total, workspace_bytes,
+                    workspace ? "" : ", null");
+    if (!aligned(workspace, 256)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    dsa::IndexerArgs a{};
+    a.q_idx = q_idx;
+    a.k_idx = k_idx;
+    a.w = w;
+    a.out = out_idx;
+    a.N = bt.n_max;
+    a.top_k = top_k;
+    a.cap = lay.cap;
+    a.sample_stride = lay.sample_stride;
+    a.fold_cap = lay.fold_cap;
+    a.force_fallback = debug_force_fallback() ? 1 : 0;
+    a.kstats = reinterpret_cast<dsa::KeyStats*>(ws + lay.off_kstats);
+    a.qstat = reinterpret_cast<dsa::QHeadStat*>(ws + lay.off_qstat);
+    a.tau = reinterpret_cast<float*>(ws + lay.off_tau);
+    a.delta = reinterpret_cast<float*>(ws + lay.off_delta);
+    a.mode = reinterpret_cast<int*>(ws + lay.off_mode);
+    a.count = reinterpret_cast<int*>(ws + lay.off_count);
+    a.fb_ctrl = reinterpret_cast<int*>(ws + lay.off_fbctrl);
+    a.fb_list = reinterpret_cast<int*>(ws + lay.off_fblist);
+    a.sample = reinterpret_cast<float*>(ws + lay.off_sample);
+    a.cand = reinterpret_cast<uint2*>(ws + lay.off_cand);
+    a.fold_s = reinterpret_cast<float*>(ws + lay.off_fold_s);
+    a.fold_i = reinterpret_cast<int*>(ws + lay.off_fold_i);
+    a.fold_bi = reinterpret_cast<int*>(ws + lay.off_fold_bi);
+    a.fold_bs = reinterpret_cast<double*>(ws + lay.off_fold_bs);
+    a.fold_bf = reinterpret_cast<float*>(ws + lay.off_fold_bf);
+    dsa::RowInfo* rows = reinterpret_cast<dsa::RowInfo*>(ws + lay.off_rowinfo);
+    dsa::SeqKeys* seqs = reinterpret_cast<dsa::SeqKeys*>(ws + lay.off_seqkeys);
+    uint16_t* k_tile = reinterpret_cast<uint16_t*>(ws + lay.off_ktile);
+    a.k_tile = k_tile;
+    a.n_ktiles = bt.tiles;
+
+    // Tables, then the key statistics (over the whole batch) and every sequence's tiled keys.
+    hipError_t e = write_batch_tables(B, cu_q, cu_k, pos0, rows, seqs, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "batch table launch");
+    a.n_kstats = dsa::key_stats_blocks(bt.tiles * dsa::kKeyTileKeys);
+    e = dsa::launch_key_stats_batch(k_idx, seqs, (int)B, bt.tiles, a.kstats, k_tile, s);
+    if (e != hipSuccess) return hip_fail(e, "key statistics launch");
+
+    // Blocks of the padded row space; sequence sq is the first one a block may hold.
+    const int64_t qb = resolve_q_block8(q_block);
+    int64_t sq = 0, sq_row0 = 0;
+    for (int64_t b0 = 0; b0 < bt.P; b0 += qb) {
+        const int64_t Lb = (bt.P - b0) < qb ? (bt.P - b0) : qb;
+        while (sq < B && sq_row0 + round8(cu_q[sq + 1] - cu_q[sq]) <= b0) {
+            sq_row0 += round8(cu_q[sq + 1] - cu_q[sq]);
+            ++sq;
+        }
+        // The most keys a row of this block sees: a sample is needed if its group needs one.
+        int64_t n_last = 0;
+        for (int64_t b = sq, r0 = sq_row0; b < B && r0 < b0 + Lb; r0 += round8(cu_q[b + 1] - cu_q[b]), ++b) {
+            const int64_t L = cu_q[b + 1] - cu_q[b];
+            const int64_t i_last = (b0 + Lb - r0 < L ? b0 + Lb - r0 : L) - 1;
+            if (i_last >= 0 && pos0[b] + i_last + 1 > n_last) n_last = pos0[b] + i_last + 1;
+        }
+        a.rows = rows + b0;
+        a.Lb = (int)Lb;
+        a.parts = dsa::key_parts((int)(Lb / dsa::kRowsPerGroup));
+        e = dsa::launch_indexer_block(a, dsa::sample_size(n_last, top_k, lay.cap) > 0, s);
+        if (e != hipSuccess) return hip_fail(e, "indexer launch");
+    }
+    return DSA_OK;
+}
+
+static size_t varlen_attention_bytes(const Batch& bt, int32_t H, int S, size_t* qinfo_bytes) {
+    const size_t qi = ((size_t)bt.T * sizeof(dsa::QueryInfo) + 255) & ~(size_t)255;
+    if (qinfo_bytes) *qinfo_bytes = qi;
+    return qi + (S > 1 ? dsa::decode_workspace_bytes(bt.T, H, S) : 0);
+}
+
+size_t dsa_sparse_prefill_varlen_workspace_bytes(int64_t B, const int64_t* cu_q, const int64_t* cu_k,
+                                                 const int64_t* pos0, int32_t H, int32_t top_k, int32_t splits) {
+    if (H <= 0 || H % 16 != 0 || H > DSA_MAX_HEADS || top_k < 1 || splits < 0 || splits > dsa::kMaxSplits) return 0;
+    Batch bt;
+    if (check_batch(B, cu_q, cu_k, pos0, &bt) != DSA_OK) {
+        g_last_error[0] = 0;
+        return 0;
+    }
+    if (bt.T == 0) return 0;
+    return varlen_attention_bytes(bt, H, resolve_splits(bt.T, top_k, splits), nullptr);
+}
+
+dsa_status_t dsa_sparse_prefill_varlen(const uint16_t* q, const uint16_t* kv, int64_t kv_stride, const int32_t* idx,
+                                       int64_t B, const int64_t* cu_q, const int64_t* cu_k, const int64_t* pos0,
+                                       int32_t H, int32_t d_latent, int32_t d_rope, int32_t top_k, float scale,
+                                       int32_t splits, uint16_t* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    Batch bt;
+    dsa_status_t st = check_batch(B, cu_q, cu_k, pos0, &bt);
+    if (st != DSA_OK) return st;
+    st = check_attention_shape(H, d_latent, d_rope, top_k, kv_stride, scale);
+    if (st != DSA_OK) return st;
+    if (splits < 0 || splits > dsa::kMaxSplits)
+        return fail(DSA_ERR_INVALID_ARG, "splits must be in 0..%d (got %d)", dsa::kMaxSplits, splits);
+    if (bt.T == 0) return DSA_OK;
+    if (!q || !kv || !idx || !out) return fail(DSA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(idx, 4) || !aligned(out, 8) || (lse && !aligned(lse, 4)))
+        return fail(DSA_ERR_INVALID_ARG, "q/kv must be 16-byte aligned, out 8-byte, idx/lse 4-byte");
+    const int S = resolve_splits(bt.T, top_k, splits);
+    size_t qi_bytes = 0;
+    const size_t need = varlen_attention_bytes(bt, H, S, &qi_bytes);
+    if (!workspace || workspace_bytes < need)
+        return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                    workspace ? "" : ", null");
+    if (!aligned(workspace, 256)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    dsa::QueryInfo* qinfo = static_cast<dsa::QueryInfo*>(workspace);
+    hipError_t e = write_batch_tables(B, cu_q, cu_k, pos0, nullptr, nullptr, qinfo, s);
+    if (e != hipSuccess) return hip_fail(e, "batch table launch");
+    float* part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + qi_bytes);
+    const int64_t rows = bt.T < dsa::kDecodeRows ? bt.T : dsa::kDecodeRows;
+    float* part_ml = part_o + (size_t)rows * S * H * 512;
+    const int64_t qb = S > 1 ? dsa::kDecodeRows : DSA_DEFAULT_Q_BLOCK;
+    for (int64_t b0 = 0; b0 < bt.T; b0 += qb) {
+        dsa::AttentionArgs a{};
+        const int64_t Lb = (bt.T - b0) < qb ? (bt.T - b0) : qb;
+        a.q = q + (size_t)b0 * H * (d_latent + d_rope);
+        a.kv = kv;
+        a.idx = idx + (size_t)b0 * top_k;
+        a.out = out + (size_t)b0 * H * d_latent;
+        a.lse = lse ? lse + (size_t)b0 * H : nullptr;
+        a.kv_stride = kv_stride;
+        a.N = bt.n_max;
+        a.qinfo = qinfo + b0;
+        a.Lb = (int)Lb;
+        a.H = H;
+        a.top_k = top_k;
+        a.scale = scale;
+        a.splits = S;
+        a.part_o = part_o;
+        a.part_ml = part_ml;
+        e = S > 1 ? dsa::launch_sparse_attention_split(a, s) : dsa::launch_sparse_attention(a, s);
+        if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
     }
     return DSA_OK;
 }

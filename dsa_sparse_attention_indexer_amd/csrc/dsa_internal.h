@@ -6,7 +6,7 @@
 
 namespace dsa {
 
-enum : int { kModeNormal = 0, kModeAll = 1 };
+enum : int { kModeNormal = 0, kModeAll = 1, kModePad = 2 };
 
 struct KeyStats {
     unsigned knorm_bits;  // max ||k_s||_2 (fp32 bits, rounded up)
@@ -104,7 +104,12 @@ struct IndexerLayout {
     size_t off_fold_s, off_fold_i, off_fold_bi, off_fold_bs, off_fold_bf;
     size_t total;
 
-    static IndexerLayout make(int64_t rows, int64_t N, int top_k) {
+    // rows: block rows; N: the most keys a query may see.  A batch of sequences also needs
+    // the tiled copies of all of them (key_tiles), its row table (row_infos) and its
+    // per-sequence key table (n_seqs).
+    size_t off_rowinfo, off_seqkeys;
+    static IndexerLayout make(int64_t rows, int64_t N, int top_k, int64_t key_tiles = -1, int64_t row_infos = 0,
+                              int64_t n_seqs = 0) {
         IndexerLayout l{};
         auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
         l.rows = (int)((rows + kRowsPerGroup - 1) & ~(int64_t)(kRowsPerGroup - 1));
@@ -121,20 +126,65 @@ struct IndexerLayout {
         l.off_fblist = o; o = al(o + 4 * (size_t)l.rows);
         l.off_sample = o; o = al(o + 4 * (size_t)l.rows * (size_t)l.sample_stride);
         l.off_cand = o; o = al(o + 8 * (size_t)l.rows * (size_t)l.cap);
-        l.off_ktile = o; o = al(o + key_tile_bytes(N));
+        l.off_ktile = o; o = al(o + (key_tiles < 0 ? key_tile_bytes(N) : (size_t)key_tiles * kKeyTileBytes));
         l.off_qstat = o; o = al(o + sizeof(QHeadStat) * 32 * (size_t)l.rows);
         l.off_fold_s = o; o = al(o + 4 * (size_t)kFallbackSlots * 2 * l.fold_cap);
         l.off_fold_i = o; o = al(o + 4 * (size_t)kFallbackSlots * 2 * l.fold_cap);
         l.off_fold_bi = o; o = al(o + 4 * (size_t)kFallbackSlots * l.fold_cap);
         l.off_fold_bs = o; o = al(o + 8 * (size_t)kFallbackSlots * l.fold_cap);
         l.off_fold_bf = o; o = al(o + 4 * (size_t)kFallbackSlots * l.fold_cap);
+        l.off_rowinfo = o; o = al(o + 40 * (size_t)row_infos);
+        l.off_seqkeys = o; o = al(o + 32 * (size_t)n_seqs);
         l.total = o;
         return l;
     }
 };
 
+// A batched block packs the query rows of one or more sequences, each sequence's run padded
+// to a multiple of the row group, so row groups never straddle sequences.  Per block row:
+struct RowInfo {
+    int64_t qrow;   // row of q_idx / w / out (of the whole batch); -1 for a padding row
+    int64_t pos;    // the query's position in its sequence
+    int64_t kbase;  // the sequence's first key in k_idx
+    int64_t tbase;  // the sequence's first 32-key tile in the tiled key copy
+    int64_t nkeys;  // keys of the sequence that any of its queries may see (last position + 1)
+};
+
+static_assert(sizeof(RowInfo) == 40, "row table entry");
+
+// A sequence's keys in a batch: where they start in k_idx, how many any of its queries may
+// see, and the range [tbase, tend) of its 32-key tiles in the tiled copy.
+struct SeqKeys {
+    int64_t kbase, nkeys, tbase, tend;
+};
+static_assert(sizeof(SeqKeys) == 32, "sequence table entry");
+
+// Per query row of a batch, for the attention: the sequence's first kv row and the query's position.
+struct QueryInfo {
+    int64_t kbase, pos;
+};
+
+// Up to kVarlenChunk sequences of a batch, passed by value to the kernel that writes the
+// tables above (so the tables need no host-to-device copy).
+constexpr int kVarlenChunk = 32;
+struct VarlenChunk {
+    int n;
+    int64_t qrow0[kVarlenChunk];  // first query row of the sequence in the batch
+    int64_t L[kVarlenChunk];      // its query rows
+    int64_t row0[kVarlenChunk];   // its first row in the padded row space of the indexer
+    int64_t pos0[kVarlenChunk];   // position of its first query
+    int64_t kbase[kVarlenChunk];  // its first key (kv row)
+    int64_t nvis[kVarlenChunk];   // keys its queries may see: pos0 + L (0 if L == 0)
+    int64_t tbase[kVarlenChunk];  // its first tile in the tiled key copy
+};
+// Writes, for sequences seq0 .. seq0 + c.n - 1: their rows of the padded row table (rows,
+// padding rows qrow = -1), their SeqKeys entries (seqs) and their query rows of the
+// attention table (qinfo); null outputs are skipped.
+hipError_t launch_varlen_tables(const VarlenChunk& c, int64_t seq0, RowInfo* rows, SeqKeys* seqs,
+                                QueryInfo* qinfo, hipStream_t s);
+
 struct IndexerArgs {
-    const uint16_t* q_idx;  // rows of this block: [Lb][32][128]
+    const uint16_t* q_idx;  // rows of this block: [Lb][32][128] (batched: the whole batch's rows)
     const uint16_t* k_idx;  // [N][128]
     const uint16_t* k_tile; // keys 0..n_ktiles*32-1 in scoring tile order (pad keys zero)
     int64_t n_ktiles;
@@ -142,6 +192,7 @@ struct IndexerArgs {
     int32_t* out;           // [Lb][top_k]
     int64_t N;
     int64_t pos0;           // position of the block's first query
+    const RowInfo* rows;    // batched: [Lb] per block row (null: one sequence, row r at pos0 + r)
     int Lb;
     int top_k;
     int cap;
@@ -188,6 +239,9 @@ struct ProfScope {
 
 // Kernel launchers (indexer.hip).  Each returns the launch status.
 hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, uint16_t* k_tile, hipStream_t s);
+// The same over a batch: seqs[0 .. n_seqs) (device), n_tiles tiles in all.
+hipError_t launch_key_stats_batch(const uint16_t* k_idx, const SeqKeys* seqs, int n_seqs, int64_t n_tiles,
+                                  KeyStats* ks, uint16_t* k_tile, hipStream_t s);
 hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s);
 hipError_t launch_causal_mask(int32_t* idx, int64_t L, int top_k, int64_t q_pos0, hipStream_t s);
 
@@ -200,6 +254,7 @@ struct AttentionArgs {
     int64_t kv_stride;
     int64_t N;
     int64_t pos0;
+    const QueryInfo* qinfo;  // batch: [Lb] per query (null: one sequence, query t at pos0 + t)
     int Lb, H, top_k;
     float scale;
     // Split over the keys (decode): splits > 1 sends split s of query t to workgroup (t, s),

@@ -41,6 +41,32 @@ namespace dsa {
 
 constexpr int kSegs = kCandSegs;  // candidate segments per row: (key half, scoring wave)
 
+// Where block row r's query, weights, output and keys live.
+struct RowRef {
+    const uint16_t* q;     // [32][128]
+    const float* w;        // [32]
+    int32_t* out;          // [top_k]
+    const uint16_t* keys;  // the sequence's k_idx rows
+    int64_t pos;           // position in the sequence
+    int64_t nkeys;         // keys of the sequence any of its queries may see
+    int64_t tbase;         // the sequence's first tile in the tiled key copy
+    int64_t ntiles;        // ... and its tile count there
+    bool valid;            // a query row (not a padding or past-the-end row)
+};
+__device__ __forceinline__ RowRef row_ref(const IndexerArgs& P, int r) {
+    if (!P.rows) {
+        const int rr = r < P.Lb ? r : 0;
+        return RowRef{P.q_idx + (size_t)rr * kIdxHeads * kIdxDim, P.w + (size_t)rr * kIdxHeads,
+                      P.out + (size_t)rr * P.top_k, P.k_idx, P.pos0 + rr, P.N, 0, P.n_ktiles, r < P.Lb};
+    }
+    const RowInfo ri = P.rows[r < P.Lb ? r : 0];
+    const bool v = r < P.Lb && ri.qrow >= 0;
+    const int64_t q = ri.qrow >= 0 ? ri.qrow : 0;
+    return RowRef{P.q_idx + (size_t)q * kIdxHeads * kIdxDim, P.w + (size_t)q * kIdxHeads,
+                  P.out + (size_t)q * P.top_k, P.k_idx + (size_t)ri.kbase * kIdxDim, ri.pos, ri.nkeys,
+                  ri.tbase, (ri.nkeys + kKeyTileKeys - 1) / kKeyTileKeys, v};
+}
+
 // ------------------------------------------------------------------ helpers
 
 __device__ __forceinline__ int bf16_lsb_exp(uint16_t b) {
@@ -114,23 +140,40 @@ static_assert(kKeyTileKeys == kKeyTile, "scoring tiles and the tiled key copy di
 // and written as eight 1-KB stores in the scoring order.  Keys past the end are zero.
 constexpr int kStatsThreads = 256;
 constexpr int kStatsRowPad = 17;  // LDS row stride in 16-byte chunks (16 + 1 against bank conflicts)
+// seqs == null: one sequence of n_keys keys.  Otherwise tile t belongs to the sequence whose
+// tile range holds it, and its keys are that sequence's.
 __global__ __launch_bounds__(kStatsThreads) void key_stats_kernel(const uint16_t* __restrict__ k_idx,
-                                                                  int64_t n_keys, KeyStats* slots,
+                                                                  int64_t n_keys, const SeqKeys* seqs,
+                                                                  int n_seqs, int64_t n_tiles,
+                                                                  KeyStats* slots,
                                                                   uint16_t* __restrict__ k_tile) {
     __shared__ u16x8 s_t[kStatsThreads / kWave][kKeyTileKeys * kStatsRowPad];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     u16x8* st = s_t[wave];
     float nmax = 0.f, amax = 0.f;
     int emin = INT_MAX;
-    const int64_t n_tiles = (n_keys + kKeyTileKeys - 1) / kKeyTileKeys;
     const int64_t n_waves = (int64_t)gridDim.x * (kStatsThreads / kWave);
     for (int64_t t = (int64_t)blockIdx.x * (kStatsThreads / kWave) + wave; t < n_tiles; t += n_waves) {
+        const uint16_t* src = k_idx;
+        int64_t kn = n_keys, tl = t;
+        if (seqs) {  // first sequence whose tiles end after t (wave-uniform search)
+            int lo = 0, hi = n_seqs - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (t < seqs[mid].tend) hi = mid;
+                else lo = mid + 1;
+            }
+            const SeqKeys sk = seqs[lo];
+            src = k_idx + (size_t)sk.kbase * kIdxDim;
+            kn = sk.nkeys;
+            tl = t - sk.tbase;
+        }
         u16x8 v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {  // chunk q = 64 i + lane: key q / 16 of the tile, dims 8 (q % 16) ..
             const int q = i * 64 + lane;
-            const int64_t key = t * kKeyTileKeys + (q >> 4);
-            v[i] = key < n_keys ? reinterpret_cast<const u16x8*>(k_idx + key * kIdxDim)[q & 15] : u16x8{};
+            const int64_t key = tl * kKeyTileKeys + (q >> 4);
+            v[i] = key < kn ? reinterpret_cast<const u16x8*>(src + key * kIdxDim)[q & 15] : u16x8{};
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -257,6 +300,9 @@ __device__ __forceinline__ void interleave_with_mfma() {
 template <bool kSample>
 struct ScoreTile {
     const IndexerArgs& P;
+    const uint16_t* keys;       // the group's sequence: k_idx rows (sample)
+    const u16x8* ktile;         // ... and its tiled copy (filter)
+    uint32_t n_kt;              // ... tiles of that copy
     const bf16x8 (&a)[kRowsPerWave][8];
     const float (&wl)[kRowsPerWave];  // per row: lane 16g + e holds the weight of its half's head e
     // Per lane half: parameters of row 2q + hf of row pair q.
@@ -286,12 +332,12 @@ struct ScoreTile {
     __device__ __forceinline__ void load(bf16x8 (&b)[8], int it) const {
         if (kSample) {
             const uint32_t key = min((uint32_t)((float)pos_of(it) * s_ratio), n0 - 1u);
-            const u16x8* kp = reinterpret_cast<const u16x8*>(P.k_idx + (size_t)key * kIdxDim + hf * 64);
+            const u16x8* kp = reinterpret_cast<const u16x8*>(keys + (size_t)key * kIdxDim + hf * 64);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) b[kk] = __builtin_bit_cast(bf16x8, kp[kk]);
         } else {
-            const uint32_t t = min(tile0 + (uint32_t)it, (uint32_t)P.n_ktiles - 1u);
-            const u16x8* kp = reinterpret_cast<const u16x8*>(P.k_tile) + (size_t)t * (kKeyTileBytes / 16) + lane;
+            const uint32_t t = min(tile0 + (uint32_t)it, n_kt - 1u);
+            const u16x8* kp = ktile + (size_t)t * (kKeyTileBytes / 16) + lane;
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) b[kk] = __builtin_bit_cast(bf16x8, kp[kk * 64]);
         }
@@ -440,17 +486,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
 
     const int seg = appended ? P.cap : P.cap / kSegs;  // capacity of this wave's list per row
     float tau_r[kRowsPerWave];
-    int row_of[kRowsPerWave];
     bool live[kRowsPerWave];
     int64_t n_keys = 0;
     const int r0 = g * kRowsPerWave;
+    const RowRef gref = row_ref(P, r0);  // a group's rows share one sequence
+    const uint16_t* qrow[kRowsPerWave];
+    const float* wrow[kRowsPerWave];
     uint32_t S = 0, n0 = 0;
 #pragma unroll
     for (int j = 0; j < kRowsPerWave; ++j) {
         const int r = r0 + j;
-        const bool valid = r < P.Lb;
-        row_of[j] = valid ? r : r0;
-        const int64_t p = P.pos0 + r;  // <= N - 1
+        const RowRef ref = row_ref(P, r);
+        const bool valid = ref.valid;
+        qrow[j] = valid ? ref.q : gref.q;
+        wrow[j] = valid ? ref.w : gref.w;
+        const int64_t p = ref.pos;  // <= nkeys - 1
         if (kSample) {
             live[j] = valid;
             tau_r[j] = 0.f;
@@ -462,7 +512,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
         }
     }
     if (kSample) {
-        const int64_t p = P.pos0 + r0;
+        const int64_t p = gref.pos;
         n0 = (uint32_t)(p + 1);
         S = (uint32_t)sample_size(n0, P.top_k, P.cap);
         n_keys = S;
@@ -470,7 +520,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
     // Weights in the order each lane half reads them: head 8*(i/4) + 4*half + i%4.
     {
         const int j = threadIdx.x >> 5, h2 = (threadIdx.x >> 4) & 1, i = threadIdx.x & 15;
-        s_w[j][h2][i] = P.w[(size_t)row_of[j] * kIdxHeads + 8 * (i >> 2) + 4 * h2 + (i & 3)];
+        s_w[j][h2][i] = wrow[j][8 * (i >> 2) + 4 * h2 + (i & 3)];
     }
     __syncthreads();
     float wl[kRowsPerWave];
@@ -482,8 +532,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
         bf16x8 a[kRowsPerWave][8];
 #pragma unroll
         for (int j = 0; j < kRowsPerWave; ++j) {
-            const u16x8* qp = reinterpret_cast<const u16x8*>(
-                P.q_idx + ((size_t)row_of[j] * kIdxHeads + col) * kIdxDim + hf * 64);
+            const u16x8* qp = reinterpret_cast<const u16x8*>(qrow[j] + (size_t)col * kIdxDim + hf * 64);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 a[j][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
@@ -497,7 +546,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
         const int n_my = n_tiles > t0 ? min(n_tiles - t0, tps) : 0;
         // Rows of a group are consecutive (invalid rows never store), so every row's
         // list is addressed from row 0's.
-        ScoreTile<kSample> T{P, a, wl,
+        ScoreTile<kSample> T{P, gref.keys,
+                             reinterpret_cast<const u16x8*>(P.k_tile) + (size_t)gref.tbase * (kKeyTileBytes / 16),
+                             (uint32_t)gref.ntiles, a, wl,
                              {hf ? tau_r[1] : tau_r[0], hf ? tau_r[3] : tau_r[2], hf ? tau_r[5] : tau_r[4],
                               hf ? tau_r[7] : tau_r[6]},
                              {hf ? live[1] : live[0], hf ? live[3] : live[2], hf ? live[5] : live[4],
@@ -505,7 +556,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
                              kSample ? P.sample + (size_t)r0 * P.sample_stride : nullptr,
                              kSample ? nullptr : P.cand + (size_t)r0 * P.cap + (appended ? 0 : (size_t)segment * seg),
                              n0, S, kSample && S > 0 ? (float)n0 / (float)S : 0.f, lane, hf, col, col - hf,
-                             (int)(P.pos0 + r0), r0, seg, cnt,
+                             (int)gref.pos, r0, seg, cnt,
                              s_stage[wave], {0, 0, 0, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0, 0}, (uint32_t)t0};
         // Tile it sits in buffer it % 3; tile it+3 is loaded once tile it's MFMAs are issued.
         bf16x8 b0[8], b1[8], b2[8];
@@ -541,7 +592,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
     if (!kSample && lane == 0) {
 #pragma unroll
         for (int j = 0; j < kRowsPerWave; ++j)
-            if (r0 + j < P.Lb && !appended) P.count[(size_t)(r0 + j) * kSegs + segment] = cnt[j];
+            if (r0 + j < P.Lb && !appended) P.count[(size_t)(r0 + j) * kSegs + segment] = cnt[j];  // pad rows too (0)
     }
 }
 
@@ -1044,8 +1095,9 @@ constexpr int kRowPrepThreads = 256;  // 8 threads per head; one radix bin per t
 
 __global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P) {
     const int r = blockIdx.x;
-    const int64_t p = P.pos0 + r;
-    const int64_t nt = (p < P.N - 1 ? p : P.N - 1) + 1;
+    const RowRef ref = row_ref(P, r);
+    const int64_t p = ref.pos;
+    const int64_t nt = (p < ref.nkeys - 1 ? p : ref.nkeys - 1) + 1;
     __shared__ double s_l1[kIdxHeads], s_l2[kIdxHeads];
     __shared__ int s_eq[kIdxHeads];
     __shared__ float s_delta;
@@ -1055,6 +1107,14 @@ __global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P
         P.fb_ctrl[1] = 0;
     }
     if (P.parts > 2 && threadIdx.x == 0) P.count[(size_t)r * kSegs] = 0;  // appended list counter
+    if (!ref.valid) {  // padding row of a batched block: nothing to select
+        if (threadIdx.x == 0) {
+            P.mode[r] = kModePad;
+            P.tau[r] = INFINITY;
+            P.delta[r] = 0.f;
+        }
+        return;
+    }
     if (nt <= P.top_k) {
         if (threadIdx.x == 0) {
             P.mode[r] = kModeAll;
@@ -1066,7 +1126,7 @@ __global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P
     // Per-head |q|_1, |q|_2^2 and lowest set-bit exponent (8 threads per head).
     {
         const int h = threadIdx.x >> 3, part = threadIdx.x & 7;
-        const u16x8* qp = reinterpret_cast<const u16x8*>(P.q_idx + ((size_t)r * kIdxHeads + h) * kIdxDim + part * 16);
+        const u16x8* qp = reinterpret_cast<const u16x8*>(ref.q + (size_t)h * kIdxDim + part * 16);
         double l1 = 0.0, l2 = 0.0;
         int em = INT_MAX;
         for (int c = 0; c < 2; ++c) {
@@ -1124,7 +1184,7 @@ __global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P
         int emin = INT_MAX;
         bool used = false, subnormal = false;
         if (h < kIdxHeads) {
-            const float wh = P.w[(size_t)r * kIdxHeads + h];
+            const float wh = ref.w[h];
             dsum = fabs((double)wh) * sqrt(s_l2[h]);
             if (wh != 0.f && s_l1[h] > 0.0) {
                 used = true;
@@ -1163,8 +1223,8 @@ __global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P
     }
     __syncthreads();
     const int g0 = r & ~(kRowsPerGroup - 1);
-    const int64_t pg = P.pos0 + g0;
-    const int64_t n0 = (pg < P.N - 1 ? pg : P.N - 1) + 1;
+    const int64_t pg = row_ref(P, g0).pos;  // the group's first row (same sequence)
+    const int64_t n0 = (pg < ref.nkeys - 1 ? pg : ref.nkeys - 1) + 1;
     const int Sn = sample_size(n0, P.top_k, P.cap);
     if (Sn == 0) {  // the whole group keeps every causal key (at most cap per row)
         if (threadIdx.x == 0) P.tau[r] = -INFINITY;
@@ -1203,11 +1263,14 @@ constexpr int kSelChunk = 16;  // candidates per thread: the block has cap / 16 
 // ascending output is a stable compaction (one block scan) of the selected positions.
 __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
     const int r = blockIdx.x;
-    const int64_t p = P.pos0 + r;
-    const int64_t nt = (p < P.N - 1 ? p : P.N - 1) + 1;
+    const int mode = P.mode[r];
+    if (mode == kModePad) return;
+    const RowRef ref = row_ref(P, r);
+    const int64_t p = ref.pos;
+    const int64_t nt = (p < ref.nkeys - 1 ? p : ref.nkeys - 1) + 1;
     const int k = P.top_k;
-    int32_t* out_row = P.out + (size_t)r * k;
-    if (P.mode[r] == kModeAll) {
+    int32_t* out_row = ref.out;
+    if (mode == kModeAll) {
         for (int j = threadIdx.x; j < k; j += blockDim.x) out_row[j] = j < nt ? j : -1;
         return;
     }
@@ -1291,8 +1354,7 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
         ok = nb <= kSelBand && n_in < k && n_in + nb >= k;
         if (ok) {
             if (delta > 0.f && nb > 0)
-                band_rescore(nb, s_band_key, s_band_s, P.q_idx + (size_t)r * kIdxHeads * kIdxDim,
-                             P.w + (size_t)r * kIdxHeads, P.qstat + (size_t)r * kIdxHeads, P.k_idx, S);
+                band_rescore(nb, s_band_key, s_band_s, ref.q, ref.w, P.qstat + (size_t)r * kIdxHeads, ref.keys, S);
             for (int x = threadIdx.x; x < nb; x += blockDim.x)
                 if (band_wins(x, nb, k - n_in, s_band_key, s_band_s))
                     atomicOr(&s_win[s_band_pos[x] >> 5], 1u << (s_band_pos[x] & 31));
@@ -1375,23 +1437,23 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
 
 // Scores keys [k0, k1) of one row with MFMA (one 32-key tile per wave per step) and
 // appends those with score > lo to (dst_s, dst_i) at *cnt (LDS counter).
-__device__ void fold_score_block(const IndexerArgs& P, int r, int64_t k0, int64_t k1, float lo,
+__device__ void fold_score_block(const RowRef& R, int64_t k0, int64_t k1, float lo,
                                  float* dst_s, int* dst_i, int* cnt, int cap) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int hf = lane >> 5, col = lane & 31;
     const int n_waves = blockDim.x >> 6;
-    const u16x8* qp = reinterpret_cast<const u16x8*>(P.q_idx + ((size_t)r * kIdxHeads + col) * kIdxDim + hf * 8);
+    const u16x8* qp = reinterpret_cast<const u16x8*>(R.q + (size_t)col * kIdxDim + hf * 8);
     bf16x8 a[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) a[kk] = __builtin_bit_cast(bf16x8, qp[2 * kk]);
     float wf[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) wf[i] = P.w[(size_t)r * kIdxHeads + 8 * (i >> 2) + 4 * hf + (i & 3)];
+    for (int i = 0; i < 16; ++i) wf[i] = R.w[8 * (i >> 2) + 4 * hf + (i & 3)];
     const int64_t n_tiles = (k1 - k0 + kKeyTile - 1) / kKeyTile;
     for (int64_t ti = wave; ti < n_tiles; ti += n_waves) {
         const int64_t pos = k0 + ti * kKeyTile + col;
         const int64_t key = pos < k1 ? pos : k1 - 1;
-        const u16x8* kp = reinterpret_cast<const u16x8*>(P.k_idx + key * kIdxDim + hf * 8);
+        const u16x8* kp = reinterpret_cast<const u16x8*>(R.keys + key * kIdxDim + hf * 8);
         f32x16 acc = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) acc = mfma_32x32x16(a[kk], __builtin_bit_cast(bf16x8, kp[2 * kk]), acc);
@@ -1441,18 +1503,19 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
         const int r = s_row;
         __syncthreads();
         if (r < 0) return;
-        const int64_t p = P.pos0 + r;
-        const int64_t nt = (p < P.N - 1 ? p : P.N - 1) + 1;
+        const RowRef ref = row_ref(P, r);
+        const int64_t p = ref.pos;
+        const int64_t nt = (p < ref.nkeys - 1 ? p : ref.nkeys - 1) + 1;
         const float delta = P.delta[r];
-        const uint16_t* q_row = P.q_idx + (size_t)r * kIdxHeads * kIdxDim;
-        const float* w_row = P.w + (size_t)r * kIdxHeads;
+        const uint16_t* q_row = ref.q;
+        const float* w_row = ref.w;
         int cur = 0, n = 0;
         float lo = -INFINITY;
         for (int64_t b0 = 0; b0 < nt; b0 += kFoldKeys) {
             const int64_t b1 = b0 + kFoldKeys < nt ? b0 + kFoldKeys : nt;
             if (threadIdx.x == 0) s_cnt = n;
             __syncthreads();
-            fold_score_block(P, r, b0, b1, lo, Rs[cur], Ri[cur], &s_cnt, P.fold_cap);
+            fold_score_block(ref, b0, b1, lo, Rs[cur], Ri[cur], &s_cnt, P.fold_cap);
             __syncthreads();
             n = s_cnt < P.fold_cap ? s_cnt : P.fold_cap;
             __syncthreads();
@@ -1464,7 +1527,7 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
                 L.i[0] = Ri[cur];
                 L.n[0] = n;
                 L.nseg = 1;
-                const bool ok = select_core(L, k, delta, q_row, w_row, P.qstat + (size_t)r * kIdxHeads, P.k_idx,
+                const bool ok = select_core(L, k, delta, q_row, w_row, P.qstat + (size_t)r * kIdxHeads, ref.keys,
                                             band_i, band_s, band_f,
                                             P.fold_cap, Ri[nxt], Rs[nxt], S);
                 (void)ok;  // band capacity == list capacity
@@ -1484,7 +1547,7 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
                 lo = lf;
             }
         }
-        int32_t* out_row = P.out + (size_t)r * k;
+        int32_t* out_row = ref.out;
         // n == k here (nt > k for every scored row): the list is the exact top-k.
         for (int j = threadIdx.x; j < k; j += blockDim.x) S.out[j] = j < n ? Ri[cur][j] : -1;
         __syncthreads();
@@ -1511,7 +1574,44 @@ hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks,
     ProfScope ps(s, kProfKeyStats);
     static_assert(kStatsThreads / kWave == 4 && kKeyTileKeys == 32, "key_stats_blocks assumes 4 waves of 32-key tiles");
     const int blocks = key_stats_blocks(n_keys);
-    key_stats_kernel<<<blocks, kStatsThreads, 0, s>>>(k_idx, n_keys, ks, k_tile);
+    key_stats_kernel<<<blocks, kStatsThreads, 0, s>>>(k_idx, n_keys, nullptr, 0,
+                                                     (n_keys + kKeyTileKeys - 1) / kKeyTileKeys, ks, k_tile);
+    return hipGetLastError();
+}
+
+hipError_t launch_key_stats_batch(const uint16_t* k_idx, const SeqKeys* seqs, int n_seqs, int64_t n_tiles,
+                                  KeyStats* ks, uint16_t* k_tile, hipStream_t s) {
+    ProfScope ps(s, kProfKeyStats);
+    const int blocks = key_stats_blocks(n_tiles * kKeyTileKeys);
+    key_stats_kernel<<<blocks, kStatsThreads, 0, s>>>(k_idx, 0, seqs, n_seqs, n_tiles, ks, k_tile);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ batch tables
+
+__global__ void varlen_tables_kernel(VarlenChunk c, int64_t seq0, RowInfo* rows, SeqKeys* seqs,
+                                     QueryInfo* qinfo) {
+    const int b = blockIdx.y;
+    const int64_t L = c.L[b];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (rows) {
+        const int64_t padded = (L + kRowsPerGroup - 1) / kRowsPerGroup * kRowsPerGroup;
+        for (int64_t i = i0; i < padded; i += stride)
+            rows[c.row0[b] + i] = RowInfo{i < L ? c.qrow0[b] + i : -1, c.pos0[b] + i, c.kbase[b], c.tbase[b],
+                                          c.nvis[b]};
+    }
+    if (qinfo)
+        for (int64_t i = i0; i < L; i += stride) qinfo[c.qrow0[b] + i] = QueryInfo{c.kbase[b], c.pos0[b] + i};
+    if (seqs && i0 == 0)
+        seqs[seq0 + b] = SeqKeys{c.kbase[b], c.nvis[b], c.tbase[b],
+                                 c.tbase[b] + (c.nvis[b] + kKeyTileKeys - 1) / kKeyTileKeys};
+}
+
+hipError_t launch_varlen_tables(const VarlenChunk& c, int64_t seq0, RowInfo* rows, SeqKeys* seqs,
+                                QueryInfo* qinfo, hipStream_t s) {
+    if (c.n <= 0) return hipSuccess;
+    varlen_tables_kernel<<<dim3(4, c.n), 256, 0, s>>>(c, seq0, rows, seqs, qinfo);
     return hipGetLastError();
 }
 

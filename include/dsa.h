@@ -5,6 +5,8 @@
  *   dsa_indexer_topk     indexer scores + exact top-k with causal masking
  *   dsa_causal_mask_topk causal masking of an externally supplied index tensor
  *   dsa_sparse_prefill   sparse absorbed-MLA attention over the selected keys
+ * plus the split-key attention for decode and short chunks (dsa_sparse_decode)
+ * and a batch of sequences of any lengths per call (the *_varlen entry points).
  *
  * Conventions shared by every entry point
  *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense,
@@ -50,6 +52,7 @@ typedef enum {
 #define DSA_D_ROPE 64        /* rope width; key/query width is 576            */
 #define DSA_MAX_HEADS 128    /* attention heads: a multiple of 16, <= 128     */
 #define DSA_DEFAULT_Q_BLOCK 1024
+#define DSA_MAX_BATCH 65536  /* sequences per *_varlen call                   */
 
 /*
  * Bytes of device workspace dsa_indexer_topk needs for these sizes.  The
@@ -163,6 +166,62 @@ dsa_status_t dsa_sparse_decode(const uint16_t* q, const uint16_t* kv, int64_t kv
                                int32_t d_latent, int32_t d_rope, int32_t top_k, int64_t q_pos0,
                                float scale, int32_t splits, uint16_t* out, float* lse,
                                void* workspace, size_t workspace_bytes, dsa_stream_t stream);
+
+/*
+ * A batch of sequences in one call (the GLM page's Evidence section names batched
+ * sparse prefill as the next step after the single-sequence path; the indexer
+ * and attention definitions above apply to each sequence on its own).  The
+ * batch is described by three HOST arrays, in the packed ("varlen") layout:
+ *
+ *   cu_q  int64 [B+1]: sequence b owns query rows cu_q[b] .. cu_q[b+1]-1 of every
+ *         per-query tensor (q_idx, w, q, idx, out, lse, out_idx); cu_q[0] = 0
+ *   cu_k  int64 [B+1]: sequence b owns key rows cu_k[b] .. cu_k[b+1]-1 of k_idx
+ *         and kv (N_b = cu_k[b+1] - cu_k[b] keys); cu_k[0] = 0
+ *   pos0  int64 [B]: position of sequence b's first query; query row cu_q[b]+i
+ *         sits at position pos0[b]+i and may use the sequence's keys 0 .. pos0[b]+i
+ *
+ * Both arrays must be non-decreasing, with 0 <= pos0[b] and pos0[b] + L_b <= N_b
+ * (L_b = cu_q[b+1] - cu_q[b]; L_b = 0 and N_b = 0 are allowed), B in
+ * 0 .. DSA_MAX_BATCH, else DSA_ERR_INVALID_ARG.  Key indices (out_idx, idx)
+ * are positions within the sequence, 0 .. N_b-1, as in the one-sequence calls;
+ * each query row's result equals the one-sequence call on its sequence alone.
+ * The host arrays are read during the call only.  A batch with no query rows
+ * is a no-op returning DSA_OK; the *_workspace_bytes functions return 0 for it
+ * and for arguments the call would reject.
+ *
+ * dsa_indexer_topk_varlen: q_idx bf16 [T][32][128], w fp32 [T][32], k_idx
+ *   bf16 [cu_k[B]][128], out_idx int32 [T][top_k] (T = cu_q[B]); n_heads,
+ *   head_dim, top_k, q_block and the errors as dsa_indexer_topk.  Workspace:
+ *   256-byte aligned, at least dsa_indexer_topk_varlen_workspace_bytes(...).
+ */
+size_t dsa_indexer_topk_varlen_workspace_bytes(int64_t B, const int64_t* cu_q, const int64_t* cu_k,
+                                               const int64_t* pos0, int32_t top_k, int32_t q_block);
+dsa_status_t dsa_indexer_topk_varlen(const uint16_t* q_idx, const uint16_t* k_idx, const float* w,
+                                     int64_t B, const int64_t* cu_q, const int64_t* cu_k,
+                                     const int64_t* pos0, int32_t n_heads, int32_t head_dim,
+                                     int32_t top_k, int32_t q_block, int32_t* out_idx,
+                                     void* workspace, size_t workspace_bytes, dsa_stream_t stream);
+
+/*
+ * dsa_sparse_prefill_varlen: the attention of dsa_sparse_prefill for each
+ * sequence of a batch (layout as above): q bf16 [T][H][576], kv bf16
+ * [cu_k[B]][kv_stride], idx int32 [T][top_k], out bf16 [T][H][512], lse fp32
+ * [T][H] or NULL.  splits as dsa_sparse_decode (1 = one workgroup per query, the
+ * dsa_sparse_prefill kernel; 0 picks a count from T, which is 1 for T >= 512).
+ * Workspace: 256-byte aligned, at least
+ * dsa_sparse_prefill_varlen_workspace_bytes(...) bytes (a per-query table, plus
+ * the split partials when splits > 1).  Other arguments and errors as
+ * dsa_sparse_decode.
+ */
+size_t dsa_sparse_prefill_varlen_workspace_bytes(int64_t B, const int64_t* cu_q, const int64_t* cu_k,
+                                                 const int64_t* pos0, int32_t H, int32_t top_k,
+                                                 int32_t splits);
+dsa_status_t dsa_sparse_prefill_varlen(const uint16_t* q, const uint16_t* kv, int64_t kv_stride,
+                                       const int32_t* idx, int64_t B, const int64_t* cu_q,
+                                       const int64_t* cu_k, const int64_t* pos0, int32_t H,
+                                       int32_t d_latent, int32_t d_rope, int32_t top_k, float scale,
+                                       int32_t splits, uint16_t* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, dsa_stream_t stream);
 
 /*
  * The sparse-prefill gate of the GLM page ("How it works": sparse only for a

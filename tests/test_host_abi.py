@@ -173,3 +173,92 @@ def test_python_binding_raises_without_library(monkeypatch, tmp_path):
             mod.load_library()
     finally:
         importlib.reload(dsa)
+
+
+# ------------------------------------------------------------------ batched (varlen) entry points
+
+def i64s(vals):
+    return (ctypes.c_int64 * max(len(vals), 1))(*vals)
+
+
+GOOD_BATCH = dict(cu_q=[0, 70, 71, 584], cu_k=[0, 5000, 25000, 28000], pos0=[100, 30, 2487])
+
+
+def call_indexer_varlen(lib, cu_q=None, cu_k=None, pos0=None, B=None, nh=32, hd=128, k=64, qb=0, ptr=1 << 20,
+                        ws=1 << 30, ws_bytes=1 << 40, arrays=True):
+    cu_q = GOOD_BATCH["cu_q"] if cu_q is None else cu_q
+    cu_k = GOOD_BATCH["cu_k"] if cu_k is None else cu_k
+    pos0 = GOOD_BATCH["pos0"] if pos0 is None else pos0
+    B = len(pos0) if B is None else B
+    p = ctypes.c_void_p(ptr) if ptr else None
+    a = (i64s(cu_q), i64s(cu_k), i64s(pos0)) if arrays else (None, None, None)
+    return lib.dsa_indexer_topk_varlen(p, p, p, B, *a, nh, hd, k, qb, p, ctypes.c_void_p(ws) if ws else None,
+                                       ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), 1), (dict(B=dsa.MAX_BATCH + 1), 1), (dict(arrays=False), 1),
+    (dict(cu_q=[1, 70, 71, 584]), 1), (dict(cu_k=[5, 5000, 25000, 28000]), 1),
+    (dict(cu_q=[0, 70, 69, 584]), 1), (dict(cu_k=[0, 5000, 4000, 28000]), 1),
+    (dict(pos0=[100, -1, 2487]), 1), (dict(pos0=[100, 30, 2488]), 1),  # pos0 + L > N
+    (dict(k=0), 1), (dict(k=4097), 1), (dict(qb=-1), 1), (dict(nh=16), 2), (dict(hd=64), 2),
+    (dict(ptr=0), 1), (dict(ptr=(1 << 20) + 2), 1), (dict(ws=0), 3), (dict(ws_bytes=1000), 3),
+])
+def test_indexer_varlen_rejects_bad_arguments(lib, kw, status):
+    assert call_indexer_varlen(lib, **kw) == status
+    assert lib.dsa_last_error() != b""
+
+
+def test_indexer_varlen_without_query_rows_is_a_no_op(lib):
+    assert call_indexer_varlen(lib, cu_q=[0], cu_k=[0], pos0=[], ptr=0, ws=0, ws_bytes=0) == 0
+    assert call_indexer_varlen(lib, cu_q=[0, 0, 0], cu_k=[0, 0, 9], pos0=[0, 9], ptr=0, ws=0, ws_bytes=0) == 0
+
+
+def test_indexer_varlen_workspace(lib):
+    f = lib.dsa_indexer_topk_varlen_workspace_bytes
+    ws = lambda cq, ck, p0, k=2048, qb=1024: f(len(p0), i64s(cq), i64s(ck), i64s(p0), k, qb)
+    one = ws([0, 2048], [0, 131072], [129024])
+    # one sequence: the single-sequence figure plus its row table (2048 x 40 B) and key table entry
+    assert one >= lib.dsa_indexer_topk_workspace_bytes(2048, 131072, 2048, 1024)
+    assert one - lib.dsa_indexer_topk_workspace_bytes(2048, 131072, 2048, 1024) <= 2048 * 40 + 512
+    # rejected batches and batches without rows size to 0
+    assert ws([0, 5], [0, 4], [0]) == 0 and ws([0], [0], []) == 0 and ws([0, 0], [0, 9], [3]) == 0
+    assert ws([0, 70], [0, 5000], [0], k=0) == 0
+    # the tiled key copies cover only the keys queries can see
+    a = ws([0, 8], [0, 100000], [0])
+    b = ws([0, 8], [0, 100000], [99992])
+    assert b - a >= (100000 // 32 - 1) * 8192
+
+
+def call_attn_varlen(lib, cu_q=None, cu_k=None, pos0=None, H=64, dl=512, dr=64, k=8, stride=576, scale=0.07,
+                     splits=1, ptr=1 << 20, ws=1 << 24, ws_bytes=1 << 30):
+    cu_q = GOOD_BATCH["cu_q"] if cu_q is None else cu_q
+    cu_k = GOOD_BATCH["cu_k"] if cu_k is None else cu_k
+    pos0 = GOOD_BATCH["pos0"] if pos0 is None else pos0
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.dsa_sparse_prefill_varlen(p, p, stride, p, len(pos0), i64s(cu_q), i64s(cu_k), i64s(pos0), H, dl, dr,
+                                         k, scale, splits, p, None, ctypes.c_void_p(ws) if ws else None, ws_bytes,
+                                         None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu_q=[0, 70, 69, 584]), 1), (dict(pos0=[100, 30, 2488]), 1), (dict(k=0), 1), (dict(splits=-1), 1),
+    (dict(splits=129), 1), (dict(H=24), 2), (dict(dl=256), 2), (dict(dr=32), 2), (dict(stride=575), 1),
+    (dict(scale=float("nan")), 1), (dict(ptr=0), 1), (dict(ws=0), 3), (dict(ws_bytes=64), 3),
+    (dict(ws=(1 << 24) + 16), 1),
+])
+def test_attention_varlen_rejects_bad_arguments(lib, kw, status):
+    assert call_attn_varlen(lib, **kw) == status
+    assert lib.dsa_last_error() != b""
+
+
+def test_attention_varlen_workspace(lib):
+    f = lib.dsa_sparse_prefill_varlen_workspace_bytes
+    c = GOOD_BATCH
+    args = (3, i64s(c["cu_q"]), i64s(c["cu_k"]), i64s(c["pos0"]))
+    T = c["cu_q"][-1]
+    table = (T * 16 + 255) // 256 * 256
+    assert f(*args, 64, 2048, 1) == table  # the per-query table only
+    assert f(*args, 64, 2048, 4) == table + T * 4 * 64 * 516 * 4
+    assert f(*args, 24, 2048, 1) == 0 and f(*args, 64, 2048, 129) == 0
+    assert call_attn_varlen(lib, cu_q=[0], cu_k=[0], pos0=[], ptr=0, ws=0, ws_bytes=0) == 0
