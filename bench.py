@@ -16,6 +16,11 @@ Prints one JSON line (see the "roofline" and "cpu_baseline" objects).
 times the decode step instead: the newest position's query (L = 1) selects its top-k
 of the N cached keys (dsa_indexer_topk) and attends over them with the split-key
 attention (dsa_sparse_decode); one JSON line of its own.
+
+    python bench.py --batch {prefill8,ragged,decode64}
+
+times one batched step over several sequences (dsa_indexer_topk_varlen, then
+dsa_sparse_prefill_varlen) beside the same sequences run one call each.
 """
 from __future__ import annotations
 
@@ -143,6 +148,8 @@ def main():
                          "times, to scale the FETCH_SIZE / WRITE_SIZE counters, and exit")
     ap.add_argument("--decode", action="store_true",
                     help="time the decode step (L = 1 indexer + split-key attention) instead")
+    ap.add_argument("--batch", choices=sorted(BATCHES),
+                    help="time a batch of sequences through the varlen entry points instead")
     ap.add_argument("--print-source-hash", metavar="KERNEL", choices=sorted(KERNEL_SOURCES),
                     help="print the source hash a traffic summary for KERNEL must carry, and exit")
     args = ap.parse_args()
@@ -176,6 +183,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
         return
     dsa.load_library()
+    if args.batch:
+        bench_batch(args, dev)
+        return
     wl = di.CONFIGS[args.config]
     t0 = time.perf_counter()
     inp = di.make_inputs(wl)
@@ -370,6 +380,153 @@ def bench_decode(args, wl, inp, dev):
         result["cpu_baseline"] = {"value": round(1.0 / secs, 3), "unit": "steps/s", "cores": 1, "kind": "oracle",
                                   "sample": f"one decode step (1 query over {n_t} keys), fp64 C oracle: "
                                             f"full-sort top-k + sparse attention; {secs:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
+# Batches of sequences (N keys, L newest queries each; top_k 2048, 64 attention heads).
+BATCHES = {
+    # eight sequences of the 16K-key, 512-query chunk
+    "prefill8": [(16384, 512)] * 8,
+    # one chunk of each size, 2K .. 128K keys
+    "ragged": [(131072, 2048), (65536, 1024), (16384, 512), (8192, 128), (2048, 64), (40000, 7)],
+    # a decode step over 64 sequences, caches of 4K .. 32K keys
+    "decode64": [(4096 + 448 * i, 1) for i in range(64)],
+}
+
+
+def bench_batch(args, dev):
+    """One step = dsa_indexer_topk_varlen + dsa_sparse_prefill_varlen over the whole batch."""
+    import numpy as np
+    import torch
+
+    import dsa_inputs as di
+    import dsa_sparse_attention_indexer_amd as dsa
+
+    top_k, H = 2048, 64
+    specs = BATCHES[args.batch]
+    t0 = time.perf_counter()
+    seqs = []
+    for i, (N, L) in enumerate(specs):
+        wl = di.Workload(f"{args.batch}{i}", N, L, top_k, H, 50 + i, "concentrated")
+        seqs.append((wl, di.make_inputs(wl)))
+    log(f"[bench] batch {args.batch}: inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    cat = lambda key: np.concatenate([inp[key] for _, inp in seqs])
+    q_idx, k_idx, q, kv = bf(cat("q_idx")), bf(cat("k_idx")), bf(cat("q")), bf(cat("kv"))
+    w = torch.from_numpy(cat("w")).to(dev)
+    cu_q = np.cumsum([0] + [wl.L for wl, _ in seqs]).astype(np.int64)
+    cu_k = np.cumsum([0] + [wl.N for wl, _ in seqs]).astype(np.int64)
+    pos0 = np.array([wl.pos0 for wl, _ in seqs], dtype=np.int64)
+    T = int(cu_q[-1])
+    splits = 0 if T < 512 else 1
+    idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(dsa.varlen_workspace_bytes(cu_q, cu_k, pos0, top_k), dtype=torch.uint8, device=dev)
+    aws = torch.empty(max(dsa.prefill_varlen_workspace_bytes(cu_q, cu_k, pos0, H, top_k, splits), 1),
+                      dtype=torch.uint8, device=dev)
+    scale = float(np.float32(di.SOFTMAX_SCALE))
+
+    def batched():
+        dsa.indexer_topk_varlen(q_idx, k_idx, w, cu_q, cu_k, pos0, top_k, out=idx, workspace=ws)
+        dsa.sparse_prefill_varlen(q, kv, idx, cu_q, cu_k, pos0, scale, splits=splits, out=out, workspace=aws)
+
+    # The same work as one call per sequence (views into the packed tensors).
+    one_ws = torch.empty(max(dsa.workspace_bytes(wl.L, wl.N, top_k) for wl, _ in seqs), dtype=torch.uint8,
+                         device=dev)
+    one_dws = torch.empty(max(max(dsa.decode_workspace_bytes(wl.L, H, top_k) for wl, _ in seqs), 1),
+                          dtype=torch.uint8, device=dev)
+
+    def per_sequence():
+        for b, (wl, _) in enumerate(seqs):
+            qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+            dsa.indexer_topk(q_idx[qs], k_idx[ks], w[qs], wl.pos0, top_k, out=idx[qs], workspace=one_ws)
+            if wl.L < 512:
+                dsa.sparse_decode(q[qs], kv[ks], idx[qs], wl.pos0, scale, out=out[qs], workspace=one_dws)
+            else:
+                dsa.sparse_prefill(q[qs], kv[ks], idx[qs], wl.pos0, scale, out=out[qs])
+
+    def timed(fn, kernels_too):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        if kernels_too:
+            dsa.profile_enable(True)
+            for k in dsa.PROFILE_KERNELS:
+                dsa.profile_read(k)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+        kern = {}
+        if kernels_too:
+            for k in dsa.PROFILE_KERNELS:
+                kms, n = dsa.profile_read(k)
+                if n:
+                    kern[k] = {"launches_per_step": round(n / args.steps, 4), "ms_per_launch": round(kms / n, 5),
+                               "ms_per_step": round(kms / args.steps, 5)}
+            dsa.profile_enable(False)
+        return ms, kern
+
+    ms_one, _ = timed(per_sequence, False)
+    ms, kernels = timed(batched, True)
+    f_idx = sum(sum(r[0] for r in workload_sizes(wl)) for wl, _ in seqs)
+    b_attn = sum(sum(r[2] for r in workload_sizes(wl)) for wl, _ in seqs)
+    result = {
+        "metric": f"batched prefill tokens/sec (indexer+topk+sparse attn), batch '{args.batch}'",
+        "value": round(T / (ms / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.batch}: {len(seqs)} sequences (N, L) = "
+                               f"{[(wl.N, wl.L) for wl, _ in seqs][:8]}{' ...' if len(seqs) > 8 else ''}, "
+                               f"top_k={top_k}, indexer 32x128 bf16, attention {H} heads x 576/512 bf16, "
+                               f"splits={splits}",
+                   "sequences": len(seqs), "query_rows": T, "keys": int(cu_k[-1]), "top_k": top_k},
+        "per_sequence_calls": {"ms_per_step": round(ms_one, 4), "tokens_per_s": round(T / (ms_one / 1000.0), 1)},
+        "kernels": kernels,
+    }
+    per = {}
+    sf = kernels.get("score_filter")
+    if sf:
+        ach = f_idx / sf["launches_per_step"] / (sf["ms_per_launch"] * 1e-3) / 1e12
+        per["score_filter"] = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                               "kernel": "score_filter"}
+    at = kernels.get("sparse_attention") or kernels.get("attn_split")
+    if at:
+        ach = b_attn / at["launches_per_step"] / (at["ms_per_launch"] * 1e-3) / 1e9
+        per["attention"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                            "kernel": "sparse_attention" if "sparse_attention" in kernels else "attn_split"}
+    if per:
+        dom = max(per, key=lambda k: kernels[per[k]["kernel"]]["ms_per_step"])
+        result["roofline"] = per[dom]
+        result["kernel_rooflines"] = per
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=False)
+        t0 = time.perf_counter()
+        n_rows = 0
+        for wl, inp in seqs[:8]:  # the newest query of up to 8 sequences
+            t = wl.L - 1
+            sel = oracle.topk(inp["q_idx"][t:t + 1], inp["k_idx"], inp["w"][t:t + 1], wl.pos0 + t, top_k)
+            oracle.attention(inp["q"][t:t + 1], inp["kv"], sel, wl.pos0 + t, di.SOFTMAX_SCALE)
+            n_rows += 1
+        secs = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(n_rows / secs, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"the newest query of {n_rows} sequences, fp64 C oracle: full-sort "
+                                            f"top-k + sparse attention; {secs:.2f} s"}
     print(json.dumps(result), flush=True)
 
 
