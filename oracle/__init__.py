@@ -12,6 +12,9 @@ Functions and the passages they follow (page titles as on the pages):
   causal_mask(...) -- "cuda : support for sparse KV indices in MMA flash
                      attention kernel", review: causality applied on the
                      top-k indices, masked entries -1.
+  retrieval_topk(...) -- LiteTopK abstract: the same Indexer-TopK operation
+                     as inner-product top-k for vector retrieval (one vector
+                     per query, no ReLU, no weights, every corpus row).
   attention(...)  -- the GLM page, How it works (sparse prefill over the
                      gathered 576-wide latent|rope rows, value = latent) and
                      The change (dense boolean-masked attention).
@@ -55,6 +58,10 @@ def _load():
         lib.dsa_oracle_head_dots.argtypes = [P, P, i32, i32, P]
         lib.dsa_oracle_topk.restype = i32
         lib.dsa_oracle_topk.argtypes = [P, P, P, i64, i64, i32, i32, i64, i32, i64, P, i64, P, P, i32]
+        lib.dsa_oracle_dot.restype = f64
+        lib.dsa_oracle_dot.argtypes = [P, P, i32]
+        lib.dsa_oracle_retrieval_topk.restype = i32
+        lib.dsa_oracle_retrieval_topk.argtypes = [P, P, i64, i64, i32, i32, P, i64, P, P, i32]
         lib.dsa_oracle_causal_mask.restype = None
         lib.dsa_oracle_causal_mask.argtypes = [P, i64, i32, i64]
         lib.dsa_oracle_attention.restype = i32
@@ -119,6 +126,40 @@ def topk(q_idx, k_idx, w, q_pos0: int, top_k: int, block: int = 0, rows=None,
                                  n_threads or default_threads())
     if rc != 0:
         raise ValueError("oracle topk: bad arguments")
+    return (out, kth) if return_kth else out
+
+
+def dot(a_bits: np.ndarray, b_bits: np.ndarray) -> float:
+    """Canonical fp64 inner product of two bf16 rows (left to right, -0 -> +0)."""
+    a = np.ascontiguousarray(a_bits, np.uint16)
+    b = np.ascontiguousarray(b_bits, np.uint16)
+    assert a.shape == b.shape and a.ndim == 1
+    return _load().dsa_oracle_dot(_ptr(a), _ptr(b), a.shape[0])
+
+
+def retrieval_topk(q, x, top_k: int, rows=None, n_threads: int | None = None, return_kth: bool = False):
+    """Inner-product top-k per query row over every corpus row (ascending, -1 padded).
+
+    q uint16 [M,d] bf16 bits; x uint16 [N,d].  Order: score desc, lower index first.
+    """
+    q = np.ascontiguousarray(q, np.uint16)
+    x = np.ascontiguousarray(x, np.uint16)
+    M, d = q.shape
+    N = x.shape[0]
+    assert x.shape[1] == d
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, np.int64)
+        n_rows = rows.shape[0]
+    else:
+        n_rows = M
+    out = np.empty((n_rows, top_k), np.int32)
+    kth = np.empty(n_rows, np.float64) if return_kth else None
+    rc = _load().dsa_oracle_retrieval_topk(_ptr(q), _ptr(x), M, N, d, top_k,
+                                           _ptr(rows) if rows is not None else None, n_rows, _ptr(out),
+                                           _ptr(kth) if kth is not None else None,
+                                           n_threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle retrieval_topk: bad arguments")
     return (out, kth) if return_kth else out
 
 

@@ -23,6 +23,13 @@
  *  - Causal masking of an index tensor (llama.cpp PR 25917, review thread:
  *    apply causality on the top-k indices with a separate op, masked = -1,
  *    assuming key index = sequence position).
+ *  - Inner-product top-k for vector retrieval (LiteTopK abstract: the same
+ *    Indexer-TopK operation serves vector retrieval in recommendation systems
+ *    and vector databases).  One query vector against every corpus vector, no
+ *    ReLU, no head weights, no causality:
+ *        s = sum_{i=0..d-1} q[i]*x[j,i]          (fp64, left to right), -0 -> +0
+ *    then the same order as the indexer's top-k (score descending, lower index
+ *    first) over all N corpus rows; output ascending, -1 padded.
  *  - Sparse prefill attention (mlx-lm PR 1997, "How it works": 576-wide joined
  *    latent|rope key, gathered top-k rows shared by all heads, absorbed latent
  *    space, value = the 512-wide latent) and the dense boolean-masked form it
@@ -342,6 +349,81 @@ int dsa_oracle_attention(const uint16_t* q, const uint16_t* kv, int64_t kv_strid
     J.out = out; J.lse = lse;
     pthread_mutex_init(&J.mu, NULL);
     run_threads(attn_worker, &J, n_threads);
+    pthread_mutex_destroy(&J.mu);
+    return 0;
+}
+
+/* ------------------------------------------------------- vector retrieval */
+
+/* Canonical inner product of two bf16 rows of length d (left to right). */
+double dsa_oracle_dot(const uint16_t* a, const uint16_t* b, int d) {
+    double s = 0.0;
+    for (int i = 0; i < d; ++i) {
+        double prod = bf16_to_double(a[i]) * bf16_to_double(b[i]);
+        s = s + prod;
+    }
+    if (s == 0.0) s = 0.0;
+    return s;
+}
+
+typedef struct {
+    const uint16_t* q;
+    const uint16_t* x;
+    int64_t M, N;
+    int d, top_k;
+    const int64_t* rows;
+    int64_t n_rows;
+    int32_t* out_idx;
+    double* out_kth;
+    int64_t next;
+    pthread_mutex_t mu;
+} retr_job_t;
+
+static void retr_row(const retr_job_t* J, int64_t t, int32_t* out, double* kth) {
+    const int k = J->top_k;
+    scored_t* list = (scored_t*)malloc(sizeof(scored_t) * (size_t)J->N);
+    for (int64_t j = 0; j < J->N; ++j) {
+        list[j].score = dsa_oracle_dot(J->q + (size_t)t * J->d, J->x + (size_t)j * J->d, J->d);
+        list[j].idx = j;
+    }
+    qsort(list, (size_t)J->N, sizeof(scored_t), cmp_rank);
+    const int64_t n_sel = J->N < k ? J->N : k;
+    if (kth) *kth = n_sel > 0 ? list[n_sel - 1].score : -INFINITY;
+    for (int64_t j = 0; j < n_sel; ++j) out[j] = (int32_t)list[j].idx;
+    qsort(out, (size_t)n_sel, sizeof(int32_t), cmp_i32);
+    for (int64_t j = n_sel; j < k; ++j) out[j] = -1;
+    free(list);
+}
+
+static void* retr_worker(void* arg) {
+    retr_job_t* J = (retr_job_t*)arg;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int64_t r = J->next++;
+        pthread_mutex_unlock(&J->mu);
+        if (r >= J->n_rows) break;
+        int64_t t = J->rows ? J->rows[r] : r;
+        retr_row(J, t, J->out_idx + (size_t)r * J->top_k, J->out_kth ? J->out_kth + r : NULL);
+    }
+    return NULL;
+}
+
+/* Inner-product top-k of the listed query rows (all if rows == NULL).
+ * q: [M][d], x: [N][d] bf16; out_idx: [n_rows][top_k]. Returns 0 or -1. */
+int dsa_oracle_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M, int64_t N, int d,
+                              int top_k, const int64_t* rows, int64_t n_rows, int32_t* out_idx,
+                              double* out_kth, int n_threads) {
+    if (!q || !x || !out_idx || M < 0 || N <= 0 || d <= 0 || top_k <= 0) return -1;
+    if (rows)
+        for (int64_t r = 0; r < n_rows; ++r)
+            if (rows[r] < 0 || rows[r] >= M) return -1;
+    retr_job_t J;
+    memset(&J, 0, sizeof J);
+    J.q = q; J.x = x; J.M = M; J.N = N; J.d = d; J.top_k = top_k;
+    J.rows = rows; J.n_rows = rows ? n_rows : M;
+    J.out_idx = out_idx; J.out_kth = out_kth;
+    pthread_mutex_init(&J.mu, NULL);
+    run_threads(retr_worker, &J, n_threads);
     pthread_mutex_destroy(&J.mu);
     return 0;
 }

@@ -307,3 +307,88 @@ def test_minus_one_and_future_indices_are_skipped(oracle_mod):
     a = oracle_mod.attention(q, kv, noisy, q_pos0, di.SOFTMAX_SCALE)
     b = oracle_mod.attention(q, kv, clean, q_pos0, di.SOFTMAX_SCALE)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ vector retrieval (inner-product top-k)
+
+def test_retrieval_integer_scores_match_integer_matmul(oracle_mod):
+    """Small integers: every fp64 partial sum is exact, so the scores are numpy's int64
+    matmul and the selection is a lexsort on (score desc, index asc)."""
+    rng = np.random.default_rng(21)
+    M, N, d, k = 5, 700, 128, 37
+    qi = rng.integers(-6, 7, size=(M, d))
+    xi = rng.integers(-6, 7, size=(N, d))
+    got, kth = oracle_mod.retrieval_topk(bf(qi), bf(xi), k, return_kth=True)
+    s = qi.astype(np.int64) @ xi.astype(np.int64).T
+    for t in range(M):
+        order = np.lexsort((np.arange(N), -s[t]))
+        assert np.array_equal(got[t], np.sort(order[:k]))
+        assert kth[t] == s[t, order[k - 1]]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_retrieval_matches_rank_count_with_exact_rationals(oracle_mod, seed):
+    """Gaussian bf16 rows of 16 dims: the fp64 sums are exact, so exact rational scores
+    plus the rank-count rule (no sorting) must give the same selection."""
+    from fractions import Fraction
+
+    rng = np.random.default_rng(100 + seed)
+    M, N, d, k = 3, 40, 16, 9
+    q = bf(rng.standard_normal((M, d)))
+    x = bf(rng.standard_normal((N, d)))
+    qf, xf = di.bf16_bits_to_f32(q), di.bf16_bits_to_f32(x)
+    got = oracle_mod.retrieval_topk(q, x, k)
+    for t in range(M):
+        scores = [sum((Fraction(float(qf[t, i])) * Fraction(float(xf[j, i])) for i in range(d)), Fraction(0))
+                  for j in range(N)]
+        assert got[t].tolist() == brute.rank_count_topk(scores, N - 1, k)
+
+
+def test_retrieval_equals_two_head_indexer_form(oracle_mod):
+    """ReLU(s) - ReLU(-s) = s: the indexer score with heads (q, -q), weights (1, -1) and
+    zero heads elsewhere is the inner product, in the canonical fp64 order too."""
+    rng = np.random.default_rng(22)
+    M, N, d, k = 4, 3000, 128, 256
+    q = bf(rng.standard_normal((M, d)))
+    x = bf(rng.standard_normal((N, d)))
+    got = oracle_mod.retrieval_topk(q, x, k)
+    for t in range(M):
+        qe = np.zeros((1, 32, d), np.uint16)
+        qe[0, 0] = q[t]
+        qe[0, 1] = q[t] ^ np.uint16(0x8000)  # bf16 negation
+        w = np.zeros((1, 32), np.float32)
+        w[0, 0], w[0, 1] = 1.0, -1.0
+        assert np.array_equal(got[t], oracle_mod.topk(qe, x, w, N - 1, k)[0])
+
+
+def test_retrieval_negative_scores_are_ranked_not_clipped(oracle_mod):
+    """q = -x_0 makes every score of a unit-norm-ish corpus negative for most rows: the
+    top-k must follow the signed score (no ReLU), which the indexer's form would clip."""
+    rng = np.random.default_rng(23)
+    N, d, k = 200, 32, 10
+    x = bf(np.abs(rng.standard_normal((N, d))))
+    q = bf(-np.ones((1, d)))
+    got = oracle_mod.retrieval_topk(q, x, k)[0]
+    s = -di.bf16_bits_to_f32(x).astype(np.float64).sum(axis=1)
+    order = np.lexsort((np.arange(N), -s))
+    assert np.array_equal(got, np.sort(order[:k]))
+    assert not np.array_equal(got, np.arange(k))  # what clipping every score to 0 would give
+
+
+def test_retrieval_ties_and_small_corpus(oracle_mod):
+    x = np.tile(bf(np.ones((1, 8))), (50, 1))
+    q = bf(np.ones((2, 8)))
+    assert np.array_equal(oracle_mod.retrieval_topk(q, x, 7), np.tile(np.arange(7), (2, 1)))
+    got = oracle_mod.retrieval_topk(q, x[:5], 8)
+    assert np.array_equal(got, np.tile([0, 1, 2, 3, 4, -1, -1, -1], (2, 1)))
+
+
+def test_dot_is_left_to_right_and_positive_zero(oracle_mod):
+    """2^60 + 1 - 2^60 is 0 left to right (the 1 is absorbed), 1 exactly: the canonical
+    order is the sequential one.  A negative-zero sum becomes +0."""
+    a = bf([2.0 ** 60, 1.0, -(2.0 ** 60)])
+    one = bf([1.0, 1.0, 1.0])
+    assert oracle_mod.dot(a, one) == 0.0
+    assert oracle_mod.dot(bf([2.0 ** 60, -(2.0 ** 60), 1.0]), one) == 1.0
+    z = oracle_mod.dot(bf([-1.0]), bf([0.0]))
+    assert z == 0.0 and math.copysign(1.0, z) == 1.0
