@@ -21,6 +21,11 @@ attention (dsa_sparse_decode); one JSON line of its own.
 
 times one batched step over several sequences (dsa_indexer_topk_varlen, then
 dsa_sparse_prefill_varlen) beside the same sequences run one call each.
+
+    python bench.py --retrieval [--retrieval-n 1048576] [--retrieval-m 1024]
+
+times the inner-product top-k over a corpus (dsa_retrieval_topk): M Gaussian queries
+against N Gaussian corpus rows of 128 dims, top_k 1,024.
 """
 from __future__ import annotations
 
@@ -150,6 +155,11 @@ def main():
                     help="time the decode step (L = 1 indexer + split-key attention) instead")
     ap.add_argument("--batch", choices=sorted(BATCHES),
                     help="time a batch of sequences through the varlen entry points instead")
+    ap.add_argument("--retrieval", action="store_true",
+                    help="time the inner-product top-k over a corpus (vector retrieval) instead")
+    ap.add_argument("--retrieval-n", type=int, default=1 << 20)
+    ap.add_argument("--retrieval-m", type=int, default=1024)
+    ap.add_argument("--retrieval-k", type=int, default=1024)
     ap.add_argument("--print-source-hash", metavar="KERNEL", choices=sorted(KERNEL_SOURCES),
                     help="print the source hash a traffic summary for KERNEL must carry, and exit")
     args = ap.parse_args()
@@ -185,6 +195,9 @@ def main():
     dsa.load_library()
     if args.batch:
         bench_batch(args, dev)
+        return
+    if args.retrieval:
+        bench_retrieval(args, dev)
         return
     wl = di.CONFIGS[args.config]
     t0 = time.perf_counter()
@@ -380,6 +393,84 @@ def bench_decode(args, wl, inp, dev):
         result["cpu_baseline"] = {"value": round(1.0 / secs, 3), "unit": "steps/s", "cores": 1, "kind": "oracle",
                                   "sample": f"one decode step (1 query over {n_t} keys), fp64 C oracle: "
                                             f"full-sort top-k + sparse attention; {secs:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
+def bench_retrieval(args, dev):
+    """One step = dsa_retrieval_topk of M queries over an N-row corpus."""
+    import numpy as np
+    import torch
+
+    import dsa_inputs as di
+    import dsa_sparse_attention_indexer_amd as dsa
+
+    M, N, k = args.retrieval_m, args.retrieval_n, args.retrieval_k
+    t0 = time.perf_counter()
+    rng = di.make_rng(90)
+    qb = di.f32_to_bf16_bits(rng.standard_normal((M, 128), dtype=np.float32))
+    xb = di.f32_to_bf16_bits(rng.standard_normal((N, 128), dtype=np.float32))
+    log(f"[bench] retrieval: inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, x = bf(qb), bf(xb)
+    out = torch.empty((M, k), dtype=torch.int32, device=dev)
+    ws = torch.empty(dsa.retrieval_workspace_bytes(M, N, k), dtype=torch.uint8, device=dev)
+
+    def step():
+        dsa.retrieval_topk(q, x, k, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    dsa.profile_enable(True)
+    for kname in dsa.PROFILE_KERNELS:
+        dsa.profile_read(kname)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    kernels = {}
+    for kname in dsa.PROFILE_KERNELS:
+        kms, n = dsa.profile_read(kname)
+        if n:
+            kernels[kname] = {"launches_per_step": round(n / args.steps, 4), "ms_per_launch": round(kms / n, 5),
+                              "ms_per_step": round(kms / args.steps, 5)}
+    dsa.profile_enable(False)
+    flops = 2.0 * M * N * 128
+    result = {
+        "metric": f"vector-retrieval queries/sec (exact inner-product top-{k}) over N={N} rows of 128 bf16",
+        "value": round(M / (ms / 1000.0), 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"retrieval: M={M} Gaussian queries x N={N} Gaussian corpus rows, dim 128 bf16, "
+                               f"top_k={k}", "M": M, "N": N, "top_k": k},
+        "kernels": kernels,
+    }
+    sf = kernels.get("retr_filter")
+    if sf:
+        ach = flops / sf["launches_per_step"] / (sf["ms_per_launch"] * 1e-3) / 1e12
+        result["roofline"] = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                              "kernel": "retr_filter"}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=False)
+        t0 = time.perf_counter()
+        oracle.retrieval_topk(qb[:1], xb, k, n_threads=1)
+        secs = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(1.0 / secs, 3), "unit": "queries/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"one query over all {N} rows, fp64 C oracle: full sort; {secs:.2f} s"}
     print(json.dumps(result), flush=True)
 
 

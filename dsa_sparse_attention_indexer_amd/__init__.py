@@ -34,10 +34,12 @@ EXPORTED = ["dsa_indexer_topk_workspace_bytes", "dsa_indexer_topk", "dsa_causal_
             "dsa_sparse_prefill", "dsa_sparse_decode_workspace_bytes", "dsa_sparse_decode",
             "dsa_indexer_topk_varlen_workspace_bytes", "dsa_indexer_topk_varlen",
             "dsa_sparse_prefill_varlen_workspace_bytes", "dsa_sparse_prefill_varlen",
+            "dsa_retrieval_topk_workspace_bytes", "dsa_retrieval_topk",
             "dsa_sparse_prefill_gate", "dsa_profile_enable",
             "dsa_profile_read", "dsa_status_string", "dsa_last_error", "dsa_version"]
 PROFILE_KERNELS = ["key_stats", "score_sample", "row_prep", "score_filter", "select", "fold",
-                   "sparse_attention", "causal_mask", "attn_split", "attn_merge"]
+                   "sparse_attention", "causal_mask", "attn_split", "attn_merge", "retr_prep", "retr_sample",
+                   "retr_filter"]
 
 _lib = None
 
@@ -79,6 +81,10 @@ def load_library(path: str | None = None):
     lib.dsa_sparse_prefill_varlen.restype = ctypes.c_int
     lib.dsa_sparse_prefill_varlen.argtypes = [P, P, i64, P, i64, P, P, P, i32, i32, i32, i32, f32, i32, P, P,
                                               P, sz, P]
+    lib.dsa_retrieval_topk_workspace_bytes.restype = sz
+    lib.dsa_retrieval_topk_workspace_bytes.argtypes = [i64, i64, i32, i32]
+    lib.dsa_retrieval_topk.restype = ctypes.c_int
+    lib.dsa_retrieval_topk.argtypes = [P, P, i64, i64, i32, i32, i32, P, P, sz, P]
     lib.dsa_sparse_prefill_gate.restype = ctypes.c_int
     lib.dsa_sparse_prefill_gate.argtypes = [i64, i64, i64, i64]
     lib.dsa_status_string.restype = ctypes.c_char_p
@@ -358,3 +364,35 @@ def sparse_prefill_varlen(q, kv, idx, cu_q, cu_k, pos0, scale: float, splits: in
                                          lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
                                          workspace.numel() * workspace.element_size(), _stream_ptr(q, stream)))
     return (out, lse) if return_lse else out
+
+
+def retrieval_workspace_bytes(M: int, N: int, top_k: int, q_block: int = DEFAULT_Q_BLOCK) -> int:
+    return int(load_library().dsa_retrieval_topk_workspace_bytes(M, N, top_k, q_block))
+
+
+def retrieval_topk(q, x, top_k: int, q_block: int = DEFAULT_Q_BLOCK, out=None, workspace=None, stream=None):
+    """Exact inner-product top-k corpus rows per query (ascending, -1 padded) -> int32 [M, top_k].
+
+    q bf16 [M, 128] queries; x bf16 [N, 128] corpus.  Ranked by q . x (fp64 left-to-right
+    order), lower row first among equal scores.
+    """
+    import torch
+
+    lib = load_library()
+    _req(q, "q", torch.bfloat16, 2)
+    _req(x, "x", torch.bfloat16, 2)
+    M, d = q.shape
+    N = x.shape[0]
+    if x.shape[1] != d:
+        raise ValueError("q and x must have the same row width")
+    if out is None:
+        out = torch.empty((M, top_k), dtype=torch.int32, device=q.device)
+    else:
+        _req(out, "out", torch.int32, 2)
+    need = lib.dsa_retrieval_topk_workspace_bytes(M, N, top_k, q_block)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
+    _check(lib.dsa_retrieval_topk(q.data_ptr(), x.data_ptr(), M, N, d, top_k, q_block, out.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream_ptr(q, stream)))
+    return out

@@ -16,7 +16,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 INCLUDE = PKG.parent / "include"
 LIB = PKG / "libdsa.so"
-SOURCES = ["dsa_api.hip", "indexer.hip", "attention.hip"]
+SOURCES = ["dsa_api.hip", "indexer.hip", "attention.hip", "retrieval.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -40,6 +40,7 @@ def hipcc() -> str:
 # where the ReLU/weight epilogue reads them without AGPR-to-VGPR copies.
 SOURCE_FLAGS = {
     "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "retrieval.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -24,7 +24,8 @@ struct ProfRecord {
 std::vector<ProfRecord> g_prof;
 const char* const kProfNames[kProfCount] = {"key_stats", "score_sample", "row_prep", "score_filter",
                                             "select", "fold", "sparse_attention", "causal_mask",
-                                            "attn_split", "attn_merge"};
+                                            "attn_split", "attn_merge", "retr_prep", "retr_sample",
+                                            "retr_filter"};
 }  // namespace
 
 ProfScope::ProfScope(hipStream_t s, int k) : stream(s), kernel(k), start(nullptr), on(false) {
@@ -655,6 +656,116 @@ dsa_status_t dsa_sparse_prefill_varlen(const uint16_t* q, const uint16_t* kv, in
         a.part_ml = part_ml;
         e = S > 1 ? dsa::launch_sparse_attention_split(a, s) : dsa::launch_sparse_attention(a, s);
         if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+    }
+    return DSA_OK;
+}
+
+
+// Vector retrieval: the indexer's workspace for min(M, q_block) rows (rounded up to a row
+// group), plus the row table and each row's two-head form and weights.
+static dsa::IndexerLayout retrieval_layout(int64_t M, int64_t N, int32_t top_k, int32_t q_block, size_t* off_qemb,
+                                           size_t* off_wemb, size_t* total, int64_t* rows_pad) {
+    const int64_t qb = resolve_q_block(q_block);
+    int64_t rows = M < qb ? M : qb;
+    if (rows < 1) rows = 1;
+    const int64_t rp = round8(rows);
+    const dsa::IndexerLayout lay = dsa::IndexerLayout::make(rows, N, top_k, -1, rp, 0);
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    *off_qemb = lay.total;
+    *off_wemb = al(*off_qemb + (size_t)rp * DSA_INDEX_HEADS * DSA_INDEX_DIM * 2);
+    *total = al(*off_wemb + (size_t)rp * DSA_INDEX_HEADS * 4);
+    *rows_pad = rp;
+    return lay;
+}
+
+size_t dsa_retrieval_topk_workspace_bytes(int64_t M, int64_t N, int32_t top_k, int32_t q_block) {
+    if (M <= 0 || N <= 0 || N > (int64_t)INT32_MAX || top_k < 1 || top_k > DSA_MAX_TOPK || q_block < 0) return 0;
+    size_t a, b, total;
+    int64_t rp;
+    retrieval_layout(M, N, top_k, q_block, &a, &b, &total, &rp);
+    return total;
+}
+
+dsa_status_t dsa_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M, int64_t N, int32_t dim,
+                                int32_t top_k, int32_t q_block, int32_t* out_idx, void* workspace,
+                                size_t workspace_bytes, dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    if (M < 0) return fail(DSA_ERR_INVALID_ARG, "M must be >= 0 (got %lld)", (long long)M);
+    if (N <= 0) return fail(DSA_ERR_INVALID_ARG, "N must be > 0 (got %lld)", (long long)N);
+    if (N > (int64_t)INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "N above 2^31-1 is not supported");
+    if (top_k < 1 || top_k > DSA_MAX_TOPK)
+        return fail(DSA_ERR_INVALID_ARG, "top_k must be in 1..%d (got %d)", DSA_MAX_TOPK, top_k);
+    if (q_block < 0) return fail(DSA_ERR_INVALID_ARG, "q_block must be >= 0 (got %d)", q_block);
+    if (dim != DSA_INDEX_DIM) return fail(DSA_ERR_UNSUPPORTED, "dim must be %d (got %d)", DSA_INDEX_DIM, dim);
+    if (M == 0) return DSA_OK;
+    if (!q || !x || !out_idx) return fail(DSA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned(q, 16) || !aligned(x, 16) || !aligned(out_idx, 4))
+        return fail(DSA_ERR_INVALID_ARG, "q/x must be 16-byte aligned, out_idx 4-byte aligned");
+    size_t off_qemb, off_wemb, total;
+    int64_t rows_pad;
+    const dsa::IndexerLayout lay = retrieval_layout(M, N, top_k, q_block, &off_qemb, &off_wemb, &total, &rows_pad);
+    if (!workspace || workspace_bytes < total)
+        return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", total, workspace_bytes,
+                    workspace ? "" : ", null");
+    if (!aligned(workspace, 256)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    dsa::IndexerArgs a{};
+    a.q_idx = reinterpret_cast<const uint16_t*>(ws + off_qemb);
+    a.w = reinterpret_cast<const float*>(ws + off_wemb);
+    a.k_idx = x;
+    a.N = N;
+    a.top_k = top_k;
+    a.cap = lay.cap;
+    a.sample_stride = lay.sample_stride;
+    a.fold_cap = lay.fold_cap;
+    a.force_fallback = debug_force_fallback() ? 1 : 0;
+    a.parts = 4;  // one appended candidate list per row
+    a.kstats = reinterpret_cast<dsa::KeyStats*>(ws + lay.off_kstats);
+    a.qstat = reinterpret_cast<dsa::QHeadStat*>(ws + lay.off_qstat);
+    a.tau = reinterpret_cast<float*>(ws + lay.off_tau);
+    a.delta = reinterpret_cast<float*>(ws + lay.off_delta);
+    a.mode = reinterpret_cast<int*>(ws + lay.off_mode);
+    a.count = reinterpret_cast<int*>(ws + lay.off_count);
+    a.fb_ctrl = reinterpret_cast<int*>(ws + lay.off_fbctrl);
+    a.fb_list = reinterpret_cast<int*>(ws + lay.off_fblist);
+    a.sample = reinterpret_cast<float*>(ws + lay.off_sample);
+    a.cand = reinterpret_cast<uint2*>(ws + lay.off_cand);
+    a.fold_s = reinterpret_cast<float*>(ws + lay.off_fold_s);
+    a.fold_i = reinterpret_cast<int*>(ws + lay.off_fold_i);
+    a.fold_bi = reinterpret_cast<int*>(ws + lay.off_fold_bi);
+    a.fold_bs = reinterpret_cast<double*>(ws + lay.off_fold_bs);
+    a.fold_bf = reinterpret_cast<float*>(ws + lay.off_fold_bf);
+    a.rows = reinterpret_cast<const dsa::RowInfo*>(ws + lay.off_rowinfo);
+    uint16_t* x_tile = reinterpret_cast<uint16_t*>(ws + lay.off_ktile);
+    a.k_tile = x_tile;
+    a.n_ktiles = (N + dsa::kKeyTileKeys - 1) / dsa::kKeyTileKeys;
+    a.n_kstats = dsa::key_stats_blocks(N);
+    hipError_t e = dsa::launch_key_stats(x, N, a.kstats, x_tile, s);
+    if (e != hipSuccess) return hip_fail(e, "key statistics launch");
+
+    dsa::RetrievalArgs r{};
+    r.x = x;
+    r.x_tile = x_tile;
+    r.N = N;
+    r.sample = a.sample;
+    r.sample_stride = lay.sample_stride;
+    r.sample_n = dsa::sample_size(N, top_k, lay.cap);
+    r.tau = a.tau;
+    r.mode = a.mode;
+    r.cand = a.cand;
+    r.count = a.count;
+    r.cap = lay.cap;
+    const int64_t qb = resolve_q_block(q_block);
+    for (int64_t b0 = 0; b0 < M; b0 += qb) {
+        const int64_t Lb = (M - b0) < qb ? (M - b0) : qb;
+        a.out = out_idx + (size_t)b0 * top_k;
+        a.Lb = (int)Lb;
+        r.q = q + (size_t)b0 * DSA_INDEX_DIM;
+        r.Lb = (int)Lb;
+        e = dsa::launch_retrieval_block(r, a, r.sample_n > 0, (int)rows_pad, s);
+        if (e != hipSuccess) return hip_fail(e, "retrieval launch");
     }
     return DSA_OK;
 }

@@ -226,7 +226,8 @@ struct IndexerArgs {
 // event before its launch and another after it on the same stream.
 enum ProfKernel : int {
     kProfKeyStats = 0, kProfScoreSample, kProfRowPrep, kProfScoreFilter, kProfSelect, kProfFold,
-    kProfAttention, kProfCausalMask, kProfAttnSplit, kProfAttnMerge, kProfCount
+    kProfAttention, kProfCausalMask, kProfAttnSplit, kProfAttnMerge, kProfRetrievalPrep,
+    kProfRetrievalSample, kProfRetrievalFilter, kProfCount
 };
 struct ProfScope {
     ProfScope(hipStream_t s, int kernel);
@@ -243,6 +244,31 @@ hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks,
 hipError_t launch_key_stats_batch(const uint16_t* k_idx, const SeqKeys* seqs, int n_seqs, int64_t n_tiles,
                                   KeyStats* ks, uint16_t* k_tile, hipStream_t s);
 hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s);
+// The stages of launch_indexer_block that follow a scoring kernel: row_prep (error bound,
+// threshold from the sample), then select and the fold.
+hipError_t launch_row_prep(const IndexerArgs& a, hipStream_t s);
+hipError_t launch_select_fold(const IndexerArgs& a, hipStream_t s);
+
+// Inner-product top-k over a corpus: the scoring kernels' arguments.  The selection runs
+// on an IndexerArgs whose rows are the two-head form (q, -q), weights (1, -1), of each query.
+struct RetrievalArgs {
+    const uint16_t* q;       // [Lb][128] this block's query rows
+    const uint16_t* x;       // [N][128] corpus (the sample reads it row-major)
+    const uint16_t* x_tile;  // the corpus in 32-row scoring tiles
+    int64_t N;
+    int Lb, n_groups, parts;
+    float* sample;           // [Lb][sample_stride]
+    int sample_stride, sample_n;
+    const float* tau;        // [Lb] filter threshold (row_prep)
+    const int* mode;         // [Lb]
+    uint2* cand;             // [Lb][cap] appended candidate lists
+    int* count;              // [Lb][kCandSegs]: entry 0 counts a row's list
+    int cap;
+};
+// Prep (two-head rows into a.q_idx / a.w, row table a.rows of n_table_rows entries), sample,
+// row_prep, filter, select and fold for one block of queries.
+hipError_t launch_retrieval_block(RetrievalArgs r, const IndexerArgs& a, bool need_sample, int n_table_rows,
+                                  hipStream_t s);
 hipError_t launch_causal_mask(int32_t* idx, int64_t L, int top_k, int64_t q_pos0, hipStream_t s);
 
 struct AttentionArgs {

@@ -1623,14 +1623,22 @@ hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStrea
         ProfScope ps(s, kProfScoreSample);
         score_kernel<true><<<score_wgs, kScoreThreads, 0, s>>>(a, groups);
     }
-    {
-        ProfScope ps(s, kProfRowPrep);
-        row_prep_kernel<<<a.Lb, kRowPrepThreads, 0, s>>>(a);
-    }
+    hipError_t e = launch_row_prep(a, s);
+    if (e != hipSuccess) return e;
     {
         ProfScope ps(s, kProfScoreFilter);
         score_kernel<false><<<score_wgs, kScoreThreads, 0, s>>>(a, groups);
     }
+    return launch_select_fold(a, s);
+}
+
+hipError_t launch_row_prep(const IndexerArgs& a, hipStream_t s) {
+    ProfScope ps(s, kProfRowPrep);
+    row_prep_kernel<<<a.Lb, kRowPrepThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_fold(const IndexerArgs& a, hipStream_t s) {
     {
         ProfScope ps(s, kProfSelect);
         select_kernel<<<a.Lb, a.cap / kSelChunk, 0, s>>>(a);

@@ -6,7 +6,8 @@
  *   dsa_causal_mask_topk causal masking of an externally supplied index tensor
  *   dsa_sparse_prefill   sparse absorbed-MLA attention over the selected keys
  * plus the split-key attention for decode and short chunks (dsa_sparse_decode)
- * and a batch of sequences of any lengths per call (the *_varlen entry points).
+ * and a batch of sequences of any lengths per call (the *_varlen entry points),
+ * and the same top-k as an inner-product search over a corpus (dsa_retrieval_topk).
  *
  * Conventions shared by every entry point
  *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense,
@@ -224,6 +225,33 @@ dsa_status_t dsa_sparse_prefill_varlen(const uint16_t* q, const uint16_t* kv, in
                                        size_t workspace_bytes, dsa_stream_t stream);
 
 /*
+ * Inner-product top-k over a corpus, for vector retrieval (LiteTopK abstract:
+ * the Indexer-TopK operation also serves vector retrieval in recommendation
+ * systems and vector databases).  For each query row t, over every corpus row j:
+ *
+ *   score(t, j) = q[t,:] . x[j,:]       (one head, no ReLU, no weights, no causality)
+ *
+ * ranked exactly as the fp64 left-to-right sum of the dim products ranks them,
+ * highest first, lower row first among equal scores (the indexer's rule; the
+ * same sample -> threshold -> candidates -> exact band re-score scheme).
+ *
+ *   q        bf16 [M][dim] queries;  x bf16 [N][dim] corpus;  dim must be 128
+ *   top_k    1 .. DSA_MAX_TOPK
+ *   q_block  queries per internal block; 0 selects 1024
+ *   out_idx  int32 [M][top_k]: selected corpus rows in ascending order, -1 padded
+ *            when N < top_k
+ *   workspace / workspace_bytes: at least
+ *            dsa_retrieval_topk_workspace_bytes(M, N, top_k, q_block) bytes,
+ *            256-byte aligned (it holds a 32-row tiled copy of the corpus)
+ * Errors as dsa_indexer_topk (dim != 128 gives DSA_ERR_UNSUPPORTED).  M == 0 is a
+ * no-op returning DSA_OK.
+ */
+size_t dsa_retrieval_topk_workspace_bytes(int64_t M, int64_t N, int32_t top_k, int32_t q_block);
+dsa_status_t dsa_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M, int64_t N, int32_t dim,
+                                int32_t top_k, int32_t q_block, int32_t* out_idx, void* workspace,
+                                size_t workspace_bytes, dsa_stream_t stream);
+
+/*
  * The sparse-prefill gate of the GLM page ("How it works": sparse only for a
  * single sequence, only in prefill, and only once the cache holds at least
  * min_context tokens; 16,384 by default).  Returns 1 when the sparse path
@@ -239,7 +267,8 @@ int dsa_sparse_prefill_gate(int64_t B, int64_t L, int64_t N, int64_t min_context
  * the number of launches since the last read of that class, and forgets them.
  * Kernel classes: "key_stats", "score_sample", "row_prep", "score_filter",
  * "select", "fold", "sparse_attention", "causal_mask", "attn_split",
- * "attn_merge".  Unknown names give DSA_ERR_INVALID_ARG.  Host only; safe to
+ * "attn_merge", "retr_prep", "retr_sample", "retr_filter".  Unknown names give
+ * DSA_ERR_INVALID_ARG.  Host only; safe to
  * call from one thread at a time.
  */
 dsa_status_t dsa_profile_enable(int on);

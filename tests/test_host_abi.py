@@ -262,3 +262,28 @@ def test_attention_varlen_workspace(lib):
     assert f(*args, 64, 2048, 4) == table + T * 4 * 64 * 516 * 4
     assert f(*args, 24, 2048, 1) == 0 and f(*args, 64, 2048, 129) == 0
     assert call_attn_varlen(lib, cu_q=[0], cu_k=[0], pos0=[], ptr=0, ws=0, ws_bytes=0) == 0
+
+
+# ------------------------------------------------------------------ vector retrieval
+
+def call_retrieval(lib, M=4, N=64, dim=128, k=8, qb=0, ptr=1 << 20, ws=1 << 30, ws_bytes=1 << 40):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.dsa_retrieval_topk(p, p, M, N, dim, k, qb, p, ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 1), (dict(N=0), 1), (dict(N=1 << 31), 2), (dict(k=0), 1), (dict(k=4097), 1), (dict(qb=-1), 1),
+    (dict(dim=64), 2), (dict(ptr=0), 1), (dict(ptr=(1 << 20) + 8), 1), (dict(ws=0), 3), (dict(ws_bytes=100), 3),
+    (dict(ws=(1 << 30) + 16), 1),
+])
+def test_retrieval_rejects_bad_arguments(lib, kw, status):
+    assert call_retrieval(lib, **kw) == status
+    assert lib.dsa_last_error() != b""
+
+
+def test_retrieval_zero_queries_and_workspace(lib):
+    assert call_retrieval(lib, M=0, ptr=0, ws=0, ws_bytes=0) == 0
+    f = lib.dsa_retrieval_topk_workspace_bytes
+    a, b = f(1024, 1 << 20, 1024, 0), f(4096, 1 << 20, 1024, 0)
+    assert a == b > (1 << 20) * 256  # bounded by the query block; holds the tiled corpus
+    assert f(0, 100, 8, 0) == 0 and f(4, 0, 8, 0) == 0 and f(4, 100, 0, 0) == 0 and f(4, 100, 8, -1) == 0
