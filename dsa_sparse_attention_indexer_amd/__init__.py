@@ -39,7 +39,7 @@ EXPORTED = ["dsa_indexer_topk_workspace_bytes", "dsa_indexer_topk", "dsa_causal_
             "dsa_profile_read", "dsa_status_string", "dsa_last_error", "dsa_version"]
 PROFILE_KERNELS = ["key_stats", "score_sample", "row_prep", "score_filter", "select", "fold",
                    "sparse_attention", "causal_mask", "attn_split", "attn_merge", "retr_prep", "retr_sample",
-                   "retr_filter"]
+                   "retr_filter", "retr_gather"]
 
 _lib = None
 

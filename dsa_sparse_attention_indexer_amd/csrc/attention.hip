@@ -49,24 +49,6 @@ __device__ __forceinline__ u16x4 lds_read_tr(const uint16_t* p) {
     return __builtin_bit_cast(u16x4, v);
 }
 
-// Global -> LDS DMA of 16 (or 4) bytes per lane: lane i's bytes land at lds + 16 i (4 i).
-// Written as inline asm on purpose: the compiler, seeing an LDS DMA in flight, would wait
-// for it before every later LDS read it cannot prove disjoint, i.e. before the current
-// tile's reads, and serialise the next tile's gather with this tile's compute.  The waits
-// for these DMAs are therefore all explicit (vmcnt before the tile barrier); the compiler's
-// own vmcnt waits for other loads can only over-wait on them (the counter is in order).
-// M0 holds the LDS address; one wait state separates its write from the DMA.
-__device__ __forceinline__ void dma_lds16(const void* src, const void* lds) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(m0) : "memory", "m0");
-}
-__device__ __forceinline__ void dma_lds4(const void* src, const void* lds) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 :: "v"(src), "s"(m0) : "memory", "m0");
-}
-
 // kSplit: workgroup (t, s) takes the tiles [s*tps, (s+1)*tps) of query t (tps = tiles per
 // split) and writes an unnormalised partial instead of the output.
 template <bool kSplit>

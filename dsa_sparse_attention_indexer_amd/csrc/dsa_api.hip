@@ -25,7 +25,7 @@ std::vector<ProfRecord> g_prof;
 const char* const kProfNames[kProfCount] = {"key_stats", "score_sample", "row_prep", "score_filter",
                                             "select", "fold", "sparse_attention", "causal_mask",
                                             "attn_split", "attn_merge", "retr_prep", "retr_sample",
-                                            "retr_filter"};
+                                            "retr_filter", "retr_gather"};
 }  // namespace
 
 ProfScope::ProfScope(hipStream_t s, int k) : stream(s), kernel(k), start(nullptr), on(false) {
@@ -663,27 +663,52 @@ dsa_status_t dsa_sparse_prefill_varlen(const uint16_t* q, const uint16_t* kv, in
 
 // Vector retrieval: the indexer's workspace for min(M, q_block) rows (rounded up to a row
 // group), plus the row table and each row's two-head form and weights.
-static dsa::IndexerLayout retrieval_layout(int64_t M, int64_t N, int32_t top_k, int32_t q_block, size_t* off_qemb,
-                                           size_t* off_wemb, size_t* total, int64_t* rows_pad) {
+struct RetrievalExtra {
+    size_t off_qemb, off_wemb, off_runs, off_ids, off_segcnt, total;
+    int64_t rows_pad;
+};
+
+// Run slots (rows x segments x capacity) and segment counters of the filter's per-lane lists
+// for a block of Lb queries.
+static size_t retrieval_run_slots(int64_t Lb, int64_t N, int32_t top_k, int cap, size_t* n_counters) {
+    const int64_t n_tiles = (N + dsa::kKeyTileKeys - 1) / dsa::kKeyTileKeys;
+    const int parts = dsa::retrieval_parts(dsa::retrieval_groups((int)Lb), n_tiles);
+    const bool keep_all = dsa::sample_size(N, top_k, cap) == 0;
+    const int seg_cap = dsa::retrieval_seg_cap(parts, n_tiles, top_k, keep_all);
+    *n_counters = (size_t)Lb * parts * 8;
+    return (size_t)Lb * parts * 8 * (size_t)seg_cap;
+}
+
+static dsa::IndexerLayout retrieval_layout(int64_t M, int64_t N, int32_t top_k, int32_t q_block, RetrievalExtra* x) {
     const int64_t qb = resolve_q_block(q_block);
     int64_t rows = M < qb ? M : qb;
     if (rows < 1) rows = 1;
     const int64_t rp = round8(rows);
     const dsa::IndexerLayout lay = dsa::IndexerLayout::make(rows, N, top_k, -1, rp, 0);
-    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    *off_qemb = lay.total;
-    *off_wemb = al(*off_qemb + (size_t)rp * DSA_INDEX_HEADS * DSA_INDEX_DIM * 2);
-    *total = al(*off_wemb + (size_t)rp * DSA_INDEX_HEADS * 4);
-    *rows_pad = rp;
+    auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    // the full block and the last (shorter) block may split the corpus differently
+    size_t c_full, c_tail = 0;
+    size_t slots = retrieval_run_slots(rows, N, top_k, lay.cap, &c_full);
+    if (M > qb && M % qb) {
+        const size_t t = retrieval_run_slots(M % qb, N, top_k, lay.cap, &c_tail);
+        slots = t > slots ? t : slots;
+    }
+    const size_t counters = c_full > c_tail ? c_full : c_tail;
+    x->off_qemb = lay.total;
+    x->off_wemb = al(x->off_qemb + (size_t)rp * DSA_INDEX_HEADS * DSA_INDEX_DIM * 2);
+    x->off_runs = al(x->off_wemb + (size_t)rp * DSA_INDEX_HEADS * 4);
+    x->off_ids = al(x->off_runs + slots * 16);
+    x->off_segcnt = al(x->off_ids + slots * 4);
+    x->total = al(x->off_segcnt + counters * 4);
+    x->rows_pad = rp;
     return lay;
 }
 
 size_t dsa_retrieval_topk_workspace_bytes(int64_t M, int64_t N, int32_t top_k, int32_t q_block) {
     if (M <= 0 || N <= 0 || N > (int64_t)INT32_MAX || top_k < 1 || top_k > DSA_MAX_TOPK || q_block < 0) return 0;
-    size_t a, b, total;
-    int64_t rp;
-    retrieval_layout(M, N, top_k, q_block, &a, &b, &total, &rp);
-    return total;
+    RetrievalExtra x;
+    retrieval_layout(M, N, top_k, q_block, &x);
+    return x.total;
 }
 
 dsa_status_t dsa_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M, int64_t N, int32_t dim,
@@ -701,19 +726,18 @@ dsa_status_t dsa_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M,
     if (!q || !x || !out_idx) return fail(DSA_ERR_INVALID_ARG, "null tensor pointer");
     if (!aligned(q, 16) || !aligned(x, 16) || !aligned(out_idx, 4))
         return fail(DSA_ERR_INVALID_ARG, "q/x must be 16-byte aligned, out_idx 4-byte aligned");
-    size_t off_qemb, off_wemb, total;
-    int64_t rows_pad;
-    const dsa::IndexerLayout lay = retrieval_layout(M, N, top_k, q_block, &off_qemb, &off_wemb, &total, &rows_pad);
-    if (!workspace || workspace_bytes < total)
-        return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", total, workspace_bytes,
+    RetrievalExtra rx;
+    const dsa::IndexerLayout lay = retrieval_layout(M, N, top_k, q_block, &rx);
+    if (!workspace || workspace_bytes < rx.total)
+        return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", rx.total, workspace_bytes,
                     workspace ? "" : ", null");
     if (!aligned(workspace, 256)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
     dsa::IndexerArgs a{};
-    a.q_idx = reinterpret_cast<const uint16_t*>(ws + off_qemb);
-    a.w = reinterpret_cast<const float*>(ws + off_wemb);
+    a.q_idx = reinterpret_cast<const uint16_t*>(ws + rx.off_qemb);
+    a.w = reinterpret_cast<const float*>(ws + rx.off_wemb);
     a.k_idx = x;
     a.N = N;
     a.top_k = top_k;
@@ -757,6 +781,9 @@ dsa_status_t dsa_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M,
     r.cand = a.cand;
     r.count = a.count;
     r.cap = lay.cap;
+    r.seg_runs = reinterpret_cast<float4*>(ws + rx.off_runs);
+    r.seg_ids = reinterpret_cast<uint32_t*>(ws + rx.off_ids);
+    r.seg_count = reinterpret_cast<int*>(ws + rx.off_segcnt);
     const int64_t qb = resolve_q_block(q_block);
     for (int64_t b0 = 0; b0 < M; b0 += qb) {
         const int64_t Lb = (M - b0) < qb ? (M - b0) : qb;
@@ -764,7 +791,7 @@ dsa_status_t dsa_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M,
         a.Lb = (int)Lb;
         r.q = q + (size_t)b0 * DSA_INDEX_DIM;
         r.Lb = (int)Lb;
-        e = dsa::launch_retrieval_block(r, a, r.sample_n > 0, (int)rows_pad, s);
+        e = dsa::launch_retrieval_block(r, a, r.sample_n > 0, (int)rx.rows_pad, s);
         if (e != hipSuccess) return hip_fail(e, "retrieval launch");
     }
     return DSA_OK;

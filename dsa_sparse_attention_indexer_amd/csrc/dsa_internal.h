@@ -114,7 +114,7 @@ struct IndexerLayout {
         auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
         l.rows = (int)((rows + kRowsPerGroup - 1) & ~(int64_t)(kRowsPerGroup - 1));
         l.cap = cand_capacity(top_k);
-        l.sample_stride = sample_size(N, top_k, l.cap);
+        l.sample_stride = (sample_size(N, top_k, l.cap) + 3) & ~3;  // rows 16-byte aligned
         l.fold_cap = top_k + kFoldKeys;
         size_t o = 0;
         l.off_kstats = o; o = al(o + sizeof(KeyStats) * kStatSlots);
@@ -227,7 +227,7 @@ struct IndexerArgs {
 enum ProfKernel : int {
     kProfKeyStats = 0, kProfScoreSample, kProfRowPrep, kProfScoreFilter, kProfSelect, kProfFold,
     kProfAttention, kProfCausalMask, kProfAttnSplit, kProfAttnMerge, kProfRetrievalPrep,
-    kProfRetrievalSample, kProfRetrievalFilter, kProfCount
+    kProfRetrievalSample, kProfRetrievalFilter, kProfRetrievalGather, kProfCount
 };
 struct ProfScope {
     ProfScope(hipStream_t s, int kernel);
@@ -264,7 +264,19 @@ struct RetrievalArgs {
     uint2* cand;             // [Lb][cap] appended candidate lists
     int* count;              // [Lb][kCandSegs]: entry 0 counts a row's list
     int cap;
+    // The filter's per-lane lists: segment (part, wave, lane half) of each row holds up to
+    // seg_cap runs of 4 consecutive corpus rows (their 4 fp32 scores and the run's id =
+    // first row / 4) of which at least one passed the threshold; gathered into cand afterwards.
+    float4* seg_runs;        // [Lb][n_segs][seg_cap]
+    uint32_t* seg_ids;       // [Lb][n_segs][seg_cap]
+    int* seg_count;          // [Lb][n_segs]
+    int seg_cap;
 };
+// Key parts of the retrieval filter for a block of Lb queries over n_tiles corpus tiles, and
+// the segment capacity its workspace needs (each row has 8 segments per part).
+int retrieval_parts(int n_groups, int64_t n_tiles);
+int retrieval_groups(int Lb);
+int retrieval_seg_cap(int parts, int64_t n_tiles, int top_k, bool keep_all);
 // Prep (two-head rows into a.q_idx / a.w, row table a.rows of n_table_rows entries), sample,
 // row_prep, filter, select and fold for one block of queries.
 hipError_t launch_retrieval_block(RetrievalArgs r, const IndexerArgs& a, bool need_sample, int n_table_rows,

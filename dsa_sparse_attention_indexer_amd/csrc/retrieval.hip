@@ -30,7 +30,6 @@ namespace dsa {
 
 constexpr int kRetSets = 4;                  // 32-query sets per workgroup
 constexpr int kRetQueries = 32 * kRetSets;   // queries per workgroup; each of its 4 waves holds all of them
-constexpr int kRetStage = 16;                // staged candidates per query per wave
 
 __global__ __launch_bounds__(256) void retrieval_prep_kernel(const uint16_t* __restrict__ q, int Lb, int64_t N,
                                                              uint16_t* __restrict__ q_emb, float* __restrict__ w_emb,
@@ -52,45 +51,30 @@ __global__ __launch_bounds__(256) void retrieval_prep_kernel(const uint16_t* __r
         w_emb[(size_t)r * kIdxHeads + threadIdx.x] = threadIdx.x == 0 ? 1.0f : (threadIdx.x == 1 ? -1.0f : 0.0f);
 }
 
-struct RetrievalScore {
-    const RetrievalArgs& A;
-    int wave, lane, hf, c;
-    const u16x8* xt;  // filter: the tiled corpus
+constexpr int kRetRing = 4;  // tiles of each wave's LDS ring (DMA runs kRetRing - 1 tiles ahead)
 
-    // A operand of tile t: lane (hf, c) supplies corpus row c of the tile, dims 64 hf + 8 kk ..
-    template <bool kSample>
-    __device__ __forceinline__ void load(u16x8 (&a)[8], int64_t t) const {
-        if (kSample) {
-            int64_t j = t * kKeyTile + c;
-            j = j < A.sample_n ? j : A.sample_n - 1;
-            const int64_t row = j * A.N / A.sample_n;
-            const u16x8* p = reinterpret_cast<const u16x8*>(A.x + (size_t)row * kIdxDim + 64 * hf);
+// DMA of the A operand of tile t into an LDS slot: chunk kk (1 KB) holds, for lane (hf, c),
+// corpus row c of the tile, dims 64 hf + 8 kk .. (lane l's 16 bytes at kk * 1024 + 16 l).
+template <bool kSample>
+__device__ __forceinline__ void ret_dma(const RetrievalArgs& A, const char* slot, int64_t t, int lane) {
+    if (kSample) {
+        int64_t j = t * kKeyTile + (lane & 31);
+        j = j < A.sample_n ? j : A.sample_n - 1;
+        const int64_t row = j * A.N / A.sample_n;
+        const char* p = reinterpret_cast<const char*>(A.x + (size_t)row * kIdxDim + 64 * (lane >> 5));
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) a[kk] = p[kk];
-        } else {
-            const u16x8* p = xt + (size_t)t * (kKeyTileBytes / 16) + lane;
+        for (int kk = 0; kk < 8; ++kk) dma_lds16(p + 16 * kk, slot + 1024 * kk);
+    } else {
+        const char* p = reinterpret_cast<const char*>(A.x_tile) + (size_t)t * kKeyTileBytes + 16 * lane;
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) a[kk] = p[kk * 64];
-        }
-    }
-};
-
-// Stages n entries of this lane's set-s query (both lane halves take part; hf 0's
-// entries first) and flushes to the row's appended list when the stage is full.
-__device__ __forceinline__ void ret_flush(const RetrievalArgs& A, const uint2* st, int n, int row, int hf, int lane,
-                                          bool go) {
-    int base = 0;
-    if (go && hf == 0) base = atomicAdd(&A.count[(size_t)row * kCandSegs], n);
-    base = __shfl(base, lane & 31);
-    if (go) {
-        const int half = (n + 1) >> 1;
-        const int j0 = hf ? half : 0, j1 = hf ? n : half;
-        uint2* dst = A.cand + (size_t)row * A.cap;
-        for (int j = j0; j < j1; ++j)
-            if (base + j < A.cap) dst[base + j] = st[j];
+        for (int kk = 0; kk < 8; ++kk) dma_lds16(p + 1024 * kk, slot + 1024 * kk);
     }
 }
 
+// Each wave streams its tiles through a ring of LDS slots filled by DMA three tiles ahead,
+// with two accumulator sets: the 32 MFMAs of tile t+1 are issued one by one between the 64
+// per-entry checks of tile t's scores, so the checks (and the rare candidate stores, into
+// the lane's private list) run in the matrix cores' shadow.
 template <bool kSample>
 __global__ __launch_bounds__(256) void retrieval_score_kernel(RetrievalArgs A) {
     // Workgroup -> (query group g, corpus part).  With a multiple of 8 parts, the groups of one
@@ -107,7 +91,9 @@ __global__ __launch_bounds__(256) void retrieval_score_kernel(RetrievalArgs A) {
     if (g >= A.n_groups) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, hf = lane >> 5, c = lane & 31;
-    __shared__ uint2 s_stage[kScoreThreads / kWave][kRetQueries][kRetStage];
+    const int n_segs = A.parts * 8;
+    const int sid = (part * (kScoreThreads / kWave) + wave) * 2 + hf;
+    __shared__ __attribute__((aligned(16))) char s_ring[kScoreThreads / kWave][kRetRing][kKeyTileBytes];
 
     // This wave's tiles: segment (part, wave) of the corpus (or of the sample).
     const int64_t n_keys = kSample ? A.sample_n : A.N;
@@ -116,129 +102,231 @@ __global__ __launch_bounds__(256) void retrieval_score_kernel(RetrievalArgs A) {
     const int64_t tps = (n_tiles + segs - 1) / segs;
     const int64_t t0 = (int64_t)(part * (kScoreThreads / kWave) + wave) * tps;
     const int64_t t1 = t0 + tps < n_tiles ? t0 + tps : n_tiles;
-    if (t0 >= t1) return;
 
     // B operand: lane (hf, c) of set s holds query 32 s + c of the group, dims 64 hf + 8 kk ..
     bf16x8 b[kRetSets][8];
     float tau[kRetSets];
     bool live[kRetSets];
-    int row[kRetSets], scnt[kRetSets];
+    int row[kRetSets], o[kRetSets];
+    float4* runs[kRetSets];
+    uint32_t* ids[kRetSets];
+    float* smp[kRetSets];
 #pragma unroll
     for (int s = 0; s < kRetSets; ++s) {
         const int r = g * kRetQueries + 32 * s + c;
         const bool valid = r < A.Lb;
         row[s] = valid ? r : 0;
-        scnt[s] = 0;
-        const u16x8* qp = reinterpret_cast<const u16x8*>(A.q + (size_t)row[s] * kIdxDim + 64 * hf);
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            b[s][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
-            asm volatile("" : "+a"(b[s][kk]));  // keep the query fragments in AGPRs
-        }
+        o[s] = 0;
         if (kSample) {
             live[s] = valid;
             tau[s] = 0.f;
+            smp[s] = A.sample + (size_t)row[s] * A.sample_stride;
         } else {
             live[s] = valid && A.mode[row[s]] == kModeNormal;
             tau[s] = live[s] ? A.tau[row[s]] : INFINITY;
+            const size_t base = ((size_t)row[s] * n_segs + sid) * A.seg_cap;
+            runs[s] = A.seg_runs + base;
+            ids[s] = A.seg_ids + base;
         }
     }
-    const RetrievalScore R{A, wave, lane, hf, c, reinterpret_cast<const u16x8*>(A.x_tile)};
-
-    auto tile = [&](const u16x8 (&a)[8], int64_t t) {
-        f32x16 acc[kRetSets];
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-            for (int s = 0; s < kRetSets; ++s)
-                acc[s] = mfma_32x32x16(__builtin_bit_cast(bf16x8, a[kk]), b[s][kk], kk == 0 ? f32x16{} : acc[s]);
-        // Lane (hf, c) holds query c's scores of tile rows 8 (i / 4) + 4 hf + i % 4.
-        const int64_t key0 = t * kKeyTile + 4 * hf;
-        const bool tail = (t + 1) * kKeyTile > n_keys;
+    if (t0 < t1) {
+        auto tl = [&](int64_t t) { return t < t1 ? t : t1 - 1; };
+        const char* ring = &s_ring[wave][0][0];
+        auto slot = [&](int64_t t) { return ring + (size_t)((t - t0) & (kRetRing - 1)) * kKeyTileBytes; };
+        // DMA of the first three tiles, then the query fragments (all loads in flight together).
+        ret_dma<kSample>(A, slot(t0), t0, lane);
+        ret_dma<kSample>(A, slot(t0 + 1), tl(t0 + 1), lane);
+        ret_dma<kSample>(A, slot(t0 + 2), tl(t0 + 2), lane);
+        u16x8 qraw[kRetSets][8];
 #pragma unroll
         for (int s = 0; s < kRetSets; ++s) {
-            if (kSample) {
-                if (live[s]) {
-                    float* dst = A.sample + (size_t)row[s] * A.sample_stride;
+            const u16x8* qp = reinterpret_cast<const u16x8*>(A.q + (size_t)row[s] * kIdxDim + 64 * hf);
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int64_t j = key0 + 8 * (i >> 2) + (i & 3);
-                        if (!tail || j < n_keys) dst[j] = acc[s][i] + 0.0f;
+            for (int kk = 0; kk < 8; ++kk) qraw[s][kk] = qp[kk];
+        }
+#pragma unroll
+        for (int s = 0; s < kRetSets; ++s)
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                b[s][kk] = __builtin_bit_cast(bf16x8, qraw[s][kk]);
+                asm volatile("" : "+a"(b[s][kk]));  // keep the query fragments in AGPRs
+            }
+
+        // Run r of set s in a tile's scores: query 32 s + c, tile rows 8 r + 4 hf + 0..3 (entries
+        // 4 r .. 4 r + 3).  Filter: a run whose largest score passes the threshold is stored
+        // whole (the gather picks its entries; rows past N in the last tile are zero padding
+        // that the gather drops).  Sample: every run is stored.
+        auto run_check = [&](const f32x16 (&cu)[kRetSets], int j, int64_t t, const float (&te)[kRetSets], bool tail) {
+            const int s = j >> 2, r = j & 3;
+            // (select canonicalises -0 when it reads candidates; the sample does it here)
+            const float z = kSample ? 0.0f : -0.0f;  // x + -0 is x, also for x = -0
+            const float4 v = make_float4(cu[s][4 * r] + z, cu[s][4 * r + 1] + z, cu[s][4 * r + 2] + z,
+                                         cu[s][4 * r + 3] + z);
+            const int64_t key = t * kKeyTile + 8 * r + 4 * hf;
+            if (kSample) {
+                if (te[s] == 0.f) {
+                    if (!tail) {
+                        *reinterpret_cast<float4*>(smp[s] + key) = v;
+                    } else {
+                        if (key < n_keys) smp[s][key] = v.x;
+                        if (key + 1 < n_keys) smp[s][key + 1] = v.y;
+                        if (key + 2 < n_keys) smp[s][key + 2] = v.z;
+                        if (key + 3 < n_keys) smp[s][key + 3] = v.w;
                     }
                 }
-                continue;
+            } else if (fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)) >= te[s]) {
+                const int slot = o[s] < A.seg_cap ? o[s] : A.seg_cap - 1;
+                runs[s][slot] = v;
+                ids[s][slot] = (uint32_t)(key >> 2);
+                ++o[s];
             }
-            bool any = false;
+        };
+        // MFMAs of tile u (A operand from its LDS slot) into nx, interleaved with the run checks
+        // of tile t = u - 1 (scores in cu), one per two MFMAs.  Its DMA was issued three tiles
+        // ago; the DMAs of the two tiles after it (16) and any stores may still be in flight.
+        auto step = [&](f32x16 (&nx)[kRetSets], int64_t u, const f32x16 (&cu)[kRetSets], int64_t t) {
+            asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+            const bool ok = t >= t0 && t < t1;
+            const bool tail = (t + 1) * kKeyTile > n_keys;
+            float te[kRetSets];  // the check threshold: +inf when tile t is not this wave's
 #pragma unroll
-            for (int i = 0; i < 16; ++i) any = any || acc[s][i] >= tau[s];
-            if (__ballot(any) == 0) continue;
-            uint32_t m = 0;
+            for (int s = 0; s < kRetSets; ++s) te[s] = kSample ? (ok && live[s] ? 0.f : 1.f) : (ok ? tau[s] : INFINITY);
+            const u16x8* sp = reinterpret_cast<const u16x8*>(slot(u)) + lane;
+            u16x8 a_cur = sp[0];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int64_t j = key0 + 8 * (i >> 2) + (i & 3);
-                if (acc[s][i] >= tau[s] && (!tail || j < n_keys)) m |= 1u << i;
+            for (int kk = 0; kk < 8; ++kk) {
+                const u16x8 a_nxt = sp[64 * (kk < 7 ? kk + 1 : 7)];
+#pragma unroll
+                for (int s = 0; s < kRetSets; ++s) {
+                    nx[s] = mfma_32x32x16(__builtin_bit_cast(bf16x8, a_cur), b[s][kk], kk == 0 ? f32x16{} : nx[s]);
+                    if ((kk * kRetSets + s) & 1) run_check(cu, (kk * kRetSets + s) >> 1, t, te, tail);
+                }
+                a_cur = a_nxt;
             }
-            const int n = __builtin_popcount(m);
-            const int n_other = __shfl_xor(n, 32);
-            const int before = hf ? n_other : 0, total = n + n_other;
-            uint2* st = &s_stage[wave][32 * s + c][0];
-            const bool full = scnt[s] + total > kRetStage;
-            ret_flush(A, st, scnt[s], row[s], hf, lane, full && scnt[s] > 0);
-            if (full) scnt[s] = 0;
+            // the slot of tile u - 1 is free again: refill it with tile u + 3
             __builtin_amdgcn_wave_barrier();
-            if (total > kRetStage) {  // more than a stage: straight to the list
-                int base = 0;
-                if (hf == 0) base = atomicAdd(&A.count[(size_t)row[s] * kCandSegs], total);
-                base = __shfl(base, lane & 31) + before;
-                uint2* dst = A.cand + (size_t)row[s] * A.cap;
-                int o = 0;
+            ret_dma<kSample>(A, slot(u + 3), tl(u + 3), lane);
+        };
+        f32x16 acc0[kRetSets], acc1[kRetSets];
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if ((m >> i) & 1u) {
-                        const uint32_t key = (uint32_t)(key0 + 8 * (i >> 2) + (i & 3));
-                        if (base + o < A.cap) dst[base + o] = make_uint2(__float_as_uint(acc[s][i] + 0.0f), key);
-                        ++o;
-                    }
-            } else {
-                int o = scnt[s] + before;
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if ((m >> i) & 1u) {
-                        const uint32_t key = (uint32_t)(key0 + 8 * (i >> 2) + (i & 3));
-                        st[o++] = make_uint2(__float_as_uint(acc[s][i] + 0.0f), key);
-                    }
-                scnt[s] += total;
-            }
-            __builtin_amdgcn_wave_barrier();
+        for (int s = 0; s < kRetSets; ++s) acc1[s] = f32x16{};
+        step(acc0, t0, acc1, t0 - 1);  // no checks: tile t0 - 1 is not this wave's
+        for (int64_t u = t0 + 1; u < t1 + 1; u += 2) {
+            step(acc1, u, acc0, u - 1);
+            step(acc0, u + 1, acc1, u);
         }
-    };
-
-    // Tile t sits in buffer (t - t0) % 3; loads run three tiles ahead (clamped to the last).
-    u16x8 a0[8], a1[8], a2[8];
-    auto tl = [&](int64_t t) { return t < t1 ? t : t1 - 1; };
-    R.template load<kSample>(a0, t0);
-    R.template load<kSample>(a1, tl(t0 + 1));
-    R.template load<kSample>(a2, tl(t0 + 2));
-    for (int64_t t = t0; t < t1; t += 3) {
-        tile(a0, t);
-        R.template load<kSample>(a0, tl(t + 3));
-        if (t + 1 < t1) tile(a1, t + 1);
-        R.template load<kSample>(a1, tl(t + 4));
-        if (t + 2 < t1) tile(a2, t + 2);
-        R.template load<kSample>(a2, tl(t + 5));
     }
     if (!kSample) {
 #pragma unroll
-        for (int s = 0; s < kRetSets; ++s) {
-            __builtin_amdgcn_wave_barrier();
-            ret_flush(A, &s_stage[wave][32 * s + c][0], scnt[s], row[s], hf, lane, scnt[s] > 0);
-        }
+        for (int s = 0; s < kRetSets; ++s)
+            if (g * kRetQueries + 32 * s + c < A.Lb) A.seg_count[(size_t)row[s] * n_segs + sid] = o[s];
     }
 }
 
+// Concatenates the entries of a row's stored runs that pass its threshold (and are corpus
+// rows, not the last tile's zero padding) into its candidate list.  The runs of all the row's
+// segments are numbered 0 .. R-1 through a prefix sum of the segment counts, and thread t
+// takes runs t, t + 256, ..: a counting pass, a scan of the per-thread counts, then a writing
+// pass.  count = cap + 1 when a segment or the list overflowed, which sends the row to the fold.
+constexpr int kGatherThreads = 256;
+constexpr int kGatherMaxSegs = 2048;  // 8 segments per part, at most 256 parts
+__global__ __launch_bounds__(kGatherThreads) void retrieval_gather_kernel(RetrievalArgs A, int n_segs) {
+    const int r = blockIdx.x;
+    if (r >= A.Lb || A.mode[r] != kModeNormal) return;
+    __shared__ int s_pre[kGatherMaxSegs + 1];  // runs before segment j
+    __shared__ int s_sum[kGatherThreads];
+    __shared__ int s_bad;
+    const float tau = A.tau[r];
+    const int* cnt = A.seg_count + (size_t)r * n_segs;
+    const size_t base = (size_t)r * n_segs * A.seg_cap;
+    const int tid = threadIdx.x;
+    // Segment counts -> exclusive prefix in s_pre (each thread scans a contiguous chunk).
+    const int per = (n_segs + kGatherThreads - 1) / kGatherThreads;
+    const int j0 = tid * per, j1 = min(n_segs, j0 + per);
+    int mine = 0;
+    bool bad = false;
+    for (int j = j0; j < j1; ++j) {
+        const int n = cnt[j];
+        bad = bad || n > A.seg_cap;
+        s_pre[j] = min(n, A.seg_cap);
+        mine += min(n, A.seg_cap);
+    }
+    if (tid == 0) s_bad = 0;
+    s_sum[tid] = mine;
+    __syncthreads();
+    if (bad) s_bad = 1;
+    for (int d = 1; d < kGatherThreads; d <<= 1) {
+        const int v = tid >= d ? s_sum[tid - d] : 0;
+        __syncthreads();
+        s_sum[tid] += v;
+        __syncthreads();
+    }
+    {
+        int run = s_sum[tid] - mine;
+        for (int j = j0; j < j1; ++j) {
+            const int n = s_pre[j];
+            s_pre[j] = run;
+            run += n;
+        }
+    }
+    const int R = s_sum[kGatherThreads - 1];
+    if (tid == 0) s_pre[n_segs] = R;
+    __syncthreads();
+    if (s_bad) {
+        if (tid == 0) A.count[(size_t)r * kCandSegs] = A.cap + 1;
+        return;
+    }
+    // Run q lives in segment j with s_pre[j] <= q < s_pre[j + 1].
+    auto locate = [&](int q) {
+        int lo = 0, hi = n_segs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_pre[mid] <= q) lo = mid;
+            else hi = mid - 1;
+        }
+        return base + (size_t)lo * A.seg_cap + (size_t)(q - s_pre[lo]);
+    };
+    auto passes = [&](float v, int64_t key) { return v >= tau && key < A.N; };
+    int n_mine = 0;
+    for (int q = tid; q < R; q += kGatherThreads) {
+        const size_t at = locate(q);
+        const float4 v = A.seg_runs[at];
+        const int64_t key = (int64_t)A.seg_ids[at] * 4;
+        n_mine += passes(v.x, key) + passes(v.y, key + 1) + passes(v.z, key + 2) + passes(v.w, key + 3);
+    }
+    __syncthreads();
+    s_sum[tid] = n_mine;
+    __syncthreads();
+    for (int d = 1; d < kGatherThreads; d <<= 1) {
+        const int v = tid >= d ? s_sum[tid - d] : 0;
+        __syncthreads();
+        s_sum[tid] += v;
+        __syncthreads();
+    }
+    const int total = s_sum[kGatherThreads - 1];
+    if (total > A.cap) {
+        if (tid == 0) A.count[(size_t)r * kCandSegs] = A.cap + 1;
+        return;
+    }
+    if (tid == 0) A.count[(size_t)r * kCandSegs] = total;
+    int off = s_sum[tid] - n_mine;
+    uint2* dst = A.cand + (size_t)r * A.cap;
+    for (int q = tid; q < R; q += kGatherThreads) {
+        const size_t at = locate(q);
+        const float4 v = A.seg_runs[at];
+        const int64_t key = (int64_t)A.seg_ids[at] * 4;
+        const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (passes(f[e], key + e)) dst[off++] = make_uint2(__float_as_uint(f[e]), (uint32_t)(key + e));
+    }
+}
+
+int retrieval_groups(int Lb) { return (Lb + kRetQueries - 1) / kRetQueries; }
+
 // Key parts per query group: enough workgroups for 256 compute units, each wave keeping
 // at least 8 tiles; a multiple of 8 when there are 8 or more (XCD-local parts).
-static int retrieval_parts(int n_groups, int64_t n_tiles) {
+int retrieval_parts(int n_groups, int64_t n_tiles) {
     int64_t p = (256 + n_groups - 1) / n_groups;
     const int64_t by_tiles = n_tiles / (8 * (kScoreThreads / kWave));
     if (p > by_tiles) p = by_tiles;
@@ -246,6 +334,22 @@ static int retrieval_parts(int n_groups, int64_t n_tiles) {
     if (p < 1) p = 1;
     if (p >= 8) p &= ~(int64_t)7;
     return (int)p;
+}
+
+// Runs per segment list: a segment's lane sees 4 runs per tile, each stored with probability
+// about 4 p (p = 2.5 top_k / N, the candidate rate); mean plus six standard deviations and 8,
+// or every run of the segment when the row keeps all keys.
+int retrieval_seg_cap(int parts, int64_t n_tiles, int top_k, bool keep_all) {
+    const int64_t tps = (n_tiles + parts * 4 - 1) / (parts * 4);
+    const int64_t most = tps * 4;  // a segment never stores more runs than that
+    if (keep_all) return (int)most;
+    const double n = (double)n_tiles * kKeyTile;
+    double p = 4.0 * 2.5 * top_k / n;
+    if (p > 1.0) p = 1.0;
+    const double mean = (double)most * p;
+    int64_t cap = (int64_t)(mean + 6.0 * sqrt(mean) + 8.0);
+    cap = (cap + 7) & ~(int64_t)7;
+    return (int)(cap < most ? cap : most);
 }
 
 hipError_t launch_retrieval_block(RetrievalArgs r, const IndexerArgs& a, bool need_sample, int n_table_rows,
@@ -257,7 +361,7 @@ hipError_t launch_retrieval_block(RetrievalArgs r, const IndexerArgs& a, bool ne
                                                    const_cast<float*>(a.w), const_cast<RowInfo*>(a.rows),
                                                    n_table_rows);
     }
-    r.n_groups = (r.Lb + kRetQueries - 1) / kRetQueries;
+    r.n_groups = retrieval_groups(r.Lb);
     if (need_sample) {
         ProfScope ps(s, kProfRetrievalSample);
         r.parts = retrieval_parts(r.n_groups, (r.sample_n + kKeyTile - 1) / kKeyTile);
@@ -267,8 +371,14 @@ hipError_t launch_retrieval_block(RetrievalArgs r, const IndexerArgs& a, bool ne
     if (e != hipSuccess) return e;
     {
         ProfScope ps(s, kProfRetrievalFilter);
-        r.parts = retrieval_parts(r.n_groups, (r.N + kKeyTile - 1) / kKeyTile);
+        const int64_t n_tiles = (r.N + kKeyTile - 1) / kKeyTile;
+        r.parts = retrieval_parts(r.n_groups, n_tiles);
+        r.seg_cap = retrieval_seg_cap(r.parts, n_tiles, a.top_k, !need_sample);
         retrieval_score_kernel<false><<<r.n_groups * r.parts, kScoreThreads, 0, s>>>(r);
+    }
+    {
+        ProfScope ps(s, kProfRetrievalGather);
+        retrieval_gather_kernel<<<r.Lb, kGatherThreads, 0, s>>>(r, r.parts * 8);
     }
     return launch_select_fold(a, s);
 }

@@ -267,7 +267,7 @@ int dsa_sparse_prefill_gate(int64_t B, int64_t L, int64_t N, int64_t min_context
  * the number of launches since the last read of that class, and forgets them.
  * Kernel classes: "key_stats", "score_sample", "row_prep", "score_filter",
  * "select", "fold", "sparse_attention", "causal_mask", "attn_split",
- * "attn_merge", "retr_prep", "retr_sample", "retr_filter".  Unknown names give
+ * "attn_merge", "retr_prep", "retr_sample", "retr_filter", "retr_gather".  Unknown names give
  * DSA_ERR_INVALID_ARG.  Host only; safe to
  * call from one thread at a time.
  */
