@@ -684,7 +684,7 @@ static dsa::IndexerLayout retrieval_layout(int64_t M, int64_t N, int32_t top_k, 
     int64_t rows = M < qb ? M : qb;
     if (rows < 1) rows = 1;
     const int64_t rp = round8(rows);
-    const dsa::IndexerLayout lay = dsa::IndexerLayout::make(rows, N, top_k, -1, rp, 0);
+    const dsa::IndexerLayout lay = dsa::IndexerLayout::make(rows, N, top_k, 0, rp, 0);  // no tiled copy
     auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
     // the full block and the last (shorter) block may split the corpus differently
     size_t c_full, c_tail = 0;
@@ -762,16 +762,12 @@ dsa_status_t dsa_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M,
     a.fold_bs = reinterpret_cast<double*>(ws + lay.off_fold_bs);
     a.fold_bf = reinterpret_cast<float*>(ws + lay.off_fold_bf);
     a.rows = reinterpret_cast<const dsa::RowInfo*>(ws + lay.off_rowinfo);
-    uint16_t* x_tile = reinterpret_cast<uint16_t*>(ws + lay.off_ktile);
-    a.k_tile = x_tile;
-    a.n_ktiles = (N + dsa::kKeyTileKeys - 1) / dsa::kKeyTileKeys;
     a.n_kstats = dsa::key_stats_blocks(N);
-    hipError_t e = dsa::launch_key_stats(x, N, a.kstats, x_tile, s);
+    hipError_t e = dsa::launch_key_stats(x, N, a.kstats, nullptr, s);  // statistics only
     if (e != hipSuccess) return hip_fail(e, "key statistics launch");
 
     dsa::RetrievalArgs r{};
     r.x = x;
-    r.x_tile = x_tile;
     r.N = N;
     r.sample = a.sample;
     r.sample_stride = lay.sample_stride;

@@ -239,6 +239,7 @@ struct ProfScope {
 };
 
 // Kernel launchers (indexer.hip).  Each returns the launch status.
+// k_tile may be null: statistics only.
 hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, uint16_t* k_tile, hipStream_t s);
 // The same over a batch: seqs[0 .. n_seqs) (device), n_tiles tiles in all.
 hipError_t launch_key_stats_batch(const uint16_t* k_idx, const SeqKeys* seqs, int n_seqs, int64_t n_tiles,
@@ -254,7 +255,6 @@ hipError_t launch_select_fold(const IndexerArgs& a, hipStream_t s);
 struct RetrievalArgs {
     const uint16_t* q;       // [Lb][128] this block's query rows
     const uint16_t* x;       // [N][128] corpus (the sample reads it row-major)
-    const uint16_t* x_tile;  // the corpus in 32-row scoring tiles
     int64_t N;
     int Lb, n_groups, parts;
     float* sample;           // [Lb][sample_stride]

@@ -192,15 +192,17 @@ __global__ __launch_bounds__(kStatsThreads) void key_stats_kernel(const uint16_t
             for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
             nmax = fmaxf(nmax, sqrtf(ss));
             const int q = i * 64 + lane;
-            st[(q >> 4) * kStatsRowPad + (q & 15)] = v[i];
+            if (k_tile) st[(q >> 4) * kStatsRowPad + (q & 15)] = v[i];
         }
         // Store i: lane l = 32 hf + c writes key c, dims 64 hf + 8 i .. (the scoring order).
         // (LDS accesses of one wave complete in order, so the reads see this tile's writes
-        // and the next tile's writes come after them.)
+        // and the next tile's writes come after them.)  No copy wanted: statistics only.
+        if (k_tile) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const u16x8 w = st[(lane & 31) * kStatsRowPad + (lane >> 5) * 8 + i];
-            reinterpret_cast<u16x8*>(k_tile)[t * (int64_t)(kKeyTileBytes / 16) + i * 64 + lane] = w;
+            for (int i = 0; i < 8; ++i) {
+                const u16x8 w = st[(lane & 31) * kStatsRowPad + (lane >> 5) * 8 + i];
+                reinterpret_cast<u16x8*>(k_tile)[t * (int64_t)(kKeyTileBytes / 16) + i * 64 + lane] = w;
+            }
         }
     }
     nmax = wave_max(nmax);

@@ -53,21 +53,28 @@ __global__ __launch_bounds__(256) void retrieval_prep_kernel(const uint16_t* __r
 
 constexpr int kRetRing = 4;  // tiles of each wave's LDS ring (DMA runs kRetRing - 1 tiles ahead)
 
-// DMA of the A operand of tile t into an LDS slot: chunk kk (1 KB) holds, for lane (hf, c),
-// corpus row c of the tile, dims 64 hf + 8 kk .. (lane l's 16 bytes at kk * 1024 + 16 l).
+// DMA of the A operand of tile t (32 corpus rows, 256 bytes each) into an LDS slot, row-major
+// with the 16-byte chunks of row rho stored at chunk position (chunk ^ (rho & 15)): the MFMA
+// reads of one k-step (32 rows, the same chunk) then hit distinct banks, and each DMA
+// instruction reads 4 whole rows (1 KB) of the corpus.  Instruction kk fills LDS bytes
+// kk * 1024 + 16 l, i.e. row 4 kk + l / 16, position l % 16.  Rows past N (the last tile)
+// repeat row N - 1; the sample's tile rows are the sampled rows.
 template <bool kSample>
 __device__ __forceinline__ void ret_dma(const RetrievalArgs& A, const char* slot, int64_t t, int lane) {
-    if (kSample) {
-        int64_t j = t * kKeyTile + (lane & 31);
-        j = j < A.sample_n ? j : A.sample_n - 1;
-        const int64_t row = j * A.N / A.sample_n;
-        const char* p = reinterpret_cast<const char*>(A.x + (size_t)row * kIdxDim + 64 * (lane >> 5));
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) dma_lds16(p + 16 * kk, slot + 1024 * kk);
-    } else {
-        const char* p = reinterpret_cast<const char*>(A.x_tile) + (size_t)t * kKeyTileBytes + 16 * lane;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) dma_lds16(p + 1024 * kk, slot + 1024 * kk);
+    for (int kk = 0; kk < 8; ++kk) {
+        const int rho = 4 * kk + (lane >> 4);
+        const int chunk = (lane & 15) ^ (rho & 15);
+        int64_t row;
+        if (kSample) {
+            int64_t j = t * kKeyTile + rho;
+            j = j < A.sample_n ? j : A.sample_n - 1;
+            row = j * A.N / A.sample_n;
+        } else {
+            row = t * kKeyTile + rho;
+            row = row < A.N ? row : A.N - 1;
+        }
+        dma_lds16(reinterpret_cast<const char*>(A.x + (size_t)row * kIdxDim) + 16 * chunk, slot + 1024 * kk);
     }
 }
 
@@ -191,11 +198,13 @@ __global__ __launch_bounds__(256) void retrieval_score_kernel(RetrievalArgs A) {
             float te[kRetSets];  // the check threshold: +inf when tile t is not this wave's
 #pragma unroll
             for (int s = 0; s < kRetSets; ++s) te[s] = kSample ? (ok && live[s] ? 0.f : 1.f) : (ok ? tau[s] : INFINITY);
-            const u16x8* sp = reinterpret_cast<const u16x8*>(slot(u)) + lane;
-            u16x8 a_cur = sp[0];
+            // lane (hf, c) reads row c, chunk 8 hf + kk (dims 64 hf + 8 kk ..) of the slot
+            const u16x8* sp = reinterpret_cast<const u16x8*>(slot(u)) + 16 * c;
+            auto rd = [&](int kk) { return sp[(8 * hf + kk) ^ (c & 15)]; };
+            u16x8 a_cur = rd(0);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                const u16x8 a_nxt = sp[64 * (kk < 7 ? kk + 1 : 7)];
+                const u16x8 a_nxt = rd(kk < 7 ? kk + 1 : 7);
 #pragma unroll
                 for (int s = 0; s < kRetSets; ++s) {
                     nx[s] = mfma_32x32x16(__builtin_bit_cast(bf16x8, a_cur), b[s][kk], kk == 0 ? f32x16{} : nx[s]);

@@ -242,7 +242,8 @@ dsa_status_t dsa_sparse_prefill_varlen(const uint16_t* q, const uint16_t* kv, in
  *            when N < top_k
  *   workspace / workspace_bytes: at least
  *            dsa_retrieval_topk_workspace_bytes(M, N, top_k, q_block) bytes,
- *            256-byte aligned (it holds a 32-row tiled copy of the corpus)
+ *            256-byte aligned; it grows with min(M, q_block) and N / top_k-sized
+ *            candidate lists, not with N alone (the corpus is read in place)
  * Errors as dsa_indexer_topk (dim != 128 gives DSA_ERR_UNSUPPORTED).  M == 0 is a
  * no-op returning DSA_OK.
  */
