@@ -286,5 +286,6 @@ def test_retrieval_zero_queries_and_workspace(lib):
     f = lib.dsa_retrieval_topk_workspace_bytes
     a, b = f(1024, 1 << 20, 1024, 0), f(4096, 1 << 20, 1024, 0)
     assert a == b > 0  # bounded by the query block
-    assert f(1024, 1 << 20, 1024, 0) < (1 << 20) * 256  # no copy of the corpus
+    # no copy of the corpus: beyond a million rows the size hardly depends on N
+    assert f(1024, 4 << 20, 1024, 0) < 1.2 * f(1024, 1 << 20, 1024, 0)
     assert f(0, 100, 8, 0) == 0 and f(4, 0, 8, 0) == 0 and f(4, 100, 0, 0) == 0 and f(4, 100, 8, -1) == 0
