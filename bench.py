@@ -26,6 +26,11 @@ dsa_sparse_prefill_varlen) beside the same sequences run one call each.
 
 times the inner-product top-k over a corpus (dsa_retrieval_topk): M Gaussian queries
 against N Gaussian corpus rows of 128 dims, top_k 1,024.
+
+    python bench.py --pack KEEP [--config C3]
+
+times the sparse attention alone, unpacked and with neighbour packing, on index rows where
+each query keeps a fraction KEEP of its predecessor's keys.
 """
 from __future__ import annotations
 
@@ -160,6 +165,8 @@ def main():
     ap.add_argument("--retrieval-n", type=int, default=1 << 20)
     ap.add_argument("--retrieval-m", type=int, default=1024)
     ap.add_argument("--retrieval-k", type=int, default=1024)
+    ap.add_argument("--pack", type=float, default=None, metavar="KEEP",
+                    help="time the attention unpacked and neighbour-packed on rows sharing KEEP of their keys")
     ap.add_argument("--print-source-hash", metavar="KERNEL", choices=sorted(KERNEL_SOURCES),
                     help="print the source hash a traffic summary for KERNEL must carry, and exit")
     args = ap.parse_args()
@@ -205,6 +212,9 @@ def main():
     log(f"[bench] {wl.name}: inputs generated in {time.perf_counter() - t0:.1f} s")
     if args.decode:
         bench_decode(args, wl, inp, dev)
+        return
+    if args.pack is not None:
+        bench_pack(args, wl, inp, dev)
         return
 
     def bf(a):
@@ -393,6 +403,58 @@ def bench_decode(args, wl, inp, dev):
         result["cpu_baseline"] = {"value": round(1.0 / secs, 3), "unit": "steps/s", "cores": 1, "kind": "oracle",
                                   "sample": f"one decode step (1 query over {n_t} keys), fp64 C oracle: "
                                             f"full-sort top-k + sparse attention; {secs:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
+def bench_pack(args, wl, inp, dev):
+    """Attention only: dsa_sparse_prefill vs dsa_sparse_prefill_packed on overlapping index rows."""
+    import numpy as np
+    import torch
+
+    import dsa_inputs as di
+    import dsa_sparse_attention_indexer_amd as dsa
+
+    rng = di.make_rng(wl.seed + 77)
+    idx_h = di.overlapping_topk_indices(rng, wl.L, wl.N, wl.top_k, wl.pos0, args.pack)
+    pairs = idx_h[0::2][: wl.L // 2], idx_h[1::2][: wl.L // 2]
+    union = np.mean([np.union1d(a[a >= 0], b[b >= 0]).size for a, b in zip(*pairs)])
+    shared = float(np.mean([np.intersect1d(a, b).size for a, b in zip(*pairs)])) / wl.top_k
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, kv, idx = bf(inp["q"]), bf(inp["kv"]), torch.from_numpy(idx_h).to(dev)
+    out = torch.empty((wl.L, wl.H, 512), dtype=torch.bfloat16, device=dev)
+    scale = float(np.float32(di.SOFTMAX_SCALE))
+    res = {}
+    for pack in (False, True):
+        for _ in range(args.warmup):
+            dsa.sparse_prefill(q, kv, idx, wl.pos0, scale, out=out, pack=pack)
+        torch.cuda.synchronize()
+        dsa.profile_enable(True)
+        dsa.profile_read("sparse_attention")
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dsa.sparse_prefill(q, kv, idx, wl.pos0, scale, out=out, pack=pack)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+        kms, n = dsa.profile_read("sparse_attention")
+        dsa.profile_enable(False)
+        res["packed" if pack else "unpacked"] = {"ms_per_step": round(ms, 4), "kernel_ms_per_step": round(kms / args.steps, 4),
+                                                 "tokens_per_s": round(wl.L / (ms / 1000.0), 1)}
+    result = {
+        "metric": f"sparse attention tokens/sec with and without neighbour packing, {wl.name} shapes",
+        "value": res["packed"]["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} attention: L={wl.L} queries, top_k={wl.top_k}, {wl.H} heads; each index "
+                               f"row keeps {args.pack} of the previous row's keys", "keep": args.pack},
+        "pair_shared_fraction": round(shared, 4),
+        "pair_union_rows": round(float(union), 1),
+        "runs": res,
+        "speedup": round(res["unpacked"]["ms_per_step"] / res["packed"]["ms_per_step"], 4),
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -235,3 +235,32 @@ def random_topk_indices(rng: np.random.Generator, L: int, N: int, top_k: int, q_
             row = out[t, :n]
             row[m] = fut
     return out
+
+
+def overlapping_topk_indices(rng: np.random.Generator, L: int, N: int, top_k: int, q_pos0: int,
+                             keep: float) -> np.ndarray:
+    """Ascending distinct causal key indices per row (-1 tail) where each row keeps about a
+    fraction `keep` of the previous row's keys and draws the rest anew: neighbouring queries'
+    sets overlap, as the LiteDSA packing assumes.  Pure index bookkeeping."""
+    out = np.full((L, top_k), -1, dtype=np.int32)
+    prev = None
+    taken = np.zeros(min(q_pos0 + L, N), dtype=bool)
+    for t in range(L):
+        p = min(q_pos0 + t, N - 1)
+        n = min(top_k, p + 1)
+        kept = prev[rng.random(prev.size) < keep][:n] if prev is not None else np.zeros(0, np.int64)
+        taken[kept] = True
+        fresh = []
+        need = n - kept.size
+        while need > 0:  # draw from the causal keys not yet in the row
+            cand = np.unique(rng.integers(0, p + 1, size=2 * need + 16))
+            cand = cand[~taken[cand]]
+            cand = cand[rng.permutation(cand.size)][:need]
+            taken[cand] = True
+            fresh.append(cand)
+            need -= cand.size
+        sel = np.sort(np.concatenate([kept] + fresh)).astype(np.int32)
+        taken[sel] = False
+        out[t, :n] = sel
+        prev = sel
+    return out

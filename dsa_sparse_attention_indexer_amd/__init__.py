@@ -31,7 +31,8 @@ DEFAULT_Q_BLOCK = 1024
 MAX_BATCH = 65536
 
 EXPORTED = ["dsa_indexer_topk_workspace_bytes", "dsa_indexer_topk", "dsa_causal_mask_topk",
-            "dsa_sparse_prefill", "dsa_sparse_decode_workspace_bytes", "dsa_sparse_decode",
+            "dsa_sparse_prefill", "dsa_sparse_prefill_packed", "dsa_sparse_decode_workspace_bytes",
+            "dsa_sparse_decode",
             "dsa_indexer_topk_varlen_workspace_bytes", "dsa_indexer_topk_varlen",
             "dsa_sparse_prefill_varlen_workspace_bytes", "dsa_sparse_prefill_varlen",
             "dsa_retrieval_topk_workspace_bytes", "dsa_retrieval_topk",
@@ -68,6 +69,8 @@ def load_library(path: str | None = None):
     lib.dsa_causal_mask_topk.argtypes = [P, i64, i32, i64, P]
     lib.dsa_sparse_prefill.restype = ctypes.c_int
     lib.dsa_sparse_prefill.argtypes = [P, P, i64, P, i64, i64, i32, i32, i32, i32, i64, f32, i32, P, P, P]
+    lib.dsa_sparse_prefill_packed.restype = ctypes.c_int
+    lib.dsa_sparse_prefill_packed.argtypes = lib.dsa_sparse_prefill.argtypes
     lib.dsa_sparse_decode_workspace_bytes.restype = sz
     lib.dsa_sparse_decode_workspace_bytes.argtypes = [i64, i32, i32, i32]
     lib.dsa_sparse_decode.restype = ctypes.c_int
@@ -196,11 +199,13 @@ def causal_mask_topk(idx, q_pos0: int, stream=None):
 
 
 def sparse_prefill(q, kv, idx, q_pos0: int, scale: float, q_block: int = DEFAULT_Q_BLOCK,
-                   return_lse: bool = False, out=None, lse=None, stream=None):
+                   return_lse: bool = False, out=None, lse=None, stream=None, pack: bool = False):
     """Sparse absorbed-MLA attention -> bf16 [L, H, 512] (and fp32 lse [L, H]).
 
     q bf16 [L, H, 576]; kv bf16 [N, >=576] (latent 0..511 | rope 512..575, the
     latent is also the value); idx int32 [L, top_k] (-1 and future keys skipped).
+    pack=True gathers the union of neighbouring queries' rows once (same result up to
+    the rounding order of the softmax sums).
     """
     import torch
 
@@ -223,9 +228,10 @@ def sparse_prefill(q, kv, idx, q_pos0: int, scale: float, q_block: int = DEFAULT
         _req(out, "out", torch.bfloat16, 3)
     if return_lse and lse is None:
         lse = torch.empty((L, H), dtype=torch.float32, device=q.device)
-    _check(lib.dsa_sparse_prefill(q.data_ptr(), kv.data_ptr(), kv.stride(0), idx.data_ptr(), L, N, H,
-                                  D_LATENT, D_ROPE, top_k, q_pos0, float(scale), q_block, out.data_ptr(),
-                                  lse.data_ptr() if lse is not None else None, _stream_ptr(q, stream)))
+    fn = lib.dsa_sparse_prefill_packed if pack else lib.dsa_sparse_prefill
+    _check(fn(q.data_ptr(), kv.data_ptr(), kv.stride(0), idx.data_ptr(), L, N, H,
+              D_LATENT, D_ROPE, top_k, q_pos0, float(scale), q_block, out.data_ptr(),
+              lse.data_ptr() if lse is not None else None, _stream_ptr(q, stream)))
     return (out, lse) if return_lse else out
 
 

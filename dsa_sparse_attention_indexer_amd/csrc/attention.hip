@@ -49,16 +49,127 @@ __device__ __forceinline__ u16x4 lds_read_tr(const uint16_t* p) {
     return __builtin_bit_cast(u16x4, v);
 }
 
+// Neighbour packing (LiteDSA page, Fig. 3 and abstract: neighbouring tokens' candidate sets
+// overlap, so they are gathered once and attended jointly, each query masking the keys it did
+// not select): workgroup b takes queries 2b and 2b + 1.  Its prologue builds the union of the
+// two index rows in LDS with a 2-bit mask per key (query q may use the key iff bit q is set);
+// each union tile is gathered once and the first H/16 waves attend for query 2b, the next
+// H/16 for query 2b + 1.  Rows that are ascending with a -1 tail (what the indexer writes)
+// are merged with duplicates removed; other rows are simply concatenated.
+constexpr int kPackMaxK = 2048;  // top_k limit of the packed kernel (LDS for the union)
+
+// Union of the pair's rows into s_ukey / s_umask (returns the entry count).  Every thread of
+// the workgroup takes part; the result is published by a barrier.
+__device__ int pack_union(const AttentionArgs& A, int t0, int* s_ra, int* s_rb, int* s_d, int* s_ukey,
+                          uint8_t* s_umask, int* s_cnt, int* s_scan) {
+    const int tid = threadIdx.x, nthreads = blockDim.x, K = A.top_k;
+    const bool has1 = t0 + 1 < A.Lb;
+    const int64_t p0 = A.pos0 + t0, p1 = p0 + 1;
+    if (tid < 4) s_cnt[tid] = 0;
+    for (int i = tid; i < K; i += nthreads) {
+        s_ra[i] = A.idx[(size_t)t0 * K + i];
+        s_rb[i] = has1 ? A.idx[(size_t)(t0 + 1) * K + i] : -1;
+    }
+    __syncthreads();
+    // Mergeable: the entries >= 0 form a strictly ascending prefix, then only -1.
+    int ca = 0, cb = 0, bad = 0;
+    for (int i = tid; i < K; i += nthreads) {
+        const int x = s_ra[i], xn = i + 1 < K ? s_ra[i + 1] : -1;
+        const int y = s_rb[i], yn = i + 1 < K ? s_rb[i + 1] : -1;
+        ca += x >= 0;
+        cb += y >= 0;
+        bad |= (x < 0 && (x != -1 || xn >= 0)) || (x >= 0 && xn >= 0 && xn <= x);
+        bad |= (y < 0 && (y != -1 || yn >= 0)) || (y >= 0 && yn >= 0 && yn <= y);
+    }
+    if (ca) atomicAdd(&s_cnt[0], ca);
+    if (cb) atomicAdd(&s_cnt[1], cb);
+    if (bad) atomicOr(&s_cnt[2], 1);
+    __syncthreads();
+    const int a = s_cnt[0], b = s_cnt[1];
+    auto bit0 = [&](int key) { return key >= 0 && key <= p0 ? 1 : 0; };
+    auto bit1 = [&](int key) { return has1 && key >= 0 && key <= p1 ? 2 : 0; };
+    if (s_cnt[2]) {  // concatenation: every entry of row 0, then every entry of row 1
+        for (int i = tid; i < K; i += nthreads) {
+            s_ukey[i] = s_ra[i];
+            s_umask[i] = (uint8_t)bit0(s_ra[i]);
+            s_ukey[K + i] = s_rb[i];
+            s_umask[K + i] = (uint8_t)bit1(s_rb[i]);
+        }
+        __syncthreads();
+        return has1 ? 2 * K : K;
+    }
+    // Sorted: number of entries of row 0 below x (and whether x occurs in it), by bisection.
+    auto lower = [&](const int* v, int n, int x) {
+        int lo = 0, hi = n;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (v[mid] < x) lo = mid + 1;
+            else hi = mid;
+        }
+        return lo;
+    };
+    // Inclusive scan of one int per thread, in thread order (Hillis-Steele in s_scan).
+    auto block_scan = [&](int v) {
+        s_scan[tid] = v;
+        __syncthreads();
+        for (int d = 1; d < nthreads; d <<= 1) {
+            const int u = tid >= d ? s_scan[tid - d] : 0;
+            __syncthreads();
+            s_scan[tid] += u;
+            __syncthreads();
+        }
+        const int r = s_scan[tid];
+        __syncthreads();
+        return r;
+    };
+    // s_d[j] = entries of row 1 before j that also occur in row 0 (each thread a chunk of j).
+    const int per = (b + nthreads - 1) / nthreads;
+    const int j0 = tid * per, j1 = min(b, j0 + per);
+    int dups = 0;
+    for (int j = j0; j < j1; ++j) dups += lower(s_ra, a, s_rb[j]) < a && s_ra[lower(s_ra, a, s_rb[j])] == s_rb[j];
+    int before = block_scan(dups) - dups;
+    for (int j = j0; j < j1; ++j) {
+        const int l = lower(s_ra, a, s_rb[j]);
+        s_d[j] = before;
+        before += l < a && s_ra[l] == s_rb[j];
+    }
+    if (tid == nthreads - 1) s_d[b] = before;  // the last chunk ends at b (or is empty): all duplicates
+    __syncthreads();
+    // Union position of a row-0 entry: i + (row-1 entries below it) - (duplicates among those);
+    // of a row-1 entry that is not in row 0: j - (duplicates before it) + (row-0 entries below it).
+    for (int i = tid; i < a; i += nthreads) {
+        const int x = s_ra[i];
+        const int l = lower(s_rb, b, x);
+        const bool dup = l < b && s_rb[l] == x;
+        const int pos = i + l - s_d[l];
+        s_ukey[pos] = x;
+        s_umask[pos] = (uint8_t)(bit0(x) | (dup ? bit1(x) : 0));
+    }
+    for (int j = tid; j < b; j += nthreads) {
+        const int y = s_rb[j];
+        const int l = lower(s_ra, a, y);
+        if (l < a && s_ra[l] == y) continue;
+        const int pos = j - s_d[j] + l;
+        s_ukey[pos] = y;
+        s_umask[pos] = (uint8_t)bit1(y);
+    }
+    __syncthreads();
+    return a + b - s_d[b];
+}
+
 // kSplit: workgroup (t, s) takes the tiles [s*tps, (s+1)*tps) of query t (tps = tiles per
-// split) and writes an unnormalised partial instead of the output.
-template <bool kSplit>
+// split) and writes an unnormalised partial instead of the output.  kPack: workgroup b takes
+// the pair (2b, 2b + 1) over the union of their rows (see pack_union).
+template <bool kSplit, bool kPack>
 __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
-    const int t = blockIdx.x;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4;
     const int c16 = lane & 15;
     const int nthreads = blockDim.x;
+    const int hq = A.H / 16;                 // waves per query
+    const int qsel = kPack ? wave / hq : 0;  // the query of the pair this wave attends for
+    const int t = kPack ? 2 * (int)blockIdx.x + qsel : (int)blockIdx.x;
     int64_t p = A.pos0 + t;
     const uint16_t* kv = A.kv;
     if (A.qinfo) {  // a batch: the query's own sequence
@@ -66,8 +177,8 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
         p = qi.pos;
         kv = A.kv + (size_t)qi.kbase * A.kv_stride;
     }
-    const bool compute = wave < A.H / 16;
-    const int h = wave * 16 + c16;
+    const bool compute = kPack ? (qsel < 2 && t < A.Lb) : wave < hq;
+    const int h = (kPack ? wave - qsel * hq : wave) * 16 + c16;
     // The K order of the value product (and, to match, the row order of the logits):
     // lane group g takes tile rows slot_row(g, 0..3) and 16 + those.  Groups 0, 1 get the
     // even rows 0..14 and groups 2, 3 the odd ones, so the transpose reads of each lane
@@ -77,22 +188,41 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
 
     __shared__ __attribute__((aligned(16))) uint16_t Kbuf[2][kAttnTile][kKrowStride];
     __shared__ int s_idx[3][kAttnTile];  // raw top-k entries of three consecutive tiles
+    // packed pair: the two rows, duplicate counts, the union and its masks
+    constexpr int kPk = kPack ? kPackMaxK : 1;
+    __shared__ int s_ra[kPk], s_rb[kPk], s_d[kPk + 1], s_ukey[2 * kPk], s_cnt[4], s_scan[kPack ? 512 : 1];
+    __shared__ uint8_t s_umask[2 * kPk];
 
     const int32_t* irow = A.idx + (size_t)t * A.top_k;
-    const int n_all = (A.top_k + kAttnTile - 1) / kAttnTile;
+    int n_union = 0;
+    if (kPack) n_union = pack_union(A, 2 * (int)blockIdx.x, s_ra, s_rb, s_d, s_ukey, s_umask, s_cnt, s_scan);
+    const int n_all = ((kPack ? n_union : A.top_k) + kAttnTile - 1) / kAttnTile;
     const int tps = kSplit ? (n_all + A.splits - 1) / A.splits : n_all;
     const int t_lo = kSplit ? (int)blockIdx.y * tps : 0;
     const int n_tiles = t_lo + tps < n_all ? t_lo + tps : n_all;  // one past this workgroup's last tile
     const int nwaves = nthreads >> 6;
     // Entry j of the row as a key this query may use, or -1.
     const int p32 = (int)p;  // <= N - 1 <= INT32_MAX - 1
+    // (packed: union entry tile_j + r, a key one of the pair may use, or -1)
     auto key_of = [&](int slot, int r, int tile_j) -> int {
+        if (kPack) {
+            const int e = tile_j + r;
+            return e < n_union && s_umask[e] ? s_ukey[e] : -1;
+        }
         const int key = s_idx[slot][r];
         return (tile_j + r < A.top_k && key >= 0 && key <= p32) ? key : -1;
     };
+    // Entry r of the tile at tile_j usable by this wave's query.
+    auto usable = [&](int slot, int r, int tile_j) -> bool {
+        if (kPack) {
+            const int e = tile_j + r;
+            return e < n_union && ((s_umask[e] >> qsel) & 1);
+        }
+        return key_of(slot, r, tile_j) >= 0;
+    };
     // DMA of the raw entries of tile j into slot (lanes past top_k fetch nothing).
     auto fetch_idx = [&](int j, int slot) {
-        if (wave == 0 && lane < kAttnTile && j * kAttnTile + lane < A.top_k)
+        if (!kPack && wave == 0 && lane < kAttnTile && j * kAttnTile + lane < A.top_k)
             dma_lds4(irow + j * kAttnTile + lane, &s_idx[slot][0]);
     };
     // DMA of the rows of tile j (entries in slot) into buffer buf: wave w takes rows
@@ -156,7 +286,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
                 s1 = mfma_16x16x32(a1, qf[ks], s1);
             }
             // Usable entries of the tile as a bit mask (bit r: entry r), one ballot per wave.
-            const uint32_t vmask = (uint32_t)__ballot(lane < kAttnTile && key_of(slot, lane & 31, tile * kAttnTile) >= 0);
+            const uint32_t vmask = (uint32_t)__ballot(lane < kAttnTile && usable(slot, lane & 31, tile * kAttnTile));
             // Element r of this lane's logits is tile row slot_row(g, r) (s0) or 16 + that (s1).
             const uint32_t mlo = vmask >> slot_row(g, 0), mhi = vmask >> (16 + slot_row(g, 0));
             float lg[8];
@@ -301,7 +431,19 @@ hipError_t launch_sparse_attention(const AttentionArgs& a, hipStream_t s) {
     int threads = 64 * (a.H / 16);
     if (threads < kAttnMinThreads) threads = kAttnMinThreads;
     ProfScope ps(s, kProfAttention);
-    sparse_attn_kernel<false><<<a.Lb, threads, 0, s>>>(a);
+    sparse_attn_kernel<false, false><<<a.Lb, threads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+bool sparse_attention_packable(const AttentionArgs& a) {
+    return !a.qinfo && a.H <= 64 && a.top_k <= kPackMaxK;
+}
+
+hipError_t launch_sparse_attention_packed(const AttentionArgs& a, hipStream_t s) {
+    int threads = 2 * 64 * (a.H / 16);
+    if (threads < kAttnMinThreads) threads = kAttnMinThreads;
+    ProfScope ps(s, kProfAttention);
+    sparse_attn_kernel<false, true><<<(a.Lb + 1) / 2, threads, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -310,7 +452,7 @@ hipError_t launch_sparse_attention_split(const AttentionArgs& a, hipStream_t s) 
     if (threads < kAttnMinThreads) threads = kAttnMinThreads;
     {
         ProfScope ps(s, kProfAttnSplit);
-        sparse_attn_kernel<true><<<dim3(a.Lb, a.splits), threads, 0, s>>>(a);
+        sparse_attn_kernel<true, false><<<dim3(a.Lb, a.splits), threads, 0, s>>>(a);
     }
     {
         ProfScope ps(s, kProfAttnMerge);

@@ -351,10 +351,10 @@ dsa_status_t dsa_causal_mask_topk(int32_t* idx, int64_t L, int32_t top_k, int64_
     return DSA_OK;
 }
 
-dsa_status_t dsa_sparse_prefill(const uint16_t* q, const uint16_t* kv, int64_t kv_stride, const int32_t* idx,
-                                int64_t L, int64_t N, int32_t H, int32_t d_latent, int32_t d_rope, int32_t top_k,
-                                int64_t q_pos0, float scale, int32_t q_block, uint16_t* out, float* lse,
-                                dsa_stream_t stream) {
+static dsa_status_t sparse_prefill_impl(const uint16_t* q, const uint16_t* kv, int64_t kv_stride,
+                                       const int32_t* idx, int64_t L, int64_t N, int32_t H, int32_t d_latent,
+                                       int32_t d_rope, int32_t top_k, int64_t q_pos0, float scale, int32_t q_block,
+                                       uint16_t* out, float* lse, dsa_stream_t stream, bool pack) {
     g_last_error[0] = 0;
     if (L < 0) return fail(DSA_ERR_INVALID_ARG, "L must be >= 0 (got %lld)", (long long)L);
     if (N <= 0) return fail(DSA_ERR_INVALID_ARG, "N must be > 0 (got %lld)", (long long)N);
@@ -395,10 +395,27 @@ dsa_status_t dsa_sparse_prefill(const uint16_t* q, const uint16_t* kv, int64_t k
         a.H = H;
         a.top_k = top_k;
         a.scale = scale;
-        hipError_t e = dsa::launch_sparse_attention(a, s);
+        hipError_t e = pack && dsa::sparse_attention_packable(a) ? dsa::launch_sparse_attention_packed(a, s)
+                                                                 : dsa::launch_sparse_attention(a, s);
         if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
     }
     return DSA_OK;
+}
+
+dsa_status_t dsa_sparse_prefill(const uint16_t* q, const uint16_t* kv, int64_t kv_stride, const int32_t* idx,
+                                int64_t L, int64_t N, int32_t H, int32_t d_latent, int32_t d_rope, int32_t top_k,
+                                int64_t q_pos0, float scale, int32_t q_block, uint16_t* out, float* lse,
+                                dsa_stream_t stream) {
+    return sparse_prefill_impl(q, kv, kv_stride, idx, L, N, H, d_latent, d_rope, top_k, q_pos0, scale, q_block, out,
+                               lse, stream, false);
+}
+
+dsa_status_t dsa_sparse_prefill_packed(const uint16_t* q, const uint16_t* kv, int64_t kv_stride, const int32_t* idx,
+                                       int64_t L, int64_t N, int32_t H, int32_t d_latent, int32_t d_rope,
+                                       int32_t top_k, int64_t q_pos0, float scale, int32_t q_block, uint16_t* out,
+                                       float* lse, dsa_stream_t stream) {
+    return sparse_prefill_impl(q, kv, kv_stride, idx, L, N, H, d_latent, d_rope, top_k, q_pos0, scale, q_block, out,
+                               lse, stream, true);
 }
 
 static int resolve_splits(int64_t L, int32_t top_k, int32_t splits) {

@@ -302,6 +302,10 @@ struct AttentionArgs {
     float* part_ml;       // [Lb][splits][H][4]: reference max (base 2), bf16-weight sum, fp32-weight sum
 };
 hipError_t launch_sparse_attention(const AttentionArgs& a, hipStream_t s);
+// Neighbour packing: pairs of consecutive queries over the union of their rows (one sequence,
+// H <= 64, top_k <= 2048: sparse_attention_packable).
+bool sparse_attention_packable(const AttentionArgs& a);
+hipError_t launch_sparse_attention_packed(const AttentionArgs& a, hipStream_t s);
 // Split-key attention and the log-sum-exp merge of its partials.
 hipError_t launch_sparse_attention_split(const AttentionArgs& a, hipStream_t s);
 

@@ -142,6 +142,25 @@ dsa_status_t dsa_sparse_prefill(const uint16_t* q, const uint16_t* kv, int64_t k
                                 dsa_stream_t stream);
 
 /*
+ * dsa_sparse_prefill with neighbour packing (LiteDSA, in the LiteTopK page's
+ * abstract and Fig. 3: neighbouring tokens' candidate sets are similar, so they
+ * are packed for joint computation and each query masks the scores it did not
+ * select).  Queries 2b and 2b + 1 of each query block share one workgroup: the
+ * rows of the union of their index rows are gathered once, and each query
+ * attends only over its own entries.  The result is the dsa_sparse_prefill
+ * result (same definition and arguments) up to the rounding order of the
+ * softmax sums.  Rows that are ascending with a -1 tail (dsa_indexer_topk's
+ * output) are merged with repeats removed, which is where the gather saves
+ * bytes; other rows are concatenated.  H > 64 or top_k > 2048 run the unpacked
+ * kernel.  Arguments and errors as dsa_sparse_prefill.
+ */
+dsa_status_t dsa_sparse_prefill_packed(const uint16_t* q, const uint16_t* kv, int64_t kv_stride,
+                                       const int32_t* idx, int64_t L, int64_t N, int32_t H,
+                                       int32_t d_latent, int32_t d_rope, int32_t top_k,
+                                       int64_t q_pos0, float scale, int32_t q_block, uint16_t* out,
+                                       float* lse, dsa_stream_t stream);
+
+/*
  * Sparse attention split over the selected keys, for decode (L = 1) and short
  * chunks ("GLM prefill now attends only to the keys its indexer picks", How it
  * works: the sparse path uses the same absorbed form decode already uses; and
