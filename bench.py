@@ -54,6 +54,29 @@ def log(msg: str):
     print(msg, file=sys.stderr, flush=True)
 
 
+def graph_ms_per_step(step, steps: int, warmup: int) -> float:
+    """Capture step() once in a HIP graph (torch.cuda.graph) and time `steps` replays."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1000.0 / steps
+
+
 # Source files that define each timed kernel; a traffic figure measured with hardware
 # counters is reported only while these files are unchanged since the measurement.
 KERNEL_SOURCES = {
@@ -165,6 +188,8 @@ def main():
     ap.add_argument("--retrieval-n", type=int, default=1 << 20)
     ap.add_argument("--retrieval-m", type=int, default=1024)
     ap.add_argument("--retrieval-k", type=int, default=1024)
+    ap.add_argument("--graph", action="store_true",
+                    help="with --decode or --batch: also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--pack", type=float, default=None, metavar="KEEP",
                     help="time the attention unpacked and neighbour-packed on rows sharing KEEP of their keys")
     ap.add_argument("--print-source-hash", metavar="KERNEL", choices=sorted(KERNEL_SOURCES),
@@ -362,6 +387,7 @@ def bench_decode(args, wl, inp, dev):
         if n:
             kernels[k] = {"launches_per_step": round(n / args.steps, 4), "ms_per_launch": round(ms / n, 5)}
     dsa.profile_enable(False)
+    graph_ms = graph_ms_per_step(step, args.steps, args.warmup) if args.graph else None
     n_t = pos + 1
     f_idx = 2 * 32 * 128 * n_t
     b_attn = wl.top_k * 576 * 2 + 4 * wl.top_k + wl.H * 576 * 2 + wl.H * 512 * 2
@@ -381,6 +407,8 @@ def bench_decode(args, wl, inp, dev):
                    "N": wl.N, "L": 1, "top_k": wl.top_k, "attn_heads": wl.H},
         "kernels": kernels,
     }
+    if graph_ms is not None:
+        result["graph"] = {"ms_per_step": round(graph_ms, 5), "steps_per_s": round(1000.0 / graph_ms, 1)}
     sp = kernels.get("attn_split")
     sf = kernels.get("score_filter")
     if sp:
@@ -627,6 +655,7 @@ def bench_batch(args, dev):
 
     ms_one, _ = timed(per_sequence, False)
     ms, kernels = timed(batched, True)
+    graph_ms = graph_ms_per_step(batched, args.steps, args.warmup) if args.graph else None
     f_idx = sum(sum(r[0] for r in workload_sizes(wl)) for wl, _ in seqs)
     b_attn = sum(sum(r[2] for r in workload_sizes(wl)) for wl, _ in seqs)
     result = {
@@ -648,6 +677,8 @@ def bench_batch(args, dev):
         "per_sequence_calls": {"ms_per_step": round(ms_one, 4), "tokens_per_s": round(T / (ms_one / 1000.0), 1)},
         "kernels": kernels,
     }
+    if graph_ms is not None:
+        result["graph"] = {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(T / (graph_ms / 1000.0), 1)}
     per = {}
     sf = kernels.get("score_filter")
     if sf:
