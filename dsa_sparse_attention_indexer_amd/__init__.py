@@ -36,7 +36,7 @@ EXPORTED = ["dsa_indexer_topk_workspace_bytes", "dsa_indexer_topk", "dsa_causal_
             "dsa_indexer_topk_varlen_workspace_bytes", "dsa_indexer_topk_varlen",
             "dsa_sparse_prefill_varlen_workspace_bytes", "dsa_sparse_prefill_varlen",
             "dsa_retrieval_topk_workspace_bytes", "dsa_retrieval_topk",
-            "dsa_sparse_prefill_gate", "dsa_profile_enable",
+            "dsa_sparse_prefill_gate", "dsa_profile_enable", "dsa_profile_set",
             "dsa_profile_read", "dsa_status_string", "dsa_last_error", "dsa_version"]
 PROFILE_KERNELS = ["key_stats", "score_sample", "row_prep", "score_filter", "select", "fold",
                    "sparse_attention", "causal_mask", "attn_split", "attn_merge", "retr_prep", "retr_sample",
@@ -98,6 +98,8 @@ def load_library(path: str | None = None):
     lib.dsa_version.argtypes = []
     lib.dsa_profile_enable.restype = ctypes.c_int
     lib.dsa_profile_enable.argtypes = [ctypes.c_int]
+    lib.dsa_profile_set.restype = ctypes.c_int
+    lib.dsa_profile_set.argtypes = [ctypes.c_char_p]
     lib.dsa_profile_read.restype = ctypes.c_int
     lib.dsa_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int64)]
@@ -140,6 +142,12 @@ def version() -> str:
 def profile_enable(on: bool = True):
     """Bracket every library kernel launch with HIP events on its stream."""
     _check(load_library().dsa_profile_enable(1 if on else 0))
+
+
+def profile_set(kernels=None):
+    """Bracket only the given kernel classes (iterable of names; None = all) and turn timing on."""
+    names = "" if kernels is None else ",".join(kernels)
+    _check(load_library().dsa_profile_set(names.encode()))
 
 
 def profile_read(kernel: str):

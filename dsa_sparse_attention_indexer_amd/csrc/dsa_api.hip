@@ -15,7 +15,7 @@
 
 namespace dsa {
 namespace {
-std::atomic<bool> g_prof_on{false};
+std::atomic<uint32_t> g_prof_mask{0};  // kernel classes bracketed by events (bit k: class k)
 std::mutex g_prof_mu;
 struct ProfRecord {
     int kernel;
@@ -29,7 +29,7 @@ const char* const kProfNames[kProfCount] = {"key_stats", "score_sample", "row_pr
 }  // namespace
 
 ProfScope::ProfScope(hipStream_t s, int k) : stream(s), kernel(k), start(nullptr), on(false) {
-    if (!g_prof_on.load(std::memory_order_relaxed)) return;
+    if (!((g_prof_mask.load(std::memory_order_relaxed) >> k) & 1u)) return;
     if (hipEventCreate(&start) != hipSuccess) return;
     if (hipEventRecord(start, s) != hipSuccess) {
         (void)hipEventDestroy(start);
@@ -206,7 +206,29 @@ const char* dsa_version(void) { return "dsa-mi355x 0.1 (gfx950)"; }
 
 dsa_status_t dsa_profile_enable(int on) {
     g_last_error[0] = 0;
-    dsa::g_prof_on.store(on != 0);
+    dsa::g_prof_mask.store(on ? (1u << dsa::kProfCount) - 1u : 0u);
+    return DSA_OK;
+}
+
+dsa_status_t dsa_profile_set(const char* kernels) {
+    g_last_error[0] = 0;
+    if (!kernels || !kernels[0]) {
+        dsa::g_prof_mask.store((1u << dsa::kProfCount) - 1u);
+        return DSA_OK;
+    }
+    uint32_t mask = 0;
+    const char* p = kernels;
+    while (*p) {
+        const char* e = strchr(p, ',');
+        const size_t n = e ? (size_t)(e - p) : strlen(p);
+        int k = -1;
+        for (int i = 0; i < dsa::kProfCount; ++i)
+            if (strlen(dsa::kProfNames[i]) == n && strncmp(dsa::kProfNames[i], p, n) == 0) k = i;
+        if (k < 0) return fail(DSA_ERR_INVALID_ARG, "unknown kernel class '%.*s'", (int)n, p);
+        mask |= 1u << k;
+        p = e ? e + 1 : p + n;
+    }
+    dsa::g_prof_mask.store(mask);
     return DSA_OK;
 }
 

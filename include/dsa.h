@@ -292,6 +292,10 @@ int dsa_sparse_prefill_gate(int64_t B, int64_t L, int64_t N, int64_t min_context
  * call from one thread at a time.
  */
 dsa_status_t dsa_profile_enable(int on);
+/* Brackets only the listed kernel classes (comma-separated names as above; NULL or
+ * "" = all of them) and turns timing on; fewer events disturb the stream less.
+ * An unknown name gives DSA_ERR_INVALID_ARG and changes nothing.  Host only. */
+dsa_status_t dsa_profile_set(const char* kernels);
 dsa_status_t dsa_profile_read(const char* kernel, double* total_ms, int64_t* launches);
 
 /* Static description of a status code. */

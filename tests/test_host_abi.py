@@ -289,3 +289,11 @@ def test_retrieval_zero_queries_and_workspace(lib):
     # no copy of the corpus: beyond a million rows the size hardly depends on N
     assert f(1024, 4 << 20, 1024, 0) < 1.2 * f(1024, 1 << 20, 1024, 0)
     assert f(0, 100, 8, 0) == 0 and f(4, 0, 8, 0) == 0 and f(4, 100, 0, 0) == 0 and f(4, 100, 8, -1) == 0
+
+
+def test_profile_set_validates_names(lib):
+    assert lib.dsa_profile_set(b"score_filter,sparse_attention") == 0
+    assert lib.dsa_profile_set(b"score_filter,bogus") == 1
+    assert b"bogus" in lib.dsa_last_error()
+    assert lib.dsa_profile_set(b"") == 0 and lib.dsa_profile_set(None) == 0
+    assert lib.dsa_profile_enable(0) == 0
