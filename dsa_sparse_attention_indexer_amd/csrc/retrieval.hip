@@ -224,6 +224,9 @@ __global__ __launch_bounds__(256) void retrieval_score_kernel(RetrievalArgs A) {
             step(acc1, u, acc0, u - 1);
             step(acc0, u + 1, acc1, u);
         }
+        // The last steps requested (clamped) tiles past t1: let those DMAs land before the
+        // wave ends, so no write reaches this workgroup's LDS after it is released.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     if (!kSample) {
 #pragma unroll
