@@ -354,7 +354,7 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
         const int64_t n_last = (last_pos < N - 1 ? last_pos : N - 1) + 1;
         const bool need_sample = dsa::sample_size(n_last, top_k, lay.cap) > 0;
         a.parts = dsa::key_parts((Lb + dsa::kRowsPerGroup - 1) / dsa::kRowsPerGroup);
-        e = dsa::launch_indexer_block(a, need_sample, s);
+        e = dsa::launch_indexer_block(a, need_sample, s, Lb <= dsa::kRowsPerGroup / 2);
         if (e != hipSuccess) return hip_fail(e, "indexer launch");
     }
     return DSA_OK;
@@ -609,16 +609,19 @@ dsa_status_t dsa_indexer_topk_varlen(const uint16_t* q_idx, const uint16_t* k_id
             ++sq;
         }
         // The most keys a row of this block sees: a sample is needed if its group needs one.
-        int64_t n_last = 0;
+        // Also count the block's query rows: mostly padding means groups of few rows.
+        int64_t n_last = 0, live = 0;
         for (int64_t b = sq, r0 = sq_row0; b < B && r0 < b0 + Lb; r0 += round8(cu_q[b + 1] - cu_q[b]), ++b) {
             const int64_t L = cu_q[b + 1] - cu_q[b];
+            const int64_t i_first = b0 > r0 ? b0 - r0 : 0;
             const int64_t i_last = (b0 + Lb - r0 < L ? b0 + Lb - r0 : L) - 1;
             if (i_last >= 0 && pos0[b] + i_last + 1 > n_last) n_last = pos0[b] + i_last + 1;
+            if (i_last >= i_first) live += i_last - i_first + 1;
         }
         a.rows = rows + b0;
         a.Lb = (int)Lb;
         a.parts = dsa::key_parts((int)(Lb / dsa::kRowsPerGroup));
-        e = dsa::launch_indexer_block(a, dsa::sample_size(n_last, top_k, lay.cap) > 0, s);
+        e = dsa::launch_indexer_block(a, dsa::sample_size(n_last, top_k, lay.cap) > 0, s, 2 * live <= Lb);
         if (e != hipSuccess) return hip_fail(e, "indexer launch");
     }
     return DSA_OK;

@@ -244,7 +244,9 @@ hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks,
 // The same over a batch: seqs[0 .. n_seqs) (device), n_tiles tiles in all.
 hipError_t launch_key_stats_batch(const uint16_t* k_idx, const SeqKeys* seqs, int n_seqs, int64_t n_tiles,
                                   KeyStats* ks, uint16_t* k_tile, hipStream_t s);
-hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s);
+// sparse_rows: most row groups hold few query rows (decode, short chunks, batches of single
+// queries): the scoring skips the MFMAs of row pairs without a live row.
+hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s, bool sparse_rows = false);
 // The stages of launch_indexer_block that follow a scoring kernel: row_prep (error bound,
 // threshold from the sample), then select and the fold.
 hipError_t launch_row_prep(const IndexerArgs& a, hipStream_t s);

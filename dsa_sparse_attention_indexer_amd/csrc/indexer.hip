@@ -299,7 +299,10 @@ __device__ __forceinline__ void interleave_with_mfma() {
     }
 }
 
-template <bool kSample>
+// kSkip: a row pair with no live row (padding, or rows that keep all keys) skips its MFMAs
+// and epilogue (wave-uniform branches); for groups holding few live rows (decode, batches of
+// single queries).  Without it the schedule is branch-free.
+template <bool kSample, bool kSkip>
 struct ScoreTile {
     const IndexerArgs& P;
     const uint16_t* keys;       // the group's sequence: k_idx rows (sample)
@@ -325,6 +328,7 @@ struct ScoreTile {
     int lcnt[kRowsPerWave];     // entries staged per row (wave-uniform)
     int gcnt[kRowsPerWave];     // entries already flushed to the segment per row
     uint32_t tile0;     // first tile of this wave's contiguous range (wave-uniform)
+    bool pl[kPairs];    // kSkip: row pair q has a live row (wave-uniform)
 
     __device__ __forceinline__ uint32_t pos_of(int it) const { return (tile0 + (uint32_t)it) * kKeyTile + col; }
 
@@ -449,6 +453,18 @@ struct ScoreTile {
     __device__ __forceinline__ void step(f32x16 (&acc)[kRowsPerWave], const bf16x8 (&b)[8], int it) {
         flush_full();
         asm volatile("" ::: "memory");
+        if (kSkip) {
+            if (pl[0]) mfma2<0>(acc, b);
+            if (pl[3]) epilogue2<6>(acc, it - 1);
+            if (pl[1]) mfma2<2>(acc, b);
+            if (pl[0]) epilogue2<0>(acc, it);
+            asm volatile("" ::: "memory");
+            if (pl[2]) mfma2<4>(acc, b);
+            if (pl[1]) epilogue2<2>(acc, it);
+            if (pl[3]) mfma2<6>(acc, b);
+            if (pl[2]) epilogue2<4>(acc, it);
+            return;
+        }
         mfma2<0>(acc, b);
         epilogue2<6>(acc, it - 1);
         mfma2<2>(acc, b);
@@ -461,7 +477,7 @@ struct ScoreTile {
     }
 };
 
-template <bool kSample>
+template <bool kSample, bool kSkip>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int n_groups) {
     // Workgroups go round-robin over the 8 XCDs: XCDs 0-3 take key half 0, 4-7 half 1.
     // Two parts: XCDs 0-3 take key half 0 and 4-7 half 1.  More parts: consecutive
@@ -548,7 +564,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
         const int n_my = n_tiles > t0 ? min(n_tiles - t0, tps) : 0;
         // Rows of a group are consecutive (invalid rows never store), so every row's
         // list is addressed from row 0's.
-        ScoreTile<kSample> T{P, gref.keys,
+        ScoreTile<kSample, kSkip> T{P, gref.keys,
                              reinterpret_cast<const u16x8*>(P.k_tile) + (size_t)gref.tbase * (kKeyTileBytes / 16),
                              (uint32_t)gref.ntiles, a, wl,
                              {hf ? tau_r[1] : tau_r[0], hf ? tau_r[3] : tau_r[2], hf ? tau_r[5] : tau_r[4],
@@ -559,7 +575,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
                              kSample ? nullptr : P.cand + (size_t)r0 * P.cap + (appended ? 0 : (size_t)segment * seg),
                              n0, S, kSample && S > 0 ? (float)n0 / (float)S : 0.f, lane, hf, col, col - hf,
                              (int)gref.pos, r0, seg, cnt,
-                             s_stage[wave], {0, 0, 0, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0, 0}, (uint32_t)t0};
+                             s_stage[wave], {0, 0, 0, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0, 0}, (uint32_t)t0,
+                             {kSkip && (live[0] || live[1]), kSkip && (live[2] || live[3]),
+                              kSkip && (live[4] || live[5]), kSkip && (live[6] || live[7])}};
         // Tile it sits in buffer it % 3; tile it+3 is loaded once tile it's MFMAs are issued.
         bf16x8 b0[8], b1[8], b2[8];
         f32x16 acc[kRowsPerWave];
@@ -567,14 +585,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
             T.load(b0, 0);
             T.load(b1, 1);
             T.load(b2, 2);
-            T.template mfma2<0>(acc, b0);
-            T.template mfma2<2>(acc, b0);
-            T.template epilogue2<0>(acc, 0);
-            T.template mfma2<4>(acc, b0);
-            T.template epilogue2<2>(acc, 0);
-            T.template mfma2<6>(acc, b0);
+            if (!kSkip || T.pl[0]) T.template mfma2<0>(acc, b0);
+            if (!kSkip || T.pl[1]) T.template mfma2<2>(acc, b0);
+            if (!kSkip || T.pl[0]) T.template epilogue2<0>(acc, 0);
+            if (!kSkip || T.pl[2]) T.template mfma2<4>(acc, b0);
+            if (!kSkip || T.pl[1]) T.template epilogue2<2>(acc, 0);
+            if (!kSkip || T.pl[3]) T.template mfma2<6>(acc, b0);
             T.load(b0, 3);
-            T.template epilogue2<4>(acc, 0);
+            if (!kSkip || T.pl[2]) T.template epilogue2<4>(acc, 0);
             int it = 1;
             for (; it + 2 < n_my; it += 3) {
                 T.step(acc, b1, it);
@@ -587,7 +605,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
             if (it < n_my) T.step(acc, b1, it);
             if (it + 1 < n_my) T.step(acc, b2, it + 1);
             T.flush_full();  // the last epilogue adds up to 32 more entries to rows 6, 7
-            T.template epilogue2<6>(acc, n_my - 1);
+            if (!kSkip || T.pl[3]) T.template epilogue2<6>(acc, n_my - 1);
             T.flush_all();
         }
     }
@@ -1617,19 +1635,21 @@ hipError_t launch_varlen_tables(const VarlenChunk& c, int64_t seq0, RowInfo* row
     return hipGetLastError();
 }
 
-hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s) {
+hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s, bool sparse_rows) {
     const int groups = (a.Lb + kRowsPerGroup - 1) / kRowsPerGroup;
     // Two key halves per group (XCD-mapped) while that fills the GPU, else more key parts.
     const int score_wgs = a.parts == 2 ? 8 * ((groups + 3) / 4) : groups * a.parts;
     if (need_sample) {
         ProfScope ps(s, kProfScoreSample);
-        score_kernel<true><<<score_wgs, kScoreThreads, 0, s>>>(a, groups);
+        if (sparse_rows) score_kernel<true, true><<<score_wgs, kScoreThreads, 0, s>>>(a, groups);
+        else score_kernel<true, false><<<score_wgs, kScoreThreads, 0, s>>>(a, groups);
     }
     hipError_t e = launch_row_prep(a, s);
     if (e != hipSuccess) return e;
     {
         ProfScope ps(s, kProfScoreFilter);
-        score_kernel<false><<<score_wgs, kScoreThreads, 0, s>>>(a, groups);
+        if (sparse_rows) score_kernel<false, true><<<score_wgs, kScoreThreads, 0, s>>>(a, groups);
+        else score_kernel<false, false><<<score_wgs, kScoreThreads, 0, s>>>(a, groups);
     }
     return launch_select_fold(a, s);
 }
