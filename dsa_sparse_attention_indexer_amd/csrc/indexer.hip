@@ -863,7 +863,7 @@ __device__ void block_bitonic_sort(int* a, int n) {
 // (16 band keys x 16 heads x 4 dims per instruction); keys failing the test take the
 // sequential path.  The head terms fl(w_h max(d_h, +0)) and their ascending-h sum are
 // always evaluated in the canonical order.
-__device__ void band_rescore(int nb, const int* band_key, double* band_s, const uint16_t* __restrict__ q_row,
+__device__ __forceinline__ void band_rescore(int nb, const int* band_key, double* band_s, const uint16_t* __restrict__ q_row,
                              const float* __restrict__ w_row, const QHeadStat* __restrict__ qs_row,
                              const uint16_t* __restrict__ k_idx, SelectScratch& S) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -1279,8 +1279,9 @@ constexpr int kSelChunk = 16;  // candidates per thread: the block has cap / 16 
 
 // Exact top-k of one row's candidates.  The eight segments written by the scoring waves
 // are each in ascending key order and cover ascending key ranges, so their concatenation
-// is sorted by key: thread t holds positions [16t, 16t+16) of it in registers, and the
-// ascending output is a stable compaction (one block scan) of the selected positions.
+// is sorted by key.  Thread t holds positions e * blockDim + t (e < 16) of it in registers,
+// so each load instruction reads consecutive entries, and the ascending output is a stable
+// compaction of the selected positions (per-element wave ballots and one block scan).
 __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
     const int r = blockIdx.x;
     const int mode = P.mode[r];
@@ -1318,11 +1319,11 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
     float v[kSelChunk];
     int key[kSelChunk];
     int nv = 0;
-    const int base = threadIdx.x * kSelChunk;
+    const int nthr = (int)blockDim.x, tid = (int)threadIdx.x;
     if (ok) {
 #pragma unroll
         for (int e = 0; e < kSelChunk; ++e) {
-            const int j = base + e;
+            const int j = e * nthr + tid;
             v[e] = -INFINITY;
             key[e] = 0;
             if (j < total) {
@@ -1338,7 +1339,7 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
                 key[e] = (int)c.y;
             }
         }
-        nv = total > base ? (total - base < kSelChunk ? total - base : kSelChunk) : 0;
+        nv = total > tid ? min((total - tid + nthr - 1) / nthr, kSelChunk) : 0;
     }
     float kth = 0.f;
     if (ok) ok = block_kth_binned(RegSrc<kSelChunk>{v, nv}, k, &kth, S);
@@ -1361,7 +1362,7 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
             const int b = wave_append(in_band, &S.sh[5]);
             if (b >= 0 && b < kSelBand) {
                 s_band_key[b] = key[e];
-                s_band_pos[b] = base + e;
+                s_band_pos[b] = e * nthr + tid;
                 s_band_s[b] = sd;
             }
         }
@@ -1381,20 +1382,27 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
             __syncthreads();
             // Selected = above the band, or a band winner.
             if (!appended) {
-                // Stable compaction: the candidate list is in key order.
-                int c = 0;
+                // Stable compaction: the candidate list is in key order, position e * blockDim + t
+                // for element e of thread t, so the output offset of (e, t) counts the selected
+                // positions of the earlier elements and of the earlier threads in element e.
+                const int nw = nthr >> 6, wv = tid >> 6;
+                uint64_t m[kSelChunk];
 #pragma unroll
                 for (int e = 0; e < kSelChunk; ++e) {
-                    const int j = base + e;
-                    c += e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u));
+                    const int j = e * nthr + tid;
+                    m[e] = __ballot(e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u)));
+                    if ((tid & 63) == 0) S.out[e * nw + wv] = __builtin_popcountll(m[e]);
                 }
-                int o = block_incl_scan(c, S) - c;
+                __syncthreads();
+                const int ce = tid < kSelChunk * nw ? S.out[tid] : 0;
+                const int pre = block_incl_scan(ce, S) - ce;
+                if (tid < kSelChunk * nw) S.out[kSelChunk * 16 + tid] = pre;
+                __syncthreads();
 #pragma unroll
                 for (int e = 0; e < kSelChunk; ++e) {
-                    const int j = base + e;
-                    if (e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u))) {
+                    if ((m[e] >> (tid & 63)) & 1u) {
+                        const int o = S.out[kSelChunk * 16 + e * nw + wv] + mbcnt64(m[e]);
                         if (o < k) out_row[o] = key[e];
-                        ++o;
                     }
                 }
             } else if (nt <= kSelBitmapKeys) {
@@ -1406,7 +1414,7 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
                 __syncthreads();
 #pragma unroll
                 for (int e = 0; e < kSelChunk; ++e) {
-                    const int j = base + e;
+                    const int j = e * nthr + tid;
                     if (e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u)))
                         atomicOr(&bm[key[e] >> 5], 1u << (key[e] & 31));
                 }
@@ -1430,13 +1438,13 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
                 int c = 0;
 #pragma unroll
                 for (int e = 0; e < kSelChunk; ++e) {
-                    const int j = base + e;
+                    const int j = e * nthr + tid;
                     c += e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u));
                 }
                 int o = block_incl_scan(c, S) - c;
 #pragma unroll
                 for (int e = 0; e < kSelChunk; ++e) {
-                    const int j = base + e;
+                    const int j = e * nthr + tid;
                     if (e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u))) {
                         if (o < k) S.out[o] = key[e];
                         ++o;
