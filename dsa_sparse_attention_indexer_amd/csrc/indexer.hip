@@ -965,6 +965,29 @@ __device__ __forceinline__ bool band_wins(int x, int nb, int need, const int* ba
     return beat < need;
 }
 
+// Sets bit band_pos[x] of win for each band entry x among the `need` best of the band under
+// (score desc, key asc).  One wave per entry: its lanes compare the band against it in
+// 64-entry slices and count what beats it with a ballot.
+__device__ __forceinline__ void band_mark_winners(int nb, int need, const int* band_key, const double* band_s,
+                                                  const int* band_pos, uint32_t* win) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
+    for (int x = wave; x < nb; x += nwaves) {
+        const double sx = band_s[x];
+        const int ix = band_key[x];
+        int beat = 0;
+        for (int y0 = 0; y0 < nb; y0 += 64) {
+            const int y = y0 + lane;
+            bool b = false;
+            if (y < nb) {
+                const double sy = band_s[y];
+                b = (sy > sx) || (sy == sx && band_key[y] < ix);
+            }
+            beat += __builtin_popcountll(__ballot(b));
+        }
+        if (lane == 0 && beat < need) atomicOr(&win[band_pos[x] >> 5], 1u << (band_pos[x] & 31));
+    }
+}
+
 // Exact top-k of an unordered candidate list under (canonical score desc, key asc), used
 // by the blocked fold.  Writes the k selected keys (unordered) to sel_i and their fp32
 // scores to sel_s.  band_i / band_s / band_f: storage for up to band_cap near-threshold
@@ -1376,9 +1399,7 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
         if (ok) {
             if (delta > 0.f && nb > 0)
                 band_rescore(nb, s_band_key, s_band_s, ref.q, ref.w, P.qstat + (size_t)r * kIdxHeads, ref.keys, S);
-            for (int x = threadIdx.x; x < nb; x += blockDim.x)
-                if (band_wins(x, nb, k - n_in, s_band_key, s_band_s))
-                    atomicOr(&s_win[s_band_pos[x] >> 5], 1u << (s_band_pos[x] & 31));
+            band_mark_winners(nb, k - n_in, s_band_key, s_band_s, s_band_pos, s_win);
             __syncthreads();
             // Selected = above the band, or a band winner.
             if (!appended) {
@@ -1522,6 +1543,7 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
     double* band_s = P.fold_bs + (size_t)slot * P.fold_cap;
     float* band_f = P.fold_bf + (size_t)slot * P.fold_cap;
     const int k = P.top_k;
+    if (P.fb_ctrl[0] == 0) return;  // final here (select has finished): nothing to fold
     for (;;) {
         if (threadIdx.x == 0) {
             const int i = atomicAdd(&P.fb_ctrl[1], 1);
