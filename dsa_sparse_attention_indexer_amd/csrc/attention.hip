@@ -278,6 +278,10 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
 
         if (compute) {
             f32x4 s0 = f32x4{}, s1 = f32x4{};
+            // The two MFMA loops run at raised wave priority: the other wave on this SIMD is
+            // then usually in its softmax, and its VALU work fills the slots the matrix pipe
+            // leaves (measured ~1% faster than equal priority).
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < kDqk / 32; ++ks) {
                 const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&Kbuf[cur][pi_c][ks * 32 + 8 * g]));
@@ -285,6 +289,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
                 s0 = mfma_16x16x32(a0, qf[ks], s0);
                 s1 = mfma_16x16x32(a1, qf[ks], s1);
             }
+            __builtin_amdgcn_s_setprio(0);
             // Usable entries of the tile as a bit mask (bit r: entry r), one ballot per wave.
             const uint32_t vmask = (uint32_t)__ballot(lane < kAttnTile && usable(slot, lane & 31, tile * kAttnTile));
             // Element r of this lane's logits is tile row slot_row(g, r) (s0) or 16 + that (s1).
@@ -341,6 +346,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
             // or 16 + that (slots 4-7), columns 4*(c16%4)..+4 of each 16-column block.
             const uint16_t* vlo = &Kbuf[cur][slot_row(g, c16 >> 2)][4 * (c16 & 3)];
             const uint16_t* vhi = vlo + 16 * kKrowStride;
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int dt = 0; dt < kDv / 16; ++dt) {
                 const u16x4 lo = lds_read_tr(vlo + dt * 16);
@@ -348,6 +354,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
                 const u16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 o[dt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, av), pbf, o[dt]);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         dma_wait();
         __syncthreads();
