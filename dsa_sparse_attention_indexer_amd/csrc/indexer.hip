@@ -1062,9 +1062,9 @@ __device__ __forceinline__ float order_key_value(uint32_t k) {
 // A value no larger than the rk-th largest of vals[0..n) (1 <= rk <= n <= 64 * 256), for
 // a block of 256 threads.  The values become order-preserving keys; the bits above the
 // highest bit in which the smallest and largest key differ are common to all of them, and
-// up to three 8-bit radix passes over the bits below find the bucket holding the rk-th
+// up to two 11-bit radix passes over the bits below find the bucket holding the rk-th
 // largest key.  Its lowest key is returned (the candidate threshold only has to be a safe
-// estimate; the bucket spans at most 2^-24 of the key range).
+// estimate; the bucket spans at most 2^-22 of the key range).
 __device__ float rank_floor_256(const float* __restrict__ vals, int n, int rk, SelectScratch& S) {
     constexpr int kPer = 64;
     uint32_t key[kPer];
@@ -1096,39 +1096,54 @@ __device__ float rank_floor_256(const float* __restrict__ vals, int n, int rk, S
     }
     __syncthreads();
     if (kmin == kmax) return order_key_value(kmin);
-    // Keys = common high bits | d, with d < 2^(top+1).  Pass p takes the 8 bits of d ending
-    // at bit top - 8p (bits under 0 read as zero); the passes stop once bit 0 is reached.
+    // Keys = common high bits | d, with d < 2^(top+1).  Pass p takes the 11 bits of d ending
+    // at bit top - 11p (bits under 0 read as zero); the passes stop once bit 0 is reached.
+    constexpr int kDigit = 11, kDigitBins = 1 << kDigit, kOwn = kDigitBins / 256;
+    static_assert(kDigitBins <= kBins, "the digit histogram lives in the selection bins");
     const int top = 31 - __builtin_clz(kmin ^ kmax);
     const uint32_t common = top == 31 ? 0u : (kmax >> (top + 1)) << (top + 1);
     uint32_t prefix = 0u;  // digits found so far, as a number
     int remaining = rk;
-    int sh = top - 7;      // d >> sh (or d << -sh) puts the current digit in bits 0..7
+    int sh = top - (kDigit - 1);  // d >> sh (or d << -sh) puts the current digit in bits 0..10
     int* hist = S.sel.hist;
-    for (int pass = 0;; ++pass, sh -= 8) {
-        hist[threadIdx.x] = 0;
+    for (int pass = 0;; ++pass, sh -= kDigit) {
+#pragma unroll
+        for (int b = 0; b < kOwn; ++b) hist[(int)threadIdx.x + 256 * b] = 0;
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             if (i * 256 >= n) break;  // uniform
             const int j = (int)threadIdx.x + i * 256;
             const uint32_t d = key[i] - common;
-            const bool in = j < n && (pass == 0 || (d >> (sh + 8)) == prefix);
-            const uint32_t digit = (sh >= 0 ? d >> sh : d << -sh) & 255u;
+            const bool in = j < n && (pass == 0 || (d >> (sh + kDigit)) == prefix);
+            const uint32_t digit = (sh >= 0 ? d >> sh : d << -sh) & (uint32_t)(kDigitBins - 1);
             if (in) atomicAdd(&hist[digit], 1);
         }
         __syncthreads();
-        // Thread t owns bin 255 - t, so the scan counts keys from the largest bin down.
-        const int c = hist[255 - threadIdx.x];
+        // Thread t owns bins kDigitBins-1-kOwn*t down to kDigitBins-kOwn*(t+1), so the scan
+        // counts keys from the largest bin down.
+        const int hi_bin = kDigitBins - 1 - kOwn * (int)threadIdx.x;
+        int c = 0;
+#pragma unroll
+        for (int b = 0; b < kOwn; ++b) c += hist[hi_bin - b];
         const int incl = block_incl_scan(c, S);
         if (incl - c < remaining && remaining <= incl) {
-            S.sh[0] = 255 - (int)threadIdx.x;
-            S.sh[1] = incl - c;
+            int acc = incl - c;
+            for (int b = 0; b < kOwn; ++b) {
+                const int h = hist[hi_bin - b];
+                if (acc + h >= remaining) {
+                    S.sh[0] = hi_bin - b;
+                    S.sh[1] = acc;
+                    break;
+                }
+                acc += h;
+            }
         }
         __syncthreads();
-        prefix = (prefix << 8) | (uint32_t)S.sh[0];
+        prefix = (prefix << kDigit) | (uint32_t)S.sh[0];
         remaining -= S.sh[1];
         __syncthreads();
-        if (sh <= 0 || pass == 2) break;  // every bit of d is decided, or 24 of them are
+        if (sh <= 0 || pass == 1) break;  // every bit of d is decided, or 22 of them are
     }
     const uint32_t floor_d = sh >= 0 ? prefix << sh : prefix >> -sh;
     return order_key_value(common + floor_d);
