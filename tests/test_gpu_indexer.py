@@ -105,6 +105,18 @@ def test_c4_sampled_rows(dsa_gpu, oracle_mod):
 
 # ------------------------------------------------------------------ edge cases
 
+def test_full_candidate_lists(dsa_gpu, oracle_mod):
+    """1,024 rows in 128 groups (two key halves, key-ordered candidate segments).  With
+    N = 8,184 = capacity - 8 no group samples a threshold: every row keeps all of its 7,161 to
+    8,184 causal keys, so select compacts lists filled almost to its 8,192 positions."""
+    wl = di.Workload("full", 8184, 1024, 2048, 16, 17, "gauss", q_pos0=8184 - 1024)
+    q, k, w = di.make_indexer_inputs(wl)
+    got = run_gpu(dsa_gpu, q, k, w, wl.pos0, wl.top_k)
+    rows = np.array([0, 1, 7, 8, 511, 512, 1016, 1022, 1023], dtype=np.int64)
+    check_rows(oracle_mod, got, q, k, w, wl.pos0, wl.top_k, rows=rows, what="full candidate lists")
+    assert (np.diff(got, axis=1) > 0).all()
+
+
 @pytest.mark.parametrize("case", [
     dict(N=300, L=300, top_k=64, q_pos0=0, kind="gauss"),      # early rows have < k keys (-1 tail)
     dict(N=9000, L=37, top_k=2048, q_pos0=8963, kind="gauss"),  # ragged group, just above capacity
