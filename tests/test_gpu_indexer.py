@@ -105,6 +105,18 @@ def test_c4_sampled_rows(dsa_gpu, oracle_mod):
 
 # ------------------------------------------------------------------ edge cases
 
+def test_max_topk_key_ordered(dsa_gpu, oracle_mod):
+    """top_k = 4,096 over 1,024 rows (128 groups, key-ordered segments): the candidate
+    capacity is 16,384, so select runs 1,024 threads (16 waves) through its ordered
+    compaction."""
+    wl = di.Workload("maxk", 20000, 1024, 4096, 16, 19, "gauss")
+    q, k, w = di.make_indexer_inputs(wl)
+    got = run_gpu(dsa_gpu, q, k, w, wl.pos0, wl.top_k)
+    rows = np.array([0, 5, 8, 300, 512, 777, 1023], dtype=np.int64)
+    check_rows(oracle_mod, got, q, k, w, wl.pos0, wl.top_k, rows=rows, what="top_k 4096, 1024 rows")
+    assert (np.diff(got, axis=1) > 0).all()
+
+
 def test_full_candidate_lists(dsa_gpu, oracle_mod):
     """1,024 rows in 128 groups (two key halves, key-ordered candidate segments).  With
     N = 8,184 = capacity - 8 no group samples a threshold: every row keeps all of its 7,161 to
