@@ -136,11 +136,7 @@ def cpu_baseline(wl, inp, target_s: float):
     import oracle
 
     oracle.build(force=False)
-    try:
-        threads = len(os.sched_getaffinity(0))
-    except AttributeError:
-        threads = os.cpu_count() or 1
-    threads = max(1, min(16, threads))
+    threads = oracle.default_threads()  # affinity CPUs, capped by OMP_NUM_THREADS (the host share of one GPU)
 
     def run(rows, n_threads):
         t0 = time.perf_counter()
@@ -161,7 +157,44 @@ def cpu_baseline(wl, inp, target_s: float):
         "cores": threads,
         "kind": "oracle",
         "sample": f"{len(rows)} of {wl.L} query rows evenly spaced over the chunk (full causal key "
-                  f"range each), fp64 C oracle: full-sort top-k + sparse attention; {secs:.1f} s wall",
+                  f"range each), fp64 C oracle: full-sort top-k + sparse attention; {secs:.1f} s wall. "
+                  f"Rows are independent, so tokens/s = rows / wall time extrapolates linearly to the "
+                  f"whole chunk (about {wl.L / len(rows) * secs:.0f} s)",
+        "host": host_description(threads),
+    }
+
+
+def host_description(threads: int) -> dict:
+    """CPU model and counts of the host the oracle ran on."""
+    model = ""
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": affinity,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "threads_used": threads,
+            "why": "threads = CPUs in this process's affinity, capped by OMP_NUM_THREADS (the host CPU "
+                   "share given to one GPU's job)"}
+
+
+def selection_summary(st: dict, wl) -> dict:
+    """Per-row selection figures of the last indexer call (dsa_indexer_topk_stats)."""
+    rows = max(st["rows"], 1)
+    return {
+        "rows": st["rows"], "rows_all_keys": st["rows_all_keys"],
+        "candidates_per_row": round(st["candidates"] / rows, 1), "candidates_max": st["candidates_max"],
+        "candidates_per_top_k": round(st["candidates"] / rows / wl.top_k, 3),
+        "band_per_row": round(st["band"] / rows, 1), "band_max": st["band_max"],
+        "rows_fallback": st["rows_fallback"], "fallback_overflow": st["fallback_overflow"],
+        "fallback_incomplete": st["fallback_incomplete"], "fallback_band": st["fallback_band"],
+        "rows_failed": st["rows_failed"], "kth_radix": st["kth_radix"],
     }
 
 
@@ -270,12 +303,19 @@ def main():
         for k in dsa.PROFILE_KERNELS:
             dsa.profile_read(k)
     torch.cuda.synchronize()  # barrier: one rank
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         step()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1000.0 / args.steps
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    ms_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
+        step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
+    selection = selection_summary(dsa.indexer_stats(ws), wl)
     kernels = {}
     if timing:
         for k in roof_kernels:
@@ -313,6 +353,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(ms_median, 4),
+        "ms_per_step_min_max": [round(step_ms[0], 4), round(step_ms[-1], 4)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -326,6 +368,7 @@ def main():
             "parallelism": "single GPU",
         },
         "step_roofline_frac": round(t_roof_ms / ms_per_step, 4),
+        "selection": selection,
     }
     if kernels:
         per = {}

@@ -29,10 +29,12 @@ D_LATENT = 512
 D_ROPE = 64
 DEFAULT_Q_BLOCK = 1024
 MAX_BATCH = 65536
+MAX_SCORE_ROWS = 64
 
 EXPORTED = ["dsa_indexer_topk_workspace_bytes", "dsa_indexer_topk", "dsa_causal_mask_topk",
             "dsa_sparse_prefill", "dsa_sparse_prefill_packed", "dsa_sparse_decode_workspace_bytes",
             "dsa_sparse_decode",
+            "dsa_indexer_topk_stats", "dsa_indexer_scores_workspace_bytes", "dsa_indexer_scores",
             "dsa_indexer_topk_varlen_workspace_bytes", "dsa_indexer_topk_varlen",
             "dsa_sparse_prefill_varlen_workspace_bytes", "dsa_sparse_prefill_varlen",
             "dsa_retrieval_topk_workspace_bytes", "dsa_retrieval_topk",
@@ -43,6 +45,13 @@ PROFILE_KERNELS = ["key_stats", "score_sample", "row_prep", "score_filter", "sel
                    "retr_filter", "retr_gather"]
 
 _lib = None
+
+
+class IndexerStats(ctypes.Structure):
+    """dsa_indexer_stats_t: selection counters of the last indexer call on a workspace."""
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "rows", "rows_all_keys", "rows_fallback", "fallback_overflow", "fallback_incomplete",
+        "fallback_band", "rows_failed", "candidates", "candidates_max", "band", "band_max", "kth_radix")]
 
 
 class DSAError(RuntimeError):
@@ -65,6 +74,12 @@ def load_library(path: str | None = None):
     lib.dsa_indexer_topk_workspace_bytes.argtypes = [i64, i64, i32, i32]
     lib.dsa_indexer_topk.restype = ctypes.c_int
     lib.dsa_indexer_topk.argtypes = [P, P, P, i64, i64, i32, i32, i64, i32, i32, P, P, sz, P]
+    lib.dsa_indexer_topk_stats.restype = ctypes.c_int
+    lib.dsa_indexer_topk_stats.argtypes = [P, P, P]
+    lib.dsa_indexer_scores_workspace_bytes.restype = sz
+    lib.dsa_indexer_scores_workspace_bytes.argtypes = [i64, i64]
+    lib.dsa_indexer_scores.restype = ctypes.c_int
+    lib.dsa_indexer_scores.argtypes = [P, P, P, i64, i64, i32, i32, i64, P, P, P, sz, P]
     lib.dsa_causal_mask_topk.restype = ctypes.c_int
     lib.dsa_causal_mask_topk.argtypes = [P, i64, i32, i64, P]
     lib.dsa_sparse_prefill.restype = ctypes.c_int
@@ -193,6 +208,38 @@ def indexer_topk(q_idx, k_idx, w, q_pos0: int, top_k: int, q_block: int = DEFAUL
                                 q_pos0, top_k, q_block, out.data_ptr(), workspace.data_ptr(),
                                 workspace.numel() * workspace.element_size(), _stream_ptr(q_idx, stream)))
     return out
+
+
+def indexer_stats(workspace, stream=None) -> dict:
+    """Selection counters of the last indexer / retrieval call made with `workspace` (a
+    uint8 device tensor).  Waits for the stream."""
+    lib = load_library()
+    st = IndexerStats()
+    _check(lib.dsa_indexer_topk_stats(workspace.data_ptr(), ctypes.byref(st), _stream_ptr(workspace, stream)))
+    return {name: int(getattr(st, name)) for name, _ in IndexerStats._fields_}
+
+
+def indexer_scores(q_idx, k_idx, w, q_pos0: int, stream=None):
+    """Diagnostic: the fp32 scores the indexer's scoring kernel computes for every causal key of
+    up to 64 query rows, and the rows' error bounds delta.  -> (fp32 [L, N] with NaN after each
+    row's position, fp32 [L])."""
+    import torch
+
+    lib = load_library()
+    _req(q_idx, "q_idx", torch.bfloat16, 3)
+    _req(k_idx, "k_idx", torch.bfloat16, 2)
+    _req(w, "w", torch.float32, 2)
+    L, nh, hd = q_idx.shape
+    N = k_idx.shape[0]
+    dev = q_idx.device
+    scores = torch.empty((L, N), dtype=torch.float32, device=dev)
+    delta = torch.empty((L,), dtype=torch.float32, device=dev)
+    need = int(lib.dsa_indexer_scores_workspace_bytes(L, N))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib.dsa_indexer_scores(q_idx.data_ptr(), k_idx.data_ptr(), w.data_ptr(), L, N, nh, hd, q_pos0,
+                                  scores.data_ptr(), delta.data_ptr(), ws.data_ptr(), ws.numel(),
+                                  _stream_ptr(q_idx, stream)))
+    return scores, delta
 
 
 def causal_mask_topk(idx, q_pos0: int, stream=None):

@@ -317,6 +317,7 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
     a.sample_stride = lay.sample_stride;
     a.fold_cap = lay.fold_cap;
     a.force_fallback = debug_force_fallback() ? 1 : 0;
+    a.diag = reinterpret_cast<unsigned long long*>(ws + lay.off_diag);
     a.kstats = reinterpret_cast<dsa::KeyStats*>(ws + lay.off_kstats);
     a.qstat = reinterpret_cast<dsa::QHeadStat*>(ws + lay.off_qstat);
     a.tau = reinterpret_cast<float*>(ws + lay.off_tau);
@@ -340,7 +341,7 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
     a.k_tile = k_tile;
     a.n_ktiles = (n_keys + dsa::kKeyTileKeys - 1) / dsa::kKeyTileKeys;
     a.n_kstats = dsa::key_stats_blocks(n_keys);
-    hipError_t e = dsa::launch_key_stats(k_idx, n_keys, a.kstats, k_tile, s);
+    hipError_t e = dsa::launch_key_stats(k_idx, n_keys, a.kstats, k_tile, a.diag, s);
     if (e != hipSuccess) return hip_fail(e, "key statistics launch");
 
     for (int64_t b0 = 0; b0 < L; b0 += qb) {
@@ -357,6 +358,119 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
         e = dsa::launch_indexer_block(a, need_sample, s, Lb <= dsa::kRowsPerGroup / 2);
         if (e != hipSuccess) return hip_fail(e, "indexer launch");
     }
+    return DSA_OK;
+}
+
+dsa_status_t dsa_indexer_topk_stats(const void* workspace, dsa_indexer_stats_t* out, dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    if (!workspace || !out) return fail(DSA_ERR_INVALID_ARG, "null workspace or output");
+    if (!aligned(workspace, 256)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    static_assert(dsa::kDiagSlots * sizeof(unsigned long long) <= dsa::kDiagBytes, "counter block");
+    unsigned long long c[dsa::kDiagSlots];
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(c, workspace, sizeof c, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "reading the selection counters");
+    out->rows = (int64_t)c[dsa::kDiagRows];
+    out->rows_all_keys = (int64_t)c[dsa::kDiagRowsAll];
+    out->rows_fallback = (int64_t)c[dsa::kDiagFallback];
+    out->fallback_overflow = (int64_t)c[dsa::kDiagFbOverflow];
+    out->fallback_incomplete = (int64_t)c[dsa::kDiagFbIncomplete];
+    out->fallback_band = (int64_t)c[dsa::kDiagFbBand];
+    out->rows_failed = (int64_t)c[dsa::kDiagFailed];
+    out->candidates = (int64_t)c[dsa::kDiagCandSum];
+    out->candidates_max = (int64_t)c[dsa::kDiagCandMax];
+    out->band = (int64_t)c[dsa::kDiagBandSum];
+    out->band_max = (int64_t)c[dsa::kDiagBandMax];
+    out->kth_radix = (int64_t)c[dsa::kDiagRadix];
+    return DSA_OK;
+}
+
+// Workspace of dsa_indexer_scores: the indexer sections it uses, with a candidate capacity
+// that holds every key of a row (each of the 8 segments one extra tile wide).
+struct ScoreDumpLayout {
+    int rows, cap;
+    size_t off_diag, off_kstats, off_tau, off_delta, off_mode, off_count, off_fbctrl, off_fblist, off_qstat,
+        off_cand, off_ktile, total;
+    static ScoreDumpLayout make(int64_t L, int64_t N) {
+        ScoreDumpLayout l{};
+        auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+        l.rows = (int)round8(L);
+        const int64_t n_tiles = (N + dsa::kKeyTileKeys - 1) / dsa::kKeyTileKeys;
+        const int64_t tps = (n_tiles + dsa::kCandSegs - 1) / dsa::kCandSegs;
+        l.cap = (int)(dsa::kCandSegs * (tps + 1) * dsa::kKeyTileKeys);
+        size_t o = 0;
+        l.off_diag = o; o = al(o + dsa::kDiagBytes);
+        l.off_kstats = o; o = al(o + sizeof(dsa::KeyStats) * dsa::kStatSlots);
+        l.off_tau = o; o = al(o + 4 * (size_t)l.rows);
+        l.off_delta = o; o = al(o + 4 * (size_t)l.rows);
+        l.off_mode = o; o = al(o + 4 * (size_t)l.rows);
+        l.off_count = o; o = al(o + 4 * (size_t)l.rows * dsa::kCandSegs);
+        l.off_fbctrl = o; o = al(o + 16);
+        l.off_fblist = o; o = al(o + 4 * (size_t)l.rows);
+        l.off_qstat = o; o = al(o + sizeof(dsa::QHeadStat) * 32 * (size_t)l.rows);
+        l.off_cand = o; o = al(o + 8 * (size_t)l.rows * (size_t)l.cap);
+        l.off_ktile = o; o = al(o + dsa::key_tile_bytes(N));
+        l.total = o;
+        return l;
+    }
+};
+
+size_t dsa_indexer_scores_workspace_bytes(int64_t L, int64_t N) {
+    if (L < 1 || L > DSA_MAX_SCORE_ROWS || N <= 0 || N > (int64_t)INT32_MAX / 2) return 0;
+    return ScoreDumpLayout::make(L, N).total;
+}
+
+dsa_status_t dsa_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, const float* w, int64_t L, int64_t N,
+                                int32_t n_heads, int32_t head_dim, int64_t q_pos0, float* scores, float* delta,
+                                void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    dsa_status_t st = check_indexer_args(q_idx, k_idx, w, L, N, n_heads, head_dim, q_pos0, 1, 0, (const int32_t*)scores);
+    if (st != DSA_OK) return st;
+    if (L > DSA_MAX_SCORE_ROWS)
+        return fail(DSA_ERR_INVALID_ARG, "at most %d rows per call (got %lld)", DSA_MAX_SCORE_ROWS, (long long)L);
+    if (N > (int64_t)INT32_MAX / 2) return fail(DSA_ERR_UNSUPPORTED, "N above 2^30-1 is not supported here");
+    if (L == 0) return DSA_OK;
+    if (q_pos0 < 1) return fail(DSA_ERR_INVALID_ARG, "q_pos0 must be >= 1 (a row at position 0 has one key)");
+    if (delta && !aligned(delta, 4)) return fail(DSA_ERR_INVALID_ARG, "delta must be 4-byte aligned");
+    const ScoreDumpLayout lay = ScoreDumpLayout::make(L, N);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", lay.total, workspace_bytes,
+                    workspace ? "" : ", null");
+    if (!aligned(workspace, 256)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    dsa::IndexerArgs a{};
+    a.q_idx = q_idx;
+    a.k_idx = k_idx;
+    a.w = w;
+    a.N = N;
+    a.pos0 = q_pos0;
+    a.Lb = (int)L;
+    a.top_k = 1;  // no row keeps all its keys but the one at position 0 (excluded above)
+    a.cap = lay.cap;
+    a.sample_stride = 0;
+    a.parts = 2;
+    a.diag = reinterpret_cast<unsigned long long*>(ws + lay.off_diag);
+    a.kstats = reinterpret_cast<dsa::KeyStats*>(ws + lay.off_kstats);
+    a.qstat = reinterpret_cast<dsa::QHeadStat*>(ws + lay.off_qstat);
+    a.tau = reinterpret_cast<float*>(ws + lay.off_tau);
+    a.delta = reinterpret_cast<float*>(ws + lay.off_delta);
+    a.mode = reinterpret_cast<int*>(ws + lay.off_mode);
+    a.count = reinterpret_cast<int*>(ws + lay.off_count);
+    a.fb_ctrl = reinterpret_cast<int*>(ws + lay.off_fbctrl);
+    a.fb_list = reinterpret_cast<int*>(ws + lay.off_fblist);
+    a.cand = reinterpret_cast<uint2*>(ws + lay.off_cand);
+    const int64_t last = q_pos0 + L - 1;
+    const int64_t n_keys = (last < N - 1 ? last : N - 1) + 1;
+    uint16_t* k_tile = reinterpret_cast<uint16_t*>(ws + lay.off_ktile);
+    a.k_tile = k_tile;
+    a.n_ktiles = (n_keys + dsa::kKeyTileKeys - 1) / dsa::kKeyTileKeys;
+    a.n_kstats = dsa::key_stats_blocks(n_keys);
+    hipError_t e = dsa::launch_key_stats(k_idx, n_keys, a.kstats, k_tile, a.diag, s);
+    if (e == hipSuccess) e = dsa::launch_score_dump(a, scores, N, delta, s);
+    if (e != hipSuccess) return hip_fail(e, "score dump launch");
     return DSA_OK;
 }
 
@@ -571,6 +685,7 @@ dsa_status_t dsa_indexer_topk_varlen(const uint16_t* q_idx, const uint16_t* k_id
     a.sample_stride = lay.sample_stride;
     a.fold_cap = lay.fold_cap;
     a.force_fallback = debug_force_fallback() ? 1 : 0;
+    a.diag = reinterpret_cast<unsigned long long*>(ws + lay.off_diag);
     a.kstats = reinterpret_cast<dsa::KeyStats*>(ws + lay.off_kstats);
     a.qstat = reinterpret_cast<dsa::QHeadStat*>(ws + lay.off_qstat);
     a.tau = reinterpret_cast<float*>(ws + lay.off_tau);
@@ -596,7 +711,7 @@ dsa_status_t dsa_indexer_topk_varlen(const uint16_t* q_idx, const uint16_t* k_id
     hipError_t e = write_batch_tables(B, cu_q, cu_k, pos0, rows, seqs, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "batch table launch");
     a.n_kstats = dsa::key_stats_blocks(bt.tiles * dsa::kKeyTileKeys);
-    e = dsa::launch_key_stats_batch(k_idx, seqs, (int)B, bt.tiles, a.kstats, k_tile, s);
+    e = dsa::launch_key_stats_batch(k_idx, seqs, (int)B, bt.tiles, a.kstats, k_tile, a.diag, s);
     if (e != hipSuccess) return hip_fail(e, "key statistics launch");
 
     // Blocks of the padded row space; sequence sq is the first one a block may hold.
@@ -788,6 +903,7 @@ dsa_status_t dsa_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M,
     a.fold_cap = lay.fold_cap;
     a.force_fallback = debug_force_fallback() ? 1 : 0;
     a.parts = 4;  // one appended candidate list per row
+    a.diag = reinterpret_cast<unsigned long long*>(ws + lay.off_diag);
     a.kstats = reinterpret_cast<dsa::KeyStats*>(ws + lay.off_kstats);
     a.qstat = reinterpret_cast<dsa::QHeadStat*>(ws + lay.off_qstat);
     a.tau = reinterpret_cast<float*>(ws + lay.off_tau);
@@ -805,7 +921,7 @@ dsa_status_t dsa_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M,
     a.fold_bf = reinterpret_cast<float*>(ws + lay.off_fold_bf);
     a.rows = reinterpret_cast<const dsa::RowInfo*>(ws + lay.off_rowinfo);
     a.n_kstats = dsa::key_stats_blocks(N);
-    hipError_t e = dsa::launch_key_stats(x, N, a.kstats, nullptr, s);  // statistics only
+    hipError_t e = dsa::launch_key_stats(x, N, a.kstats, nullptr, a.diag, s);  // statistics only
     if (e != hipSuccess) return hip_fail(e, "key statistics launch");
 
     dsa::RetrievalArgs r{};

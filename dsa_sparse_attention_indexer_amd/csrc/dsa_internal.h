@@ -97,9 +97,29 @@ struct QHeadStat {
     int pad;
 };
 
+// Selection counters of one indexer call, the first bytes of its workspace.  The call's
+// first kernel (key statistics) clears them; select and the fold add to them with device
+// atomics; dsa_indexer_topk_stats copies them out.
+enum DiagSlot : int {
+    kDiagRows = 0,      // rows finished by the candidate path
+    kDiagRowsAll,       // rows with at most top_k causal keys (no selection)
+    kDiagFallback,      // rows handed to the blocked fold ...
+    kDiagFbOverflow,    // ... because a candidate segment overflowed (or the fold was forced)
+    kDiagFbIncomplete,  // ... because the candidates were not provably a superset of the top-k
+    kDiagFbBand,        // ... because the band outgrew select's buffer
+    kDiagFailed,        // rows no path could finish (emitted as -1; never expected)
+    kDiagCandSum,       // candidates, summed over the candidate-path rows
+    kDiagCandMax,       // most candidates of one such row
+    kDiagBandSum,       // keys re-scored in fp64, summed over those rows
+    kDiagBandMax,       // most re-scored keys of one row
+    kDiagRadix,         // rows whose k-th search needed the radix select
+    kDiagSlots = 16
+};
+constexpr size_t kDiagBytes = 256;
+
 struct IndexerLayout {
     int rows, cap, sample_stride, fold_cap;
-    size_t off_kstats, off_tau, off_delta, off_mode, off_count, off_fbctrl, off_fblist;
+    size_t off_diag, off_kstats, off_tau, off_delta, off_mode, off_count, off_fbctrl, off_fblist;
     size_t off_sample, off_cand, off_ktile, off_qstat;
     size_t off_fold_s, off_fold_i, off_fold_bi, off_fold_bs, off_fold_bf;
     size_t total;
@@ -117,6 +137,7 @@ struct IndexerLayout {
         l.sample_stride = (sample_size(N, top_k, l.cap) + 3) & ~3;  // rows 16-byte aligned
         l.fold_cap = top_k + kFoldKeys;
         size_t o = 0;
+        l.off_diag = o; o = al(o + kDiagBytes);
         l.off_kstats = o; o = al(o + sizeof(KeyStats) * kStatSlots);
         l.off_tau = o; o = al(o + 4 * (size_t)l.rows);
         l.off_delta = o; o = al(o + 4 * (size_t)l.rows);
@@ -204,6 +225,7 @@ struct IndexerArgs {
     // groups): every wave of every part appends to the row's single list through an atomic
     // counter (count[r][0]), and the selection sorts its output.
     int parts;
+    unsigned long long* diag;  // [kDiagSlots] selection counters of the call
     KeyStats* kstats;       // [n_kstats] partial key statistics, one per key-statistics block
     QHeadStat* qstat;       // [Lb][32] per-head q statistics (row prep)
     int n_kstats;
@@ -240,10 +262,12 @@ struct ProfScope {
 
 // Kernel launchers (indexer.hip).  Each returns the launch status.
 // k_tile may be null: statistics only.
-hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, uint16_t* k_tile, hipStream_t s);
+// It also clears the call's selection counters (diag).
+hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, uint16_t* k_tile,
+                            unsigned long long* diag, hipStream_t s);
 // The same over a batch: seqs[0 .. n_seqs) (device), n_tiles tiles in all.
 hipError_t launch_key_stats_batch(const uint16_t* k_idx, const SeqKeys* seqs, int n_seqs, int64_t n_tiles,
-                                  KeyStats* ks, uint16_t* k_tile, hipStream_t s);
+                                  KeyStats* ks, uint16_t* k_tile, unsigned long long* diag, hipStream_t s);
 // sparse_rows: most row groups hold few query rows (decode, short chunks, batches of single
 // queries): the scoring skips the MFMAs of row pairs without a live row.
 hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s, bool sparse_rows = false);
@@ -284,6 +308,12 @@ int retrieval_seg_cap(int parts, int64_t n_tiles, int top_k, bool keep_all);
 hipError_t launch_retrieval_block(RetrievalArgs r, const IndexerArgs& a, bool need_sample, int n_table_rows,
                                   hipStream_t s);
 hipError_t launch_causal_mask(int32_t* idx, int64_t L, int top_k, int64_t q_pos0, hipStream_t s);
+// Diagnostic: row_prep and the production filter kernel (two key halves, parts = 2) with every
+// row's threshold at -inf, then each row's stored (score, key) entries scattered into
+// scores[row][key] (NaN elsewhere) and the rows' error bounds into delta_out.  The caller
+// sets a.top_k = 1 and a.cap large enough that no row samples and every segment holds its
+// keys.
+hipError_t launch_score_dump(const IndexerArgs& a, float* scores, int64_t n_cols, float* delta_out, hipStream_t s);
 
 struct AttentionArgs {
     const uint16_t* q;    // [Lb][H][576]

@@ -146,7 +146,9 @@ __global__ __launch_bounds__(kStatsThreads) void key_stats_kernel(const uint16_t
                                                                   int64_t n_keys, const SeqKeys* seqs,
                                                                   int n_seqs, int64_t n_tiles,
                                                                   KeyStats* slots,
-                                                                  uint16_t* __restrict__ k_tile) {
+                                                                  uint16_t* __restrict__ k_tile,
+                                                                  unsigned long long* diag) {
+    if (blockIdx.x == 0 && threadIdx.x < kDiagSlots) diag[threadIdx.x] = 0ull;
     __shared__ u16x8 s_t[kStatsThreads / kWave][kKeyTileKeys * kStatsRowPad];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     u16x8* st = s_t[wave];
@@ -714,12 +716,72 @@ struct RegSrc {
     }
 };
 
-// k-th largest value (1-based) under the float order (-0 == +0), by value-linear binning
-// (LiteTopK's bins: cheap even when every score shares an exponent) refined up to three
-// times, then a rank count over the crossing bin.  Requires 1 <= k <= total.  Returns
-// false (uniformly) if a bin still holds more than kDirect distinct values after that.
+// Histogram hist[0..nbins) is complete; `above` values lie above every bin.  Finds, from
+// the top bin down, the bin b holding the k-th largest value (1 <= k <= above + total) and
+// leaves b in S.sh[0] (-1 if none), the values above b (including `above`) in S.sh[1] and
+// hist[b] in S.sh[2].  Thread t sums bins nbins-1-t*per down to nbins-(t+1)*per with
+// per = ceil(nbins / blockDim), so every bin is counted whatever the block size.
+__device__ __forceinline__ void block_find_crossing(const int* hist, int nbins, int k, int above, SelectScratch& S) {
+    const int per = (nbins + (int)blockDim.x - 1) / (int)blockDim.x;
+    const int top = nbins - 1 - (int)threadIdx.x * per;
+    int c = 0;
+    for (int j = 0; j < per; ++j)
+        if (top - j >= 0) c += hist[top - j];
+    const int incl = block_incl_scan(c, S) + above;
+    const int excl = incl - c;
+    if (threadIdx.x == 0) S.sh[0] = -1;
+    __syncthreads();
+    if (excl < k && k <= incl) {
+        int acc = excl;
+        for (int j = 0; j < per && top - j >= 0; ++j) {
+            const int b = top - j;
+            if (acc + hist[b] >= k) {
+                S.sh[0] = b;
+                S.sh[1] = acc;
+                S.sh[2] = hist[b];
+                break;
+            }
+            acc += hist[b];
+        }
+    }
+    __syncthreads();
+}
+
+// k-th largest value (1-based, 1 <= k <= total) under the float order (-0 == +0) by an
+// exact radix select over the order-preserving keys: three passes of 11, 11 and 10 bits
+// from the top, each over the values whose higher bits match the digits found so far.
+// Cannot fail; the selection's last resort when value binning does not converge.
 template <class Src>
-__device__ bool block_kth_binned(const Src& src, int k, float* out, SelectScratch& S) {
+__device__ float block_kth_radix(const Src& src, int k, SelectScratch& S) {
+    uint32_t prefix = 0u;  // the digits found so far
+    int remaining = k;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int hi = 32 - 11 * pass;             // this pass decides bits [lo, hi)
+        const int lo = hi > 11 ? hi - 11 : 0;
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+        for (int i = threadIdx.x; i < kBins; i += blockDim.x) S.sel.hist[i] = 0;
+        __syncthreads();
+        src.for_each([&](float v) {
+            const uint32_t key = float_order_key(v);
+            if (pass == 0 || (key >> hi) == prefix) atomicAdd(&S.sel.hist[(key >> lo) & dmask], 1);
+        });
+        __syncthreads();
+        block_find_crossing(S.sel.hist, (int)dmask + 1, remaining, 0, S);
+        const int b = S.sh[0];
+        remaining -= S.sh[1];
+        __syncthreads();
+        prefix = (prefix << (hi - lo)) | (uint32_t)b;
+    }
+    return order_key_float(prefix);
+}
+
+// k-th largest value (1-based, 1 <= k <= total) under the float order (-0 == +0), by
+// value-linear binning (LiteTopK's bins: cheap even when every score shares an exponent)
+// refined up to three times, then a rank count over the crossing bin.  When a bin still
+// holds more than kDirect values after three levels (scores spread over many scales), the
+// exact radix select above finishes the search.  Sets *used_radix when it did.
+template <class Src>
+__device__ float block_kth_binned(const Src& src, int k, SelectScratch& S, bool* used_radix = nullptr) {
     constexpr int kLevels = 3;
     float vmin = INFINITY, vmax = -INFINITY;
     src.for_each([&](float v) {
@@ -739,10 +801,7 @@ __device__ bool block_kth_binned(const Src& src, int k, float* out, SelectScratc
         return in;
     };
     for (;;) {
-        if (vmin == vmax) {
-            *out = vmin;
-            return true;
-        }
+        if (vmin == vmax) return vmin;
         const double scale = (double)kBins / ((double)vmax - (double)vmin);
         for (int i = threadIdx.x; i < kBins; i += blockDim.x) S.sel.hist[i] = 0;
         __syncthreads();
@@ -750,33 +809,15 @@ __device__ bool block_kth_binned(const Src& src, int k, float* out, SelectScratc
             if (active(v)) atomicAdd(&S.sel.hist[bin_of(v, vmin, scale)], 1);
         });
         __syncthreads();
-        // Descending bin order: thread t owns bins kBins-1-t*per down to kBins-per-t*per.
-        const int per = kBins / blockDim.x;
-        int c = 0;
-        for (int j = 0; j < per; ++j) c += S.sel.hist[kBins - 1 - threadIdx.x * per - j];
-        const int incl = block_incl_scan(c, S) + above;
-        const int excl = incl - c;
-        if (threadIdx.x == 0) S.sh[0] = -1;
-        __syncthreads();
-        if (excl < k && k <= incl) {
-            int acc = excl;
-            for (int j = 0; j < per; ++j) {
-                const int b = kBins - 1 - threadIdx.x * per - j;
-                if (acc + S.sel.hist[b] >= k) {
-                    S.sh[0] = b;
-                    S.sh[1] = acc;
-                    S.sh[2] = S.sel.hist[b];
-                    break;
-                }
-                acc += S.sel.hist[b];
-            }
-        }
-        __syncthreads();
+        block_find_crossing(S.sel.hist, kBins, k, above, S);
         const int b = S.sh[0];
         above = S.sh[1];
         const int nb = S.sh[2];
         __syncthreads();
-        if (b < 0) return false;  // unreachable for 1 <= k <= total
+        if (b < 0 || (nb > kDirect && nlv + 1 == kLevels)) {  // (b < 0 only if k > total)
+            if (used_radix) *used_radix = true;
+            return block_kth_radix(src, k, S);
+        }
 #pragma unroll
         for (int l = 0; l < kLevels; ++l)
             if (l == nlv) {
@@ -806,11 +847,10 @@ __device__ bool block_kth_binned(const Src& src, int k, float* out, SelectScratc
                 if (gt < r && r <= ge) S.red_f[31] = vx;  // every writer holds the same value
             }
             __syncthreads();
-            *out = S.red_f[31];
+            const float kth = S.red_f[31];
             __syncthreads();
-            return true;
+            return kth;
         }
-        if (nlv == kLevels) return false;
         vmin = INFINITY;
         vmax = -INFINITY;
         src.for_each([&](float v) {
@@ -997,8 +1037,7 @@ __device__ bool select_core(const CandList& L, int k, float delta, const uint16_
                             const uint16_t* __restrict__ k_idx, int* band_i,
                             double* band_s, float* band_f, int band_cap, int* sel_i, float* sel_s,
                             SelectScratch& S) {
-    float kth;
-    if (!block_kth_binned(ListSrc{L}, k, &kth, S)) return false;
+    const float kth = block_kth_binned(ListSrc{L}, k, S);
     const double lo = (double)kth - 2.0 * (double)delta;
     const double hi = (double)kth + 2.0 * (double)delta;
     if (threadIdx.x == 0) {
@@ -1331,6 +1370,7 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
     int32_t* out_row = ref.out;
     if (mode == kModeAll) {
         for (int j = threadIdx.x; j < k; j += blockDim.x) out_row[j] = j < nt ? j : -1;
+        if (threadIdx.x == 0) atomicAdd(&P.diag[kDiagRowsAll], 1ull);
         return;
     }
     __shared__ SelectScratch S;
@@ -1351,6 +1391,7 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
         start[w] = total;
         total += cnt[w];
     }
+    int why = ok ? kDiagFbIncomplete : kDiagFbOverflow;  // the reason if the row falls back
     ok = ok && total >= k;
     const float tau_f = P.tau[r];
     const float delta = P.delta[r];
@@ -1380,10 +1421,12 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
         nv = total > tid ? min((total - tid + nthr - 1) / nthr, kSelChunk) : 0;
     }
     float kth = 0.f;
-    if (ok) ok = block_kth_binned(RegSrc<kSelChunk>{v, nv}, k, &kth, S);
+    bool radix = false;
+    if (ok) kth = block_kth_binned(RegSrc<kSelChunk>{v, nv}, k, S, &radix);
     const double lo = (double)kth - 2.0 * (double)delta;
     const double hi = (double)kth + 2.0 * (double)delta;
     if (ok && tau_f != -INFINITY && lo < (double)tau_f) ok = false;  // candidate set not provably complete
+    int nb_row = 0;
     if (ok) {
         if (threadIdx.x == 0) {
             S.sh[4] = 0;
@@ -1411,6 +1454,8 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
         const int nb = S.sh[5];
         __syncthreads();
         ok = nb <= kSelBand && n_in < k && n_in + nb >= k;
+        why = kDiagFbBand;
+        nb_row = nb;
         if (ok) {
             if (delta > 0.f && nb > 0)
                 band_rescore(nb, s_band_key, s_band_s, ref.q, ref.w, P.qstat + (size_t)r * kIdxHeads, ref.keys, S);
@@ -1494,6 +1539,16 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
     if (!ok && threadIdx.x == 0) {
         const int slot = atomicAdd(&P.fb_ctrl[0], 1);
         P.fb_list[slot] = r;
+        atomicAdd(&P.diag[kDiagFallback], 1ull);
+        atomicAdd(&P.diag[why], 1ull);
+    }
+    if (ok && threadIdx.x == 0) {
+        atomicAdd(&P.diag[kDiagRows], 1ull);
+        atomicAdd(&P.diag[kDiagCandSum], (unsigned long long)total);
+        atomicMax(&P.diag[kDiagCandMax], (unsigned long long)total);
+        atomicAdd(&P.diag[kDiagBandSum], (unsigned long long)nb_row);
+        atomicMax(&P.diag[kDiagBandMax], (unsigned long long)nb_row);
+        if (radix) atomicAdd(&P.diag[kDiagRadix], 1ull);
     }
 }
 
@@ -1576,7 +1631,8 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
         const float* w_row = ref.w;
         int cur = 0, n = 0;
         float lo = -INFINITY;
-        for (int64_t b0 = 0; b0 < nt; b0 += kFoldKeys) {
+        bool failed = false;
+        for (int64_t b0 = 0; b0 < nt && !failed; b0 += kFoldKeys) {
             const int64_t b1 = b0 + kFoldKeys < nt ? b0 + kFoldKeys : nt;
             if (threadIdx.x == 0) s_cnt = n;
             __syncthreads();
@@ -1592,11 +1648,16 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
                 L.i[0] = Ri[cur];
                 L.n[0] = n;
                 L.nseg = 1;
+                // The k-th search cannot fail and the band fits (its capacity is the list's), so
+                // select_core succeeds; should it not, the row is emitted as -1 and counted.
                 const bool ok = select_core(L, k, delta, q_row, w_row, P.qstat + (size_t)r * kIdxHeads, ref.keys,
                                             band_i, band_s, band_f,
                                             P.fold_cap, Ri[nxt], Rs[nxt], S);
-                (void)ok;  // band capacity == list capacity
                 __syncthreads();
+                if (!ok) {  // uniform over the block
+                    failed = true;
+                    break;
+                }
                 cur = nxt;
                 n = k;
                 CandList R{};
@@ -1604,8 +1665,7 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
                 R.i[0] = Ri[cur];
                 R.n[0] = n;
                 R.nseg = 1;
-                float kth = -INFINITY;
-                block_kth_binned(ListSrc{R}, k, &kth, S);
+                const float kth = block_kth_binned(ListSrc{R}, k, S);
                 const double l = (double)kth - 2.0 * (double)delta;
                 float lf = (float)l;
                 if ((double)lf > l) lf = nextafterf(lf, -INFINITY);
@@ -1613,6 +1673,12 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
             }
         }
         int32_t* out_row = ref.out;
+        if (failed) {
+            for (int j = threadIdx.x; j < k; j += blockDim.x) out_row[j] = -1;
+            if (threadIdx.x == 0) atomicAdd(&P.diag[kDiagFailed], 1ull);
+            __syncthreads();
+            continue;
+        }
         // n == k here (nt > k for every scored row): the list is the exact top-k.
         for (int j = threadIdx.x; j < k; j += blockDim.x) S.out[j] = j < n ? Ri[cur][j] : -1;
         __syncthreads();
@@ -1635,20 +1701,20 @@ __global__ void causal_mask_kernel(int32_t* idx, int64_t L, int top_k, int64_t q
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks, uint16_t* k_tile,
-                             hipStream_t s) {
+                             unsigned long long* diag, hipStream_t s) {
     ProfScope ps(s, kProfKeyStats);
     static_assert(kStatsThreads / kWave == 4 && kKeyTileKeys == 32, "key_stats_blocks assumes 4 waves of 32-key tiles");
     const int blocks = key_stats_blocks(n_keys);
     key_stats_kernel<<<blocks, kStatsThreads, 0, s>>>(k_idx, n_keys, nullptr, 0,
-                                                     (n_keys + kKeyTileKeys - 1) / kKeyTileKeys, ks, k_tile);
+                                                     (n_keys + kKeyTileKeys - 1) / kKeyTileKeys, ks, k_tile, diag);
     return hipGetLastError();
 }
 
 hipError_t launch_key_stats_batch(const uint16_t* k_idx, const SeqKeys* seqs, int n_seqs, int64_t n_tiles,
-                                  KeyStats* ks, uint16_t* k_tile, hipStream_t s) {
+                                  KeyStats* ks, uint16_t* k_tile, unsigned long long* diag, hipStream_t s) {
     ProfScope ps(s, kProfKeyStats);
     const int blocks = key_stats_blocks(n_tiles * kKeyTileKeys);
-    key_stats_kernel<<<blocks, kStatsThreads, 0, s>>>(k_idx, 0, seqs, n_seqs, n_tiles, ks, k_tile);
+    key_stats_kernel<<<blocks, kStatsThreads, 0, s>>>(k_idx, 0, seqs, n_seqs, n_tiles, ks, k_tile, diag);
     return hipGetLastError();
 }
 
@@ -1714,6 +1780,40 @@ hipError_t launch_select_fold(const IndexerArgs& a, hipStream_t s) {
         ProfScope ps(s, kProfFold);
         fold_kernel<<<kFallbackSlots, kSelectThreads, 0, s>>>(a);
     }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ score dump (diagnostic)
+
+// One workgroup per block row: the row of `scores` is set to NaN, then every (score, key)
+// entry the filter stored for the row (its kSegs segments of cap / kSegs entries) is written
+// to its key's column.  With tau = -inf the filter stores every causal key.
+__global__ __launch_bounds__(256) void score_dump_kernel(IndexerArgs P, float* scores, int64_t n_cols,
+                                                         float* delta_out) {
+    const int r = blockIdx.x;
+    float* row = scores + (size_t)r * n_cols;
+    for (int64_t c = threadIdx.x; c < n_cols; c += blockDim.x) row[c] = __uint_as_float(0x7fc00000u);
+    __syncthreads();
+    const int seg = P.cap / kSegs;
+    for (int w = 0; w < kSegs; ++w) {
+        const int n = min(P.count[(size_t)r * kSegs + w], seg);
+        const uint2* e = P.cand + (size_t)r * P.cap + (size_t)w * seg;
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+            const uint2 c = e[i];
+            if ((int64_t)c.y < n_cols) row[c.y] = __uint_as_float(c.x);
+        }
+    }
+    if (threadIdx.x == 0 && delta_out) delta_out[r] = P.delta[r];
+}
+
+hipError_t launch_score_dump(const IndexerArgs& a, float* scores, int64_t n_cols, float* delta_out, hipStream_t s) {
+    const int groups = (a.Lb + kRowsPerGroup - 1) / kRowsPerGroup;
+    hipError_t e = launch_row_prep(a, s);
+    if (e != hipSuccess) return e;
+    score_kernel<false, false><<<8 * ((groups + 3) / 4), kScoreThreads, 0, s>>>(a, groups);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    score_dump_kernel<<<a.Lb, 256, 0, s>>>(a, scores, n_cols, delta_out);
     return hipGetLastError();
 }
 

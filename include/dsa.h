@@ -99,6 +99,63 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
                               void* workspace, size_t workspace_bytes, dsa_stream_t stream);
 
 /*
+ * Selection counters of the last dsa_indexer_topk, dsa_indexer_topk_varlen or
+ * dsa_retrieval_topk call made with this workspace (diagnostics; no result
+ * depends on them).  They show how the LiteTopK abstract's threshold scheme
+ * behaved on the call's inputs: how many candidates each row wrote back above
+ * its sampled threshold, how many keys within the error bound of the k-th score
+ * were re-scored in fp64, and how many rows needed the GLM page's blocked
+ * 4,096-key fold (How it works) because their candidates could not be proven to
+ * hold the top-k.  Counts run over the whole call (every query block).
+ */
+typedef struct {
+    int64_t rows;                /* rows finished from their candidate lists            */
+    int64_t rows_all_keys;       /* rows with at most top_k causal keys (no selection)  */
+    int64_t rows_fallback;       /* rows finished by the blocked fold, because ...      */
+    int64_t fallback_overflow;   /*   a candidate segment overflowed                    */
+    int64_t fallback_incomplete; /*   the candidates could miss a top-k key             */
+    int64_t fallback_band;       /*   the fp64 band outgrew the selection buffer        */
+    int64_t rows_failed;         /* rows no path finished (written as -1): 0 expected   */
+    int64_t candidates;          /* candidates summed over `rows`                       */
+    int64_t candidates_max;      /* most candidates of one of those rows                */
+    int64_t band;                /* keys re-scored in fp64, summed over `rows`          */
+    int64_t band_max;            /* most keys re-scored for one row                     */
+    int64_t kth_radix;           /* rows whose k-th search needed the exact radix pass  */
+} dsa_indexer_stats_t;
+
+/*
+ * Copies the counters above out of `workspace` (the device workspace of the
+ * call) into *out.  Enqueued on `stream` after the call and waits for the
+ * stream: a host synchronisation, unlike the entry points.  workspace must be
+ * non-null and 256-byte aligned (else DSA_ERR_INVALID_ARG).
+ */
+dsa_status_t dsa_indexer_topk_stats(const void* workspace, dsa_indexer_stats_t* out, dsa_stream_t stream);
+
+/*
+ * The fp32 indexer scores that the selection starts from, for up to
+ * DSA_MAX_SCORE_ROWS query rows (a diagnostic: it lets a caller check the error
+ * bound that makes the selection exact, "GLM prefill now attends only to the
+ * keys its indexer picks", How it works: the sparse path picks the same keys as
+ * the stock indexer).  The production scoring kernel (bf16 matrix cores, ReLU,
+ * weighted head sum) runs with every row's threshold at -infinity, so it keeps
+ * every causal key, and the kept scores are scattered out:
+ *
+ *   scores fp32 [L][N]: row t holds score(t, s) for s <= q_pos0 + t, NaN after
+ *   delta  fp32 [L] or NULL: the bound delta_t on |fp32 score - fp64 score| the
+ *          selection uses for row t (0 when the row's fp32 scores are exact)
+ *
+ * Arguments as dsa_indexer_topk, with 1 <= q_pos0 and L <= DSA_MAX_SCORE_ROWS
+ * (else DSA_ERR_INVALID_ARG); workspace: at least
+ * dsa_indexer_scores_workspace_bytes(L, N) bytes, 256-byte aligned (it holds
+ * every key of every row as a candidate).  Not a hot-path call.
+ */
+#define DSA_MAX_SCORE_ROWS 64
+size_t dsa_indexer_scores_workspace_bytes(int64_t L, int64_t N);
+dsa_status_t dsa_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, const float* w, int64_t L,
+                                int64_t N, int32_t n_heads, int32_t head_dim, int64_t q_pos0, float* scores,
+                                float* delta, void* workspace, size_t workspace_bytes, dsa_stream_t stream);
+
+/*
  * Causal masking of an index tensor ("cuda : support for sparse KV indices in
  * MMA flash attention kernel", review thread: apply causality to the top-k
  * indices with a separate op, masked entries becoming -1, assuming key index =

@@ -9,6 +9,8 @@ Functions and the passages they follow (page titles as on the pages):
   topk(...)       -- "GLM prefill now attends only to the keys its indexer
                      picks", How it works: indexer top-k over 32 heads, full
                      argpartition or the blocked 4,096-key fold.
+  scores(...)     -- the same page: the canonical score of every causal key
+                     of a row (what the top-k ranks).
   causal_mask(...) -- "cuda : support for sparse KV indices in MMA flash
                      attention kernel", review: causality applied on the
                      top-k indices, masked entries -1.
@@ -58,6 +60,8 @@ def _load():
         lib.dsa_oracle_head_dots.argtypes = [P, P, i32, i32, P]
         lib.dsa_oracle_topk.restype = i32
         lib.dsa_oracle_topk.argtypes = [P, P, P, i64, i64, i32, i32, i64, i32, i64, P, i64, P, P, i32]
+        lib.dsa_oracle_scores.restype = i32
+        lib.dsa_oracle_scores.argtypes = [P, P, P, i64, i64, i32, i32, i64, P, i64, P, i32]
         lib.dsa_oracle_dot.restype = f64
         lib.dsa_oracle_dot.argtypes = [P, P, i32]
         lib.dsa_oracle_retrieval_topk.restype = i32
@@ -76,10 +80,16 @@ def _ptr(a: np.ndarray):
 
 
 def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when that is set (the CPU share a shared host grants one job)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def score(q_row: np.ndarray, k_row: np.ndarray, w_row: np.ndarray) -> float:
@@ -127,6 +137,29 @@ def topk(q_idx, k_idx, w, q_pos0: int, top_k: int, block: int = 0, rows=None,
     if rc != 0:
         raise ValueError("oracle topk: bad arguments")
     return (out, kth) if return_kth else out
+
+
+def scores(q_idx, k_idx, w, q_pos0: int, rows=None, n_threads: int | None = None) -> np.ndarray:
+    """Canonical fp64 scores of the listed query rows against every key -> float64 [n_rows, N];
+    NaN for keys after the row's position."""
+    q_idx = np.ascontiguousarray(q_idx, np.uint16)
+    k_idx = np.ascontiguousarray(k_idx, np.uint16)
+    w = np.ascontiguousarray(w, np.float32)
+    L, H, d = q_idx.shape
+    N = k_idx.shape[0]
+    assert k_idx.shape[1] == d and w.shape == (L, H)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, np.int64)
+        n_rows = rows.shape[0]
+    else:
+        n_rows = L
+    out = np.empty((n_rows, N), np.float64)
+    rc = _load().dsa_oracle_scores(_ptr(q_idx), _ptr(k_idx), _ptr(w), L, N, H, d, q_pos0,
+                                   _ptr(rows) if rows is not None else None, n_rows, _ptr(out),
+                                   n_threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle scores: bad arguments")
+    return out
 
 
 def dot(a_bits: np.ndarray, b_bits: np.ndarray) -> float:

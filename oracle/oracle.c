@@ -214,6 +214,62 @@ int dsa_oracle_topk(const uint16_t* q_idx, const uint16_t* k_idx, const float* w
     return 0;
 }
 
+/* Canonical scores of the listed rows against every key (all rows if rows == NULL):
+ * out[r][s] = dsa_oracle_score(row, key s) for s <= p_t, NaN for the later keys.  Used by
+ * the tests that compare the GPU's fp32 scores with the canonical order. */
+typedef struct {
+    const topk_job_t* J;
+    double* out;
+    int64_t next;
+    pthread_mutex_t mu;
+} scores_job_t;
+
+static void* scores_worker(void* arg) {
+    scores_job_t* S = (scores_job_t*)arg;
+    const topk_job_t* J = S->J;
+    for (;;) {
+        pthread_mutex_lock(&S->mu);
+        int64_t r = S->next++;
+        pthread_mutex_unlock(&S->mu);
+        if (r >= J->n_rows) break;
+        const int64_t t = J->rows ? J->rows[r] : r;
+        const int64_t p = J->q_pos0 + t;
+        const uint16_t* q_row = J->q_idx + (size_t)t * J->n_heads * J->head_dim;
+        const float* w_row = J->w + (size_t)t * J->n_heads;
+        double* o = S->out + (size_t)r * J->N;
+        for (int64_t s = 0; s < J->N; ++s)
+            o[s] = s <= p ? dsa_oracle_score(q_row, J->k_idx + (size_t)s * J->head_dim, w_row, J->n_heads,
+                                             J->head_dim)
+                          : NAN;
+    }
+    return NULL;
+}
+
+int dsa_oracle_scores(const uint16_t* q_idx, const uint16_t* k_idx, const float* w, int64_t L, int64_t N,
+                      int n_heads, int head_dim, int64_t q_pos0, const int64_t* rows, int64_t n_rows,
+                      double* out, int n_threads) {
+    if (!q_idx || !k_idx || !w || !out || L < 0 || N <= 0 || q_pos0 < 0 || q_pos0 + L > N || n_heads <= 0 ||
+        head_dim <= 0)
+        return -1;
+    if (rows)
+        for (int64_t r = 0; r < n_rows; ++r)
+            if (rows[r] < 0 || rows[r] >= L) return -1;
+    topk_job_t J;
+    memset(&J, 0, sizeof J);
+    J.q_idx = q_idx; J.k_idx = k_idx; J.w = w;
+    J.L = L; J.N = N; J.q_pos0 = q_pos0;
+    J.n_heads = n_heads; J.head_dim = head_dim;
+    J.rows = rows; J.n_rows = rows ? n_rows : L;
+    scores_job_t S;
+    memset(&S, 0, sizeof S);
+    S.J = &J;
+    S.out = out;
+    pthread_mutex_init(&S.mu, NULL);
+    run_threads(scores_worker, &S, n_threads);
+    pthread_mutex_destroy(&S.mu);
+    return 0;
+}
+
 /* Causal mask on an index tensor: any index greater than the query's position
  * becomes -1 (idempotent; -1 stays -1). */
 void dsa_oracle_causal_mask(int32_t* idx, int64_t L, int top_k, int64_t q_pos0) {

@@ -1,5 +1,7 @@
 """Helpers for the GPU parity tests: numpy <-> torch device tensors and the
 attention tolerance check.  No method arithmetic lives here."""
+import functools
+
 import numpy as np
 
 # Attention tolerance on bf16 outputs: max |gpu - oracle| and relative L2 error of the
@@ -48,3 +50,13 @@ def assert_attn_close(gpu: np.ndarray, ref: np.ndarray, what: str = ""):
 
 def report(msg: str):
     print(msg, flush=True)
+
+
+@functools.lru_cache(maxsize=3)
+def config_inputs(name: str):
+    """make_inputs of a named configuration or integer twin ("C3", "C4i"), kept for reuse
+    across tests (C4's draws take seconds)."""
+    import dsa_inputs as di
+
+    wl = di.int_twin(name[:2]) if name.endswith("i") else di.CONFIGS[name]
+    return wl, di.make_inputs(wl)

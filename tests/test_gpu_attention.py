@@ -114,22 +114,3 @@ def test_c1_full_with_gpu_indices(dsa_gpu, oracle_mod):
     assert np.array_equal(idx[rows], want_idx)
     got, lse = run_gpu(dsa_gpu, inp["q"], inp["kv"], idx, wl.pos0)
     check(oracle_mod, inp["q"], inp["kv"], idx, wl.pos0, got, lse, rows=rows, what="C1 attention")
-
-
-def test_c3_end_to_end_sampled_rows(dsa_gpu, oracle_mod):
-    """The headline configuration exactly as timed: both calls, q_block 1024."""
-    import torch
-
-    wl = di.CONFIGS["C3"]
-    inp = di.make_inputs(wl)
-    idx_d = dsa_gpu.indexer_topk(to_dev_bf16(inp["q_idx"]), to_dev_bf16(inp["k_idx"]), to_dev(inp["w"]),
-                                 wl.pos0, wl.top_k, q_block=1024)
-    out_d, lse_d = dsa_gpu.sparse_prefill(to_dev_bf16(inp["q"]), to_dev_bf16(inp["kv"]), idx_d, wl.pos0,
-                                          SCALE, q_block=1024, return_lse=True)
-    torch.cuda.synchronize()
-    idx = idx_d.cpu().numpy()
-    rows = np.array([0, 1, 511, 1023, 1024, 1500, 2047], dtype=np.int64)
-    want_idx = oracle_mod.topk(inp["q_idx"], inp["k_idx"], inp["w"], wl.pos0, wl.top_k, rows=rows)
-    assert np.array_equal(idx[rows], want_idx)
-    check(oracle_mod, inp["q"], inp["kv"], idx, wl.pos0, bf16_dev_to_f64(out_d),
-          lse_d.cpu().numpy().astype(np.float64), rows=rows, what="C3 end to end")

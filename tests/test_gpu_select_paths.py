@@ -1,0 +1,90 @@
+"""GPU tests of the selection's less common paths, against the oracle.
+
+- top_k between 2,048 and 4,096: the select kernel then runs a block size that does not
+  divide its 2,048 histogram bins (576 .. 960 threads); every bin must still be counted,
+  so rows finish on the candidate path instead of falling back.
+- Scores spread over many scales (zeros, 2^-100, 2^-66, 2^-33, values near 1): value
+  binning cannot isolate the k-th score in three levels, and the exact radix select
+  finishes the search, both in select and in the blocked fold.
+
+The selection counters (dsa_indexer_topk_stats) show which path each row took.
+"""
+import numpy as np
+import pytest
+
+import dsa_inputs as di
+from tests.gpu_util import report, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def run_with_stats(dsa, q, k, w, q_pos0, top_k, q_block=1024):
+    import torch
+
+    L, N = q.shape[0], k.shape[0]
+    ws = torch.empty(dsa.workspace_bytes(L, N, top_k, q_block), dtype=torch.uint8, device="cuda:0")
+    out = dsa.indexer_topk(to_dev_bf16(q), to_dev_bf16(k), to_dev(w), q_pos0, top_k, q_block=q_block,
+                           workspace=ws)
+    stats = dsa.indexer_stats(ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), stats
+
+
+def multiscale_case(N, L, seed):
+    """One live head reading key dimension 0: score(s) = ReLU(k[s, 0]).  200 keys score
+    between 1 and 3 (distinct), three score 2^-33, 2^-66 and 2^-100, every other key 0."""
+    rng = np.random.default_rng(seed)
+    q = np.zeros((L, 32, 128), np.float32)
+    q[:, 0, 0] = 1.0
+    w = np.zeros((L, 32), np.float32)
+    w[:, 0] = 1.0
+    k = np.zeros((N, 128), np.float32)
+    vals = np.concatenate([1.0 + np.arange(128) / 128.0, 2.0 + np.arange(72) / 32.0]).astype(np.float32)
+    big = rng.choice(N - L - 16, size=vals.size, replace=False)
+    k[big, 0] = vals
+    tiny = rng.choice(np.setdiff1d(np.arange(N - L), big), size=3, replace=False)
+    k[tiny, 0] = np.array([2.0 ** -33, 2.0 ** -66, 2.0 ** -100], np.float32)
+    # other dimensions of the keys carry values the live head does not read
+    k[:, 1:] = rng.integers(-2, 3, size=(N, 127))
+    return di.f32_to_bf16_bits(q), di.f32_to_bf16_bits(k), w
+
+
+def test_multiscale_scores_radix_in_select(dsa_gpu, oracle_mod):
+    """Every causal key is a candidate (N below the candidate capacity) and the fp64 band
+    (the zeros and the three tiny scores) fits select's buffer: select finds the k-th score
+    (0) with the radix pass and ranks the band exactly."""
+    N, L, top_k = 1000, 8, 256
+    q, k, w = multiscale_case(N, L, 1)
+    got, st = run_with_stats(dsa_gpu, q, k, w, N - L, top_k)
+    report(f"multiscale select: {st}")
+    want = oracle_mod.topk(q, k, w, N - L, top_k)
+    assert np.array_equal(got, want)
+    assert st["rows"] == L and st["kth_radix"] == L and st["rows_fallback"] == 0 and st["rows_failed"] == 0
+
+
+def test_multiscale_scores_radix_in_fold(dsa_gpu, oracle_mod):
+    """The band (about 6,800 keys scoring 0 or nearly 0) outgrows select's buffer, so the rows
+    go to the blocked fold, whose k-th searches need the radix pass."""
+    N, L, top_k = 7000, 8, 2048
+    q, k, w = multiscale_case(N, L, 2)
+    got, st = run_with_stats(dsa_gpu, q, k, w, N - L, top_k)
+    report(f"multiscale fold: {st}")
+    want = oracle_mod.topk(q, k, w, N - L, top_k)
+    assert np.array_equal(got, want)
+    assert st["rows_fallback"] == L and st["fallback_band"] == L and st["rows_failed"] == 0
+
+
+@pytest.mark.parametrize("top_k", [2049, 3000, 3840])
+def test_topk_between_2048_and_4096(dsa_gpu, oracle_mod, top_k):
+    """1,024 rows (128 row groups, key-ordered candidate segments); select runs cap / 16
+    threads = 576 .. 960."""
+    wl = di.Workload("k3000", 60000, 1024, top_k, 16, 23, "gauss")
+    q, k, w = di.make_indexer_inputs(wl)
+    got, st = run_with_stats(dsa_gpu, q, k, w, wl.pos0, top_k)
+    report(f"top_k {top_k}: {st}")
+    rows = np.array([0, 1, 7, 8, 100, 511, 512, 700, 1015, 1023], dtype=np.int64)
+    want = oracle_mod.topk(q, k, w, wl.pos0, top_k, rows=rows)
+    assert np.array_equal(got[rows], want)
+    assert (np.diff(got, axis=1) > 0).all()
+    assert st["rows_failed"] == 0
+    assert st["rows_fallback"] <= wl.L // 100, "rows should finish on the candidate path"

@@ -297,3 +297,34 @@ def test_profile_set_validates_names(lib):
     assert b"bogus" in lib.dsa_last_error()
     assert lib.dsa_profile_set(b"") == 0 and lib.dsa_profile_set(None) == 0
     assert lib.dsa_profile_enable(0) == 0
+
+
+def test_stats_rejects_bad_arguments(lib):
+    st = dsa.IndexerStats()
+    f = lib.dsa_indexer_topk_stats
+    assert f(None, ctypes.byref(st), None) == 1
+    assert f(ctypes.c_void_p((1 << 20) + 16), ctypes.byref(st), None) == 1  # not 256-byte aligned
+    assert f(ctypes.c_void_p(1 << 20), None, None) == 1
+
+
+def call_scores(lib, L=4, N=64, nh=32, hd=128, q_pos0=60, ptr=1 << 20, ws=1 << 30, ws_bytes=1 << 40):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return lib.dsa_indexer_scores(p, p, p, L, N, nh, hd, q_pos0, p, p,
+                                  ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=65, N=200, q_pos0=100), 1), (dict(q_pos0=0), 1), (dict(q_pos0=61), 1), (dict(nh=16), 2),
+    (dict(ptr=0), 1), (dict(ws=0), 3), (dict(ws_bytes=10), 3), (dict(ws=(1 << 30) + 8), 1),
+])
+def test_scores_rejects_bad_arguments(lib, kw, status):
+    assert call_scores(lib, **kw) == status
+    assert lib.dsa_last_error() != b""
+
+
+def test_scores_workspace(lib):
+    f = lib.dsa_indexer_scores_workspace_bytes
+    assert f(0, 100) == 0 and f(dsa.MAX_SCORE_ROWS + 1, 100) == 0 and f(4, 0) == 0
+    # every key of every (row-group-padded) row fits as a candidate
+    assert f(8, 131072) > 8 * 131072 * 8
+    assert f(1, 1000) == f(8, 1000)

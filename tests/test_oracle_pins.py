@@ -100,6 +100,26 @@ def test_integer_scores_are_exact(oracle_mod):
         assert oracle_mod.score(q[t], k[s], w[t]) == float(brute.exact_score(q[t], k[s], w[t]))
 
 
+def test_row_scores_match_exact_rationals_and_stop_at_the_position(oracle_mod):
+    """oracle.scores: every causal key's score equals the exact rational score; keys after
+    the row's position are NaN."""
+    rng = np.random.default_rng(21)
+    L, N, H, d, q_pos0 = 3, 12, 4, 6, 8
+    q = bf(rng.integers(-3, 4, size=(L, H, d)))
+    k = bf(rng.standard_normal((N, d)))
+    w = rng.choice(np.array([-0.25, 0.125, 0.5], np.float32), size=(L, H))
+    got = oracle_mod.scores(q, k, w, q_pos0)
+    for t in range(L):
+        p = q_pos0 + t
+        for s in range(N):
+            if s <= p:
+                assert got[t, s] == float(brute.exact_score(q[t], k[s], w[t]))
+            else:
+                assert np.isnan(got[t, s])
+    sub = oracle_mod.scores(q, k, w, q_pos0, rows=np.array([2, 0]))
+    assert np.array_equal(sub, got[[2, 0]], equal_nan=True)
+
+
 # ------------------------------------------------------------------ top-k
 
 def _tiny_case(rng, L, N, H, d, lo, hi):
