@@ -377,6 +377,7 @@ dsa_status_t dsa_indexer_topk_stats(const void* workspace, dsa_indexer_stats_t* 
     out->fallback_overflow = (int64_t)c[dsa::kDiagFbOverflow];
     out->fallback_incomplete = (int64_t)c[dsa::kDiagFbIncomplete];
     out->fallback_band = (int64_t)c[dsa::kDiagFbBand];
+    out->fallback_kth = (int64_t)c[dsa::kDiagFbKth];
     out->rows_failed = (int64_t)c[dsa::kDiagFailed];
     out->candidates = (int64_t)c[dsa::kDiagCandSum];
     out->candidates_max = (int64_t)c[dsa::kDiagCandMax];

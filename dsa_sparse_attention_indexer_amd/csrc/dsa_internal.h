@@ -107,12 +107,13 @@ enum DiagSlot : int {
     kDiagFbOverflow,    // ... because a candidate segment overflowed (or the fold was forced)
     kDiagFbIncomplete,  // ... because the candidates were not provably a superset of the top-k
     kDiagFbBand,        // ... because the band outgrew select's buffer
+    kDiagFbKth,         // ... because value binning did not isolate the k-th score
     kDiagFailed,        // rows no path could finish (emitted as -1; never expected)
     kDiagCandSum,       // candidates, summed over the candidate-path rows
     kDiagCandMax,       // most candidates of one such row
     kDiagBandSum,       // keys re-scored in fp64, summed over those rows
     kDiagBandMax,       // most re-scored keys of one row
-    kDiagRadix,         // rows whose k-th search needed the radix select
+    kDiagRadix,         // fold rows whose k-th searches needed the radix select
     kDiagSlots = 16
 };
 constexpr size_t kDiagBytes = 256;

@@ -777,11 +777,14 @@ __device__ float block_kth_radix(const Src& src, int k, SelectScratch& S) {
 
 // k-th largest value (1-based, 1 <= k <= total) under the float order (-0 == +0), by
 // value-linear binning (LiteTopK's bins: cheap even when every score shares an exponent)
-// refined up to three times, then a rank count over the crossing bin.  When a bin still
-// holds more than kDirect values after three levels (scores spread over many scales), the
-// exact radix select above finishes the search.  Sets *used_radix when it did.
-template <class Src>
-__device__ float block_kth_binned(const Src& src, int k, SelectScratch& S, bool* used_radix = nullptr) {
+// refined up to three times, then a rank count over the crossing bin.  A bin may still
+// hold more than kDirect values after three levels (scores spread over many scales); then
+// *stuck is set and, with kRadix, the exact radix select above finishes the search (its
+// result is returned); without it the return value is meaningless.  (select leaves the
+// radix out: inlined over its register-resident candidates it costs spills on every row;
+// such rows go to the fold, which has it.)
+template <bool kRadix, class Src>
+__device__ float block_kth_binned(const Src& src, int k, SelectScratch& S, bool* stuck) {
     constexpr int kLevels = 3;
     float vmin = INFINITY, vmax = -INFINITY;
     src.for_each([&](float v) {
@@ -815,8 +818,9 @@ __device__ float block_kth_binned(const Src& src, int k, SelectScratch& S, bool*
         const int nb = S.sh[2];
         __syncthreads();
         if (b < 0 || (nb > kDirect && nlv + 1 == kLevels)) {  // (b < 0 only if k > total)
-            if (used_radix) *used_radix = true;
-            return block_kth_radix(src, k, S);
+            *stuck = true;
+            if (kRadix) return block_kth_radix(src, k, S);
+            return 0.f;
         }
 #pragma unroll
         for (int l = 0; l < kLevels; ++l)
@@ -1036,8 +1040,8 @@ __device__ bool select_core(const CandList& L, int k, float delta, const uint16_
                             const float* __restrict__ w_row, const QHeadStat* __restrict__ qs_row,
                             const uint16_t* __restrict__ k_idx, int* band_i,
                             double* band_s, float* band_f, int band_cap, int* sel_i, float* sel_s,
-                            SelectScratch& S) {
-    const float kth = block_kth_binned(ListSrc{L}, k, S);
+                            SelectScratch& S, bool* used_radix) {
+    const float kth = block_kth_binned<true>(ListSrc{L}, k, S, used_radix);
     const double lo = (double)kth - 2.0 * (double)delta;
     const double hi = (double)kth + 2.0 * (double)delta;
     if (threadIdx.x == 0) {
@@ -1421,8 +1425,12 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
         nv = total > tid ? min((total - tid + nthr - 1) / nthr, kSelChunk) : 0;
     }
     float kth = 0.f;
-    bool radix = false;
-    if (ok) kth = block_kth_binned(RegSrc<kSelChunk>{v, nv}, k, S, &radix);
+    bool stuck = false;
+    if (ok) kth = block_kth_binned<false>(RegSrc<kSelChunk>{v, nv}, k, S, &stuck);
+    if (stuck) {
+        ok = false;
+        why = kDiagFbKth;
+    }
     const double lo = (double)kth - 2.0 * (double)delta;
     const double hi = (double)kth + 2.0 * (double)delta;
     if (ok && tau_f != -INFINITY && lo < (double)tau_f) ok = false;  // candidate set not provably complete
@@ -1548,7 +1556,6 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
         atomicMax(&P.diag[kDiagCandMax], (unsigned long long)total);
         atomicAdd(&P.diag[kDiagBandSum], (unsigned long long)nb_row);
         atomicMax(&P.diag[kDiagBandMax], (unsigned long long)nb_row);
-        if (radix) atomicAdd(&P.diag[kDiagRadix], 1ull);
     }
 }
 
@@ -1631,7 +1638,7 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
         const float* w_row = ref.w;
         int cur = 0, n = 0;
         float lo = -INFINITY;
-        bool failed = false;
+        bool failed = false, radix = false;
         for (int64_t b0 = 0; b0 < nt && !failed; b0 += kFoldKeys) {
             const int64_t b1 = b0 + kFoldKeys < nt ? b0 + kFoldKeys : nt;
             if (threadIdx.x == 0) s_cnt = n;
@@ -1652,7 +1659,7 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
                 // select_core succeeds; should it not, the row is emitted as -1 and counted.
                 const bool ok = select_core(L, k, delta, q_row, w_row, P.qstat + (size_t)r * kIdxHeads, ref.keys,
                                             band_i, band_s, band_f,
-                                            P.fold_cap, Ri[nxt], Rs[nxt], S);
+                                            P.fold_cap, Ri[nxt], Rs[nxt], S, &radix);
                 __syncthreads();
                 if (!ok) {  // uniform over the block
                     failed = true;
@@ -1665,7 +1672,7 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
                 R.i[0] = Ri[cur];
                 R.n[0] = n;
                 R.nseg = 1;
-                const float kth = block_kth_binned(ListSrc{R}, k, S);
+                const float kth = block_kth_binned<true>(ListSrc{R}, k, S, &radix);
                 const double l = (double)kth - 2.0 * (double)delta;
                 float lf = (float)l;
                 if ((double)lf > l) lf = nextafterf(lf, -INFINITY);
@@ -1673,6 +1680,7 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
             }
         }
         int32_t* out_row = ref.out;
+        if (radix && threadIdx.x == 0) atomicAdd(&P.diag[kDiagRadix], 1ull);
         if (failed) {
             for (int j = threadIdx.x; j < k; j += blockDim.x) out_row[j] = -1;
             if (threadIdx.x == 0) atomicAdd(&P.diag[kDiagFailed], 1ull);

@@ -4,8 +4,8 @@
   divide its 2,048 histogram bins (576 .. 960 threads); every bin must still be counted,
   so rows finish on the candidate path instead of falling back.
 - Scores spread over many scales (zeros, 2^-100, 2^-66, 2^-33, values near 1): value
-  binning cannot isolate the k-th score in three levels, and the exact radix select
-  finishes the search, both in select and in the blocked fold.
+  binning cannot isolate the k-th score in three levels; select hands such rows to the
+  blocked fold, where the exact radix select finishes the search.
 
 The selection counters (dsa_indexer_topk_stats) show which path each row took.
 """
@@ -49,17 +49,18 @@ def multiscale_case(N, L, seed):
     return di.f32_to_bf16_bits(q), di.f32_to_bf16_bits(k), w
 
 
-def test_multiscale_scores_radix_in_select(dsa_gpu, oracle_mod):
+def test_multiscale_scores_kth_not_isolated_in_select(dsa_gpu, oracle_mod):
     """Every causal key is a candidate (N below the candidate capacity) and the fp64 band
-    (the zeros and the three tiny scores) fits select's buffer: select finds the k-th score
-    (0) with the radix pass and ranks the band exactly."""
+    (the zeros and the three tiny scores) would fit select's buffer, but value binning
+    cannot isolate the k-th score (0): select hands the rows to the fold, whose k-th search
+    finishes with the radix pass."""
     N, L, top_k = 1000, 8, 256
     q, k, w = multiscale_case(N, L, 1)
     got, st = run_with_stats(dsa_gpu, q, k, w, N - L, top_k)
     report(f"multiscale select: {st}")
     want = oracle_mod.topk(q, k, w, N - L, top_k)
     assert np.array_equal(got, want)
-    assert st["rows"] == L and st["kth_radix"] == L and st["rows_fallback"] == 0 and st["rows_failed"] == 0
+    assert st["fallback_kth"] == L and st["kth_radix"] == L and st["rows_failed"] == 0
 
 
 def test_multiscale_scores_radix_in_fold(dsa_gpu, oracle_mod):
@@ -71,7 +72,8 @@ def test_multiscale_scores_radix_in_fold(dsa_gpu, oracle_mod):
     report(f"multiscale fold: {st}")
     want = oracle_mod.topk(q, k, w, N - L, top_k)
     assert np.array_equal(got, want)
-    assert st["rows_fallback"] == L and st["fallback_band"] == L and st["rows_failed"] == 0
+    assert st["rows_fallback"] == L and st["fallback_band"] == L and st["kth_radix"] == L
+    assert st["rows_failed"] == 0
 
 
 @pytest.mark.parametrize("top_k", [2049, 3000, 3840])
