@@ -30,11 +30,12 @@ D_ROPE = 64
 DEFAULT_Q_BLOCK = 1024
 MAX_BATCH = 65536
 MAX_SCORE_ROWS = 64
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = ["dsa_indexer_topk_workspace_bytes", "dsa_indexer_topk", "dsa_causal_mask_topk",
             "dsa_sparse_prefill", "dsa_sparse_prefill_packed", "dsa_sparse_decode_workspace_bytes",
             "dsa_sparse_decode",
-            "dsa_indexer_topk_stats", "dsa_indexer_scores_workspace_bytes", "dsa_indexer_scores",
+            "dsa_indexer_topk_noalloc", "dsa_indexer_topk_stats", "dsa_indexer_scores_workspace_bytes", "dsa_indexer_scores",
             "dsa_indexer_topk_varlen_workspace_bytes", "dsa_indexer_topk_varlen",
             "dsa_sparse_prefill_varlen_workspace_bytes", "dsa_sparse_prefill_varlen",
             "dsa_retrieval_topk_workspace_bytes", "dsa_retrieval_topk",
@@ -74,6 +75,8 @@ def load_library(path: str | None = None):
     lib.dsa_indexer_topk_workspace_bytes.argtypes = [i64, i64, i32, i32]
     lib.dsa_indexer_topk.restype = ctypes.c_int
     lib.dsa_indexer_topk.argtypes = [P, P, P, i64, i64, i32, i32, i64, i32, i32, P, P, sz, P]
+    lib.dsa_indexer_topk_noalloc.restype = ctypes.c_int
+    lib.dsa_indexer_topk_noalloc.argtypes = [P, P, P, i64, i64, i32, i32, i64, i32, i32, P, P]
     lib.dsa_indexer_topk_stats.restype = ctypes.c_int
     lib.dsa_indexer_topk_stats.argtypes = [P, P, P]
     lib.dsa_indexer_scores_workspace_bytes.restype = sz

@@ -13,6 +13,12 @@
 #include "dsa.h"
 #include "dsa_internal.h"
 
+// Device scratch of dsa_indexer_topk_noalloc: one copy per GPU the library runs on, held
+// until the process ends.  Host code never uses this name as an address (on the host it
+// is only a stand-in for the symbol): it asks each device for the address of its copy once
+// (hipGetSymbolAddress, with that device current) and passes that pointer on.
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
 namespace dsa {
 namespace {
 std::atomic<uint32_t> g_prof_mask{0};  // kernel classes bracketed by events (bit k: class k)
@@ -473,6 +479,55 @@ dsa_status_t dsa_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, co
     if (e == hipSuccess) e = dsa::launch_score_dump(a, scores, N, delta, s);
     if (e != hipSuccess) return hip_fail(e, "score dump launch");
     return DSA_OK;
+}
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+dsa_status_t scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(DSA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                    kScratchDevices - 1);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> g(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+            if (!p) return fail(DSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return DSA_OK;
+}
+}  // namespace
+
+dsa_status_t dsa_indexer_topk_noalloc(const uint16_t* q_idx, const uint16_t* k_idx, const float* w, int64_t L,
+                                      int64_t N, int32_t n_heads, int32_t head_dim, int64_t q_pos0, int32_t top_k,
+                                      int32_t q_block, int32_t* out_idx, dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    dsa_status_t st = check_indexer_args(q_idx, k_idx, w, L, N, n_heads, head_dim, q_pos0, top_k, q_block, out_idx);
+    if (st != DSA_OK) return st;
+    if (L == 0) return DSA_OK;
+    const size_t need = dsa_indexer_topk_workspace_bytes(L, N, top_k, q_block);
+    if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES)
+        return fail(DSA_ERR_WORKSPACE,
+                    "these sizes need %zu bytes of scratch, above the %zu-byte static scratch of the "
+                    "no-allocation entry point (a smaller q_block may fit)",
+                    need, (size_t)DSA_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != DSA_OK) return st;
+    return dsa_indexer_topk(q_idx, k_idx, w, L, N, n_heads, head_dim, q_pos0, top_k, q_block, out_idx, ws,
+                            (size_t)DSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 dsa_status_t dsa_causal_mask_topk(int32_t* idx, int64_t L, int32_t top_k, int64_t q_pos0, dsa_stream_t stream) {

@@ -99,6 +99,27 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
                               void* workspace, size_t workspace_bytes, dsa_stream_t stream);
 
 /*
+ * dsa_indexer_topk without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The scratch is a static device array of
+ * DSA_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held until the
+ * process ends; this call allocates nothing and calls no allocating routine (with
+ * kernel timing, dsa_profile_enable, off).  Arguments, results and errors are those
+ * of dsa_indexer_topk; sizes whose dsa_indexer_topk_workspace_bytes exceeds
+ * DSA_NOALLOC_SCRATCH_BYTES return DSA_ERR_WORKSPACE (a smaller q_block may fit:
+ * the decode step at N = 131,072 needs about 39 MiB, a 512-query chunk at 16,384 keys
+ * about 44 MiB).  Every call on one GPU uses that GPU's one array, so calls that
+ * overlap on one GPU (other streams, other host threads) race and give wrong
+ * results; calls in one stream's order are safe.  The scratch needs no clearing:
+ * every counter the kernels read is set by an earlier kernel of the same call.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dsa_status_t dsa_indexer_topk_noalloc(const uint16_t* q_idx, const uint16_t* k_idx, const float* w,
+                                      int64_t L, int64_t N, int32_t n_heads, int32_t head_dim,
+                                      int64_t q_pos0, int32_t top_k, int32_t q_block, int32_t* out_idx,
+                                      dsa_stream_t stream);
+
+/*
  * Selection counters of the last dsa_indexer_topk, dsa_indexer_topk_varlen or
  * dsa_retrieval_topk call made with this workspace (diagnostics; no result
  * depends on them).  They show how the LiteTopK abstract's threshold scheme

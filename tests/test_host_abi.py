@@ -328,3 +328,14 @@ def test_scores_workspace(lib):
     # every key of every (row-group-padded) row fits as a candidate
     assert f(8, 131072) > 8 * 131072 * 8
     assert f(1, 1000) == f(8, 1000)
+
+
+def test_noalloc_rejects_before_touching_the_device(lib):
+    p = ctypes.c_void_p(1 << 20)
+    f = lib.dsa_indexer_topk_noalloc
+    # a C3 chunk in one 2,048-query block needs more than the static scratch
+    assert lib.dsa_indexer_topk_workspace_bytes(2048, 131072, 2048, 2048) > dsa.NOALLOC_SCRATCH_BYTES
+    assert f(p, p, p, 2048, 131072, 32, 128, 129024, 2048, 2048, p, None) == 3
+    assert b"static scratch" in lib.dsa_last_error()
+    assert f(p, p, p, 4, 64, 16, 128, 60, 8, 0, p, None) == 2   # the indexer's own checks first
+    assert f(None, None, None, 0, 64, 32, 128, 0, 8, 0, None, None) == 0  # L = 0: no-op
