@@ -193,7 +193,7 @@ def selection_summary(st: dict, wl) -> dict:
         "candidates_per_top_k": round(st["candidates"] / rows / wl.top_k, 3),
         "band_per_row": round(st["band"] / rows, 1), "band_max": st["band_max"],
         "rows_fallback": st["rows_fallback"], "fallback_overflow": st["fallback_overflow"],
-        "fallback_incomplete": st["fallback_incomplete"], "fallback_band": st["fallback_band"], "fallback_kth": st["fallback_kth"],
+        "fallback_incomplete": st["fallback_incomplete"], "fallback_band": st["fallback_band"],
         "rows_failed": st["rows_failed"], "kth_radix": st["kth_radix"],
     }
 

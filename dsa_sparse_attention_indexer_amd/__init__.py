@@ -52,7 +52,7 @@ class IndexerStats(ctypes.Structure):
     """dsa_indexer_stats_t: selection counters of the last indexer call on a workspace."""
     _fields_ = [(n, ctypes.c_int64) for n in (
         "rows", "rows_all_keys", "rows_fallback", "fallback_overflow", "fallback_incomplete",
-        "fallback_band", "fallback_kth", "rows_failed", "candidates", "candidates_max", "band", "band_max", "kth_radix")]
+        "fallback_band", "rows_failed", "candidates", "candidates_max", "band", "band_max", "kth_radix")]
 
 
 class DSAError(RuntimeError):

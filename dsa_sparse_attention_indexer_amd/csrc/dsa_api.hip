@@ -333,7 +333,7 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
     a.fb_ctrl = reinterpret_cast<int*>(ws + lay.off_fbctrl);
     a.fb_list = reinterpret_cast<int*>(ws + lay.off_fblist);
     a.sample = reinterpret_cast<float*>(ws + lay.off_sample);
-    a.cand = reinterpret_cast<uint2*>(ws + lay.off_cand);
+    a.cand = reinterpret_cast<uint32_t*>(ws + lay.off_cand);
     a.fold_s = reinterpret_cast<float*>(ws + lay.off_fold_s);
     a.fold_i = reinterpret_cast<int*>(ws + lay.off_fold_i);
     a.fold_bi = reinterpret_cast<int*>(ws + lay.off_fold_bi);
@@ -383,7 +383,6 @@ dsa_status_t dsa_indexer_topk_stats(const void* workspace, dsa_indexer_stats_t* 
     out->fallback_overflow = (int64_t)c[dsa::kDiagFbOverflow];
     out->fallback_incomplete = (int64_t)c[dsa::kDiagFbIncomplete];
     out->fallback_band = (int64_t)c[dsa::kDiagFbBand];
-    out->fallback_kth = (int64_t)c[dsa::kDiagFbKth];
     out->rows_failed = (int64_t)c[dsa::kDiagFailed];
     out->candidates = (int64_t)c[dsa::kDiagCandSum];
     out->candidates_max = (int64_t)c[dsa::kDiagCandMax];
@@ -468,7 +467,7 @@ dsa_status_t dsa_indexer_scores(const uint16_t* q_idx, const uint16_t* k_idx, co
     a.count = reinterpret_cast<int*>(ws + lay.off_count);
     a.fb_ctrl = reinterpret_cast<int*>(ws + lay.off_fbctrl);
     a.fb_list = reinterpret_cast<int*>(ws + lay.off_fblist);
-    a.cand = reinterpret_cast<uint2*>(ws + lay.off_cand);
+    a.cand = reinterpret_cast<uint32_t*>(ws + lay.off_cand);
     const int64_t last = q_pos0 + L - 1;
     const int64_t n_keys = (last < N - 1 ? last : N - 1) + 1;
     uint16_t* k_tile = reinterpret_cast<uint16_t*>(ws + lay.off_ktile);
@@ -751,7 +750,7 @@ dsa_status_t dsa_indexer_topk_varlen(const uint16_t* q_idx, const uint16_t* k_id
     a.fb_ctrl = reinterpret_cast<int*>(ws + lay.off_fbctrl);
     a.fb_list = reinterpret_cast<int*>(ws + lay.off_fblist);
     a.sample = reinterpret_cast<float*>(ws + lay.off_sample);
-    a.cand = reinterpret_cast<uint2*>(ws + lay.off_cand);
+    a.cand = reinterpret_cast<uint32_t*>(ws + lay.off_cand);
     a.fold_s = reinterpret_cast<float*>(ws + lay.off_fold_s);
     a.fold_i = reinterpret_cast<int*>(ws + lay.off_fold_i);
     a.fold_bi = reinterpret_cast<int*>(ws + lay.off_fold_bi);
@@ -969,7 +968,7 @@ dsa_status_t dsa_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M,
     a.fb_ctrl = reinterpret_cast<int*>(ws + lay.off_fbctrl);
     a.fb_list = reinterpret_cast<int*>(ws + lay.off_fblist);
     a.sample = reinterpret_cast<float*>(ws + lay.off_sample);
-    a.cand = reinterpret_cast<uint2*>(ws + lay.off_cand);
+    a.cand = reinterpret_cast<uint32_t*>(ws + lay.off_cand);
     a.fold_s = reinterpret_cast<float*>(ws + lay.off_fold_s);
     a.fold_i = reinterpret_cast<int*>(ws + lay.off_fold_i);
     a.fold_bi = reinterpret_cast<int*>(ws + lay.off_fold_bi);

@@ -27,11 +27,12 @@ __host__ __device__ inline int key_stats_blocks(int64_t n_keys) {
     return (int)b;
 }
 
-// Candidate capacity per query row: expected candidates are 2.5 * top_k.
+// Candidate capacity per query row: expected candidates are 2.5 * top_k.  A multiple of
+// 2,048, so select (cap / 32 threads) runs whole waves.
 __host__ __device__ inline int cand_capacity(int top_k) {
     int c = 4 * top_k;
     if (c < 8192) c = 8192;
-    return (c + 1023) & ~1023;
+    return (c + 2047) & ~2047;
 }
 
 constexpr int kRowsPerGroup = 8;  // indexer query rows scored together (one sample each)
@@ -107,7 +108,6 @@ enum DiagSlot : int {
     kDiagFbOverflow,    // ... because a candidate segment overflowed (or the fold was forced)
     kDiagFbIncomplete,  // ... because the candidates were not provably a superset of the top-k
     kDiagFbBand,        // ... because the band outgrew select's buffer
-    kDiagFbKth,         // ... because value binning did not isolate the k-th score
     kDiagFailed,        // rows no path could finish (emitted as -1; never expected)
     kDiagCandSum,       // candidates, summed over the candidate-path rows
     kDiagCandMax,       // most candidates of one such row
@@ -237,7 +237,8 @@ struct IndexerArgs {
     int* fb_ctrl;           // [0] flagged rows, [1] next row to take
     int* fb_list;
     float* sample;
-    uint2* cand;            // [Lb][cap] (fp32 score bits, key) in kCandSegs segments
+    uint32_t* cand;         // [Lb][2][cap] words: a row's candidate scores (fp32 bits) in its
+                            // first cap words, their keys in the next cap (kCandSegs segments each)
     float* fold_s;          // [slots][2][fold_cap]
     int* fold_i;            // [slots][2][fold_cap]
     int* fold_bi;           // [slots][fold_cap]
@@ -288,7 +289,7 @@ struct RetrievalArgs {
     int sample_stride, sample_n;
     const float* tau;        // [Lb] filter threshold (row_prep)
     const int* mode;         // [Lb]
-    uint2* cand;             // [Lb][cap] appended candidate lists
+    uint32_t* cand;          // [Lb][2][cap] appended candidate lists (scores, then keys)
     int* count;              // [Lb][kCandSegs]: entry 0 counts a row's list
     int cap;
     // The filter's per-lane lists: segment (part, wave, lane half) of each row holds up to

@@ -316,7 +316,7 @@ struct ScoreTile {
     float tau_m[kPairs];     // candidate threshold (+inf for rows the filter skips)
     bool live_m[kPairs];
     float* sample0;     // sample: row 0's sample list (rows are sample_stride apart)
-    uint2* cand0;       // filter: row 0's segment (rows are cap apart)
+    uint32_t* cand0;    // filter: row 0's scores of this segment (rows 2 cap words apart, keys cap after)
     uint32_t n0;        // sample: keys of the group's first row
     uint32_t S;         // sample: sample size
     float s_ratio;      // sample: key stride n0 / S (any in-range keys would do)
@@ -428,7 +428,11 @@ struct ScoreTile {
         if (lane < lcnt[j]) {
             const uint2 e = lbuf[j * kStageSlots + lane];
             const uint32_t o = base + (uint32_t)lane;
-            if (o < (uint32_t)seg) cand0[(uint32_t)j * (uint32_t)P.cap + o] = e;
+            if (o < (uint32_t)seg) {
+                uint32_t* dst = cand0 + (uint32_t)j * 2u * (uint32_t)P.cap + o;
+                dst[0] = e.x;
+                dst[P.cap] = e.y;
+            }
         }
         gcnt[j] += lcnt[j];
         lcnt[j] = 0;
@@ -574,7 +578,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
                              {hf ? live[1] : live[0], hf ? live[3] : live[2], hf ? live[5] : live[4],
                               hf ? live[7] : live[6]},
                              kSample ? P.sample + (size_t)r0 * P.sample_stride : nullptr,
-                             kSample ? nullptr : P.cand + (size_t)r0 * P.cap + (appended ? 0 : (size_t)segment * seg),
+                             kSample ? nullptr : P.cand + (size_t)r0 * 2 * P.cap + (appended ? 0 : (size_t)segment * seg),
                              n0, S, kSample && S > 0 ? (float)n0 / (float)S : 0.f, lane, hf, col, col - hf,
                              (int)gref.pos, r0, seg, cnt,
                              s_stage[wave], {0, 0, 0, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0, 0}, (uint32_t)t0,
@@ -650,7 +654,8 @@ struct SelectScratch {
     int sh[16];
 };
 
-__device__ __forceinline__ void block_minmax(float& mn, float& mx, SelectScratch& S) {
+template <class Sc>
+__device__ __forceinline__ void block_minmax(float& mn, float& mx, Sc& S) {
     mn = wave_min(mn);
     mx = wave_max(mx);
     const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -670,7 +675,8 @@ __device__ __forceinline__ void block_minmax(float& mn, float& mx, SelectScratch
 }
 
 // Inclusive scan of one int per thread in thread order (block of at most 16 waves).
-__device__ __forceinline__ int block_incl_scan(int v, SelectScratch& S) {
+template <class Sc>
+__device__ __forceinline__ int block_incl_scan(int v, Sc& S) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int x = v;
     for (int o = 1; o < 64; o <<= 1) {
@@ -721,12 +727,15 @@ struct RegSrc {
 // leaves b in S.sh[0] (-1 if none), the values above b (including `above`) in S.sh[1] and
 // hist[b] in S.sh[2].  Thread t sums bins nbins-1-t*per down to nbins-(t+1)*per with
 // per = ceil(nbins / blockDim), so every bin is counted whatever the block size.
-__device__ __forceinline__ void block_find_crossing(const int* hist, int nbins, int k, int above, SelectScratch& S) {
+template <class Sc>
+__device__ __forceinline__ void block_find_crossing(const int* hist, int nbins, int k, int above, Sc& S) {
     const int per = (nbins + (int)blockDim.x - 1) / (int)blockDim.x;
     const int top = nbins - 1 - (int)threadIdx.x * per;
     int c = 0;
-    for (int j = 0; j < per; ++j)
-        if (top - j >= 0) c += hist[top - j];
+    for (int j = 0; j < per; ++j) {  // branch-free: the reads of a thread are in flight together
+        const int h = hist[max(top - j, 0)];
+        c += top - j >= 0 ? h : 0;
+    }
     const int incl = block_incl_scan(c, S) + above;
     const int excl = incl - c;
     if (threadIdx.x == 0) S.sh[0] = -1;
@@ -751,8 +760,8 @@ __device__ __forceinline__ void block_find_crossing(const int* hist, int nbins, 
 // exact radix select over the order-preserving keys: three passes of 11, 11 and 10 bits
 // from the top, each over the values whose higher bits match the digits found so far.
 // Cannot fail; the selection's last resort when value binning does not converge.
-template <class Src>
-__device__ float block_kth_radix(const Src& src, int k, SelectScratch& S) {
+template <class Src, class Sc>
+__device__ float block_kth_radix(const Src& src, int k, Sc& S) {
     uint32_t prefix = 0u;  // the digits found so far
     int remaining = k;
     for (int pass = 0; pass < 3; ++pass) {
@@ -783,8 +792,8 @@ __device__ float block_kth_radix(const Src& src, int k, SelectScratch& S) {
 // result is returned); without it the return value is meaningless.  (select leaves the
 // radix out: inlined over its register-resident candidates it costs spills on every row;
 // such rows go to the fold, which has it.)
-template <bool kRadix, class Src>
-__device__ float block_kth_binned(const Src& src, int k, SelectScratch& S, bool* stuck) {
+template <bool kRadix, class Src, class Sc>
+__device__ float block_kth_binned(const Src& src, int k, Sc& S, bool* stuck) {
     constexpr int kLevels = 3;
     float vmin = INFINITY, vmax = -INFINITY;
     src.for_each([&](float v) {
@@ -1352,18 +1361,188 @@ __device__ void write_sorted_output(int* sel, int k, int32_t* out_row) {
     for (int i = threadIdx.x; i < k; i += blockDim.x) out_row[i] = sel[i];
 }
 
-constexpr int kSelBand = 1024;
-// Appended candidate lists are put back in key order through a bitmap of the causal keys
-// held in the re-score's term array, when the keys fit it.
-constexpr int kSelBitmapKeys = kRescoreRound * kIdxHeads * 64;  // 32 KB of bits
-constexpr int kSelChunk = 16;  // candidates per thread: the block has cap / 16 threads
+constexpr int kSelBand = 1024;     // band entries select re-scores (more: the row goes to the fold)
+constexpr int kSelPer = 32;        // candidates per thread: the block has cap / 32 threads
+constexpr int kSelMaxThreads = 4 * kMaxTopK / kSelPer;  // cap <= 4 * kMaxTopK
+constexpr int kOneLevel = 256;     // a crossing bin this small ends the k-th search
+// Appended candidate lists are put back in key order through a bitmap of the causal keys,
+// when they fit it.
+constexpr int kSelBitmapWords = 8192;
+constexpr int kSelBitmapKeys = kSelBitmapWords * 32;  // 262,144 keys
+
+// select's shared memory.  The phases use the union in turn: the k-th search (sel), the
+// band (band), then the output compaction (cmp, bitmap or out).  Small enough (~34 KB) for
+// four rows per compute unit.
+struct SelectLds {
+    union {
+        struct {
+            int hist[kBins];
+            float direct[kDirect];
+        } sel;
+        struct {
+            int key[kSelBand];
+            int pos[kSelBand];    // candidate position of the entry
+            double s[kSelBand];   // fp32 score, then its canonical fp64 score
+            u16x8 q[kIdxHeads * kIdxDim / 8];  // the row's query (re-score operands)
+            float w[kIdxHeads];
+            QHeadStat qs[kIdxHeads];
+        } band;
+        struct {
+            int cnt[kSelPer * 8];  // selected entries per (element, wave), <= 8 waves
+            int pre[kSelPer * 8];
+        } cmp;
+        uint32_t bitmap[kSelBitmapWords];
+        int out[kMaxTopK];
+    };
+    uint32_t win[kSelMaxThreads * kSelPer / 32];  // bit j: candidate position j is selected
+    float red_f[32];
+    int red_i[32];
+    int sh[16];
+};
+
+// x of lane c - 1 of the lane's 16-lane row (lane 0 of a row gets 0).
+__device__ __forceinline__ double dpp_row_shr1(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x111, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x111, 0xf, 0xf, false);
+    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// sum_i q_h[i] k[i] in fp64 with i ascending (bf16 x bf16 products are exact in fp64, so
+// each fma rounds as the canonical add does).
+__device__ double canonical_dot(const uint16_t* __restrict__ q_h, const uint16_t* __restrict__ k_row) {
+    double d = 0.0;
+    const u16x8* qa = reinterpret_cast<const u16x8*>(q_h);
+    const u16x8* ka = reinterpret_cast<const u16x8*>(k_row);
+    for (int c = 0; c < kIdxDim / 8; ++c) {
+        const u16x8 qv = qa[c], kv = ka[c];
+        for (int j = 0; j < 8; ++j)
+            d = __builtin_fma((double)bf16_bits_to_float(qv[j]), (double)bf16_bits_to_float(kv[j]), d);
+    }
+    return d;
+}
+
+// Canonical fp64 scores of band entries [0, nb), in place into band_s (keys in band_key).
+// One wave per block of 16 entries, all 32 heads, as two halves of 16 heads: an fp64 MFMA
+// chain (16 keys x 16 heads x 4 dims per instruction) gives the head dot products when they
+// are provably exact in any order (the test of band_rescore); a (key, head) that fails it
+// takes the sequential evaluation in its lane.  The head terms fl(w_h max(d_h, +0)) are then
+// added in ascending h exactly as the canonical order does: lane c of a 16-lane row holds
+// head c of the half for four keys, and a chain of row shifts adds one head per step,
+// continuing from the first half's sum into the second.  No block barrier.
+__device__ __forceinline__ void band_rescore_waves(int nb, const int* band_key, double* band_s,
+                                                   const u16x8* q_lds, const float* w_lds,
+                                                   const QHeadStat* qs_lds, const uint16_t* __restrict__ q_row,
+                                                   const uint16_t* __restrict__ k_idx) {
+#pragma clang fp contract(off)
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    if (16 * wave >= nb) return;
+    // A operand of block mb: lane (g, c) supplies key mb + c, dimensions 32g .. 32g+31.
+    auto load_keys = [&](int mb, u16x8 (&kv)[4]) {
+        const int key = band_key[mb + c < nb ? mb + c : mb];
+        const u16x8* kp = reinterpret_cast<const u16x8*>(k_idx + (size_t)key * kIdxDim + 32 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kv[j] = kp[j];
+    };
+    for (int mb = 16 * wave; mb < nb; mb += 16 * nwaves) {
+        u16x8 kv[4];
+        load_keys(mb, kv);
+        float kinf = 0.f;
+        int ke = INT_MAX;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kinf = fmaxf(kinf, fabsf(bf16_bits_to_float(kv[j][e])));
+                if ((kv[j][e] & 0x7fff) != 0) ke = min(ke, bf16_lsb_exp(kv[j][e]));
+            }
+        kinf = fmaxf(kinf, __shfl_xor(kinf, 16));
+        kinf = fmaxf(kinf, __shfl_xor(kinf, 32));
+        ke = min(ke, __shfl_xor(ke, 16));
+        ke = min(ke, __shfl_xor(ke, 32));
+        double acc[4];  // ascending-h partial sums of entries mb + g + 4i, carried across the halves
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int head = 16 * half + c;
+            // B operand: head c of the half, dimensions 32g .. 32g+31, from the row's query in
+            // LDS (read per block: held across the block loop, both halves' fragments and
+            // their conversions would take 64 more registers).
+            u16x8 qv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qv[j] = q_lds[(head * kIdxDim + 32 * g) / 8 + j];
+            // Two chains (even and odd K-steps) halve the dependent MFMA latency; their sum is
+            // exact whenever the result is used (the exactness test below).
+            f64x4 d = {0.0, 0.0, 0.0, 0.0}, d1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int ks = 0; ks < 32; ks += 2) {
+                d = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_bits_to_float(kv[ks >> 3][ks & 7]),
+                                                         (double)bf16_bits_to_float(qv[ks >> 3][ks & 7]), d,
+                                                         0, 0, 0);
+                d1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_bits_to_float(kv[(ks + 1) >> 3][(ks + 1) & 7]),
+                                                          (double)bf16_bits_to_float(qv[(ks + 1) >> 3][(ks + 1) & 7]),
+                                                          d1, 0, 0, 0);
+            }
+            d += d1;
+            // Lane (g, c): the dot products of entries mb + g + 4i (i < 4) with this head.
+            const double wh = (double)w_lds[head];
+            const double l1 = qs_lds[head].l1;
+            const int eh = qs_lds[head].e;
+            double t[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = g + 4 * i;
+                const float kinf_m = __shfl(kinf, m);
+                const int ke_m = __shfl(ke, m);
+                double dh = d[i];
+                const bool exact = kinf_m == 0.f || eh == INT_MAX || l1 * (double)kinf_m < ldexp(1.0, 53 + eh + ke_m);
+                if (!exact && mb + m < nb)
+                    dh = canonical_dot(q_row + head * kIdxDim, k_idx + (size_t)band_key[mb + m] * kIdxDim);
+                t[i] = wh * (dh > 0.0 ? dh : 0.0);
+            }
+            // After step h, lane h of the row holds the sum through head 16 * half + h.
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const double carry = half ? __shfl(acc[i], 16 * g + 15) : 0.0;
+                acc[i] = half && c == 0 ? carry + t[i] : t[i];
+            }
+#pragma unroll
+            for (int step = 1; step < 16; ++step)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const double prev = dpp_row_shr1(acc[i]);
+                    if (c == step) acc[i] = prev + t[i];
+                }
+        }
+        if (c == 15) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = mb + g + 4 * i;
+                double x = acc[i];
+                if (x == 0.0) x = 0.0;  // -0 -> +0
+                if (m < nb) band_s[m] = x;
+            }
+        }
+    }
+}
 
 // Exact top-k of one row's candidates.  The eight segments written by the scoring waves
 // are each in ascending key order and cover ascending key ranges, so their concatenation
-// is sorted by key.  Thread t holds positions e * blockDim + t (e < 16) of it in registers,
-// so each load instruction reads consecutive entries, and the ascending output is a stable
-// compaction of the selected positions (per-element wave ballots and one block scan).
-__global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
+// is sorted by key.  Thread t holds the scores of positions e * blockDim + t (e < 32) in
+// registers (each load instruction reads consecutive entries); keys are read from the
+// list only for band entries and for the output, so a row takes 4 waves and ~34 KB of
+// LDS and every row of a 1,024-row block is resident at once.
+//
+//   1. k-th search: a value-linear histogram over [min, max] of the row's scores, then the
+//      exact range of the bin holding the k-th score; a second or third level narrows it
+//      while that bin holds many scores.  The range widened by 2 delta (and a rounding
+//      margin) is the band: scores above it are selected, scores below it are not.  Scores
+//      over many scales can leave a band too wide for select; the row then goes to the fold.
+//   2. band: the entries between are re-scored in the canonical fp64 order (one wave per
+//      16 entries) and ranked by (score desc, key asc) for the remaining slots.
+//   3. output: a stable compaction of the selected positions (per-element wave ballots and
+//      one block scan); the ascending key order of the list is the output order.
+__global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P) {
     const int r = blockIdx.x;
     const int mode = P.mode[r];
     if (mode == kModePad) return;
@@ -1377,180 +1556,271 @@ __global__ __launch_bounds__(1024) void select_kernel(IndexerArgs P) {
         if (threadIdx.x == 0) atomicAdd(&P.diag[kDiagRowsAll], 1ull);
         return;
     }
-    __shared__ SelectScratch S;
-    __shared__ int s_band_key[kSelBand];
-    __shared__ int s_band_pos[kSelBand];
-    __shared__ double s_band_s[kSelBand];
-    __shared__ uint32_t s_win[kSelChunk * 1024 / 32];
+    __shared__ SelectLds S;
+    const int nthr = (int)blockDim.x, tid = (int)threadIdx.x;
     // Eight key-ordered segments, or (more key parts) one appended list in no key order.
     const bool appended = P.parts > 2;
     const int seg = appended ? P.cap : P.cap / kSegs;
-    int cnt[kSegs], start[kSegs];
+    int start[kSegs];
     int total = 0;
     bool ok = !P.force_fallback;
 #pragma unroll
     for (int w = 0; w < kSegs; ++w) {
-        cnt[w] = appended && w > 0 ? 0 : P.count[(size_t)r * kSegs + w];
-        ok = ok && cnt[w] <= seg;
+        const int c = appended && w > 0 ? 0 : P.count[(size_t)r * kSegs + w];
+        ok = ok && c <= seg;
         start[w] = total;
-        total += cnt[w];
+        total += c;
     }
     int why = ok ? kDiagFbIncomplete : kDiagFbOverflow;  // the reason if the row falls back
     ok = ok && total >= k;
     const float tau_f = P.tau[r];
     const float delta = P.delta[r];
-    float v[kSelChunk];
-    int key[kSelChunk];
+    // The row's list: scores in words [0, cap), keys in [cap, 2 cap), read through 32-bit byte
+    // offsets from a uniform base (one address register per load instead of two).
+    const char* crow = reinterpret_cast<const char*>(P.cand + (size_t)r * 2 * P.cap);
+    const char* ckey = crow + (size_t)4 * P.cap;
+    auto word = [](const char* base, uint32_t i) { return *reinterpret_cast<const uint32_t*>(base + 4u * i); };
+    // Offset of the entry of candidate position j < total.
+    auto entry = [&](int j) -> uint32_t {
+        int w = 0, s0 = 0;
+#pragma unroll
+        for (int x = 1; x < kSegs; ++x)
+            if (j >= start[x]) {
+                w = x;
+                s0 = start[x];
+            }
+        return (uint32_t)(w * seg + (j - s0));
+    };
+    if (tid == 0) {
+        S.sh[4] = 0;
+        S.sh[5] = 0;
+    }
+    float v[kSelPer];
     int nv = 0;
-    const int nthr = (int)blockDim.x, tid = (int)threadIdx.x;
+    float vmin = INFINITY, vmax = -INFINITY;
     if (ok) {
+        // Branch-free loads (positions past the list re-read its last entry), so all of them
+        // are in flight before the first use.
 #pragma unroll
-        for (int e = 0; e < kSelChunk; ++e) {
-            const int j = e * nthr + tid;
-            v[e] = -INFINITY;
-            key[e] = 0;
-            if (j < total) {
-                int w = 0, s0 = 0;
+        for (int e = 0; e < kSelPer; ++e) v[e] = __uint_as_float(word(crow, entry(min(e * nthr + tid, total - 1))));
 #pragma unroll
-                for (int x = 1; x < kSegs; ++x)
-                    if (j >= start[x]) {
-                        w = x;
-                        s0 = start[x];
-                    }
-                const uint2 c = P.cand[(size_t)r * P.cap + (size_t)w * seg + (j - s0)];
-                v[e] = __uint_as_float(c.x) + 0.0f;
-                key[e] = (int)c.y;
+        for (int e = 0; e < kSelPer; ++e) {
+            const bool in = e * nthr + tid < total;
+            v[e] = in ? v[e] + 0.0f : -INFINITY;
+            if (in) {
+                vmin = fminf(vmin, v[e]);
+                vmax = fmaxf(vmax, v[e]);
             }
         }
-        nv = total > tid ? min((total - tid + nthr - 1) / nthr, kSelChunk) : 0;
+        nv = total > tid ? min((total - tid + nthr - 1) / nthr, kSelPer) : 0;
     }
-    float kth = 0.f;
-    bool stuck = false;
-    if (ok) kth = block_kth_binned<false>(RegSrc<kSelChunk>{v, nv}, k, S, &stuck);
-    if (stuck) {
-        ok = false;
-        why = kDiagFbKth;
-    }
-    const double lo = (double)kth - 2.0 * (double)delta;
-    const double hi = (double)kth + 2.0 * (double)delta;
-    if (ok && tau_f != -INFINITY && lo < (double)tau_f) ok = false;  // candidate set not provably complete
-    int nb_row = 0;
+    // 1. The band [lo, hi] around the k-th score.  [blo, bhi] holds the k-th score and
+    // `above` scores lie above bhi.  A level bins the scores in [blo, bhi]; if the bin b
+    // holding the k-th score is small (or three levels are done), the k-th score lies
+    // within b's edges, up to the rounding of the bin arithmetic (margin), else the next
+    // level narrows [blo, bhi] to the exact range of bin b (bins are monotonic in the score,
+    // so that range holds exactly bin b's scores).
+    double lo = 0.0, hi = 0.0;
     if (ok) {
-        if (threadIdx.x == 0) {
-            S.sh[4] = 0;
-            S.sh[5] = 0;
+        block_minmax(vmin, vmax, S);
+        float blo = vmin, bhi = vmax;
+        double elo = vmin, ehi = vmax;  // the k-th score lies in [elo, ehi] (up to margin)
+        int above = 0;
+        for (int level = 0; level < 3 && blo != bhi; ++level) {
+            const double scale = (double)kBins / ((double)bhi - (double)blo);
+            for (int i = tid; i < kBins; i += nthr) S.sel.hist[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < kSelPer; ++e)
+                if (e < nv && v[e] >= blo && v[e] <= bhi) atomicAdd(&S.sel.hist[bin_of(v[e], blo, scale)], 1);
+            __syncthreads();
+            block_find_crossing(S.sel.hist, kBins, k, above, S);
+            const int b = S.sh[0];  // >= 0: the k-th score lies in [blo, bhi]
+            above = S.sh[1];
+            const int nbin = S.sh[2];
+            if (nbin <= kOneLevel || level == 2) {
+                elo = (double)blo + (double)b / scale;
+                ehi = (double)blo + (double)(b + 1) / scale;
+                break;
+            }
+            float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < kSelPer; ++e)
+                if (e < nv && v[e] >= blo && v[e] <= bhi && bin_of(v[e], blo, scale) == b) {
+                    mn = fminf(mn, v[e]);
+                    mx = fmaxf(mx, v[e]);
+                }
+            block_minmax(mn, mx, S);
+            blo = mn;
+            bhi = mx;
+            elo = mn;
+            ehi = mx;
         }
-        for (int i = threadIdx.x; i < kSelChunk * 1024 / 32; i += blockDim.x) s_win[i] = 0u;
-        __syncthreads();
+        const double d2 = 2.0 * (double)delta;
+        const double margin = (fabs(elo) + fabs(ehi) + 2.0 * d2) * 0x1p-40;
+        lo = elo - d2 - margin;
+        hi = ehi + d2 + margin;
+    }
+    if (ok && tau_f != -INFINITY && lo < (double)tau_f) ok = false;  // candidate set not provably complete
+    // 2. The band: collect, re-score, rank.
+    int nb_row = 0, n_in = 0;
+    if (ok) {
+        // Positions above the band get their bit of S.win now (one wave owns the 64 bits of an
+        // element's ballot); band winners are added after the re-score.  The scores are not
+        // needed after this pass.
         int n_above = 0;
 #pragma unroll
-        for (int e = 0; e < kSelChunk; ++e) {
+        for (int e = 0; e < kSelPer; ++e) {
             const double sd = (double)v[e];
-            n_above += e < nv && sd > hi;
-            const bool in_band = e < nv && sd <= hi && sd >= lo;
-            const int b = wave_append(in_band, &S.sh[5]);
+            const uint64_t am = __ballot(e < nv && sd > hi);
+            if ((tid & 63) == 0) {
+                const int w0 = (e * nthr + (tid & ~63)) >> 5;
+                S.win[w0] = (uint32_t)am;
+                S.win[w0 + 1] = (uint32_t)(am >> 32);
+                n_above += __builtin_popcountll(am);
+            }
+            const int b = wave_append(e < nv && sd <= hi && sd >= lo, &S.sh[5]);
             if (b >= 0 && b < kSelBand) {
-                s_band_key[b] = key[e];
-                s_band_pos[b] = e * nthr + tid;
-                s_band_s[b] = sd;
+                S.band.pos[b] = e * nthr + tid;
+                S.band.s[b] = sd;
             }
         }
-        for (int o = 32; o > 0; o >>= 1) n_above += __shfl_xor(n_above, o);
-        if ((threadIdx.x & 63) == 0) atomicAdd(&S.sh[4], n_above);
+        // The row's query, weights and head statistics for the re-score.
+        if (delta > 0.f) {
+            const u16x8* qg = reinterpret_cast<const u16x8*>(ref.q);
+            for (int i = tid; i < kIdxHeads * kIdxDim / 8; i += nthr) S.band.q[i] = qg[i];
+            if (tid < kIdxHeads) {
+                S.band.w[tid] = ref.w[tid];
+                S.band.qs[tid] = P.qstat[(size_t)r * kIdxHeads + tid];
+            }
+        }
+        if ((tid & 63) == 0) atomicAdd(&S.sh[4], n_above);
         __syncthreads();
-        const int n_in = S.sh[4];
+        n_in = S.sh[4];
         const int nb = S.sh[5];
-        __syncthreads();
         ok = nb <= kSelBand && n_in < k && n_in + nb >= k;
         why = kDiagFbBand;
         nb_row = nb;
         if (ok) {
-            if (delta > 0.f && nb > 0)
-                band_rescore(nb, s_band_key, s_band_s, ref.q, ref.w, P.qstat + (size_t)r * kIdxHeads, ref.keys, S);
-            band_mark_winners(nb, k - n_in, s_band_key, s_band_s, s_band_pos, s_win);
+            // The band entries' keys, all loads in flight at once.
+            for (int x = tid; x < nb; x += nthr) S.band.key[x] = (int)word(ckey, entry(S.band.pos[x]));
             __syncthreads();
-            // Selected = above the band, or a band winner.
-            if (!appended) {
-                // Stable compaction: the candidate list is in key order, position e * blockDim + t
-                // for element e of thread t, so the output offset of (e, t) counts the selected
-                // positions of the earlier elements and of the earlier threads in element e.
-                const int nw = nthr >> 6, wv = tid >> 6;
-                uint64_t m[kSelChunk];
+            if (delta > 0.f && nb > 0)
+                band_rescore_waves(nb, S.band.key, S.band.s, S.band.q, S.band.w, S.band.qs, ref.q, ref.keys);
+            __syncthreads();
+            // Entry x wins if fewer than k - n_in band entries beat it (branch-free compares
+            // over batches of 8 entries, so the LDS reads of a batch are in flight together).
+            const int need = k - n_in;
+            for (int x = tid; x < nb; x += nthr) {
+                const double sx = S.band.s[x];
+                const int ix = S.band.key[x];
+                int beat = 0;
+                for (int y0 = 0; y0 < nb; y0 += 8) {
+                    double sy[8];
+                    int ky[8];
 #pragma unroll
-                for (int e = 0; e < kSelChunk; ++e) {
-                    const int j = e * nthr + tid;
-                    m[e] = __ballot(e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u)));
-                    if ((tid & 63) == 0) S.out[e * nw + wv] = __builtin_popcountll(m[e]);
-                }
-                __syncthreads();
-                const int ce = tid < kSelChunk * nw ? S.out[tid] : 0;
-                const int pre = block_incl_scan(ce, S) - ce;
-                if (tid < kSelChunk * nw) S.out[kSelChunk * 16 + tid] = pre;
-                __syncthreads();
-#pragma unroll
-                for (int e = 0; e < kSelChunk; ++e) {
-                    if ((m[e] >> (tid & 63)) & 1u) {
-                        const int o = S.out[kSelChunk * 16 + e * nw + wv] + mbcnt64(m[e]);
-                        if (o < k) out_row[o] = key[e];
+                    for (int u = 0; u < 8; ++u) {
+                        const int y = min(y0 + u, nb - 1);
+                        sy[u] = S.band.s[y];
+                        ky[u] = S.band.key[y];
                     }
-                }
-            } else if (nt <= kSelBitmapKeys) {
-                // Appended list (no key order), causal keys within the bitmap: mark the
-                // selected keys, then each thread emits its words' keys at its scanned offset.
-                uint32_t* bm = reinterpret_cast<uint32_t*>(&S.term[0][0]);
-                const int nw = (int)((nt + 31) >> 5);
-                for (int i = threadIdx.x; i < nw; i += blockDim.x) bm[i] = 0u;
-                __syncthreads();
 #pragma unroll
-                for (int e = 0; e < kSelChunk; ++e) {
-                    const int j = e * nthr + tid;
-                    if (e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u)))
-                        atomicOr(&bm[key[e] >> 5], 1u << (key[e] & 31));
+                    for (int u = 0; u < 8; ++u)
+                        beat += (int)((y0 + u < nb) & ((sy[u] > sx) | ((sy[u] == sx) & (ky[u] < ix))));
                 }
-                __syncthreads();
-                const int per = (nw + (int)blockDim.x - 1) / (int)blockDim.x;
-                const int w0 = (int)threadIdx.x * per, w1 = min(nw, w0 + per);
-                int c = 0;
-                for (int i = w0; i < w1; ++i) c += __builtin_popcount(bm[i]);
-                int o = block_incl_scan(c, S) - c;
-                for (int i = w0; i < w1; ++i) {
-                    uint32_t b = bm[i];
-                    while (b) {
-                        const int bit = __builtin_ctz(b);
-                        b &= b - 1u;
-                        if (o < k) out_row[o] = i * 32 + bit;
-                        ++o;
-                    }
-                }
-            } else {
-                // Appended list over a larger key range: gather the selection, then sort it.
-                int c = 0;
-#pragma unroll
-                for (int e = 0; e < kSelChunk; ++e) {
-                    const int j = e * nthr + tid;
-                    c += e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u));
-                }
-                int o = block_incl_scan(c, S) - c;
-#pragma unroll
-                for (int e = 0; e < kSelChunk; ++e) {
-                    const int j = e * nthr + tid;
-                    if (e < nv && ((double)v[e] > hi || ((s_win[j >> 5] >> (j & 31)) & 1u))) {
-                        if (o < k) S.out[o] = key[e];
-                        ++o;
-                    }
-                }
-                __syncthreads();
-                write_sorted_output(S.out, k, out_row);
+                if (beat < need) atomicOr(&S.win[S.band.pos[x] >> 5], 1u << (S.band.pos[x] & 31));
             }
+            __syncthreads();
         }
     }
-    if (!ok && threadIdx.x == 0) {
+    // 3. Output: selected = above the band, or a band winner.
+    if (ok) {
+        // Bit e: position e * blockDim + tid is selected (all 32 words read at once).
+        uint32_t selmask = 0u;
+        {
+            uint32_t wd[kSelPer];
+#pragma unroll
+            for (int e = 0; e < kSelPer; ++e) wd[e] = S.win[(e * nthr + tid) >> 5];
+#pragma unroll
+            for (int e = 0; e < kSelPer; ++e) selmask |= ((wd[e] >> ((e * nthr + tid) & 31)) & 1u) << e;
+        }
+        auto selected = [&](int e) { return ((selmask >> e) & 1u) != 0u; };
+        if (!appended) {
+            // Stable compaction: position e * blockDim + t comes after every position of the
+            // earlier elements and of the earlier threads of element e.
+            const int nw = nthr >> 6, wv = tid >> 6;
+#pragma unroll
+            for (int e = 0; e < kSelPer; ++e) {
+                const uint64_t m = __ballot(selected(e));
+                if ((tid & 63) == 0) S.cmp.cnt[e * nw + wv] = __builtin_popcountll(m);
+            }
+            __syncthreads();
+            const int ce = tid < kSelPer * nw ? S.cmp.cnt[tid] : 0;
+            const int pre = block_incl_scan(ce, S) - ce;
+            if (tid < kSelPer * nw) S.cmp.pre[tid] = pre;
+            __syncthreads();
+            int key[kSelPer];  // branch-free loads, as for the scores
+#pragma unroll
+            for (int e = 0; e < kSelPer; ++e) key[e] = (int)word(ckey, entry(min(e * nthr + tid, total - 1)));
+#pragma unroll
+            for (int e = 0; e < kSelPer; ++e) {
+                const bool sel = selected(e);
+                const uint64_t m = __ballot(sel);
+                if (sel) {
+                    const int o = S.cmp.pre[e * nw + wv] + mbcnt64(m);
+                    if (o < k) out_row[o] = key[e];
+                }
+            }
+        } else if (nt <= kSelBitmapKeys) {
+            // Appended list (no key order), causal keys within the bitmap: mark the selected
+            // keys, then each thread emits its words' keys at its scanned offset.
+            const int nw = (int)((nt + 31) >> 5);
+            for (int i = tid; i < nw; i += nthr) S.bitmap[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < kSelPer; ++e)
+                if (selected(e)) {
+                    const int key = (int)word(ckey, entry(e * nthr + tid));
+                    atomicOr(&S.bitmap[key >> 5], 1u << (key & 31));
+                }
+            __syncthreads();
+            const int per = (nw + nthr - 1) / nthr;
+            const int w0 = tid * per, w1 = min(nw, w0 + per);
+            int c = 0;
+            for (int i = w0; i < w1; ++i) c += __builtin_popcount(S.bitmap[i]);
+            int o = block_incl_scan(c, S) - c;
+            for (int i = w0; i < w1; ++i) {
+                uint32_t bits = S.bitmap[i];
+                while (bits) {
+                    const int bit = __builtin_ctz(bits);
+                    bits &= bits - 1u;
+                    if (o < k) out_row[o] = i * 32 + bit;
+                    ++o;
+                }
+            }
+        } else {
+            // Appended list over a larger key range: gather the selection, then sort it.
+            int c = 0;
+#pragma unroll
+            for (int e = 0; e < kSelPer; ++e) c += selected(e);
+            int o = block_incl_scan(c, S) - c;
+#pragma unroll
+            for (int e = 0; e < kSelPer; ++e)
+                if (selected(e)) {
+                    if (o < k) S.out[o] = (int)word(ckey, entry(e * nthr + tid));
+                    ++o;
+                }
+            __syncthreads();
+            write_sorted_output(S.out, k, out_row);
+        }
+    }
+    if (!ok && tid == 0) {
         const int slot = atomicAdd(&P.fb_ctrl[0], 1);
         P.fb_list[slot] = r;
         atomicAdd(&P.diag[kDiagFallback], 1ull);
         atomicAdd(&P.diag[why], 1ull);
     }
-    if (ok && threadIdx.x == 0) {
+    if (ok && tid == 0) {
         atomicAdd(&P.diag[kDiagRows], 1ull);
         atomicAdd(&P.diag[kDiagCandSum], (unsigned long long)total);
         atomicMax(&P.diag[kDiagCandMax], (unsigned long long)total);
@@ -1782,7 +2052,7 @@ hipError_t launch_row_prep(const IndexerArgs& a, hipStream_t s) {
 hipError_t launch_select_fold(const IndexerArgs& a, hipStream_t s) {
     {
         ProfScope ps(s, kProfSelect);
-        select_kernel<<<a.Lb, a.cap / kSelChunk, 0, s>>>(a);
+        select_kernel<<<a.Lb, a.cap / kSelPer, 0, s>>>(a);
     }
     {
         ProfScope ps(s, kProfFold);
@@ -1805,10 +2075,10 @@ __global__ __launch_bounds__(256) void score_dump_kernel(IndexerArgs P, float* s
     const int seg = P.cap / kSegs;
     for (int w = 0; w < kSegs; ++w) {
         const int n = min(P.count[(size_t)r * kSegs + w], seg);
-        const uint2* e = P.cand + (size_t)r * P.cap + (size_t)w * seg;
+        const uint32_t* e = P.cand + (size_t)r * 2 * P.cap + (size_t)w * seg;
         for (int i = threadIdx.x; i < n; i += blockDim.x) {
-            const uint2 c = e[i];
-            if ((int64_t)c.y < n_cols) row[c.y] = __uint_as_float(c.x);
+            const uint32_t key = e[P.cap + i];
+            if ((int64_t)key < n_cols) row[key] = __uint_as_float(e[i]);
         }
     }
     if (threadIdx.x == 0 && delta_out) delta_out[r] = P.delta[r];

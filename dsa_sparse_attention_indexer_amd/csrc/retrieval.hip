@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kGatherThreads) void retrieval_gather_kernel(Retrie
     }
     if (tid == 0) A.count[(size_t)r * kCandSegs] = total;
     int off = s_sum[tid] - n_mine;
-    uint2* dst = A.cand + (size_t)r * A.cap;
+    uint32_t* dst = A.cand + (size_t)r * 2 * A.cap;
     for (int q = tid; q < R; q += kGatherThreads) {
         const size_t at = locate(q);
         const float4 v = A.seg_runs[at];
@@ -330,7 +330,11 @@ __global__ __launch_bounds__(kGatherThreads) void retrieval_gather_kernel(Retrie
         const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (passes(f[e], key + e)) dst[off++] = make_uint2(__float_as_uint(f[e]), (uint32_t)(key + e));
+            if (passes(f[e], key + e)) {
+                dst[off] = __float_as_uint(f[e]);
+                dst[A.cap + off] = (uint32_t)(key + e);
+                ++off;
+            }
     }
 }
 

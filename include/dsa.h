@@ -136,7 +136,6 @@ typedef struct {
     int64_t fallback_overflow;   /*   a candidate segment overflowed                    */
     int64_t fallback_incomplete; /*   the candidates could miss a top-k key             */
     int64_t fallback_band;       /*   the fp64 band outgrew the selection buffer        */
-    int64_t fallback_kth;        /*   value binning could not isolate the k-th score    */
     int64_t rows_failed;         /* rows no path finished (written as -1): 0 expected   */
     int64_t candidates;          /* candidates summed over `rows`                       */
     int64_t candidates_max;      /* most candidates of one of those rows                */

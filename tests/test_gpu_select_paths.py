@@ -4,8 +4,9 @@
   divide its 2,048 histogram bins (576 .. 960 threads); every bin must still be counted,
   so rows finish on the candidate path instead of falling back.
 - Scores spread over many scales (zeros, 2^-100, 2^-66, 2^-33, values near 1): value
-  binning cannot isolate the k-th score in three levels; select hands such rows to the
-  blocked fold, where the exact radix select finishes the search.
+  binning cannot isolate the k-th score in three levels.  Select still bounds it by the
+  narrowest bin's range and ranks that band exactly when it fits its buffer; otherwise the
+  row goes to the blocked fold, whose k-th search finishes with the exact radix select.
 
 The selection counters (dsa_indexer_topk_stats) show which path each row took.
 """
@@ -49,31 +50,33 @@ def multiscale_case(N, L, seed):
     return di.f32_to_bf16_bits(q), di.f32_to_bf16_bits(k), w
 
 
-def test_multiscale_scores_kth_not_isolated_in_select(dsa_gpu, oracle_mod):
-    """Every causal key is a candidate (N below the candidate capacity) and the fp64 band
-    (the zeros and the three tiny scores) would fit select's buffer, but value binning
-    cannot isolate the k-th score (0): select hands the rows to the fold, whose k-th search
-    finishes with the radix pass."""
+def test_multiscale_scores_in_select(dsa_gpu, oracle_mod):
+    """Every causal key is a candidate (N below the candidate capacity).  Three levels of
+    bins leave the k-th score (0) in a bin that still holds the zeros and 2^-100; widened by
+    2 delta, the band is the zeros and the three tiny scores (about 800 entries), which
+    select re-scores in fp64 (2^-100 takes the sequential evaluation) and ranks."""
     N, L, top_k = 1000, 8, 256
     q, k, w = multiscale_case(N, L, 1)
     got, st = run_with_stats(dsa_gpu, q, k, w, N - L, top_k)
     report(f"multiscale select: {st}")
     want = oracle_mod.topk(q, k, w, N - L, top_k)
     assert np.array_equal(got, want)
-    assert st["fallback_kth"] == L and st["kth_radix"] == L and st["rows_failed"] == 0
+    assert st["rows"] == L and st["rows_fallback"] == 0 and st["rows_failed"] == 0
+    assert st["band_max"] >= 790
 
 
 def test_multiscale_scores_radix_in_fold(dsa_gpu, oracle_mod):
-    """The same scores over 7,000 keys: the rows go to the blocked fold, whose 4,096-key blocks
-    each hold about 4,000 keys within the error bound of the k-th score (far more than
-    select's band buffer) and whose k-th searches need the radix pass."""
+    """The same scores over 7,000 keys: about 6,800 keys lie within the error bound of the k-th
+    score, far more than select's band buffer, so the rows go to the blocked fold, whose k-th
+    searches need the radix pass."""
     N, L, top_k = 7000, 8, 2048
     q, k, w = multiscale_case(N, L, 2)
     got, st = run_with_stats(dsa_gpu, q, k, w, N - L, top_k)
     report(f"multiscale fold: {st}")
     want = oracle_mod.topk(q, k, w, N - L, top_k)
     assert np.array_equal(got, want)
-    assert st["rows_fallback"] == L and st["kth_radix"] == L and st["rows_failed"] == 0
+    assert st["rows_fallback"] == L and st["fallback_band"] == L and st["kth_radix"] == L
+    assert st["rows_failed"] == 0
 
 
 @pytest.mark.parametrize("top_k", [2049, 3000, 3840])
