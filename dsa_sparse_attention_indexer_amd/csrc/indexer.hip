@@ -554,15 +554,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
     int cnt[kRowsPerWave] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (n_keys > 0) {
         bf16x8 a[kRowsPerWave][8];
+        // All 64 loads are issued before the first is pinned to its AGPRs (pinning each right
+        // after its load made every load wait for the previous one).
 #pragma unroll
         for (int j = 0; j < kRowsPerWave; ++j) {
             const u16x8* qp = reinterpret_cast<const u16x8*>(qrow[j] + (size_t)col * kIdxDim + hf * 64);
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                a[j][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
-                asm volatile("" : "+a"(a[j][kk]));  // keep the query fragments in AGPRs
-            }
+            for (int kk = 0; kk < 8; ++kk) a[j][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
         }
+#pragma unroll
+        for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(a[j][kk]));  // keep the query fragments in AGPRs
         // Segment s covers the contiguous tile range [s*tps, (s+1)*tps).
         const int n_tiles = (int)((n_keys + kKeyTile - 1) / kKeyTile);
         const int tps = (n_tiles + n_segs - 1) / n_segs;
@@ -1121,13 +1124,26 @@ __device__ float rank_floor_256(const float* __restrict__ vals, int n, int rk, S
     constexpr int kPer = 64;
     uint32_t key[kPer];
     uint32_t kmin = 0xffffffffu, kmax = 0u;
+    // Chunks of 16 values per thread, each chunk's loads branch-free (clamped index) so that
+    // they are in flight together; chunks past n are skipped (a uniform test).
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int j = (int)threadIdx.x + i * 256;
-        key[i] = j < n ? order_key(vals[j]) : 0u;
-        if (j < n) {
-            kmin = min(kmin, key[i]);
-            kmax = max(kmax, key[i]);
+    for (int c0 = 0; c0 < kPer; c0 += 16) {
+        if (c0 * 256 < n) {
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = vals[min((int)threadIdx.x + (c0 + i) * 256, n - 1)];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const bool in = (int)threadIdx.x + (c0 + i) * 256 < n;
+                key[c0 + i] = in ? order_key(x[i]) : 0u;
+                if (in) {
+                    kmin = min(kmin, key[c0 + i]);
+                    kmax = max(kmax, key[c0 + i]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) key[c0 + i] = 0u;
         }
     }
     for (int o = 32; o > 0; o >>= 1) {
@@ -1239,8 +1255,9 @@ __global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P
         const u16x8* qp = reinterpret_cast<const u16x8*>(ref.q + (size_t)h * kIdxDim + part * 16);
         double l1 = 0.0, l2 = 0.0;
         int em = INT_MAX;
+        const u16x8 q2[2] = {qp[0], qp[1]};
         for (int c = 0; c < 2; ++c) {
-            const u16x8 v = qp[c];
+            const u16x8 v = q2[c];
             for (int j = 0; j < 8; ++j) {
                 const double x = (double)bf16_bits_to_float(v[j]);
                 l1 += fabs(x);
@@ -1266,13 +1283,15 @@ __global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P
     if (threadIdx.x < 64) {
         unsigned kn = 0u, ki = 0u;
         int ke = INT_MAX;
+        KeyStats e[kStatSlots / 64];
 #pragma unroll
-        for (int u = 0; u < kStatSlots / 64; ++u) {  // loads issued together
-            const int i = (int)threadIdx.x + 64 * u;
-            const KeyStats e = i < P.n_kstats ? P.kstats[i] : KeyStats{0u, 0u, INT_MAX, 0};
-            kn = max(kn, e.knorm_bits);
-            ki = max(ki, e.kinf_bits);
-            ke = min(ke, e.kexp_min);
+        for (int u = 0; u < kStatSlots / 64; ++u)  // branch-free: the loads are in flight together
+            e[u] = P.kstats[min((int)threadIdx.x + 64 * u, P.n_kstats - 1)];
+#pragma unroll
+        for (int u = 0; u < kStatSlots / 64; ++u) {
+            kn = max(kn, e[u].knorm_bits);
+            ki = max(ki, e[u].kinf_bits);
+            ke = min(ke, e[u].kexp_min);
         }
         for (int o = 32; o > 0; o >>= 1) {
             kn = max(kn, (unsigned)__shfl_xor((int)kn, o));
@@ -1745,6 +1764,9 @@ __global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P
             for (int e = 0; e < kSelPer; ++e) selmask |= ((wd[e] >> ((e * nthr + tid) & 31)) & 1u) << e;
         }
         auto selected = [&](int e) { return ((selmask >> e) & 1u) != 0u; };
+        int key[kSelPer];  // branch-free loads, as for the scores
+#pragma unroll
+        for (int e = 0; e < kSelPer; ++e) key[e] = (int)word(ckey, entry(min(e * nthr + tid, total - 1)));
         if (!appended) {
             // Stable compaction: position e * blockDim + t comes after every position of the
             // earlier elements and of the earlier threads of element e.
@@ -1759,9 +1781,6 @@ __global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P
             const int pre = block_incl_scan(ce, S) - ce;
             if (tid < kSelPer * nw) S.cmp.pre[tid] = pre;
             __syncthreads();
-            int key[kSelPer];  // branch-free loads, as for the scores
-#pragma unroll
-            for (int e = 0; e < kSelPer; ++e) key[e] = (int)word(ckey, entry(min(e * nthr + tid, total - 1)));
 #pragma unroll
             for (int e = 0; e < kSelPer; ++e) {
                 const bool sel = selected(e);
@@ -1779,10 +1798,7 @@ __global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P
             __syncthreads();
 #pragma unroll
             for (int e = 0; e < kSelPer; ++e)
-                if (selected(e)) {
-                    const int key = (int)word(ckey, entry(e * nthr + tid));
-                    atomicOr(&S.bitmap[key >> 5], 1u << (key & 31));
-                }
+                if (selected(e)) atomicOr(&S.bitmap[key[e] >> 5], 1u << (key[e] & 31));
             __syncthreads();
             const int per = (nw + nthr - 1) / nthr;
             const int w0 = tid * per, w1 = min(nw, w0 + per);
@@ -1807,7 +1823,7 @@ __global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P
 #pragma unroll
             for (int e = 0; e < kSelPer; ++e)
                 if (selected(e)) {
-                    if (o < k) S.out[o] = (int)word(ckey, entry(e * nthr + tid));
+                    if (o < k) S.out[o] = key[e];
                     ++o;
                 }
             __syncthreads();
