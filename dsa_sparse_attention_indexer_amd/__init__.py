@@ -35,7 +35,8 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTED = ["dsa_indexer_topk_workspace_bytes", "dsa_indexer_topk", "dsa_causal_mask_topk",
             "dsa_sparse_prefill", "dsa_sparse_prefill_packed", "dsa_sparse_decode_workspace_bytes",
             "dsa_sparse_decode",
-            "dsa_indexer_topk_noalloc", "dsa_indexer_topk_stats", "dsa_indexer_scores_workspace_bytes", "dsa_indexer_scores",
+            "dsa_indexer_topk_noalloc", "dsa_indexer_key_cache_bytes", "dsa_indexer_key_cache_append",
+            "dsa_indexer_topk_cached_workspace_bytes", "dsa_indexer_topk_cached", "dsa_indexer_topk_stats", "dsa_indexer_scores_workspace_bytes", "dsa_indexer_scores",
             "dsa_indexer_topk_varlen_workspace_bytes", "dsa_indexer_topk_varlen",
             "dsa_sparse_prefill_varlen_workspace_bytes", "dsa_sparse_prefill_varlen",
             "dsa_retrieval_topk_workspace_bytes", "dsa_retrieval_topk",
@@ -75,6 +76,14 @@ def load_library(path: str | None = None):
     lib.dsa_indexer_topk_workspace_bytes.argtypes = [i64, i64, i32, i32]
     lib.dsa_indexer_topk.restype = ctypes.c_int
     lib.dsa_indexer_topk.argtypes = [P, P, P, i64, i64, i32, i32, i64, i32, i32, P, P, sz, P]
+    lib.dsa_indexer_key_cache_bytes.restype = sz
+    lib.dsa_indexer_key_cache_bytes.argtypes = [i64]
+    lib.dsa_indexer_key_cache_append.restype = ctypes.c_int
+    lib.dsa_indexer_key_cache_append.argtypes = [P, i64, i64, P, sz, P]
+    lib.dsa_indexer_topk_cached_workspace_bytes.restype = sz
+    lib.dsa_indexer_topk_cached_workspace_bytes.argtypes = [i64, i64, i32, i32]
+    lib.dsa_indexer_topk_cached.restype = ctypes.c_int
+    lib.dsa_indexer_topk_cached.argtypes = [P, P, P, i64, i64, i32, i32, i64, i32, i32, P, P, sz, i64, P, sz, P]
     lib.dsa_indexer_topk_noalloc.restype = ctypes.c_int
     lib.dsa_indexer_topk_noalloc.argtypes = [P, P, P, i64, i64, i32, i32, i64, i32, i32, P, P]
     lib.dsa_indexer_topk_stats.restype = ctypes.c_int
@@ -243,6 +252,65 @@ def indexer_scores(q_idx, k_idx, w, q_pos0: int, stream=None):
                                   scores.data_ptr(), delta.data_ptr(), ws.data_ptr(), ws.numel(),
                                   _stream_ptr(q_idx, stream)))
     return scores, delta
+
+
+class KeyCache:
+    """An append-only indexer key cache on a GPU (dsa_indexer_key_cache_*): holds the tiled
+    layout and error-bound statistics of up to `capacity` keys."""
+
+    def __init__(self, capacity: int, device="cuda:0"):
+        import torch
+
+        lib = load_library()
+        n = int(lib.dsa_indexer_key_cache_bytes(capacity))
+        if n == 0:
+            raise ValueError(f"bad key cache capacity {capacity}")
+        self.capacity = capacity
+        self.buffer = torch.empty(n, dtype=torch.uint8, device=device)
+        self.n = 0
+
+    def append(self, k_idx, n_new: int | None = None, stream=None):
+        """Append rows self.n .. n_new-1 of k_idx (bf16 [>= n_new, 128]); n_new defaults to all rows."""
+        import torch
+
+        _req(k_idx, "k_idx", torch.bfloat16, 2)
+        n_new = k_idx.shape[0] if n_new is None else n_new
+        _check(load_library().dsa_indexer_key_cache_append(k_idx.data_ptr(), self.n, n_new, self.buffer.data_ptr(),
+                                                           self.buffer.numel(), _stream_ptr(k_idx, stream)))
+        self.n = n_new
+
+    def reset(self):
+        self.n = 0
+
+
+def cached_workspace_bytes(L: int, N: int, top_k: int, q_block: int = DEFAULT_Q_BLOCK) -> int:
+    return int(load_library().dsa_indexer_topk_cached_workspace_bytes(L, N, top_k, q_block))
+
+
+def indexer_topk_cached(q_idx, k_idx, w, q_pos0: int, top_k: int, cache: "KeyCache",
+                        q_block: int = DEFAULT_Q_BLOCK, out=None, workspace=None, stream=None):
+    """indexer_topk with the keys' layout and statistics from a KeyCache holding cache.n keys."""
+    import torch
+
+    lib = load_library()
+    _req(q_idx, "q_idx", torch.bfloat16, 3)
+    _req(k_idx, "k_idx", torch.bfloat16, 2)
+    _req(w, "w", torch.float32, 2)
+    L, nh, hd = q_idx.shape
+    N = k_idx.shape[0]
+    dev = q_idx.device
+    if out is None:
+        out = torch.empty((L, top_k), dtype=torch.int32, device=dev)
+    else:
+        _req(out, "out", torch.int32, 2)
+    if workspace is None:
+        need = lib.dsa_indexer_topk_cached_workspace_bytes(L, N, top_k, q_block)
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=dev)
+    _check(lib.dsa_indexer_topk_cached(q_idx.data_ptr(), k_idx.data_ptr(), w.data_ptr(), L, N, nh, hd, q_pos0,
+                                       top_k, q_block, out.data_ptr(), cache.buffer.data_ptr(),
+                                       cache.buffer.numel(), cache.n, workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), _stream_ptr(q_idx, stream)))
+    return out
 
 
 def causal_mask_topk(idx, q_pos0: int, stream=None):

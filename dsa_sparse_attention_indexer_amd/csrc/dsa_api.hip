@@ -295,24 +295,41 @@ size_t dsa_indexer_topk_workspace_bytes(int64_t L, int64_t N, int32_t top_k, int
     return dsa::IndexerLayout::make(rows, N, top_k).total;
 }
 
-dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, const float* w, int64_t L,
-                              int64_t N, int32_t n_heads, int32_t head_dim, int64_t q_pos0, int32_t top_k,
-                              int32_t q_block, int32_t* out_idx, void* workspace, size_t workspace_bytes,
-                              dsa_stream_t stream) {
+}  // extern "C"
+
+namespace {
+// dsa_indexer_topk, optionally over a key cache (key_cache != null): the cache's tiled copy
+// and statistics replace the call's own key statistics pass.
+dsa_status_t indexer_topk_impl(const uint16_t* q_idx, const uint16_t* k_idx, const float* w, int64_t L, int64_t N,
+                               int32_t n_heads, int32_t head_dim, int64_t q_pos0, int32_t top_k, int32_t q_block,
+                               int32_t* out_idx, void* workspace, size_t workspace_bytes, dsa_stream_t stream,
+                               const void* key_cache, size_t key_cache_bytes, int64_t cached_keys) {
     g_last_error[0] = 0;
     dsa_status_t st = check_indexer_args(q_idx, k_idx, w, L, N, n_heads, head_dim, q_pos0, top_k, q_block, out_idx);
     if (st != DSA_OK) return st;
     if (L == 0) return DSA_OK;
-    const size_t need = dsa_indexer_topk_workspace_bytes(L, N, top_k, q_block);
-    if (!workspace || workspace_bytes < need)
-        return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+    const bool cached = key_cache != nullptr;
+    // Keys any query of the chunk may see.
+    const int64_t last = q_pos0 + L - 1;
+    const int64_t n_keys = (last < N - 1 ? last : N - 1) + 1;
+    if (cached) {
+        if (!aligned(key_cache, 256)) return fail(DSA_ERR_INVALID_ARG, "key cache must be 256-byte aligned");
+        if (cached_keys < n_keys || cached_keys > N)
+            return fail(DSA_ERR_INVALID_ARG, "the key cache must hold the %lld keys the queries see (holds %lld, N=%lld)",
+                        (long long)n_keys, (long long)cached_keys, (long long)N);
+        if (key_cache_bytes < dsa::key_cache_bytes(n_keys))
+            return fail(DSA_ERR_INVALID_ARG, "key cache of %zu bytes is smaller than %zu", key_cache_bytes,
+                        dsa::key_cache_bytes(n_keys));
+    }
+    const int qb = resolve_q_block(q_block);
+    const int64_t rows = L < qb ? L : qb;
+    const dsa::IndexerLayout lay = dsa::IndexerLayout::make(rows, N, top_k, cached ? 0 : -1);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", lay.total, workspace_bytes,
                     workspace ? "" : ", null");
     if (!aligned(workspace, 256)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const int qb = resolve_q_block(q_block);
-    const int64_t rows = L < qb ? L : qb;
-    const dsa::IndexerLayout lay = dsa::IndexerLayout::make(rows, N, top_k);
     char* ws = static_cast<char*>(workspace);
 
     dsa::IndexerArgs a{};
@@ -324,7 +341,6 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
     a.fold_cap = lay.fold_cap;
     a.force_fallback = debug_force_fallback() ? 1 : 0;
     a.diag = reinterpret_cast<unsigned long long*>(ws + lay.off_diag);
-    a.kstats = reinterpret_cast<dsa::KeyStats*>(ws + lay.off_kstats);
     a.qstat = reinterpret_cast<dsa::QHeadStat*>(ws + lay.off_qstat);
     a.tau = reinterpret_cast<float*>(ws + lay.off_tau);
     a.delta = reinterpret_cast<float*>(ws + lay.off_delta);
@@ -339,16 +355,24 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
     a.fold_bi = reinterpret_cast<int*>(ws + lay.off_fold_bi);
     a.fold_bs = reinterpret_cast<double*>(ws + lay.off_fold_bs);
     a.fold_bf = reinterpret_cast<float*>(ws + lay.off_fold_bf);
-
-    // Key statistics and the tiled key copy, over every key any query of the chunk may see.
-    const int64_t last = q_pos0 + L - 1;
-    const int64_t n_keys = (last < N - 1 ? last : N - 1) + 1;
-    uint16_t* k_tile = reinterpret_cast<uint16_t*>(ws + lay.off_ktile);
-    a.k_tile = k_tile;
     a.n_ktiles = (n_keys + dsa::kKeyTileKeys - 1) / dsa::kKeyTileKeys;
-    a.n_kstats = dsa::key_stats_blocks(n_keys);
-    hipError_t e = dsa::launch_key_stats(k_idx, n_keys, a.kstats, k_tile, a.diag, s);
-    if (e != hipSuccess) return hip_fail(e, "key statistics launch");
+    if (cached) {
+        // The cache's statistics cover every key appended to it (a superset of the keys
+        // seen here, which only widens the band the exact re-score covers).
+        char* kc = const_cast<char*>(static_cast<const char*>(key_cache));
+        a.kstats = reinterpret_cast<dsa::KeyStats*>(kc);
+        a.n_kstats = 1;
+        a.k_tile = reinterpret_cast<uint16_t*>(kc + dsa::kKeyCacheHeader);
+        a.clear_diag = 1;
+    } else {
+        // Key statistics and the tiled key copy, over every key any query of the chunk may see.
+        a.kstats = reinterpret_cast<dsa::KeyStats*>(ws + lay.off_kstats);
+        a.n_kstats = dsa::key_stats_blocks(n_keys);
+        uint16_t* k_tile = reinterpret_cast<uint16_t*>(ws + lay.off_ktile);
+        a.k_tile = k_tile;
+        hipError_t e = dsa::launch_key_stats(k_idx, n_keys, a.kstats, k_tile, a.diag, s);
+        if (e != hipSuccess) return hip_fail(e, "key statistics launch");
+    }
 
     for (int64_t b0 = 0; b0 < L; b0 += qb) {
         const int64_t Lb = (L - b0) < qb ? (L - b0) : qb;
@@ -361,10 +385,70 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
         const int64_t n_last = (last_pos < N - 1 ? last_pos : N - 1) + 1;
         const bool need_sample = dsa::sample_size(n_last, top_k, lay.cap) > 0;
         a.parts = dsa::key_parts((Lb + dsa::kRowsPerGroup - 1) / dsa::kRowsPerGroup);
-        e = dsa::launch_indexer_block(a, need_sample, s, Lb <= dsa::kRowsPerGroup / 2);
+        hipError_t e = dsa::launch_indexer_block(a, need_sample, s, Lb <= dsa::kRowsPerGroup / 2);
         if (e != hipSuccess) return hip_fail(e, "indexer launch");
+        a.clear_diag = 0;  // later blocks add to the counters
     }
     return DSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, const float* w, int64_t L,
+                              int64_t N, int32_t n_heads, int32_t head_dim, int64_t q_pos0, int32_t top_k,
+                              int32_t q_block, int32_t* out_idx, void* workspace, size_t workspace_bytes,
+                              dsa_stream_t stream) {
+    return indexer_topk_impl(q_idx, k_idx, w, L, N, n_heads, head_dim, q_pos0, top_k, q_block, out_idx, workspace,
+                             workspace_bytes, stream, nullptr, 0, 0);
+}
+
+size_t dsa_indexer_key_cache_bytes(int64_t capacity) {
+    if (capacity <= 0 || capacity > (int64_t)INT32_MAX) return 0;
+    return dsa::key_cache_bytes(capacity);
+}
+
+dsa_status_t dsa_indexer_key_cache_append(const uint16_t* k_idx, int64_t n_old, int64_t n_new, void* key_cache,
+                                          size_t key_cache_bytes, dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    if (n_old < 0 || n_new < n_old || n_new > (int64_t)INT32_MAX)
+        return fail(DSA_ERR_INVALID_ARG, "need 0 <= n_old <= n_new <= 2^31-1 (n_old=%lld n_new=%lld)",
+                    (long long)n_old, (long long)n_new);
+    if (!key_cache) return fail(DSA_ERR_INVALID_ARG, "null key cache");
+    if (!aligned(key_cache, 256)) return fail(DSA_ERR_INVALID_ARG, "key cache must be 256-byte aligned");
+    if (key_cache_bytes < dsa::key_cache_bytes(n_new > 0 ? n_new : 1))
+        return fail(DSA_ERR_INVALID_ARG, "key cache of %zu bytes cannot hold %lld keys", key_cache_bytes,
+                    (long long)n_new);
+    if (n_new > n_old && !k_idx) return fail(DSA_ERR_INVALID_ARG, "null key pointer");
+    if (k_idx && !aligned(k_idx, 16)) return fail(DSA_ERR_INVALID_ARG, "k_idx must be 16-byte aligned");
+    if (n_new == n_old && n_old > 0) return DSA_OK;
+    char* kc = static_cast<char*>(key_cache);
+    hipError_t e = dsa::launch_key_cache_append(k_idx, n_old, n_new, reinterpret_cast<dsa::KeyStats*>(kc),
+                                                reinterpret_cast<uint16_t*>(kc + dsa::kKeyCacheHeader),
+                                                reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "key cache append launch");
+    return DSA_OK;
+}
+
+size_t dsa_indexer_topk_cached_workspace_bytes(int64_t L, int64_t N, int32_t top_k, int32_t q_block) {
+    if (L < 0 || N <= 0 || N > (int64_t)INT32_MAX || top_k < 1 || top_k > DSA_MAX_TOPK || q_block < 0) return 0;
+    int64_t qb = resolve_q_block(q_block);
+    int64_t rows = L < qb ? L : qb;
+    if (rows < 1) rows = 1;
+    return dsa::IndexerLayout::make(rows, N, top_k, 0).total;
+}
+
+dsa_status_t dsa_indexer_topk_cached(const uint16_t* q_idx, const uint16_t* k_idx, const float* w, int64_t L,
+                                     int64_t N, int32_t n_heads, int32_t head_dim, int64_t q_pos0, int32_t top_k,
+                                     int32_t q_block, int32_t* out_idx, const void* key_cache,
+                                     size_t key_cache_bytes, int64_t cached_keys, void* workspace,
+                                     size_t workspace_bytes, dsa_stream_t stream) {
+    if (!key_cache) {
+        g_last_error[0] = 0;
+        return fail(DSA_ERR_INVALID_ARG, "null key cache");
+    }
+    return indexer_topk_impl(q_idx, k_idx, w, L, N, n_heads, head_dim, q_pos0, top_k, q_block, out_idx, workspace,
+                             workspace_bytes, stream, key_cache, key_cache_bytes, cached_keys);
 }
 
 dsa_status_t dsa_indexer_topk_stats(const void* workspace, dsa_indexer_stats_t* out, dsa_stream_t stream) {

@@ -221,6 +221,7 @@ struct IndexerArgs {
     int sample_stride;
     int fold_cap;
     int force_fallback;     // debug: send every scored row through the fallback fold
+    int clear_diag;         // row_prep clears diag (the call's first block, when key_stats did not run)
     // Key parts per row group.  2 (the key halves, XCD-mapped): the 8 candidate segments of
     // a row are written in key order by the 2 x 4 scoring waves.  More parts (few row
     // groups): every wave of every part appends to the row's single list through an atomic
@@ -270,6 +271,15 @@ hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks,
 // The same over a batch: seqs[0 .. n_seqs) (device), n_tiles tiles in all.
 hipError_t launch_key_stats_batch(const uint16_t* k_idx, const SeqKeys* seqs, int n_seqs, int64_t n_tiles,
                                   KeyStats* ks, uint16_t* k_tile, unsigned long long* diag, hipStream_t s);
+// Appends keys [n_old, n_new) of k_idx to a key cache: their tiled copy (the tile holding key
+// n_old is redone whole) and the running statistics in *stats (reset first when n_old == 0).
+hipError_t launch_key_cache_append(const uint16_t* k_idx, int64_t n_old, int64_t n_new, KeyStats* stats,
+                                   uint16_t* k_tile, hipStream_t s);
+
+// An append-only key cache: a 256-byte header (the KeyStats of every appended key) and the
+// tiled copy of capacity keys.
+constexpr size_t kKeyCacheHeader = 256;
+inline size_t key_cache_bytes(int64_t capacity) { return kKeyCacheHeader + key_tile_bytes(capacity); }
 // sparse_rows: most row groups hold few query rows (decode, short chunks, batches of single
 // queries): the scoring skips the MFMAs of row pairs without a live row.
 hipError_t launch_indexer_block(const IndexerArgs& a, bool need_sample, hipStream_t s, bool sparse_rows = false);

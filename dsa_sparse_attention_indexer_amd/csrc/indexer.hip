@@ -141,21 +141,23 @@ static_assert(kKeyTileKeys == kKeyTile, "scoring tiles and the tiled key copy di
 constexpr int kStatsThreads = 256;
 constexpr int kStatsRowPad = 17;  // LDS row stride in 16-byte chunks (16 + 1 against bank conflicts)
 // seqs == null: one sequence of n_keys keys.  Otherwise tile t belongs to the sequence whose
-// tile range holds it, and its keys are that sequence's.
+// tile range holds it, and its keys are that sequence's.  Tiles [t_begin, n_tiles) are done.
+// merge: the statistics are folded into slots[0] with atomics (an append-only key cache)
+// instead of one slot per block.
 __global__ __launch_bounds__(kStatsThreads) void key_stats_kernel(const uint16_t* __restrict__ k_idx,
                                                                   int64_t n_keys, const SeqKeys* seqs,
-                                                                  int n_seqs, int64_t n_tiles,
+                                                                  int n_seqs, int64_t t_begin, int64_t n_tiles,
                                                                   KeyStats* slots,
                                                                   uint16_t* __restrict__ k_tile,
-                                                                  unsigned long long* diag) {
-    if (blockIdx.x == 0 && threadIdx.x < kDiagSlots) diag[threadIdx.x] = 0ull;
+                                                                  unsigned long long* diag, bool merge) {
+    if (diag && blockIdx.x == 0 && threadIdx.x < kDiagSlots) diag[threadIdx.x] = 0ull;
     __shared__ u16x8 s_t[kStatsThreads / kWave][kKeyTileKeys * kStatsRowPad];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     u16x8* st = s_t[wave];
     float nmax = 0.f, amax = 0.f;
     int emin = INT_MAX;
     const int64_t n_waves = (int64_t)gridDim.x * (kStatsThreads / kWave);
-    for (int64_t t = (int64_t)blockIdx.x * (kStatsThreads / kWave) + wave; t < n_tiles; t += n_waves) {
+    for (int64_t t = t_begin + (int64_t)blockIdx.x * (kStatsThreads / kWave) + wave; t < n_tiles; t += n_waves) {
         const uint16_t* src = k_idx;
         int64_t kn = n_keys, tl = t;
         if (seqs) {  // first sequence whose tiles end after t (wave-uniform search)
@@ -227,7 +229,13 @@ __global__ __launch_bounds__(kStatsThreads) void key_stats_kernel(const uint16_t
         }
         // 128 fp32 squares+adds and the sqrt: relative error < 2^-16; pad by 2^-14.
         const float up = nmax * (1.0f + 1.0f / 16384.0f);
-        slots[blockIdx.x] = KeyStats{__float_as_uint(up), __float_as_uint(amax), emin, 0};
+        if (merge) {  // non-negative floats order as their bit patterns
+            atomicMax(&slots[0].knorm_bits, __float_as_uint(up));
+            atomicMax(&slots[0].kinf_bits, __float_as_uint(amax));
+            atomicMin(&slots[0].kexp_min, emin);
+        } else {
+            slots[blockIdx.x] = KeyStats{__float_as_uint(up), __float_as_uint(amax), emin, 0};
+        }
     }
 }
 
@@ -1232,6 +1240,7 @@ __global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P
         P.fb_ctrl[0] = 0;
         P.fb_ctrl[1] = 0;
     }
+    if (P.clear_diag && r == 0 && threadIdx.x < kDiagSlots) P.diag[threadIdx.x] = 0ull;
     if (P.parts > 2 && threadIdx.x == 0) P.count[(size_t)r * kSegs] = 0;  // appended list counter
     if (!ref.valid) {  // padding row of a batched block: nothing to select
         if (threadIdx.x == 0) {
@@ -1381,7 +1390,8 @@ __device__ void write_sorted_output(int* sel, int k, int32_t* out_row) {
 }
 
 constexpr int kSelBand = 1024;     // band entries select re-scores (more: the row goes to the fold)
-constexpr int kSelPer = 32;        // candidates per thread: the block has cap / 32 threads
+constexpr int kSelPer = 32;        // candidates per thread (blocks of many rows): cap / 32 threads
+constexpr int kSelPerFew = 16;     // ... blocks of few rows: cap / 16 threads, shorter rows
 constexpr int kSelMaxThreads = 4 * kMaxTopK / kSelPer;  // cap <= 4 * kMaxTopK
 constexpr int kOneLevel = 256;     // a crossing bin this small ends the k-th search
 // Appended candidate lists are put back in key order through a bitmap of the causal keys,
@@ -1407,7 +1417,7 @@ struct SelectLds {
             QHeadStat qs[kIdxHeads];
         } band;
         struct {
-            int cnt[kSelPer * 8];  // selected entries per (element, wave), <= 8 waves
+            int cnt[kSelPer * 8];  // selected entries per (element, wave): kPer * waves <= 256
             int pre[kSelPer * 8];
         } cmp;
         uint32_t bitmap[kSelBitmapWords];
@@ -1561,7 +1571,9 @@ __device__ __forceinline__ void band_rescore_waves(int nb, const int* band_key, 
 //      16 entries) and ranked by (score desc, key asc) for the remaining slots.
 //   3. output: a stable compaction of the selected positions (per-element wave ballots and
 //      one block scan); the ascending key order of the list is the output order.
-__global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P) {
+template <int kPer>
+__global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerArgs P) {
+    static_assert(kPer == 16 || kPer == 32, "per-thread candidates");
     const int r = blockIdx.x;
     const int mode = P.mode[r];
     if (mode == kModePad) return;
@@ -1614,16 +1626,16 @@ __global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P
         S.sh[4] = 0;
         S.sh[5] = 0;
     }
-    float v[kSelPer];
+    float v[kPer];
     int nv = 0;
     float vmin = INFINITY, vmax = -INFINITY;
     if (ok) {
         // Branch-free loads (positions past the list re-read its last entry), so all of them
         // are in flight before the first use.
 #pragma unroll
-        for (int e = 0; e < kSelPer; ++e) v[e] = __uint_as_float(word(crow, entry(min(e * nthr + tid, total - 1))));
+        for (int e = 0; e < kPer; ++e) v[e] = __uint_as_float(word(crow, entry(min(e * nthr + tid, total - 1))));
 #pragma unroll
-        for (int e = 0; e < kSelPer; ++e) {
+        for (int e = 0; e < kPer; ++e) {
             const bool in = e * nthr + tid < total;
             v[e] = in ? v[e] + 0.0f : -INFINITY;
             if (in) {
@@ -1631,7 +1643,7 @@ __global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P
                 vmax = fmaxf(vmax, v[e]);
             }
         }
-        nv = total > tid ? min((total - tid + nthr - 1) / nthr, kSelPer) : 0;
+        nv = total > tid ? min((total - tid + nthr - 1) / nthr, kPer) : 0;
     }
     // 1. The band [lo, hi] around the k-th score.  [blo, bhi] holds the k-th score and
     // `above` scores lie above bhi.  A level bins the scores in [blo, bhi]; if the bin b
@@ -1650,7 +1662,7 @@ __global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P
             for (int i = tid; i < kBins; i += nthr) S.sel.hist[i] = 0;
             __syncthreads();
 #pragma unroll
-            for (int e = 0; e < kSelPer; ++e)
+            for (int e = 0; e < kPer; ++e)
                 if (e < nv && v[e] >= blo && v[e] <= bhi) atomicAdd(&S.sel.hist[bin_of(v[e], blo, scale)], 1);
             __syncthreads();
             block_find_crossing(S.sel.hist, kBins, k, above, S);
@@ -1664,7 +1676,7 @@ __global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P
             }
             float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < kSelPer; ++e)
+            for (int e = 0; e < kPer; ++e)
                 if (e < nv && v[e] >= blo && v[e] <= bhi && bin_of(v[e], blo, scale) == b) {
                     mn = fminf(mn, v[e]);
                     mx = fmaxf(mx, v[e]);
@@ -1689,7 +1701,7 @@ __global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P
         // needed after this pass.
         int n_above = 0;
 #pragma unroll
-        for (int e = 0; e < kSelPer; ++e) {
+        for (int e = 0; e < kPer; ++e) {
             const double sd = (double)v[e];
             const uint64_t am = __ballot(e < nv && sd > hi);
             if ((tid & 63) == 0) {
@@ -1757,32 +1769,32 @@ __global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P
         // Bit e: position e * blockDim + tid is selected (all 32 words read at once).
         uint32_t selmask = 0u;
         {
-            uint32_t wd[kSelPer];
+            uint32_t wd[kPer];
 #pragma unroll
-            for (int e = 0; e < kSelPer; ++e) wd[e] = S.win[(e * nthr + tid) >> 5];
+            for (int e = 0; e < kPer; ++e) wd[e] = S.win[(e * nthr + tid) >> 5];
 #pragma unroll
-            for (int e = 0; e < kSelPer; ++e) selmask |= ((wd[e] >> ((e * nthr + tid) & 31)) & 1u) << e;
+            for (int e = 0; e < kPer; ++e) selmask |= ((wd[e] >> ((e * nthr + tid) & 31)) & 1u) << e;
         }
         auto selected = [&](int e) { return ((selmask >> e) & 1u) != 0u; };
-        int key[kSelPer];  // branch-free loads, as for the scores
+        int key[kPer];  // branch-free loads, as for the scores
 #pragma unroll
-        for (int e = 0; e < kSelPer; ++e) key[e] = (int)word(ckey, entry(min(e * nthr + tid, total - 1)));
+        for (int e = 0; e < kPer; ++e) key[e] = (int)word(ckey, entry(min(e * nthr + tid, total - 1)));
         if (!appended) {
             // Stable compaction: position e * blockDim + t comes after every position of the
             // earlier elements and of the earlier threads of element e.
             const int nw = nthr >> 6, wv = tid >> 6;
 #pragma unroll
-            for (int e = 0; e < kSelPer; ++e) {
+            for (int e = 0; e < kPer; ++e) {
                 const uint64_t m = __ballot(selected(e));
                 if ((tid & 63) == 0) S.cmp.cnt[e * nw + wv] = __builtin_popcountll(m);
             }
             __syncthreads();
-            const int ce = tid < kSelPer * nw ? S.cmp.cnt[tid] : 0;
+            const int ce = tid < kPer * nw ? S.cmp.cnt[tid] : 0;
             const int pre = block_incl_scan(ce, S) - ce;
-            if (tid < kSelPer * nw) S.cmp.pre[tid] = pre;
+            if (tid < kPer * nw) S.cmp.pre[tid] = pre;
             __syncthreads();
 #pragma unroll
-            for (int e = 0; e < kSelPer; ++e) {
+            for (int e = 0; e < kPer; ++e) {
                 const bool sel = selected(e);
                 const uint64_t m = __ballot(sel);
                 if (sel) {
@@ -1797,7 +1809,7 @@ __global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P
             for (int i = tid; i < nw; i += nthr) S.bitmap[i] = 0u;
             __syncthreads();
 #pragma unroll
-            for (int e = 0; e < kSelPer; ++e)
+            for (int e = 0; e < kPer; ++e)
                 if (selected(e)) atomicOr(&S.bitmap[key[e] >> 5], 1u << (key[e] & 31));
             __syncthreads();
             const int per = (nw + nthr - 1) / nthr;
@@ -1818,10 +1830,10 @@ __global__ __launch_bounds__(kSelMaxThreads, 4) void select_kernel(IndexerArgs P
             // Appended list over a larger key range: gather the selection, then sort it.
             int c = 0;
 #pragma unroll
-            for (int e = 0; e < kSelPer; ++e) c += selected(e);
+            for (int e = 0; e < kPer; ++e) c += selected(e);
             int o = block_incl_scan(c, S) - c;
 #pragma unroll
-            for (int e = 0; e < kSelPer; ++e)
+            for (int e = 0; e < kPer; ++e)
                 if (selected(e)) {
                     if (o < k) S.out[o] = key[e];
                     ++o;
@@ -1999,8 +2011,9 @@ hipError_t launch_key_stats(const uint16_t* k_idx, int64_t n_keys, KeyStats* ks,
     ProfScope ps(s, kProfKeyStats);
     static_assert(kStatsThreads / kWave == 4 && kKeyTileKeys == 32, "key_stats_blocks assumes 4 waves of 32-key tiles");
     const int blocks = key_stats_blocks(n_keys);
-    key_stats_kernel<<<blocks, kStatsThreads, 0, s>>>(k_idx, n_keys, nullptr, 0,
-                                                     (n_keys + kKeyTileKeys - 1) / kKeyTileKeys, ks, k_tile, diag);
+    key_stats_kernel<<<blocks, kStatsThreads, 0, s>>>(k_idx, n_keys, nullptr, 0, 0,
+                                                     (n_keys + kKeyTileKeys - 1) / kKeyTileKeys, ks, k_tile, diag,
+                                                     false);
     return hipGetLastError();
 }
 
@@ -2008,7 +2021,27 @@ hipError_t launch_key_stats_batch(const uint16_t* k_idx, const SeqKeys* seqs, in
                                   KeyStats* ks, uint16_t* k_tile, unsigned long long* diag, hipStream_t s) {
     ProfScope ps(s, kProfKeyStats);
     const int blocks = key_stats_blocks(n_tiles * kKeyTileKeys);
-    key_stats_kernel<<<blocks, kStatsThreads, 0, s>>>(k_idx, 0, seqs, n_seqs, n_tiles, ks, k_tile, diag);
+    key_stats_kernel<<<blocks, kStatsThreads, 0, s>>>(k_idx, 0, seqs, n_seqs, 0, n_tiles, ks, k_tile, diag, false);
+    return hipGetLastError();
+}
+
+__global__ void key_cache_reset_kernel(KeyStats* stats) {
+    if (threadIdx.x == 0) *stats = KeyStats{0u, 0u, INT_MAX, 0};
+}
+
+hipError_t launch_key_cache_append(const uint16_t* k_idx, int64_t n_old, int64_t n_new, KeyStats* stats,
+                                   uint16_t* k_tile, hipStream_t s) {
+    ProfScope ps(s, kProfKeyStats);
+    if (n_old == 0) {
+        key_cache_reset_kernel<<<1, 64, 0, s>>>(stats);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // The tile holding key n_old is laid out again whole (its keys below n_old included).
+    const int64_t t0 = n_old / kKeyTileKeys, t1 = (n_new + kKeyTileKeys - 1) / kKeyTileKeys;
+    if (t1 <= t0) return hipSuccess;
+    const int blocks = key_stats_blocks((t1 - t0) * kKeyTileKeys);
+    key_stats_kernel<<<blocks, kStatsThreads, 0, s>>>(k_idx, n_new, nullptr, 0, t0, t1, stats, k_tile, nullptr, true);
     return hipGetLastError();
 }
 
@@ -2068,7 +2101,10 @@ hipError_t launch_row_prep(const IndexerArgs& a, hipStream_t s) {
 hipError_t launch_select_fold(const IndexerArgs& a, hipStream_t s) {
     {
         ProfScope ps(s, kProfSelect);
-        select_kernel<<<a.Lb, a.cap / kSelPer, 0, s>>>(a);
+        // Blocks of few rows (decode, short chunks) give each row twice the threads: with all
+        // rows resident anyway, a row's latency is the launch time.
+        if (a.Lb >= 512) select_kernel<kSelPer><<<a.Lb, a.cap / kSelPer, 0, s>>>(a);
+        else select_kernel<kSelPerFew><<<a.Lb, a.cap / kSelPerFew, 0, s>>>(a);
     }
     {
         ProfScope ps(s, kProfFold);

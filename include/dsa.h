@@ -99,6 +99,40 @@ dsa_status_t dsa_indexer_topk(const uint16_t* q_idx, const uint16_t* k_idx, cons
                               void* workspace, size_t workspace_bytes, dsa_stream_t stream);
 
 /*
+ * An append-only cache of the indexer keys in the layout the scoring kernel reads, for
+ * decode and chunked prefill over a growing cache ("GLM prefill now attends only to the
+ * keys its indexer picks", Evidence: decode continues after a sparse prefill).
+ * dsa_indexer_topk lays out all the keys its queries see on every call; a caller that keeps
+ * a key cache lays out only the keys appended since its last step.
+ *
+ *   dsa_indexer_key_cache_bytes(capacity): device bytes of a cache for up to capacity keys
+ *       (0 for capacity outside 1 .. 2^31-1).
+ *   dsa_indexer_key_cache_append(k_idx, n_old, n_new, cache, bytes, stream): keys n_old ..
+ *       n_new-1 of k_idx (bf16 [n_new][128], rows 0 .. n_old-1 unchanged since they were
+ *       appended) join the cache; n_old = 0 starts it afresh.  The cache also keeps the
+ *       error-bound statistics (largest key norm and element, lowest set bit) of every key
+ *       appended since the last restart.  cache: caller-owned device memory, 256-byte
+ *       aligned, at least dsa_indexer_key_cache_bytes(n_new) bytes; contents need no
+ *       initialisation before a restart.  Asynchronous on `stream`.
+ *   dsa_indexer_topk_cached(..., cache, bytes, cached_keys, workspace, ...): dsa_indexer_topk
+ *       (same arguments, results and errors) with the keys' layout and statistics taken from
+ *       the cache, which holds cached_keys keys (at least the min(N, q_pos0 + L) keys the
+ *       queries see, at most N; else DSA_ERR_INVALID_ARG).  k_idx is still read (the exact
+ *       re-score reads key rows).  Workspace: at least
+ *       dsa_indexer_topk_cached_workspace_bytes(L, N, top_k, q_block) bytes (no key copy).
+ * The indices equal dsa_indexer_topk's bit for bit.  A cache is used by one stream at a time.
+ */
+size_t dsa_indexer_key_cache_bytes(int64_t capacity);
+dsa_status_t dsa_indexer_key_cache_append(const uint16_t* k_idx, int64_t n_old, int64_t n_new, void* key_cache,
+                                          size_t key_cache_bytes, dsa_stream_t stream);
+size_t dsa_indexer_topk_cached_workspace_bytes(int64_t L, int64_t N, int32_t top_k, int32_t q_block);
+dsa_status_t dsa_indexer_topk_cached(const uint16_t* q_idx, const uint16_t* k_idx, const float* w, int64_t L,
+                                     int64_t N, int32_t n_heads, int32_t head_dim, int64_t q_pos0, int32_t top_k,
+                                     int32_t q_block, int32_t* out_idx, const void* key_cache,
+                                     size_t key_cache_bytes, int64_t cached_keys, void* workspace,
+                                     size_t workspace_bytes, dsa_stream_t stream);
+
+/*
  * dsa_indexer_topk without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  The scratch is a static device array of

@@ -339,3 +339,25 @@ def test_noalloc_rejects_before_touching_the_device(lib):
     assert b"static scratch" in lib.dsa_last_error()
     assert f(p, p, p, 4, 64, 16, 128, 60, 8, 0, p, None) == 2   # the indexer's own checks first
     assert f(None, None, None, 0, 64, 32, 128, 0, 8, 0, None, None) == 0  # L = 0: no-op
+
+
+def test_key_cache_rejects_bad_arguments(lib):
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.dsa_indexer_key_cache_bytes(0) == 0
+    n = lib.dsa_indexer_key_cache_bytes(100)
+    assert n >= 256 + 4 * 32 * 128 * 2  # header and four 32-key tiles
+    f = lib.dsa_indexer_key_cache_append
+    assert f(p, 5, 4, p, n, None) == 1            # n_new < n_old
+    assert f(p, 0, 10, None, n, None) == 1        # no cache
+    assert f(p, 0, 10, ctypes.c_void_p((1 << 20) + 64), n, None) == 1  # unaligned cache
+    assert f(p, 0, 200, p, n, None) == 1          # too small for 200 keys
+    assert f(None, 0, 10, p, n, None) == 1        # no keys to append
+    g = lib.dsa_indexer_topk_cached
+    ws = lib.dsa_indexer_topk_cached_workspace_bytes(4, 64, 8, 0)
+    assert 0 < ws < lib.dsa_indexer_topk_workspace_bytes(4, 64, 8, 0)  # no key copy in it
+    args = (p, p, p, 4, 64, 32, 128, 60, 8, 0, p)
+    assert g(*args, None, n, 64, p, ws, None) == 1          # no cache
+    assert g(*args, p, n, 63, p, ws, None) == 1             # cache holds fewer keys than the queries see
+    assert g(*args, p, n, 65, p, ws, None) == 1             # more keys than N
+    assert g(*args, p, 16, 64, p, ws, None) == 1            # cache buffer too small
+    assert g(*args, p, n, 64, p, 10, None) == 3             # workspace too small
