@@ -331,7 +331,8 @@ def sparse_prefill(q, kv, idx, q_pos0: int, scale: float, q_block: int = DEFAULT
     q bf16 [L, H, 576]; kv bf16 [N, >=576] (latent 0..511 | rope 512..575, the
     latent is also the value); idx int32 [L, top_k] (-1 and future keys skipped).
     pack=True gathers the union of neighbouring queries' rows once (same result up to
-    the rounding order of the softmax sums).
+    the rounding order of the softmax sums); on MI355X it is slower than the default at
+    every overlap measured (0.59x-0.97x).
     """
     import torch
 
