@@ -1402,6 +1402,10 @@ constexpr int kSelBitmapKeys = kSelBitmapWords * 32;  // 262,144 keys
 // select's shared memory.  The phases use the union in turn: the k-th search (sel), the
 // band (band), then the output compaction (cmp, bitmap or out).  Small enough (~34 KB) for
 // four rows per compute unit.
+// Per workgroup, 16 entries x (32 / waves) heads of re-score terms per wave; 512 doubles for
+// any wave count up to 16 (they sit in the union's room beside the bitmap).
+constexpr int kSelTermSlots = 512;
+
 struct SelectLds {
     union {
         struct {
@@ -1415,6 +1419,7 @@ struct SelectLds {
             u16x8 q[kIdxHeads * kIdxDim / 8];  // the row's query (re-score operands)
             float w[kIdxHeads];
             QHeadStat qs[kIdxHeads];
+            double tb[kSelTermSlots];  // head terms on their way to the entries' lanes
         } band;
         struct {
             int cnt[kSelPer * 8];  // selected entries per (element, wave): kPer * waves <= 256
@@ -1428,14 +1433,6 @@ struct SelectLds {
     int red_i[32];
     int sh[16];
 };
-
-// x of lane c - 1 of the lane's 16-lane row (lane 0 of a row gets 0).
-__device__ __forceinline__ double dpp_row_shr1(double x) {
-    const uint64_t u = (uint64_t)__double_as_longlong(x);
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x111, 0xf, 0xf, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x111, 0xf, 0xf, false);
-    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
-}
 
 // sum_i q_h[i] k[i] in fp64 with i ascending (bf16 x bf16 products are exact in fp64, so
 // each fma rounds as the canonical add does).
@@ -1456,17 +1453,23 @@ __device__ double canonical_dot(const uint16_t* __restrict__ q_h, const uint16_t
 // chain (16 keys x 16 heads x 4 dims per instruction) gives the head dot products when they
 // are provably exact in any order (the test of band_rescore); a (key, head) that fails it
 // takes the sequential evaluation in its lane.  The head terms fl(w_h max(d_h, +0)) are then
-// added in ascending h exactly as the canonical order does: lane c of a 16-lane row holds
-// head c of the half for four keys, and a chain of row shifts adds one head per step,
-// continuing from the first half's sum into the second.  No block barrier.
+// added in ascending h exactly as the canonical order does: after the MFMAs lane (g, c) holds
+// head c of the half for entries g, g+4, g+8, g+12; the terms are transposed through LDS so
+// that lane m < 16 holds entry m's, and that lane adds them one head at a time, continuing
+// from the first half's sum into the second.  No block barrier.
 __device__ __forceinline__ void band_rescore_waves(int nb, const int* band_key, double* band_s,
                                                    const u16x8* q_lds, const float* w_lds,
-                                                   const QHeadStat* qs_lds, const uint16_t* __restrict__ q_row,
+                                                   const QHeadStat* qs_lds, double* tb_lds,
+                                                   const uint16_t* __restrict__ q_row,
                                                    const uint16_t* __restrict__ k_idx) {
 #pragma clang fp contract(off)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
     const int g = lane >> 4, c = lane & 15;
     if (16 * wave >= nb) return;
+    // The head terms reach the lane that sums them through this wave's slice of tb_lds, hp
+    // heads at a time (16 x hp doubles; hp a power of two with nwaves * 16 * hp <= 512).
+    const int hp = nwaves <= 4 ? 8 : (nwaves <= 8 ? 4 : 2);
+    double* tb = tb_lds + wave * 16 * hp;
     // A operand of block mb: lane (g, c) supplies key mb + c, dimensions 32g .. 32g+31.
     auto load_keys = [&](int mb, u16x8 (&kv)[4]) {
         const int key = band_key[mb + c < nb ? mb + c : mb];
@@ -1490,7 +1493,7 @@ __device__ __forceinline__ void band_rescore_waves(int nb, const int* band_key, 
         kinf = fmaxf(kinf, __shfl_xor(kinf, 32));
         ke = min(ke, __shfl_xor(ke, 16));
         ke = min(ke, __shfl_xor(ke, 32));
-        double acc[4];  // ascending-h partial sums of entries mb + g + 4i, carried across the halves
+        double acc = 0.0;  // lanes 0-15: the ascending-h sum of entry mb + lane so far
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int head = 16 * half + c;
@@ -1529,28 +1532,35 @@ __device__ __forceinline__ void band_rescore_waves(int nb, const int* band_key, 
                     dh = canonical_dot(q_row + head * kIdxDim, k_idx + (size_t)band_key[mb + m] * kIdxDim);
                 t[i] = wh * (dh > 0.0 ? dh : 0.0);
             }
-            // After step h, lane h of the row holds the sum through head 16 * half + h.
+            // Lane m < 16 adds the terms of entry m in ascending head order: heads p0 .. p0+hp-1
+            // pass through LDS (entry-major, columns XOR-swizzled by the entry against bank
+            // conflicts), then the next hp.  A wave's LDS accesses complete in issue order, so
+            // the reads see the writes before them; the wave barriers keep the compiler from
+            // moving them across each other.
+            for (int p0 = 0; p0 < 16; p0 += hp) {
+                if (c >= p0 && c < p0 + hp) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const double carry = half ? __shfl(acc[i], 16 * g + 15) : 0.0;
-                acc[i] = half && c == 0 ? carry + t[i] : t[i];
-            }
-#pragma unroll
-            for (int step = 1; step < 16; ++step)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const double prev = dpp_row_shr1(acc[i]);
-                    if (c == step) acc[i] = prev + t[i];
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = g + 4 * i;
+                        tb[m * hp + ((c - p0) ^ (m & (hp - 1)))] = t[i];
+                    }
                 }
-        }
-        if (c == 15) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = mb + g + 4 * i;
-                double x = acc[i];
-                if (x == 0.0) x = 0.0;  // -0 -> +0
-                if (m < nb) band_s[m] = x;
+                __builtin_amdgcn_wave_barrier();
+                asm volatile("" ::: "memory");
+                if (lane < 16) {
+                    for (int j = 0; j < hp; ++j) {
+                        const double x = tb[lane * hp + (j ^ (lane & (hp - 1)))];
+                        acc = half == 0 && p0 == 0 && j == 0 ? x : acc + x;
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
+                asm volatile("" ::: "memory");
             }
+        }
+        if (lane < 16 && mb + lane < nb) {
+            double x = acc;
+            if (x == 0.0) x = 0.0;  // -0 -> +0
+            band_s[mb + lane] = x;
         }
     }
 }
@@ -1737,7 +1747,8 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
             for (int x = tid; x < nb; x += nthr) S.band.key[x] = (int)word(ckey, entry(S.band.pos[x]));
             __syncthreads();
             if (delta > 0.f && nb > 0)
-                band_rescore_waves(nb, S.band.key, S.band.s, S.band.q, S.band.w, S.band.qs, ref.q, ref.keys);
+                band_rescore_waves(nb, S.band.key, S.band.s, S.band.q, S.band.w, S.band.qs, S.band.tb, ref.q,
+                                   ref.keys);
             __syncthreads();
             // Entry x wins if fewer than k - n_in band entries beat it (branch-free compares
             // over batches of 8 entries, so the LDS reads of a batch are in flight together).
