@@ -1566,11 +1566,11 @@ __device__ __forceinline__ void band_rescore_waves(int nb, const int* band_key, 
 }
 
 // Exact top-k of one row's candidates.  The eight segments written by the scoring waves
-// are each in ascending key order and cover ascending key ranges, so their concatenation
-// is sorted by key.  Thread t holds the scores of positions e * blockDim + t (e < 32) in
-// registers (each load instruction reads consecutive entries); keys are read from the
-// list only for band entries and for the output, so a row takes 4 waves and ~34 KB of
-// LDS and every row of a 1,024-row block is resident at once.
+// are each in ascending key order and cover ascending key ranges, so the list's slots in
+// use, in slot order, are sorted by key.  Thread t holds the scores of slots e * blockDim
+// + t (e < 32; a "position" below) in registers (each load instruction reads consecutive
+// slots); keys are read from the list only for band entries and for the output, so a row
+// takes 4 waves and ~35 KB of LDS and every row of a 1,024-row block is resident at once.
 //
 //   1. k-th search: a value-linear histogram over [min, max] of the row's scores, then the
 //      exact range of the bin holding the k-th score; a second or third level narrows it
@@ -1602,58 +1602,61 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
     // Eight key-ordered segments, or (more key parts) one appended list in no key order.
     const bool appended = P.parts > 2;
     const int seg = appended ? P.cap : P.cap / kSegs;
-    int start[kSegs];
+    // The row's list: scores in words [0, cap), keys in [cap, 2 cap), read through 32-bit byte
+    // offsets from a uniform base (one address register per load instead of two).  Thread t's
+    // element e is slot e * blockDim + t of the list: segment w holds slots [w seg, w seg +
+    // cnt[w]), so element e lies in segment e / (kPer / 8) and the slots in use are a mask;
+    // slot order is key order (segments cover ascending key ranges), gaps aside.
+    const char* crow = reinterpret_cast<const char*>(P.cand + (size_t)r * 2 * P.cap);
+    const char* ckey = crow + (size_t)4 * P.cap;
+    auto word = [](const char* base, uint32_t i) { return *reinterpret_cast<const uint32_t*>(base + 4u * i); };
+    // Loads of every slot first, branch-free (unused slots hold stale words, masked below) and
+    // guarded only by a kernel argument: they are in flight before the count loads are issued,
+    // so waiting for the counts does not wait for them.
+    float v[kPer];
+    if (!P.force_fallback) {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) v[e] = __uint_as_float(word(crow, (uint32_t)(e * nthr + tid)));
+    }
+    int cnt[kSegs];
     int total = 0;
     bool ok = !P.force_fallback;
 #pragma unroll
     for (int w = 0; w < kSegs; ++w) {
-        const int c = appended && w > 0 ? 0 : P.count[(size_t)r * kSegs + w];
+        const int c_ld = P.count[(size_t)r * kSegs + w];  // (appended lists use word 0 only)
+        const int c = appended && w > 0 ? 0 : c_ld;
         ok = ok && c <= seg;
-        start[w] = total;
+        cnt[w] = c;
         total += c;
     }
     int why = ok ? kDiagFbIncomplete : kDiagFbOverflow;  // the reason if the row falls back
     ok = ok && total >= k;
     const float tau_f = P.tau[r];
     const float delta = P.delta[r];
-    // The row's list: scores in words [0, cap), keys in [cap, 2 cap), read through 32-bit byte
-    // offsets from a uniform base (one address register per load instead of two).
-    const char* crow = reinterpret_cast<const char*>(P.cand + (size_t)r * 2 * P.cap);
-    const char* ckey = crow + (size_t)4 * P.cap;
-    auto word = [](const char* base, uint32_t i) { return *reinterpret_cast<const uint32_t*>(base + 4u * i); };
-    // Offset of the entry of candidate position j < total.
-    auto entry = [&](int j) -> uint32_t {
-        int w = 0, s0 = 0;
-#pragma unroll
-        for (int x = 1; x < kSegs; ++x)
-            if (j >= start[x]) {
-                w = x;
-                s0 = start[x];
-            }
-        return (uint32_t)(w * seg + (j - s0));
-    };
+    constexpr int kPerSeg = kPer / kSegs;  // elements per key-ordered segment
+    uint32_t used = 0u;                     // bit e: element e holds a candidate (set below)
+    auto in_use = [&](int e) { return ((used >> e) & 1u) != 0u; };
     if (tid == 0) {
         S.sh[4] = 0;
         S.sh[5] = 0;
     }
-    float v[kPer];
-    int nv = 0;
     float vmin = INFINITY, vmax = -INFINITY;
     if (ok) {
-        // Branch-free loads (positions past the list re-read its last entry), so all of them
-        // are in flight before the first use.
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) v[e] = __uint_as_float(word(crow, entry(min(e * nthr + tid, total - 1))));
 #pragma unroll
         for (int e = 0; e < kPer; ++e) {
-            const bool in = e * nthr + tid < total;
+            const int lim = appended ? cnt[0] - e * nthr : cnt[e / kPerSeg] - (e % kPerSeg) * nthr;
+            used |= (uint32_t)(tid < lim) << e;
+        }
+        asm volatile("" : "+v"(used));  // one register holds the mask (not 32 partial ones)
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const bool in = in_use(e);
             v[e] = in ? v[e] + 0.0f : -INFINITY;
             if (in) {
                 vmin = fminf(vmin, v[e]);
                 vmax = fmaxf(vmax, v[e]);
             }
         }
-        nv = total > tid ? min((total - tid + nthr - 1) / nthr, kPer) : 0;
     }
     // 1. The band [lo, hi] around the k-th score.  [blo, bhi] holds the k-th score and
     // `above` scores lie above bhi.  A level bins the scores in [blo, bhi]; if the bin b
@@ -1673,7 +1676,7 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
             __syncthreads();
 #pragma unroll
             for (int e = 0; e < kPer; ++e)
-                if (e < nv && v[e] >= blo && v[e] <= bhi) atomicAdd(&S.sel.hist[bin_of(v[e], blo, scale)], 1);
+                if (in_use(e) && v[e] >= blo && v[e] <= bhi) atomicAdd(&S.sel.hist[bin_of(v[e], blo, scale)], 1);
             __syncthreads();
             block_find_crossing(S.sel.hist, kBins, k, above, S);
             const int b = S.sh[0];  // >= 0: the k-th score lies in [blo, bhi]
@@ -1687,7 +1690,7 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
             float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
             for (int e = 0; e < kPer; ++e)
-                if (e < nv && v[e] >= blo && v[e] <= bhi && bin_of(v[e], blo, scale) == b) {
+                if (in_use(e) && v[e] >= blo && v[e] <= bhi && bin_of(v[e], blo, scale) == b) {
                     mn = fminf(mn, v[e]);
                     mx = fmaxf(mx, v[e]);
                 }
@@ -1713,14 +1716,14 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
 #pragma unroll
         for (int e = 0; e < kPer; ++e) {
             const double sd = (double)v[e];
-            const uint64_t am = __ballot(e < nv && sd > hi);
+            const uint64_t am = __ballot(in_use(e) && sd > hi);
             if ((tid & 63) == 0) {
                 const int w0 = (e * nthr + (tid & ~63)) >> 5;
                 S.win[w0] = (uint32_t)am;
                 S.win[w0 + 1] = (uint32_t)(am >> 32);
                 n_above += __builtin_popcountll(am);
             }
-            const int b = wave_append(e < nv && sd <= hi && sd >= lo, &S.sh[5]);
+            const int b = wave_append(in_use(e) && sd <= hi && sd >= lo, &S.sh[5]);
             if (b >= 0 && b < kSelBand) {
                 S.band.pos[b] = e * nthr + tid;
                 S.band.s[b] = sd;
@@ -1744,7 +1747,7 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
         nb_row = nb;
         if (ok) {
             // The band entries' keys, all loads in flight at once.
-            for (int x = tid; x < nb; x += nthr) S.band.key[x] = (int)word(ckey, entry(S.band.pos[x]));
+            for (int x = tid; x < nb; x += nthr) S.band.key[x] = (int)word(ckey, (uint32_t)S.band.pos[x]);
             __syncthreads();
             if (delta > 0.f && nb > 0)
                 band_rescore_waves(nb, S.band.key, S.band.s, S.band.q, S.band.w, S.band.qs, S.band.tb, ref.q,
@@ -1789,7 +1792,7 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
         auto selected = [&](int e) { return ((selmask >> e) & 1u) != 0u; };
         int key[kPer];  // branch-free loads, as for the scores
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) key[e] = (int)word(ckey, entry(min(e * nthr + tid, total - 1)));
+        for (int e = 0; e < kPer; ++e) key[e] = (int)word(ckey, (uint32_t)(e * nthr + tid));
         if (!appended) {
             // Stable compaction: position e * blockDim + t comes after every position of the
             // earlier elements and of the earlier threads of element e.
