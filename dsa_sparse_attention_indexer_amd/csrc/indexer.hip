@@ -1613,10 +1613,15 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
     // Loads of every slot first, branch-free (unused slots hold stale words, masked below) and
     // guarded only by a kernel argument: they are in flight before the count loads are issued,
     // so waiting for the counts does not wait for them.
+    // With four elements per segment, the fourth (segment offsets 3/4 seg and up) is loaded only
+    // when the segment's count reaches it (after the counts arrive; a wave-uniform test):
+    // segments hold about 0.65 seg on average, so this skips a quarter of the bytes.
+    constexpr int kPerSeg = kPer / kSegs;  // elements per key-ordered segment
+    auto late = [&](int e) { return kPerSeg == 4 && !appended && e % kPerSeg == 3; };
     float v[kPer];
     if (!P.force_fallback) {
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) v[e] = __uint_as_float(word(crow, (uint32_t)(e * nthr + tid)));
+        for (int e = 0; e < kPer; ++e) v[e] = late(e) ? 0.f : __uint_as_float(word(crow, (uint32_t)(e * nthr + tid)));
     }
     int cnt[kSegs];
     int total = 0;
@@ -1633,7 +1638,11 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
     ok = ok && total >= k;
     const float tau_f = P.tau[r];
     const float delta = P.delta[r];
-    constexpr int kPerSeg = kPer / kSegs;  // elements per key-ordered segment
+    if (ok) {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+            if (late(e) && cnt[e / kPerSeg] > (e % kPerSeg) * nthr) v[e] = __uint_as_float(word(crow, (uint32_t)(e * nthr + tid)));
+    }
     uint32_t used = 0u;                     // bit e: element e holds a candidate (set below)
     auto in_use = [&](int e) { return ((used >> e) & 1u) != 0u; };
     if (tid == 0) {
@@ -1790,9 +1799,11 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
             for (int e = 0; e < kPer; ++e) selmask |= ((wd[e] >> ((e * nthr + tid) & 31)) & 1u) << e;
         }
         auto selected = [&](int e) { return ((selmask >> e) & 1u) != 0u; };
-        int key[kPer];  // branch-free loads, as for the scores
+        // Branch-free key loads, as for the scores; a slot that is not selected re-reads the
+        // wave's first slot (a line the wave touches anyway), so only selected slots cost traffic.
+        int key[kPer];
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) key[e] = (int)word(ckey, (uint32_t)(e * nthr + tid));
+        for (int e = 0; e < kPer; ++e) key[e] = (int)word(ckey, (uint32_t)(selected(e) ? e * nthr + tid : tid));
         if (!appended) {
             // Stable compaction: position e * blockDim + t comes after every position of the
             // earlier elements and of the earlier threads of element e.
