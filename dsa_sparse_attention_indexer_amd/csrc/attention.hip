@@ -157,6 +157,24 @@ __device__ int pack_union(const AttentionArgs& A, int t0, int* s_ra, int* s_rb, 
     return a + b - s_d[b];
 }
 
+// Reductions over the four 16-lane groups of a wave (lanes c16, c16+16, c16+32, c16+48 hold
+// one head): a row swap (lanes l and l^16) then a half swap (l and l^32), each one VALU
+// instruction instead of an LDS permute and its wait.  Both lanes of a swapped pair combine
+// the same two values (max, and + are commutative), so every lane of a head gets the same
+// result: ((x0 + x16) + (x32 + x48)) for the sum.
+__device__ __forceinline__ float max_lane_groups(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_lane_groups(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // kSplit: workgroup (t, s) takes the tiles [s*tps, (s+1)*tps) of query t (tps = tiles per
 // split) and writes an unnormalised partial instead of the output.  kPack: workgroup b takes
 // the pair (2b, 2b + 1) over the union of their rows (see pack_union).
@@ -298,13 +316,19 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
             float tmax = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                lg[r] = (mlo >> (2 * r)) & 1u ? s0[r] * sl2 : -INFINITY;
-                lg[4 + r] = (mhi >> (2 * r)) & 1u ? s1[r] * sl2 : -INFINITY;
+                lg[r] = s0[r] * sl2;
+                lg[4 + r] = s1[r] * sl2;
+            }
+            if (vmask != 0xffffffffu) {  // wave-uniform: most tiles have every entry usable
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    lg[r] = (mlo >> (2 * r)) & 1u ? lg[r] : -INFINITY;
+                    lg[4 + r] = (mhi >> (2 * r)) & 1u ? lg[4 + r] : -INFINITY;
+                }
             }
 #pragma unroll
             for (int r = 0; r < 8; ++r) tmax = fmaxf(tmax, lg[r]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            tmax = max_lane_groups(tmax);
             // The exponentials are taken against a reference m that moves only when a tile's
             // maximum exceeds it by more than 2^8 (weights then stay below 256, well inside
             // bf16 and fp32), so the accumulator rescale is skipped on most tiles.
@@ -335,10 +359,8 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
                     pe += e0 + e1;
                 }
             }
-            ps += __shfl_xor(ps, 16);
-            ps += __shfl_xor(ps, 32);
-            pe += __shfl_xor(pe, 16);
-            pe += __shfl_xor(pe, 32);
+            ps = sum_lane_groups(ps);
+            pe = sum_lane_groups(pe);
             lsum += ps;
             lexp += pe;
             const bf16x8 pbf = __builtin_bit_cast(bf16x8, pb);
