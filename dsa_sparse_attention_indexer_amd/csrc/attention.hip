@@ -245,9 +245,17 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(AttentionArgs A) {
     };
     // DMA of the rows of tile j (entries in slot) into buffer buf: wave w takes rows
     // w, w + nwaves, ...; a row is 72 pieces, one 64-lane request and one of 8 lanes.
+    // The wave's rows are wave + nwaves * i (i < kAttnTile / nwaves <= 8, nwaves >= 4): lane i
+    // looks up row i's key, all in one LDS access, and each row's DMA takes its key from that
+    // lane, so the rows' lookups do not wait on the LDS one after another.
     auto fetch_rows = [&](int j, int slot, int buf) {
-        for (int r = wave; r < kAttnTile; r += nwaves) {
-            int key = __builtin_amdgcn_readfirstlane(key_of(slot, r, j * kAttnTile));
+        const int ri = wave + nwaves * (lane & 7);
+        const int kl = ri < kAttnTile ? key_of(slot, ri, j * kAttnTile) : 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = wave + nwaves * i;
+            if (r >= kAttnTile) break;
+            int key = __builtin_amdgcn_readlane(kl, i);
             key = key < 0 ? 0 : key;  // masked later; any valid row will do
             const char* src = reinterpret_cast<const char*>(kv + (size_t)key * A.kv_stride);
             char* dst = reinterpret_cast<char*>(&Kbuf[buf][r][0]);
