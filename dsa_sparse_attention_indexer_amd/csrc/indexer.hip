@@ -271,41 +271,48 @@ static_assert(kKeyHalves * (kScoreThreads / kWave) == kSegs, "one candidate segm
 // for the lanes of its 16-lane row g: DPP row_newbcast:e hands that lane's value to every
 // lane of the row, so the weights take one register per query row instead of 16.  A DPP
 // source needs two wait states after a VALU write of it; W is written once, before the
-// scoring loop, and the build checks the generated code for any closer write.
+// scoring loop, and the build checks the generated code for any closer write.  The chain is
+// four asm statements of four instructions: the scheduler places each statement as one unit,
+// and pieces of four spread under the MFMAs better than two of eight (3% on the filter) or
+// sixteen single ones.
 __device__ __forceinline__ float weighted_head_sum(float W, const float (&r)[16]) {
     float p;
     asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
         "v_fmac_f32_dpp %0, %1, %3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
         "v_fmac_f32_dpp %0, %1, %4 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %0, %1, %6 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %0, %1, %7 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %0, %1, %8 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %0, %1, %9 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf"
         : "=&v"(p)
-        : "v"(W), "v"(r[0]), "v"(r[1]), "v"(r[2]), "v"(r[3]), "v"(r[4]), "v"(r[5]), "v"(r[6]), "v"(r[7]));
+        : "v"(W), "v"(r[0]), "v"(r[1]), "v"(r[2]), "v"(r[3]));
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %3 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %4 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:7 row_mask:0xf bank_mask:0xf"
+        : "+v"(p)
+        : "v"(W), "v"(r[4]), "v"(r[5]), "v"(r[6]), "v"(r[7]));
     asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
         "v_fmac_f32_dpp %0, %1, %3 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
         "v_fmac_f32_dpp %0, %1, %4 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %0, %1, %6 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %0, %1, %7 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %0, %1, %8 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %0, %1, %9 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:11 row_mask:0xf bank_mask:0xf"
         : "+v"(p)
-        : "v"(W), "v"(r[8]), "v"(r[9]), "v"(r[10]), "v"(r[11]), "v"(r[12]), "v"(r[13]), "v"(r[14]), "v"(r[15]));
+        : "v"(W), "v"(r[8]), "v"(r[9]), "v"(r[10]), "v"(r[11]));
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %3 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %4 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+        : "+v"(p)
+        : "v"(W), "v"(r[12]), "v"(r[13]), "v"(r[14]), "v"(r[15]));
     return p;
 }
 
-// Scheduling pattern for the region ending here (the next pair's 16 MFMAs and this
-// pair's epilogue): one MFMA, then two VALU instructions, repeated.  Spreading the
-// epilogue thinly keeps the matrix pipe fed (the default schedule bunches the VALU work
-// and leaves the last MFMAs back to back).
+// Scheduling pattern for the region ending here (the next pair's 16 MFMAs, this pair's
+// head sums and an earlier pair's tail): one MFMA, then three VALU instructions, repeated.
+// Spreading the VALU work thinly keeps the matrix pipe fed (the default schedule bunches it
+// and leaves the last MFMAs back to back); three per MFMA measured better than two or four.
 __device__ __forceinline__ void interleave_with_mfma() {
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x2, 2, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x2, 3, 0);  // VALU
     }
 }
 
@@ -334,11 +341,13 @@ struct ScoreTile {
     int first_row;      // the group's first row in the block
     int seg;
     int (&cnt)[kRowsPerWave];   // survivors so far per row (including any past seg)
-    uint2* lbuf;                // filter: this wave's LDS staging lists, kStageSlots per row
+    uint2* lbuf;                // filter: this wave's LDS staging lists, kStageSlots per row, then
+                                // one spare slot per lane for stores that keep nothing
     int lcnt[kRowsPerWave];     // entries staged per row (wave-uniform)
     int gcnt[kRowsPerWave];     // entries already flushed to the segment per row
     uint32_t tile0;     // first tile of this wave's contiguous range (wave-uniform)
     bool pl[kPairs];    // kSkip: row pair q has a live row (wave-uniform)
+    float s4;           // pair 2's scores (rows 4, 5) of the last tile, their tail not yet done
 
     __device__ __forceinline__ uint32_t pos_of(int it) const { return (tile0 + (uint32_t)it) * kKeyTile + col; }
 
@@ -372,11 +381,10 @@ struct ScoreTile {
         acc[J0 + 1] = c1;
     }
 
-    // Scores of rows J0, J0+1 for tile it: ReLU, weighted head sum, then the sample store
-    // or the threshold filter.
+    // Scores of rows J0, J0+1 (the ReLU and the weighted head sum): lane half hf gets row
+    // J0 + hf's score of its key.
     template <int J0>
-    __device__ __forceinline__ void epilogue2(const f32x16 (&acc)[kRowsPerWave], int it) {
-        const uint32_t pos = pos_of(it);
+    __device__ __forceinline__ float hsum2(const f32x16 (&acc)[kRowsPerWave]) const {
         float part[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
@@ -392,9 +400,18 @@ struct ScoreTile {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]),
                                                          false, false);
         const float s_mine = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + 0.0f;
+        interleave_with_mfma();
+        return s_mine;
+    }
+
+    // The sample store, or the threshold filter, of rows J0, J0+1's scores for tile it.
+    // Branch-free (every lane stores: a survivor at its slot, any other lane at its own
+    // spare slot), so that it can issue under the MFMAs of the region it sits in.
+    template <int J0>
+    __device__ __forceinline__ void tail2(float s_mine, int it) {
+        const uint32_t pos = pos_of(it);
         const uint32_t j_mine = J0 + hf;
         constexpr int q = J0 / 2;
-        interleave_with_mfma();
         if (kSample) {
             if (pos < S && live_m[q]) sample0[j_mine * (uint32_t)P.sample_stride + pos] = s_mine;
         } else {
@@ -406,20 +423,24 @@ struct ScoreTile {
             const bool above = s_mine >= tau_m[q], causal = colm <= lim;
             const uint64_t m = __builtin_amdgcn_ballot_w64(above) & __builtin_amdgcn_ballot_w64(causal);
             const bool keep = above && causal;
-            if (m) {
-                const uint32_t m0 = (uint32_t)m, m1 = (uint32_t)(m >> 32);
-                // Slot within the row's staging list: entries already staged plus the
-                // survivors among the lower lanes of this half.
-                const uint32_t below = __builtin_amdgcn_mbcnt_hi(m1, __builtin_amdgcn_mbcnt_lo(hf ? 0u : m0, 0u));
-                const uint32_t o = (uint32_t)(hf ? lcnt[J0 + 1] : lcnt[J0]) + below;  // < kStageSlots
-                if (keep) lbuf[j_mine * kStageSlots + o] = uint2{__float_as_uint(s_mine), pos};
-                const int c0 = __builtin_popcount(m0), c1 = __builtin_popcount(m1);
-                lcnt[J0] += c0;
-                lcnt[J0 + 1] += c1;
-                cnt[J0] += c0;
-                cnt[J0 + 1] += c1;
-            }
+            const uint32_t m0 = (uint32_t)m, m1 = (uint32_t)(m >> 32);
+            // Slot within the row's staging list: entries already staged plus the survivors
+            // among the lower lanes of this half.
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi(m1, __builtin_amdgcn_mbcnt_lo(hf ? 0u : m0, 0u));
+            const uint32_t o = (uint32_t)(hf ? lcnt[J0 + 1] : lcnt[J0]) + below;  // < kStageSlots
+            const uint32_t slot = keep ? j_mine * kStageSlots + o : (uint32_t)(kRowsPerWave * kStageSlots + lane);
+            lbuf[slot] = uint2{__float_as_uint(s_mine), pos};
+            const int c0 = __builtin_popcount(m0), c1 = __builtin_popcount(m1);
+            lcnt[J0] += c0;
+            lcnt[J0 + 1] += c1;
+            cnt[J0] += c0;
+            cnt[J0 + 1] += c1;
         }
+    }
+
+    template <int J0>
+    __device__ __forceinline__ void epilogue2(const f32x16 (&acc)[kRowsPerWave], int it) {
+        tail2<J0>(hsum2<J0>(acc), it);
     }
 
     // Staged survivors of row j -> its global segment: one coalesced 8-byte store per lane.
@@ -461,33 +482,45 @@ struct ScoreTile {
             if (lcnt[j] > 0) flush_row(j);
     }
 
-    // One tile: each pair's MFMA chains run under the epilogue of the pair before (pair 3
-    // of tile it-1 for pair 0).  The two compiler memory barriers keep each half-step's
-    // staging-list accesses in their half-step (measured slightly faster than without).
+    // One tile: each pair's MFMA chains run under the head sums of the pair before (pair 3
+    // of tile it-1 for pair 0) and the tail (filter, staging) of the pair before that, so
+    // no tail waits after a region's last head sum with the matrix pipe idle.  Pair 2's tail
+    // (rows 4, 5) moves to the next tile's first region; every row still gets one tail
+    // between two flush checks.  The two compiler memory barriers keep each half-step's
+    // staging-list accesses in their half-step.
     __device__ __forceinline__ void step(f32x16 (&acc)[kRowsPerWave], const bf16x8 (&b)[8], int it) {
         flush_full();
         asm volatile("" ::: "memory");
+        float s6 = 0.f, s0 = 0.f, s2 = 0.f;
         if (kSkip) {
             if (pl[0]) mfma2<0>(acc, b);
-            if (pl[3]) epilogue2<6>(acc, it - 1);
+            if (pl[3]) s6 = hsum2<6>(acc);
+            if (pl[2]) tail2<4>(s4, it - 1);
             if (pl[1]) mfma2<2>(acc, b);
-            if (pl[0]) epilogue2<0>(acc, it);
+            if (pl[0]) s0 = hsum2<0>(acc);
+            if (pl[3]) tail2<6>(s6, it - 1);
             asm volatile("" ::: "memory");
             if (pl[2]) mfma2<4>(acc, b);
-            if (pl[1]) epilogue2<2>(acc, it);
+            if (pl[1]) s2 = hsum2<2>(acc);
+            if (pl[0]) tail2<0>(s0, it);
             if (pl[3]) mfma2<6>(acc, b);
-            if (pl[2]) epilogue2<4>(acc, it);
+            if (pl[2]) s4 = hsum2<4>(acc);
+            if (pl[1]) tail2<2>(s2, it);
             return;
         }
         mfma2<0>(acc, b);
-        epilogue2<6>(acc, it - 1);
+        s6 = hsum2<6>(acc);
+        tail2<4>(s4, it - 1);
         mfma2<2>(acc, b);
-        epilogue2<0>(acc, it);
+        s0 = hsum2<0>(acc);
+        tail2<6>(s6, it - 1);
         asm volatile("" ::: "memory");
         mfma2<4>(acc, b);
-        epilogue2<2>(acc, it);
+        s2 = hsum2<2>(acc);
+        tail2<0>(s0, it);
         mfma2<6>(acc, b);
-        epilogue2<4>(acc, it);
+        s4 = hsum2<4>(acc);
+        tail2<2>(s2, it);
     }
 };
 
@@ -514,7 +547,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
     const int segment = part * (kScoreThreads / kWave) + wave;
     const int n_segs = P.parts * (kScoreThreads / kWave);
     __shared__ __attribute__((aligned(16))) float s_w[kRowsPerWave][2][16];
-    __shared__ uint2 s_stage[kScoreThreads / kWave][kRowsPerWave * kStageSlots];
+    __shared__ uint2 s_stage[kScoreThreads / kWave][kRowsPerWave * kStageSlots + kWave];
 
     const int seg = appended ? P.cap : P.cap / kSegs;  // capacity of this wave's list per row
     float tau_r[kRowsPerWave];
@@ -592,9 +625,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
                              kSample ? nullptr : P.cand + (size_t)r0 * 2 * P.cap + (appended ? 0 : (size_t)segment * seg),
                              n0, S, kSample && S > 0 ? (float)n0 / (float)S : 0.f, lane, hf, col, col - hf,
                              (int)gref.pos, r0, seg, cnt,
-                             s_stage[wave], {0, 0, 0, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0, 0}, (uint32_t)t0,
+                             s_stage[wave], {0, 0, 0, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0, 0},
+                             (uint32_t)t0,
                              {kSkip && (live[0] || live[1]), kSkip && (live[2] || live[3]),
-                              kSkip && (live[4] || live[5]), kSkip && (live[6] || live[7])}};
+                              kSkip && (live[4] || live[5]), kSkip && (live[6] || live[7])},
+                             0.f};
         // Tile it sits in buffer it % 3; tile it+3 is loaded once tile it's MFMAs are issued.
         bf16x8 b0[8], b1[8], b2[8];
         f32x16 acc[kRowsPerWave];
@@ -609,7 +644,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
             if (!kSkip || T.pl[1]) T.template epilogue2<2>(acc, 0);
             if (!kSkip || T.pl[3]) T.template mfma2<6>(acc, b0);
             T.load(b0, 3);
-            if (!kSkip || T.pl[2]) T.template epilogue2<4>(acc, 0);
+            if (!kSkip || T.pl[2]) T.s4 = T.template hsum2<4>(acc);
             int it = 1;
             for (; it + 2 < n_my; it += 3) {
                 T.step(acc, b1, it);
@@ -621,7 +656,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
             }
             if (it < n_my) T.step(acc, b1, it);
             if (it + 1 < n_my) T.step(acc, b2, it + 1);
-            T.flush_full();  // the last epilogue adds up to 32 more entries to rows 6, 7
+            T.flush_full();  // the last tails add up to 32 more entries to rows 4-7
+            if (!kSkip || T.pl[2]) T.template tail2<4>(T.s4, n_my - 1);
             if (!kSkip || T.pl[3]) T.template epilogue2<6>(acc, n_my - 1);
             T.flush_all();
         }
