@@ -332,7 +332,7 @@ def sparse_prefill(q, kv, idx, q_pos0: int, scale: float, q_block: int = DEFAULT
     latent is also the value); idx int32 [L, top_k] (-1 and future keys skipped).
     pack=True gathers the union of neighbouring queries' rows once (same result up to
     the rounding order of the softmax sums); on MI355X it is slower than the default at
-    every overlap measured (0.59x-0.97x).
+    every overlap measured (0.59x-0.96x).
     """
     import torch
 

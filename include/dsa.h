@@ -266,8 +266,8 @@ dsa_status_t dsa_sparse_prefill(const uint16_t* q, const uint16_t* kv, int64_t k
  * bytes; other rows are concatenated.  H > 64 or top_k > 2048 run the unpacked
  * kernel.  Arguments and errors as dsa_sparse_prefill.
  * Performance: on MI355X this is slower than dsa_sparse_prefill at every overlap
- * measured (0.59x of its speed with no shared rows, 0.87x when neighbours share
- * 80% of their rows, 0.97x at 95%): the attention's per-key compute, which
+ * measured (0.59x of its speed with no shared rows, 0.88x when neighbours share
+ * 80% of their rows, 0.96x at 95%): the attention's per-key compute, which
  * packing does not reduce, outweighs the gather it saves.  dsa_sparse_prefill is
  * the default path.
  */
