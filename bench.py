@@ -198,6 +198,49 @@ def selection_summary(st: dict, wl) -> dict:
     }
 
 
+def measured_ceilings(dsa, dev, mfma_iters: int = 4000, copy_mib: int = 2048, reps: int = 5):
+    """What the GPU reaches on plain streams of the two kinds of work the path is bound by
+    (dsa_ceiling_*): bf16 MFMA chains alone at one and two waves per SIMD, with constant and
+    random operands, and a 16-byte streaming copy. Timed with the library's events."""
+    import torch
+
+    out = {}
+    buf = torch.empty(dsa.ceiling_mfma_threads(2), dtype=torch.float32, device=dev)
+    for wps in (1, 2):
+        for rnd in (True, False):
+            dsa.ceiling_mfma(buf, 50, rnd, wps)  # warm-up
+            torch.cuda.synchronize()
+            dsa.profile_set(["ceiling_mfma"])
+            dsa.profile_read("ceiling_mfma")
+            flops = sum(dsa.ceiling_mfma(buf, mfma_iters, rnd, wps) for _ in range(reps))
+            torch.cuda.synchronize()
+            ms, n = dsa.profile_read("ceiling_mfma")
+            key = f"mfma_bf16_{'random' if rnd else 'constant'}_{wps}wave_per_simd_TFLOPs"
+            out[key] = round(flops / (ms * 1e-3) / 1e12, 1)
+    n16 = copy_mib * (1 << 20) // 16
+    src = torch.ones(n16 * 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.empty(dsa.ceiling_stream_sink_words(), dtype=torch.int32, device=dev)
+    nbytes = copy_mib * (1 << 20)
+    for name, d, nt, moved in (("read_GBs", None, False, nbytes), ("read_nontemporal_GBs", None, True, nbytes),
+                               ("copy_read_plus_write_GBs", dst, False, 2 * nbytes),
+                               ("copy_nontemporal_read_plus_write_GBs", dst, True, 2 * nbytes)):
+        dsa.ceiling_stream(src, d, sink, nt)
+        torch.cuda.synchronize()
+        dsa.profile_set(["ceiling_copy"])
+        dsa.profile_read("ceiling_copy")
+        for _ in range(reps):
+            dsa.ceiling_stream(src, d, sink, nt)
+        torch.cuda.synchronize()
+        ms, n = dsa.profile_read("ceiling_copy")
+        out[name] = round(moved * n / (ms * 1e-3) / 1e9, 1)
+    dsa.profile_enable(False)
+    out["note"] = (f"dsa_ceiling_mfma_bf16 (MFMA chains only, {mfma_iters} x 8 MFMAs per wave) and "
+                   f"dsa_ceiling_stream ({copy_mib} MiB read, or read and written), {reps} launches each, HIP events")
+    del buf, src, dst, sink
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +268,9 @@ def main():
                     help="also time the step captured once in a HIP graph and replayed (reported beside the eager step)")
     ap.add_argument("--pack", type=float, default=None, metavar="KEEP",
                     help="time the attention unpacked and neighbour-packed on rows sharing KEEP of their keys")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the MFMA-only and streaming-copy ceilings, print them, and exit")
+    ap.add_argument("--no-ceilings", action="store_true", help="do not measure the ceilings in the default mode")
     ap.add_argument("--print-source-hash", metavar="KERNEL", choices=sorted(KERNEL_SOURCES),
                     help="print the source hash a traffic summary for KERNEL must carry, and exit")
     args = ap.parse_args()
@@ -258,6 +304,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 3}))
         return
     dsa.load_library()
+    if args.ceilings:
+        print(json.dumps({"measured_ceilings": measured_ceilings(dsa, dev)}), flush=True)
+        return
     if args.batch:
         bench_batch(args, dev)
         return
@@ -394,6 +443,15 @@ def main():
             r["kernel"] = dom
             result["roofline"] = r
         result["kernels"] = {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()}
+        if not args.no_ceilings:
+            ceil = measured_ceilings(dsa, dev)
+            result["measured_ceilings"] = ceil
+            if "score_filter" in per:
+                per["score_filter"]["frac_of_measured"] = round(
+                    per["score_filter"]["achieved"] / ceil["mfma_bf16_random_1wave_per_simd_TFLOPs"], 4)
+            if "sparse_attention" in per:
+                per["sparse_attention"]["frac_of_measured"] = round(
+                    per["sparse_attention"]["achieved"] / max(ceil["read_GBs"], ceil["read_nontemporal_GBs"]), 4)
         result["kernel_rooflines"] = per
     if graph_ms is not None:
         result["graph"] = {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(wl.L / (graph_ms / 1000.0), 1)}

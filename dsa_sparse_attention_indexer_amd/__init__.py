@@ -40,11 +40,13 @@ EXPORTED = ["dsa_indexer_topk_workspace_bytes", "dsa_indexer_topk", "dsa_causal_
             "dsa_indexer_topk_varlen_workspace_bytes", "dsa_indexer_topk_varlen",
             "dsa_sparse_prefill_varlen_workspace_bytes", "dsa_sparse_prefill_varlen",
             "dsa_retrieval_topk_workspace_bytes", "dsa_retrieval_topk",
-            "dsa_sparse_prefill_gate", "dsa_profile_enable", "dsa_profile_set",
+            "dsa_sparse_prefill_gate", "dsa_ceiling_mfma_threads", "dsa_ceiling_mfma_bf16",
+            "dsa_ceiling_stream_sink_words", "dsa_ceiling_stream",
+            "dsa_profile_enable", "dsa_profile_set",
             "dsa_profile_read", "dsa_status_string", "dsa_last_error", "dsa_version"]
 PROFILE_KERNELS = ["key_stats", "score_sample", "row_prep", "score_filter", "select", "fold",
                    "sparse_attention", "causal_mask", "attn_split", "attn_merge", "retr_prep", "retr_sample",
-                   "retr_filter", "retr_gather"]
+                   "retr_filter", "retr_gather", "ceiling_mfma", "ceiling_copy"]
 
 _lib = None
 
@@ -117,6 +119,16 @@ def load_library(path: str | None = None):
     lib.dsa_retrieval_topk.argtypes = [P, P, i64, i64, i32, i32, i32, P, P, sz, P]
     lib.dsa_sparse_prefill_gate.restype = ctypes.c_int
     lib.dsa_sparse_prefill_gate.argtypes = [i64, i64, i64, i64]
+    lib.dsa_ceiling_mfma_threads.restype = i64
+    lib.dsa_ceiling_mfma_threads.argtypes = [ctypes.c_int32]
+    lib.dsa_ceiling_mfma_bf16.restype = ctypes.c_int
+    lib.dsa_ceiling_mfma_bf16.argtypes = [ctypes.c_void_p, i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    lib.dsa_ceiling_stream_sink_words.restype = i64
+    lib.dsa_ceiling_stream_sink_words.argtypes = []
+    lib.dsa_ceiling_stream.restype = ctypes.c_int
+    lib.dsa_ceiling_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, i64,
+                                       ctypes.c_int32, ctypes.c_void_p]
     lib.dsa_status_string.restype = ctypes.c_char_p
     lib.dsa_status_string.argtypes = [ctypes.c_int]
     lib.dsa_last_error.restype = ctypes.c_char_p
@@ -191,6 +203,47 @@ def workspace_bytes(L: int, N: int, top_k: int, q_block: int = DEFAULT_Q_BLOCK) 
 
 def sparse_prefill_gate(B: int, L: int, N: int, min_context: int = 16384) -> bool:
     return bool(load_library().dsa_sparse_prefill_gate(B, L, N, min_context))
+
+
+def ceiling_mfma(out, iters: int, random_operands: bool, waves_per_simd: int = 1, stream=None) -> float:
+    """Enqueue the MFMA-only ceiling loop (dsa_ceiling_mfma_bf16) writing to the fp32 GPU tensor
+    out (at least ceiling_mfma_threads(waves_per_simd) elements); returns the launch's flops."""
+    import torch
+
+    lib = load_library()
+    if not (isinstance(out, torch.Tensor) and out.is_cuda and out.dtype == torch.float32 and out.is_contiguous()):
+        raise ValueError("out must be a contiguous fp32 GPU tensor")
+    flops = ctypes.c_double()
+    _check(lib.dsa_ceiling_mfma_bf16(out.data_ptr(), out.numel(), iters, 1 if random_operands else 0,
+                                     waves_per_simd, ctypes.byref(flops), _stream_ptr(out, stream)))
+    return flops.value
+
+
+def ceiling_mfma_threads(waves_per_simd: int = 1) -> int:
+    return int(load_library().dsa_ceiling_mfma_threads(waves_per_simd))
+
+
+def ceiling_stream(src, dst=None, sink=None, nontemporal: bool = False, stream=None):
+    """Enqueue the streaming ceiling (dsa_ceiling_stream): a copy of src into dst (same byte size),
+    or with dst None a read of src whose per-thread XORs go to sink (int32 GPU tensor of at least
+    ceiling_stream_sink_words() elements)."""
+    import torch
+
+    lib = load_library()
+    for t, n in ((src, "src"), (dst, "dst"), (sink, "sink")):
+        if t is not None and not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{n} must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst is not None and dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same byte size")
+    _check(lib.dsa_ceiling_stream(src.data_ptr(), dst.data_ptr() if dst is not None else None, nbytes,
+                                  sink.data_ptr() if sink is not None else None,
+                                  sink.numel() if sink is not None else 0, 1 if nontemporal else 0,
+                                  _stream_ptr(src, stream)))
+
+
+def ceiling_stream_sink_words() -> int:
+    return int(load_library().dsa_ceiling_stream_sink_words())
 
 
 def indexer_topk(q_idx, k_idx, w, q_pos0: int, top_k: int, q_block: int = DEFAULT_Q_BLOCK,

@@ -16,7 +16,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 INCLUDE = PKG.parent / "include"
 LIB = PKG / "libdsa.so"
-SOURCES = ["dsa_api.hip", "indexer.hip", "attention.hip", "retrieval.hip"]
+SOURCES = ["dsa_api.hip", "indexer.hip", "attention.hip", "retrieval.hip", "ceiling.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -31,7 +31,7 @@ std::vector<ProfRecord> g_prof;
 const char* const kProfNames[kProfCount] = {"key_stats", "score_sample", "row_prep", "score_filter",
                                             "select", "fold", "sparse_attention", "causal_mask",
                                             "attn_split", "attn_merge", "retr_prep", "retr_sample",
-                                            "retr_filter", "retr_gather"};
+                                            "retr_filter", "retr_gather", "ceiling_mfma", "ceiling_copy"};
 }  // namespace
 
 ProfScope::ProfScope(hipStream_t s, int k) : stream(s), kernel(k), start(nullptr), on(false) {
@@ -279,6 +279,51 @@ const char* dsa_status_string(dsa_status_t s) {
         case DSA_ERR_HIP: return "HIP runtime error";
     }
     return "unknown status";
+}
+
+int64_t dsa_ceiling_mfma_threads(int32_t waves_per_simd) {
+    if (waves_per_simd != 1 && waves_per_simd != 2) return 0;
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return (int64_t)n_cu * 256 * waves_per_simd;
+}
+
+dsa_status_t dsa_ceiling_mfma_bf16(float* out, int64_t out_len, int32_t iters, int32_t random_operands,
+                                   int32_t waves_per_simd, double* flops, dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    if (waves_per_simd != 1 && waves_per_simd != 2)
+        return fail(DSA_ERR_INVALID_ARG, "waves_per_simd must be 1 or 2 (got %d)", waves_per_simd);
+    if (iters < 1) return fail(DSA_ERR_INVALID_ARG, "iters must be >= 1 (got %d)", iters);
+    if (!out || !flops) return fail(DSA_ERR_INVALID_ARG, "out and flops must be non-null");
+    const int64_t threads = dsa_ceiling_mfma_threads(waves_per_simd);
+    if (threads <= 0) return fail(DSA_ERR_HIP, "could not query the current device's compute units");
+    if (out_len < threads)
+        return fail(DSA_ERR_INVALID_ARG, "out needs %lld floats (got %lld)", (long long)threads, (long long)out_len);
+    const int n_cu = (int)(threads / (256 * waves_per_simd));
+    const hipError_t e = dsa::launch_ceiling_mfma(out, n_cu, iters, random_operands != 0, waves_per_simd,
+                                                  reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "ceiling_mfma launch");
+    *flops = (double)(threads / 64) * (double)iters * 8.0 * 32768.0;
+    return DSA_OK;
+}
+
+int64_t dsa_ceiling_stream_sink_words(void) { return (int64_t)dsa::kCeilingCopyBlocks * 256; }
+
+dsa_status_t dsa_ceiling_stream(const void* src, void* dst, size_t bytes, uint32_t* sink, int64_t sink_len,
+                                int32_t nontemporal, dsa_stream_t stream) {
+    g_last_error[0] = 0;
+    if (!src) return fail(DSA_ERR_INVALID_ARG, "src must be non-null");
+    if (!aligned(src, 16) || (dst && !aligned(dst, 16)) || bytes % 16 != 0)
+        return fail(DSA_ERR_INVALID_ARG, "src, dst and bytes must be multiples of 16");
+    if (!dst && (!sink || sink_len < dsa_ceiling_stream_sink_words()))
+        return fail(DSA_ERR_INVALID_ARG, "a read-only stream needs a sink of %lld words",
+                    (long long)dsa_ceiling_stream_sink_words());
+    if (bytes == 0) return DSA_OK;
+    const hipError_t e = dsa::launch_ceiling_copy(src, dst, bytes, sink, nontemporal != 0,
+                                                  reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "ceiling_stream launch");
+    return DSA_OK;
 }
 
 int dsa_sparse_prefill_gate(int64_t B, int64_t L, int64_t N, int64_t min_context) {

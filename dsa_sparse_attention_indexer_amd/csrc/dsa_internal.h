@@ -252,7 +252,8 @@ struct IndexerArgs {
 enum ProfKernel : int {
     kProfKeyStats = 0, kProfScoreSample, kProfRowPrep, kProfScoreFilter, kProfSelect, kProfFold,
     kProfAttention, kProfCausalMask, kProfAttnSplit, kProfAttnMerge, kProfRetrievalPrep,
-    kProfRetrievalSample, kProfRetrievalFilter, kProfRetrievalGather, kProfCount
+    kProfRetrievalSample, kProfRetrievalFilter, kProfRetrievalGather, kProfCeilingMfma, kProfCeilingCopy,
+    kProfCount
 };
 struct ProfScope {
     ProfScope(hipStream_t s, int kernel);
@@ -352,6 +353,13 @@ bool sparse_attention_packable(const AttentionArgs& a);
 hipError_t launch_sparse_attention_packed(const AttentionArgs& a, hipStream_t s);
 // Split-key attention and the log-sum-exp merge of its partials.
 hipError_t launch_sparse_attention_split(const AttentionArgs& a, hipStream_t s);
+
+// Measured ceilings (ceiling.hip): an MFMA-only bf16 loop on n_cu workgroups of 4 * waves_per_simd
+// waves, iters x 8 MFMAs per wave, one value per thread to out; a 16-byte streaming copy.
+hipError_t launch_ceiling_mfma(float* out, int n_cu, int iters, bool random, int waves_per_simd, hipStream_t s);
+constexpr int kCeilingCopyBlocks = 2048;  // workgroups of 256 threads of the copy / read stream
+hipError_t launch_ceiling_copy(const void* src, void* dst, size_t bytes, uint32_t* sink, bool nontemporal,
+                               hipStream_t s);
 
 // Workspace of the split-key attention: the partials of min(L, 1024) queries.
 constexpr int kDecodeRows = 1024;

@@ -397,6 +397,39 @@ dsa_status_t dsa_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M,
 int dsa_sparse_prefill_gate(int64_t B, int64_t L, int64_t N, int64_t min_context);
 
 /*
+ * Measured ceilings beside the published peaks (not part of the DSA path; bench.py
+ * reports them): what the GPU actually reaches on a plain stream of the same kind of
+ * work as a kernel, to set its roofline fraction beside:
+ *
+ * dsa_ceiling_mfma_bf16: bf16 32x32x16 MFMA chains and nothing else (operands in
+ * registers, eight independent accumulators per wave, no memory traffic in the loop),
+ * one workgroup per compute unit with 4 * waves_per_simd waves, i.e. one or two waves
+ * per SIMD (the indexer's scoring kernel runs one).  random_operands != 0 draws the
+ * operands as bf16 values of random sign and mantissa (exponents in [2^-3, 2^1)),
+ * else every operand is 1.0: the matrix units draw more power on random data and the
+ * clock drops.  Each wave runs iters x 8 MFMAs; one float per thread is written to
+ * out (device memory, out_len >= dsa_ceiling_mfma_threads(waves_per_simd)) so that no
+ * work is dropped.  *flops (host) receives the launch's MFMA flops (32768 per MFMA).
+ * Errors: waves_per_simd outside {1, 2}, iters < 1, null pointers or a short out give
+ * DSA_ERR_INVALID_ARG.  Asynchronous on stream; time it with the "ceiling_mfma"
+ * timing class below.
+ *
+ * dsa_ceiling_stream: streams bytes (a multiple of 16; 16-byte aligned device
+ * pointers) from src with 16-byte loads, eight in flight per lane, one contiguous chunk
+ * per workgroup (timing class "ceiling_copy").  dst non-null: a copy to dst (bytes read and bytes written).  dst
+ * null: reads only; each thread writes the XOR of what it read to sink (device,
+ * sink_len >= dsa_ceiling_stream_sink_words() words) so that no load is dropped.
+ * nontemporal != 0 marks the loads and stores nontemporal.  Bad pointers, alignment or
+ * sizes give DSA_ERR_INVALID_ARG; bytes == 0 is a no-op.
+ */
+int64_t dsa_ceiling_mfma_threads(int32_t waves_per_simd);
+dsa_status_t dsa_ceiling_mfma_bf16(float* out, int64_t out_len, int32_t iters, int32_t random_operands,
+                                   int32_t waves_per_simd, double* flops, dsa_stream_t stream);
+int64_t dsa_ceiling_stream_sink_words(void);
+dsa_status_t dsa_ceiling_stream(const void* src, void* dst, size_t bytes, uint32_t* sink, int64_t sink_len,
+                                int32_t nontemporal, dsa_stream_t stream);
+
+/*
  * Kernel timing diagnostics.  While enabled (on != 0), every kernel the library
  * launches is bracketed by a pair of HIP events recorded on the caller's stream;
  * the events add no synchronisation.  dsa_profile_read waits for the recorded
@@ -404,7 +437,8 @@ int dsa_sparse_prefill_gate(int64_t B, int64_t L, int64_t N, int64_t min_context
  * the number of launches since the last read of that class, and forgets them.
  * Kernel classes: "key_stats", "score_sample", "row_prep", "score_filter",
  * "select", "fold", "sparse_attention", "causal_mask", "attn_split",
- * "attn_merge", "retr_prep", "retr_sample", "retr_filter", "retr_gather".  Unknown names give
+ * "attn_merge", "retr_prep", "retr_sample", "retr_filter", "retr_gather", "ceiling_mfma",
+ * "ceiling_copy".  Unknown names give
  * DSA_ERR_INVALID_ARG.  Host only; safe to
  * call from one thread at a time.
  */

@@ -361,3 +361,25 @@ def test_key_cache_rejects_bad_arguments(lib):
     assert g(*args, p, n, 65, p, ws, None) == 1             # more keys than N
     assert g(*args, p, 16, 64, p, ws, None) == 1            # cache buffer too small
     assert g(*args, p, n, 64, p, 10, None) == 3             # workspace too small
+
+
+def test_ceilings_reject_bad_arguments(lib):
+    """The measured-ceiling kernels validate before touching the GPU."""
+    fl = ctypes.c_double()
+    p = ctypes.c_void_p(1 << 20)
+    f = lib.dsa_ceiling_mfma_bf16
+    assert f(p, 1 << 20, 10, 1, 3, ctypes.byref(fl), None) == 1  # waves per SIMD 1 or 2
+    assert f(p, 1 << 20, 0, 1, 1, ctypes.byref(fl), None) == 1  # iters >= 1
+    assert f(None, 1 << 20, 10, 1, 1, ctypes.byref(fl), None) == 1
+    assert f(p, 1 << 20, 10, 1, 1, None, None) == 1
+    assert lib.dsa_ceiling_mfma_threads(3) == 0
+    c = lib.dsa_ceiling_stream
+    assert c(None, p, 1024, None, 0, 0, None) == 1
+    assert c(p, ctypes.c_void_p((1 << 20) + 8), 1024, None, 0, 0, None) == 1  # 16-byte alignment
+    assert c(p, p, 1000, None, 0, 0, None) == 1  # a multiple of 16 bytes
+    assert c(p, None, 1024, None, 0, 0, None) == 1  # a read-only stream needs a sink
+    assert c(p, None, 1024, p, lib.dsa_ceiling_stream_sink_words() - 1, 0, None) == 1
+    assert c(p, p, 0, None, 0, 0, None) == 0  # nothing to stream
+    assert "ceiling_mfma" in dsa.PROFILE_KERNELS and "ceiling_copy" in dsa.PROFILE_KERNELS
+    assert lib.dsa_profile_set(b"ceiling_mfma,ceiling_copy") == 0
+    assert lib.dsa_profile_enable(0) == 0
