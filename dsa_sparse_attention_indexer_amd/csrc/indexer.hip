@@ -135,11 +135,38 @@ __device__ double canonical_head_term(const uint16_t* __restrict__ q_h,
 
 static_assert(kKeyTileKeys == kKeyTile, "scoring tiles and the tiled key copy disagree");
 
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+
+// Sum over each row of 16 lanes, left in every lane of the row: DPP quad swaps, then the
+// half-row and row mirrors (each step adds the value of a lane in the other group, so all
+// lanes of a row end with the same bits).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f32<0x141>(x);  // row_half_mirror
+    x += dpp_f32<0x140>(x);  // row_mirror
+    return x;
+}
+
 // One wave per 32-key tile (tile = global wave index, then strided): eight 1-KB row-major
-// loads (16 lanes per key row), the statistics, then the tile is re-ordered through LDS
-// and written as eight 1-KB stores in the scoring order.  Keys past the end are zero.
+// loads (16 lanes per key row; the next tile's loads are issued before this tile's
+// arithmetic), the statistics, then the tile is re-ordered through LDS and written as eight
+// 1-KB stores in the scoring order.  Keys past the end are zero.
+//
+// Per element: its square (fp32 FMA; the 16 lanes of a key row are summed by DPP and the
+// largest sum is kept, so one square root at the end gives max ||k||), its magnitude, and
+// the exponent of its lowest set bit, max(e, 1) - 134 + min(ctz(m), 7) for a bf16 with
+// biased exponent e and mantissa m (7 when m = 0), over nonzero elements.  The last runs on
+// both halves of a 32-bit word at once: 16-bit lanes hold max(e, 1) + min(ctz, 7), plus 512
+// for a zero half so that it never wins the minimum.
 constexpr int kStatsThreads = 256;
 constexpr int kStatsRowPad = 17;  // LDS row stride in 16-byte chunks (16 + 1 against bank conflicts)
+constexpr unsigned short kStatsZeroBias = 512;
 // seqs == null: one sequence of n_keys keys.  Otherwise tile t belongs to the sequence whose
 // tile range holds it, and its keys are that sequence's.  Tiles [t_begin, n_tiles) are done.
 // merge: the statistics are folded into slots[0] with atomics (an append-only key cache)
@@ -154,13 +181,16 @@ __global__ __launch_bounds__(kStatsThreads) void key_stats_kernel(const uint16_t
     __shared__ u16x8 s_t[kStatsThreads / kWave][kKeyTileKeys * kStatsRowPad];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     u16x8* st = s_t[wave];
-    float nmax = 0.f, amax = 0.f;
-    int emin = INT_MAX;
+    float ssmax = 0.f, amax = 0.f;
+    u16x2 emin2 = {0xffff, 0xffff};
     const int64_t n_waves = (int64_t)gridDim.x * (kStatsThreads / kWave);
-    for (int64_t t = t_begin + (int64_t)blockIdx.x * (kStatsThreads / kWave) + wave; t < n_tiles; t += n_waves) {
+
+    // Loads of tile t (wave-uniform): lane chunk q = 64 i + lane is key q / 16 of the tile,
+    // dims 8 (q % 16) ..; rows past the tile's last key re-read that key (zeroed later).
+    auto issue = [&](int64_t t, u16x8 (&v)[8]) -> int {
         const uint16_t* src = k_idx;
         int64_t kn = n_keys, tl = t;
-        if (seqs) {  // first sequence whose tiles end after t (wave-uniform search)
+        if (seqs) {  // first sequence whose tiles end after t
             int lo = 0, hi = n_seqs - 1;
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
@@ -172,31 +202,53 @@ __global__ __launch_bounds__(kStatsThreads) void key_stats_kernel(const uint16_t
             kn = sk.nkeys;
             tl = t - sk.tbase;
         }
-        u16x8 v[8];
+        const int64_t left = kn - tl * kKeyTileKeys;
+        const int nv = left < kKeyTileKeys ? (int)left : kKeyTileKeys;
+        const u16x8* row = reinterpret_cast<const u16x8*>(src + tl * kKeyTileKeys * kIdxDim);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {  // chunk q = 64 i + lane: key q / 16 of the tile, dims 8 (q % 16) ..
-            const int q = i * 64 + lane;
-            const int64_t key = tl * kKeyTileKeys + (q >> 4);
-            v[i] = key < kn ? reinterpret_cast<const u16x8*>(src + key * kIdxDim)[q & 15] : u16x8{};
+        for (int i = 0; i < 8; ++i) {
+            const int key = 4 * i + (lane >> 4);
+            v[i] = row[(key < nv ? key : nv - 1) * (kIdxDim / 8) + (lane & 15)];
+        }
+        return nv;
+    };
+
+    int64_t t = t_begin + (int64_t)blockIdx.x * (kStatsThreads / kWave) + wave;
+    u16x8 cur[8];
+    int nv_cur = t < n_tiles ? issue(t, cur) : 0;
+    for (; t < n_tiles; t += n_waves) {
+        u16x8 nxt[8];
+        const int64_t tn = t + n_waves;
+        const int nv_nxt = issue(tn < n_tiles ? tn : t, nxt);
+        if (nv_cur < kKeyTileKeys) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (4 * i + (lane >> 4) >= nv_cur) cur[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+            const uint4 wv = __builtin_bit_cast(uint4, cur[i]);
+            const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
             float ss = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t b = v[i][j];
-                const float x = bf16_bits_to_float((uint16_t)b);
-                ss = fmaf(x, x, ss);
-                amax = fmaxf(amax, fabsf(x));
-                // exponent of the lowest set bit (branch-free form of bf16_lsb_exp)
-                const uint32_t mag = b & 0x7fffu, e = mag >> 7, m = mag & 0x7fu;
-                const int l = (int)(e ? e : 1u) - 134 + __builtin_ctz((e ? 0x80u : 0u) | m | (mag ? 0u : 1u));
-                emin = mag ? min(emin, l) : emin;
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t w = words[j];
+                const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+                ss = fmaf(lo, lo, ss);
+                ss = fmaf(hi, hi, ss);
+                amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+                const uint32_t c = w & 0x7fff7fffu;
+                const u16x2 c2 = __builtin_bit_cast(u16x2, c);
+                const u16x2 e1 = __builtin_elementwise_max(c2 >> (unsigned short)7, (u16x2){1, 1});
+                const u16x2 zero = (c2 - (unsigned short)1) >> (unsigned short)15;  // 1 for a zero half
+                const uint32_t c80 = c | 0x00800080u;
+                const uint32_t tz = (uint32_t)__builtin_ctz(c80) | ((uint32_t)__builtin_ctz(c80 >> 16) << 16);
+                const u16x2 sv = zero * kStatsZeroBias + e1 + __builtin_bit_cast(u16x2, tz);
+                emin2 = __builtin_elementwise_min(emin2, sv);
             }
-            for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
-            nmax = fmaxf(nmax, sqrtf(ss));
+            ssmax = fmaxf(ssmax, row16_sum(ss));
             const int q = i * 64 + lane;
-            if (k_tile) st[(q >> 4) * kStatsRowPad + (q & 15)] = v[i];
+            if (k_tile) st[(q >> 4) * kStatsRowPad + (q & 15)] = cur[i];
         }
         // Store i: lane l = 32 hf + c writes key c, dims 64 hf + 8 i .. (the scoring order).
         // (LDS accesses of one wave complete in order, so the reads see this tile's writes
@@ -208,6 +260,15 @@ __global__ __launch_bounds__(kStatsThreads) void key_stats_kernel(const uint16_t
                 reinterpret_cast<u16x8*>(k_tile)[t * (int64_t)(kKeyTileBytes / 16) + i * 64 + lane] = w;
             }
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
+        nv_cur = nv_nxt;
+    }
+    float nmax = sqrtf(ssmax);
+    int emin;
+    {
+        const unsigned short m = emin2.x < emin2.y ? emin2.x : emin2.y;
+        emin = m >= kStatsZeroBias ? INT_MAX : (int)m - 134;
     }
     nmax = wave_max(nmax);
     amax = wave_max(amax);
