@@ -237,11 +237,12 @@ __global__ __launch_bounds__(256) void retrieval_score_kernel(RetrievalArgs A) {
 
 // Concatenates the entries of a row's stored runs that pass its threshold (and are corpus
 // rows, not the last tile's zero padding) into its candidate list.  The runs of all the row's
-// segments are numbered 0 .. R-1 through a prefix sum of the segment counts, and thread t
-// takes runs t, t + 256, ..: a counting pass, a scan of the per-thread counts, then a writing
-// pass.  count = cap + 1 when a segment or the list overflowed, which sends the row to the fold.
+// segments are numbered 0 .. R-1 through a prefix sum of the segment counts; each chunk of
+// runs is read once, counted, scanned and written.  count = cap + 1 when a segment or the
+// list overflowed, which sends the row to the fold.
 constexpr int kGatherThreads = 256;
 constexpr int kGatherMaxSegs = 2048;  // 8 segments per part, at most 256 parts
+constexpr int kGatherPer = 8;        // runs per thread per chunk
 __global__ __launch_bounds__(kGatherThreads) void retrieval_gather_kernel(RetrievalArgs A, int n_segs) {
     const int r = blockIdx.x;
     if (r >= A.Lb || A.mode[r] != kModeNormal) return;
@@ -299,43 +300,55 @@ __global__ __launch_bounds__(kGatherThreads) void retrieval_gather_kernel(Retrie
         return base + (size_t)lo * A.seg_cap + (size_t)(q - s_pre[lo]);
     };
     auto passes = [&](float v, int64_t key) { return v >= tau && key < A.N; };
-    int n_mine = 0;
-    for (int q = tid; q < R; q += kGatherThreads) {
-        const size_t at = locate(q);
-        const float4 v = A.seg_runs[at];
-        const int64_t key = (int64_t)A.seg_ids[at] * 4;
-        n_mine += passes(v.x, key) + passes(v.y, key + 1) + passes(v.z, key + 2) + passes(v.w, key + 3);
-    }
-    __syncthreads();
-    s_sum[tid] = n_mine;
-    __syncthreads();
-    for (int d = 1; d < kGatherThreads; d <<= 1) {
-        const int v = tid >= d ? s_sum[tid - d] : 0;
-        __syncthreads();
-        s_sum[tid] += v;
-        __syncthreads();
-    }
-    const int total = s_sum[kGatherThreads - 1];
-    if (total > A.cap) {
-        if (tid == 0) A.count[(size_t)r * kCandSegs] = A.cap + 1;
-        return;
-    }
-    if (tid == 0) A.count[(size_t)r * kCandSegs] = total;
-    int off = s_sum[tid] - n_mine;
+    // One pass over the runs, in chunks of kGatherThreads * kGatherPer: thread t loads runs
+    // q0 + j * kGatherThreads + t (all loads in flight together), counts their passing
+    // entries, and after a block scan of the counts writes them from the running offset.
     uint32_t* dst = A.cand + (size_t)r * 2 * A.cap;
-    for (int q = tid; q < R; q += kGatherThreads) {
-        const size_t at = locate(q);
-        const float4 v = A.seg_runs[at];
-        const int64_t key = (int64_t)A.seg_ids[at] * 4;
-        const float f[4] = {v.x, v.y, v.z, v.w};
+    int written = 0;  // entries of earlier chunks (block-uniform)
+    for (int q0 = 0; q0 < R; q0 += kGatherThreads * kGatherPer) {
+        float4 v[kGatherPer];
+        uint32_t id[kGatherPer];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (passes(f[e], key + e)) {
-                dst[off] = __float_as_uint(f[e]);
-                dst[A.cap + off] = (uint32_t)(key + e);
-                ++off;
-            }
+        for (int j = 0; j < kGatherPer; ++j) {
+            const int q = q0 + j * kGatherThreads + tid;
+            const size_t at = locate(q < R ? q : R - 1);
+            v[j] = A.seg_runs[at];
+            id[j] = A.seg_ids[at];
+        }
+        int n_mine = 0;
+#pragma unroll
+        for (int j = 0; j < kGatherPer; ++j) {
+            if (q0 + j * kGatherThreads + tid >= R) id[j] = UINT32_MAX;  // past the runs: keys beyond N
+            const int64_t key = (int64_t)id[j] * 4;
+            n_mine += passes(v[j].x, key) + passes(v[j].y, key + 1) + passes(v[j].z, key + 2) + passes(v[j].w, key + 3);
+        }
+        __syncthreads();
+        s_sum[tid] = n_mine;
+        __syncthreads();
+        for (int d = 1; d < kGatherThreads; d <<= 1) {
+            const int x = tid >= d ? s_sum[tid - d] : 0;
+            __syncthreads();
+            s_sum[tid] += x;
+            __syncthreads();
+        }
+        int off = written + s_sum[tid] - n_mine;
+#pragma unroll
+        for (int j = 0; j < kGatherPer; ++j) {
+            const int64_t key = (int64_t)id[j] * 4;
+            const float f[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (passes(f[e], key + e)) {
+                    if (off < A.cap) {
+                        dst[off] = __float_as_uint(f[e]);
+                        dst[A.cap + off] = (uint32_t)(key + e);
+                    }
+                    ++off;
+                }
+        }
+        written += s_sum[kGatherThreads - 1];
     }
+    if (tid == 0) A.count[(size_t)r * kCandSegs] = written > A.cap ? A.cap + 1 : written;
 }
 
 int retrieval_groups(int Lb) { return (Lb + kRetQueries - 1) / kRetQueries; }
