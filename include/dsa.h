@@ -25,6 +25,10 @@
  *   - Results are deterministic and identical run to run and for every
  *     q_block value.  Calls may run concurrently on different streams when
  *     each has its own workspace.
+ *   - Inputs are finite, and the indexer's fp32 work stays in fp32 range:
+ *     key elements below 2^60 in magnitude (so that squared key norms are
+ *     finite) and indexer scores below 2^120.  Outside that (or with NaN or
+ *     infinite inputs) the indices are unspecified.
  */
 #ifndef DSA_H_
 #define DSA_H_
