@@ -1014,6 +1014,69 @@ __device__ void block_bitonic_sort(int* a, int n) {
     }
 }
 
+// Register form of the same network for n = E * blockDim.x: thread t holds elements
+// t*E .. t*E+E-1.  A compare-exchange whose partner is in the same thread is a register
+// swap, one with a partner in another lane of the wave a shuffle, and only strides that
+// cross waves go through LDS (two block barriers each).
+template <int E, int S>
+__device__ __forceinline__ void bitonic_in_thread(int (&x)[E], int size, int t) {
+    if constexpr (S < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if ((e & S) == 0) {
+                const bool asc = ((t * E + e) & size) == 0;  // the same for e and e | S (S < size)
+                const int lo = min(x[e], x[e | S]), hi = max(x[e], x[e | S]);
+                x[e] = asc ? lo : hi;
+                x[e | S] = asc ? hi : lo;
+            }
+    }
+}
+
+template <int E>
+__device__ void block_bitonic_sort_regs(int* a, int n) {
+    const int t = threadIdx.x;
+    int x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = a[t * E + e];
+    for (int size = 2; size <= n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= E) {
+                const int ts = stride / E;  // partner thread t ^ ts, same element
+                int y[E];
+                if (ts < kWave) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) y[e] = __shfl_xor(x[e], ts);
+                } else {
+                    __syncthreads();  // earlier reads of a[] are done
+#pragma unroll
+                    for (int e = 0; e < E; ++e) a[t * E + e] = x[e];
+                    __syncthreads();
+#pragma unroll
+                    for (int e = 0; e < E; ++e) y[e] = a[(t ^ ts) * E + e];
+                }
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int i = t * E + e;
+                    const bool lower = (i & stride) == 0, asc = (i & size) == 0;
+                    x[e] = lower == asc ? min(x[e], y[e]) : max(x[e], y[e]);
+                }
+            } else if (stride == 1) {
+                bitonic_in_thread<E, 1>(x, size, t);
+            } else if (stride == 2) {
+                bitonic_in_thread<E, 2>(x, size, t);
+            } else if (stride == 4) {
+                bitonic_in_thread<E, 4>(x, size, t);
+            } else {
+                bitonic_in_thread<E, 8>(x, size, t);
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e) a[t * E + e] = x[e];
+    __syncthreads();
+}
+
 // fp64 canonical scores of band entries [0, nb) (keys in band_key), in place into band_s.
 //
 // The canonical head dot product d_h = sum_i q_i k_i is a sequential fp64 sum of exact
@@ -1482,7 +1545,14 @@ __device__ void write_sorted_output(int* sel, int k, int32_t* out_row) {
     while (n2 < k) n2 <<= 1;
     for (int i = k + threadIdx.x; i < n2; i += blockDim.x) sel[i] = INT_MAX;
     __syncthreads();
-    block_bitonic_sort(sel, n2);
+    const int per = n2 / (int)blockDim.x;  // elements per thread in the register form
+    if (n2 < (int)blockDim.x) block_bitonic_sort(sel, n2);
+    else if (per == 1) block_bitonic_sort_regs<1>(sel, n2);
+    else if (per == 2) block_bitonic_sort_regs<2>(sel, n2);
+    else if (per == 4) block_bitonic_sort_regs<4>(sel, n2);
+    else if (per == 8) block_bitonic_sort_regs<8>(sel, n2);
+    else if (per == 16) block_bitonic_sort_regs<16>(sel, n2);
+    else block_bitonic_sort(sel, n2);
     for (int i = threadIdx.x; i < k; i += blockDim.x) out_row[i] = sel[i];
 }
 
