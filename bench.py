@@ -198,6 +198,24 @@ def selection_summary(st: dict, wl) -> dict:
     }
 
 
+# Kernels of the selection steps (key layout and statistics, threshold sample, row prep, exact
+# select, fallback fold) and of the sparse attention: the byte-bound part of the step.
+TOPK_ATTENTION_KERNELS = ["key_stats", "score_sample", "row_prep", "select", "fold", "sparse_attention"]
+
+
+def topk_attention_hbm(kernels: dict, b_topk: float, b_attn: float):
+    """Top-k selection plus sparse attention against the HBM roofline: their algorithmic bytes
+    per step (B_topk = 20 L k, B_attn as in the attention roofline) over the time their kernels
+    take per step.  None unless the select and attention kernels were timed."""
+    if "select" not in kernels or "sparse_attention" not in kernels:
+        return None
+    names = [k for k in TOPK_ATTENTION_KERNELS if k in kernels]
+    t_ms = sum(kernels[k]["ms_per_step"] for k in names)
+    ach = (b_topk + b_attn) / (t_ms * 1e-3) / 1e9
+    return {"bytes_per_step": int(b_topk + b_attn), "ms_per_step": round(t_ms, 4), "achieved": round(ach, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "kernels": names}
+
+
 def measured_ceilings(dsa, dev, mfma_iters: int = 4000, copy_mib: int = 2048, reps: int = 5):
     """What the GPU reaches on plain streams of the two kinds of work the path is bound by
     (dsa_ceiling_*): bf16 MFMA chains alone at one and two waves per SIMD, with constant and
@@ -453,6 +471,9 @@ def main():
                 per["sparse_attention"]["frac_of_measured"] = round(
                     per["sparse_attention"]["achieved"] / max(ceil["read_GBs"], ceil["read_nontemporal_GBs"]), 4)
         result["kernel_rooflines"] = per
+        tah = topk_attention_hbm(kernels, b_topk, b_attn)
+        if tah:
+            result["topk_attention_hbm"] = tah
     if graph_ms is not None:
         result["graph"] = {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(wl.L / (graph_ms / 1000.0), 1)}
     if not args.no_cpu_baseline:

@@ -37,3 +37,18 @@ def test_c3_roofline_terms():
     peak_bytes = bench.PEAK_HBM_GBS * 1e9
     t_roof = f_idx / peak_flops + 20 * 2048 * 2048 / peak_bytes + max(f_attn / peak_flops, b_attn / peak_bytes)
     assert abs(t_roof * 1e3 - 1.525) < 1e-3  # ms; indexer 0.873 + selection 0.010 + attention 0.642
+
+
+def test_topk_attention_hbm_fraction():
+    """Selection + attention bytes over their kernels' time, against 8 TB/s."""
+    import bench
+
+    kernels = {"key_stats": {"ms_per_step": 0.02}, "score_sample": {"ms_per_step": 0.07},
+               "row_prep": {"ms_per_step": 0.04}, "select": {"ms_per_step": 0.2},
+               "fold": {"ms_per_step": 0.01}, "sparse_attention": {"ms_per_step": 0.66},
+               "score_filter": {"ms_per_step": 1.6}}
+    r = bench.topk_attention_hbm(kernels, 84e6, 5.13e9)
+    assert r["ms_per_step"] == 1.0 and r["bytes_per_step"] == int(84e6 + 5.13e9)
+    assert abs(r["achieved"] - 5214.0) < 0.1 and abs(r["frac"] - 5214.0 / 8000.0) < 1e-4
+    assert "score_filter" not in r["kernels"]
+    assert bench.topk_attention_hbm({"select": {"ms_per_step": 1.0}}, 1.0, 1.0) is None
