@@ -136,7 +136,7 @@ struct IndexerLayout {
         l.rows = (int)((rows + kRowsPerGroup - 1) & ~(int64_t)(kRowsPerGroup - 1));
         l.cap = cand_capacity(top_k);
         l.sample_stride = (sample_size(N, top_k, l.cap) + 3) & ~3;  // rows 16-byte aligned
-        l.fold_cap = top_k + kFoldKeys;
+        l.fold_cap = top_k + 2 * kFoldKeys;  // the fold's list: its top-k plus up to two blocks' admissions
         size_t o = 0;
         l.off_diag = o; o = al(o + kDiagBytes);
         l.off_kstats = o; o = al(o + sizeof(KeyStats) * kStatSlots);

@@ -2098,8 +2098,9 @@ __device__ void fold_score_block(const RowRef& R, int64_t k0, int64_t k1, float 
 }
 
 // Persistent: each workgroup takes flagged rows one at a time and runs the exact
-// blocked fold over 4,096-key blocks (running list = exact top-k after each block,
-// new keys admitted only if score > kth(list) - 2 delta).
+// blocked fold over 4,096-key blocks (the running list is cut back to its exact top-k
+// whenever the next block could overflow it; new keys are admitted only if score >
+// kth(list at the last cut) - 2 delta).
 __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
     __shared__ SelectScratch S;
     __shared__ int s_row, s_cnt;
@@ -2137,7 +2138,12 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
             __syncthreads();
             n = s_cnt < P.fold_cap ? s_cnt : P.fold_cap;
             __syncthreads();
-            if (n > k) {
+            // The list is cut back to its exact top-k only when the next block could overflow
+            // it, and after the last block: admitted keys accumulate over many blocks in
+            // between (the admission threshold from the last cut stays a valid lower bound, as
+            // the list's k-th score only rises), so the cut runs a few times per row, not once
+            // per 4,096 keys.
+            if (n > k && (n > P.fold_cap - kFoldKeys || b1 >= nt)) {
                 // Keep exactly the top-k of the list; their fp32 scores go to the other buffer.
                 const int nxt = cur ^ 1;
                 CandList L{};

@@ -36,7 +36,7 @@ def run(lib, noalloc, q, k, w, pos0, top_k, q_block):
 def test_noalloc_matches_the_workspace_entry_point(dsa_gpu):
     lib = dsa_gpu.load_library()
     cases = [
-        di.Workload("na1", 16384, 512, 2048, 16, 1, "gauss"),          # 44 MiB of scratch
+        di.Workload("na1", 16384, 512, 2048, 16, 1, "gauss"),          # 48 MiB of scratch
         di.Workload("na2", 9000, 37, 512, 16, 2, "concentrated"),      # smaller, ragged group
     ]
     for wl in cases:
