@@ -2066,13 +2066,25 @@ __device__ void fold_score_block(const RowRef& R, int64_t k0, int64_t k1, float 
 #pragma unroll
     for (int i = 0; i < 16; ++i) wf[i] = R.w[8 * (i >> 2) + 4 * hf + (i & 3)];
     const int64_t n_tiles = (k1 - k0 + kKeyTile - 1) / kKeyTile;
-    for (int64_t ti = wave; ti < n_tiles; ti += n_waves) {
+    // The next tile's key loads are issued before this tile's MFMAs (tile indices clamped).
+    auto load = [&](int64_t ti, bf16x8 (&b)[8]) {
         const int64_t pos = k0 + ti * kKeyTile + col;
         const int64_t key = pos < k1 ? pos : k1 - 1;
         const u16x8* kp = reinterpret_cast<const u16x8*>(R.keys + key * kIdxDim + hf * 8);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) b[kk] = __builtin_bit_cast(bf16x8, kp[2 * kk]);
+    };
+    bf16x8 b[8];
+    if (wave < n_tiles) load(wave, b);
+    for (int64_t ti = wave; ti < n_tiles; ti += n_waves) {
+        const int64_t pos = k0 + ti * kKeyTile + col;
+        bf16x8 bn[8];
+        load(ti + n_waves < n_tiles ? ti + n_waves : ti, bn);
         f32x16 acc = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) acc = mfma_32x32x16(a[kk], __builtin_bit_cast(bf16x8, kp[2 * kk]), acc);
+        for (int kk = 0; kk < 8; ++kk) acc = mfma_32x32x16(a[kk], b[kk], acc);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) b[kk] = bn[kk];
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) part += wf[i] * fmaxf(acc[i], 0.f);
