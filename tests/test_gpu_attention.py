@@ -114,3 +114,24 @@ def test_c1_full_with_gpu_indices(dsa_gpu, oracle_mod):
     assert np.array_equal(idx[rows], want_idx)
     got, lse = run_gpu(dsa_gpu, inp["q"], inp["kv"], idx, wl.pos0)
     check(oracle_mod, inp["q"], inp["kv"], idx, wl.pos0, got, lse, rows=rows, what="C1 attention")
+
+
+@pytest.mark.parametrize("H", [16, 64])
+def test_padded_kv_rows(dsa_gpu, oracle_mod, H):
+    """kv rows wider than the 576 used (kv_stride 640: a latent|rope cache with padding after each
+    row, passed as a column view): bit-identical to the packed rows, and the oracle agrees."""
+    import torch
+
+    q, kv, idx = attn_case(70 + H, L=23, N=2500, H=H, k=300, q_pos0=2477, sharp=True)
+    wide = np.zeros((kv.shape[0], 640), np.uint16)
+    wide[:, :576] = kv
+    wide[:, 576:] = 0x7FC0  # NaN padding: any read of it would show
+    kv_wide = to_dev_bf16(wide)[:, :576]
+    assert kv_wide.stride(0) == 640
+    out_w, lse_w = dsa_gpu.sparse_prefill(to_dev_bf16(q), kv_wide, to_dev(idx), 2477, SCALE, return_lse=True)
+    out_p, lse_p = dsa_gpu.sparse_prefill(to_dev_bf16(q), to_dev_bf16(kv), to_dev(idx), 2477, SCALE, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_w.view(torch.int16), out_p.view(torch.int16)), "padded rows change the output"
+    assert torch.equal(lse_w, lse_p)
+    check(oracle_mod, q, kv, idx, 2477, bf16_dev_to_f64(out_w), lse_w.cpu().numpy().astype(np.float64),
+          what=f"kv_stride 640, H={H}")
