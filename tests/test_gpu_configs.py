@@ -6,12 +6,15 @@ sparse attention matches dense attention, and that query blocks give the same re
 Here, against the fp64 oracle:
 - indices bit-exact on sampled rows that include every query-block boundary
   (0, 1023, 1024, ..., L-1), plus structural checks on every row (ascending, distinct,
-  causal, no -1: each query of C0-C4 has at least top_k causal keys);
+  causal, no -1: each query of C0-C4 has at least top_k causal keys); C2 and C3 also on
+  every row;
 - attention within max-abs 2e-2 / rel-L2 5e-3 on the same rows, its lse within 1e-4;
 - a sharp-logit twin at C3's shape (64 heads, top_k 2,048, the indexer's own indices),
   where the softmax actually weighs the keys unevenly;
 - the result at C3 bit-identical for query blocks of 2,048, 1,024 and 256.
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -129,3 +132,49 @@ def test_integer_twin_indices(dsa_gpu, oracle_mod, name, n_random):
     rows = sample_rows(wl.L, n_random, seed=wl.seed + 100)
     check_indices(oracle_mod, inp, wl, idx, rows, name)
     report(f"{name}: {rows.size} rows bit-exact")
+
+
+def test_c2_every_row_bit_exact(dsa_gpu, oracle_mod):
+    """C2 (65,536 keys, 1,024 queries, its first 64 keys heavier) on every row, not a sample: the
+    oracle's full-sort top-k of all 1,024 rows (about 0.5 GFLOP of fp64 per row on the host)."""
+    import time
+
+    import torch
+
+    wl, inp = config_inputs("C2")
+    idx = dsa_gpu.indexer_topk(to_dev_bf16(inp["q_idx"]), to_dev_bf16(inp["k_idx"]), to_dev(inp["w"]), wl.pos0,
+                               wl.top_k)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    t0 = time.perf_counter()
+    want = oracle_mod.topk(inp["q_idx"], inp["k_idx"], inp["w"], wl.pos0, wl.top_k)
+    bad = np.nonzero((idx != want).any(axis=1))[0]
+    assert bad.size == 0, f"C2: {bad.size} of {wl.L} rows differ (first: row {bad[0]})"
+    report(f"C2: all {wl.L} rows bit-exact (oracle {time.perf_counter() - t0:.1f} s)")
+
+
+@functools.lru_cache(maxsize=1)
+def _c3_indices(dsa):
+    import torch
+
+    wl, inp = config_inputs("C3")
+    idx = dsa.indexer_topk(to_dev_bf16(inp["q_idx"]), to_dev_bf16(inp["k_idx"]), to_dev(inp["w"]), wl.pos0,
+                           wl.top_k)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_c3_every_row_bit_exact(dsa_gpu, oracle_mod, part):
+    """C3 on every row, in four parts of 512 rows (each about 20 s of the fp64 oracle on 16 host
+    threads): the bench's launch form (query blocks of 1,024) against the full-sort top-k."""
+    import time
+
+    wl, inp = config_inputs("C3")
+    idx = _c3_indices(dsa_gpu)
+    rows = np.arange(part * 512, (part + 1) * 512, dtype=np.int64)
+    t0 = time.perf_counter()
+    want = oracle_mod.topk(inp["q_idx"], inp["k_idx"], inp["w"], wl.pos0, wl.top_k, rows=rows)
+    bad = np.nonzero((idx[rows] != want).any(axis=1))[0]
+    assert bad.size == 0, f"C3 rows {rows[0]}..{rows[-1]}: {bad.size} differ (first: row {rows[bad[0]]})"
+    report(f"C3 rows {rows[0]}..{rows[-1]} bit-exact (oracle {time.perf_counter() - t0:.1f} s)")
