@@ -178,3 +178,30 @@ def test_c3_every_row_bit_exact(dsa_gpu, oracle_mod, part):
     bad = np.nonzero((idx[rows] != want).any(axis=1))[0]
     assert bad.size == 0, f"C3 rows {rows[0]}..{rows[-1]}: {bad.size} differ (first: row {rows[bad[0]]})"
     report(f"C3 rows {rows[0]}..{rows[-1]} bit-exact (oracle {time.perf_counter() - t0:.1f} s)")
+
+
+@pytest.mark.parametrize("name", ["C2", "C3"])
+def test_attention_every_row(dsa_gpu, oracle_mod, name):
+    """The attention of every row of C2 and C3 (with the GPU's own indices, as in the bench's step)
+    against the oracle, within the tolerance, and its lse within 1e-4."""
+    import time
+
+    import torch
+
+    wl, inp = config_inputs(name)
+    idx = _c3_indices(dsa_gpu) if name == "C3" else None
+    if idx is None:
+        d = dsa_gpu.indexer_topk(to_dev_bf16(inp["q_idx"]), to_dev_bf16(inp["k_idx"]), to_dev(inp["w"]), wl.pos0,
+                                 wl.top_k)
+        torch.cuda.synchronize()
+        idx = d.cpu().numpy()
+    out_d, lse_d = dsa_gpu.sparse_prefill(to_dev_bf16(inp["q"]), to_dev_bf16(inp["kv"]), to_dev(idx), wl.pos0,
+                                          SCALE, return_lse=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ref, ref_lse = oracle_mod.attention(inp["q"], inp["kv"], idx, wl.pos0, SCALE)
+    got = bf16_dev_to_f64(out_d)
+    ma, rel = assert_attn_close(got, ref, f"{name} every row")
+    assert np.max(np.abs(lse_d.cpu().numpy().astype(np.float64) - ref_lse)) < 1e-4, f"{name}: lse"
+    report(f"{name}: attention of all {wl.L} rows, max_abs={ma:.3g} rel_l2={rel:.3g} "
+           f"(oracle {time.perf_counter() - t0:.1f} s)")
