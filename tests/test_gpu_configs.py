@@ -180,9 +180,9 @@ def test_c3_every_row_bit_exact(dsa_gpu, oracle_mod, part):
     report(f"C3 rows {rows[0]}..{rows[-1]} bit-exact (oracle {time.perf_counter() - t0:.1f} s)")
 
 
-@pytest.mark.parametrize("name", ["C2", "C3"])
+@pytest.mark.parametrize("name", ["C1", "C2", "C3"])
 def test_attention_every_row(dsa_gpu, oracle_mod, name):
-    """The attention of every row of C2 and C3 (with the GPU's own indices, as in the bench's step)
+    """The attention of every row of C1, C2 and C3 (with the GPU's own indices, as in the bench's step)
     against the oracle, within the tolerance, and its lse within 1e-4."""
     import time
 
