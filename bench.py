@@ -266,6 +266,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="C3", help="C0..C4 (default C3, the headline workload)")
     ap.add_argument("--q-block", type=int, default=1024)
+    ap.add_argument("--recency", action="store_true",
+                    help="indexer keys scaled by 1 + s/N (scores favour recent keys) in place of the "
+                         "configuration's own; not a headline measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
@@ -332,6 +335,8 @@ def main():
         bench_retrieval(args, dev)
         return
     wl = di.CONFIGS[args.config]
+    if args.recency:
+        wl = di.replace(wl, name=wl.name + "-recency", indexer="recency")
     t0 = time.perf_counter()
     inp = di.make_inputs(wl)
     log(f"[bench] {wl.name}: inputs generated in {time.perf_counter() - t0:.1f} s")

@@ -20,6 +20,9 @@ numpy.random.Generator(SFC64(seed)) (PCG64 is ~10x slower on small hosts and
 C4 needs ~0.9e9 normals) in the order q_idx, k_idx (c first, then the noise),
 w, q, kv, as float32 in fixed chunks, then round-to-nearest-even to bf16.
 
+A further indexer kind, "recency" (N(0,1) keys scaled by 1 + s/N), stands in for an
+indexer that favours recent keys; it is a test workload, not one of the five.
+
 "Integer twins" round the indexer draws to small integers (q in [-4,4],
 k in [-12,12]) and w to {+-1/8, +-1/4} so that every fp32 score is exact.
 """
@@ -48,7 +51,7 @@ class Workload:
     top_k: int
     H: int
     seed: int
-    indexer: str  # "int" | "gauss" | "sink" | "concentrated" | "zero" | "wide"
+    indexer: str  # "int" | "gauss" | "sink" | "concentrated" | "recency" | "zero" | "wide"
     attention: str = "small"  # "small" = N(0,1)/24, "sharp" = q 2*N(0,1), kv N(0,1), "zero_q"
     int_twin: bool = False
     q_pos0: int | None = None  # default N - L
@@ -168,6 +171,12 @@ def make_indexer_inputs(wl: Workload, rng: np.random.Generator | None = None):
         k = _normal_f32(rng, N * IDX_HEAD_DIM).reshape(kshape)
         k *= np.exp2(rng.integers(-24, 25, size=kshape)).astype(np.float32)
         q *= np.exp2(rng.integers(-24, 25, size=qshape)).astype(np.float32)
+    elif wl.indexer == "recency":
+        # key s scaled by 1 + s/N: key norms grow with position, so a row's largest scores
+        # crowd its newest keys (about a quarter of the top 2.5 k in the newest eighth at
+        # 128K keys)
+        k = _normal_f32(rng, N * IDX_HEAD_DIM).reshape(kshape)
+        k *= (np.float32(1.0) + np.arange(N, dtype=np.float32) / np.float32(N))[:, None]
     elif wl.indexer == "concentrated":
         c = rng.standard_normal(IDX_HEAD_DIM, dtype=np.float32)
         k = _normal_f32(rng, N * IDX_HEAD_DIM).reshape(kshape)

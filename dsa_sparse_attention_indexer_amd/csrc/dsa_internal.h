@@ -78,7 +78,7 @@ inline int key_parts(int groups) {
 
 constexpr int kFallbackSlots = 32;
 constexpr int kFoldKeys = 4096;
-constexpr int kCandSegs = 8;  // candidate segments per row: 2 key halves x 4 scoring waves
+constexpr int kCandSegs = 8;  // count words per row; key ranges per row group: 2 key halves x 4 scoring waves
 
 // Indexer keys are re-laid out once per call as 32-key tiles of 8 KB in the order the
 // scoring MFMA's B operand is loaded: [tile][k-step 0..7][lane 0..63][8 bf16], where lane
@@ -222,10 +222,11 @@ struct IndexerArgs {
     int fold_cap;
     int force_fallback;     // debug: send every scored row through the fallback fold
     int clear_diag;         // row_prep clears diag (the call's first block, when key_stats did not run)
-    // Key parts per row group.  2 (the key halves, XCD-mapped): the 8 candidate segments of
-    // a row are written in key order by the 2 x 4 scoring waves.  More parts (few row
-    // groups): every wave of every part appends to the row's single list through an atomic
-    // counter (count[r][0]), and the selection sorts its output.
+    // Key parts per row group.  2 (the key halves, XCD-mapped): each half's 4 scoring waves
+    // append to the row's list through the workgroup's LDS counter, half 0 from the list's
+    // bottom and half 1 from its top.  More parts (few row groups): every wave of every part
+    // appends to the row's list from its bottom through a global counter (count[r][0]).
+    // Either way the selection puts its output in key order through a bitmap.
     int parts;
     unsigned long long* diag;  // [kDiagSlots] selection counters of the call
     KeyStats* kstats;       // [n_kstats] partial key statistics, one per key-statistics block
@@ -234,12 +235,14 @@ struct IndexerArgs {
     float* tau;
     float* delta;
     int* mode;
-    int* count;             // [Lb][kCandSegs] survivors per (row, segment)
+    int* count;             // [Lb][kCandSegs]: list entries of key half 0 ([0]) and half 1 ([1]);
+                            // more key parts: [0] counts the row's appended list
     int* fb_ctrl;           // [0] flagged rows, [1] next row to take
     int* fb_list;
     float* sample;
     uint32_t* cand;         // [Lb][2][cap] words: a row's candidate scores (fp32 bits) in its
-                            // first cap words, their keys in the next cap (kCandSegs segments each)
+                            // first cap words, their keys in the next cap; key half 0 fills
+                            // slots from 0 up, half 1 from cap - 1 down
     float* fold_s;          // [slots][2][fold_cap]
     int* fold_i;            // [slots][2][fold_cap]
     int* fold_bi;           // [slots][fold_cap]

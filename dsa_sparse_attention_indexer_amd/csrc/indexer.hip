@@ -305,8 +305,7 @@ __global__ __launch_bounds__(kStatsThreads) void key_stats_kernel(const uint16_t
 // One workgroup = 8 consecutive query rows over one half of their causal keys (two
 // workgroups per row group; the half follows the XCD the workgroup lands on, so each
 // XCD's L2 streams only its half of the key cache).  Each of the 4 waves scores all 8
-// rows over its own contiguous quarter of that half: candidate segment 4*half + wave, so
-// a row's 8 segments cover ascending key ranges.  Eight rows per wave means every key
+// rows over its own contiguous quarter of that half.  Eight rows per wave means every key
 // byte brought into the CU feeds 8 x 32 heads of MFMA work, which halves the per-CU key
 // stream that the vector L1 has to sustain compared with four rows.
 //
@@ -320,13 +319,18 @@ __global__ __launch_bounds__(kStatsThreads) void key_stats_kernel(const uint16_t
 // (ReLU, weighted head sum, filter) of the previous pair.  After the cross-half add both
 // lane halves hold the scores of both rows of a pair, so the low half files survivors
 // of the first row and the high half those of the second.  Survivors are staged in LDS
-// per (wave, row) and flushed to the row's segment as coalesced (score, key) runs, with
-// wave-uniform counters (no atomics).
+// per (wave, row) and flushed to the row's list as coalesced (score, key) runs.  A row's
+// list of cap slots is shared by its two key halves: half 0 fills it from slot 0 upward
+// and half 1 from slot cap - 1 downward, each half's four waves reserving their runs
+// through one LDS counter per row.  However a row's survivors spread over its keys (a
+// recency bias puts most of them in the newest keys), the list overflows only when their
+// total exceeds cap; the two halves' regions can then overlap, and the row, flagged by
+// its counts, goes to the fold.
 constexpr int kRowsPerWave = kRowsPerGroup;   // 8
 constexpr int kPairs = kRowsPerWave / 2;
 constexpr int kKeyHalves = 2;
 constexpr int kStageSlots = 64;  // LDS staging entries per (wave, row) for filter survivors
-static_assert(kKeyHalves * (kScoreThreads / kWave) == kSegs, "one candidate segment per (half, wave)");
+static_assert(kKeyHalves * (kScoreThreads / kWave) == kSegs, "key parts and scoring waves per row group");
 
 // sum_e w_e * r[e] with e ascending (fused multiply-adds), where lane 16g + e of W holds w_e
 // for the lanes of its 16-lane row g: DPP row_newbcast:e hands that lane's value to every
@@ -392,7 +396,7 @@ struct ScoreTile {
     float tau_m[kPairs];     // candidate threshold (+inf for rows the filter skips)
     bool live_m[kPairs];
     float* sample0;     // sample: row 0's sample list (rows are sample_stride apart)
-    uint32_t* cand0;    // filter: row 0's scores of this segment (rows 2 cap words apart, keys cap after)
+    uint32_t* cand0;    // filter: row 0's list (rows 2 cap words apart: cap scores, then cap keys)
     uint32_t n0;        // sample: keys of the group's first row
     uint32_t S;         // sample: sample size
     float s_ratio;      // sample: key stride n0 / S (any in-range keys would do)
@@ -400,12 +404,11 @@ struct ScoreTile {
     int colm;           // col - hf
     int first_pos;      // position of the group's first row
     int first_row;      // the group's first row in the block
-    int seg;
-    int (&cnt)[kRowsPerWave];   // survivors so far per row (including any past seg)
+    int down;           // key half 1 of two: the half fills the row's list from its top down
+    int* rcnt;          // two key parts: the workgroup's LDS counters of list entries per row
     uint2* lbuf;                // filter: this wave's LDS staging lists, kStageSlots per row, then
                                 // one spare slot per lane for stores that keep nothing
     int lcnt[kRowsPerWave];     // entries staged per row (wave-uniform)
-    int gcnt[kRowsPerWave];     // entries already flushed to the segment per row
     uint32_t tile0;     // first tile of this wave's contiguous range (wave-uniform)
     bool pl[kPairs];    // kSkip: row pair q has a live row (wave-uniform)
     float s4;           // pair 2's scores (rows 4, 5) of the last tile, their tail not yet done
@@ -494,8 +497,6 @@ struct ScoreTile {
             const int c0 = __builtin_popcount(m0), c1 = __builtin_popcount(m1);
             lcnt[J0] += c0;
             lcnt[J0 + 1] += c1;
-            cnt[J0] += c0;
-            cnt[J0 + 1] += c1;
         }
     }
 
@@ -504,27 +505,27 @@ struct ScoreTile {
         tail2<J0>(hsum2<J0>(acc), it);
     }
 
-    // Staged survivors of row j -> its global segment: one coalesced 8-byte store per lane.
-    // Entries past the segment's capacity are dropped (the row is then re-done by the
-    // fold, which the count past seg signals).
+    // Staged survivors of row j -> the row's list: one coalesced 8-byte store per lane.
+    // The run's slots are reserved on the row's counter: the workgroup's LDS counter (two
+    // key parts; key half 1 counts its slots down from the list's top) or the row's global
+    // counter (more parts).  Entries past the list's capacity are dropped (the row is then
+    // re-done by the fold, which its counts signal).
     __device__ __forceinline__ void flush_row(int j) {
-        uint32_t base = (uint32_t)gcnt[j];
-        if (P.parts > 2) {  // shared list: reserve the slots (one atomic per flush)
-            uint32_t b = 0u;
-            if (lane == 0) b = atomicAdd(reinterpret_cast<unsigned*>(&P.count[(size_t)(first_row + j) * kSegs]),
-                                         (unsigned)lcnt[j]);
-            base = __builtin_amdgcn_readfirstlane(b);
-        }
+        uint32_t b = 0u;
+        if (lane == 0)
+            b = P.parts > 2 ? atomicAdd(reinterpret_cast<unsigned*>(&P.count[(size_t)(first_row + j) * kSegs]),
+                                        (unsigned)lcnt[j])
+                            : atomicAdd(reinterpret_cast<unsigned*>(&rcnt[j]), (unsigned)lcnt[j]);
+        const uint32_t base = __builtin_amdgcn_readfirstlane(b);
         if (lane < lcnt[j]) {
             const uint2 e = lbuf[j * kStageSlots + lane];
             const uint32_t o = base + (uint32_t)lane;
-            if (o < (uint32_t)seg) {
-                uint32_t* dst = cand0 + (uint32_t)j * 2u * (uint32_t)P.cap + o;
+            if (o < (uint32_t)P.cap) {
+                uint32_t* dst = cand0 + (uint32_t)j * 2u * (uint32_t)P.cap + (down ? (uint32_t)P.cap - 1u - o : o);
                 dst[0] = e.x;
                 dst[P.cap] = e.y;
             }
         }
-        gcnt[j] += lcnt[j];
         lcnt[j] = 0;
     }
     // A tile adds at most 32 survivors per row, so rows holding kStageSlots/2 or more are
@@ -609,8 +610,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
     const int n_segs = P.parts * (kScoreThreads / kWave);
     __shared__ __attribute__((aligned(16))) float s_w[kRowsPerWave][2][16];
     __shared__ uint2 s_stage[kScoreThreads / kWave][kRowsPerWave * kStageSlots + kWave];
+    __shared__ int s_rcnt[kRowsPerWave];  // two key parts: list entries per row from this half
 
-    const int seg = appended ? P.cap : P.cap / kSegs;  // capacity of this wave's list per row
     float tau_r[kRowsPerWave];
     bool live[kRowsPerWave];
     int64_t n_keys = 0;
@@ -648,12 +649,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
         const int j = threadIdx.x >> 5, h2 = (threadIdx.x >> 4) & 1, i = threadIdx.x & 15;
         s_w[j][h2][i] = wrow[j][8 * (i >> 2) + 4 * h2 + (i & 3)];
     }
+    if (threadIdx.x < kRowsPerWave) s_rcnt[threadIdx.x] = 0;
     __syncthreads();
     float wl[kRowsPerWave];
 #pragma unroll
     for (int j = 0; j < kRowsPerWave; ++j) wl[j] = s_w[j][hf][lane & 15];
 
-    int cnt[kRowsPerWave] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (n_keys > 0) {
         bf16x8 a[kRowsPerWave][8];
         // All 64 loads are issued before the first is pinned to its AGPRs (pinning each right
@@ -674,7 +675,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
         const int t0 = segment * tps;
         const int n_my = n_tiles > t0 ? min(n_tiles - t0, tps) : 0;
         // Rows of a group are consecutive (invalid rows never store), so every row's
-        // list is addressed from row 0's.
+        // list is addressed from row 0's.  With two key parts, half 1 fills the lists
+        // from their tops down.
         ScoreTile<kSample, kSkip> T{P, gref.keys,
                              reinterpret_cast<const u16x8*>(P.k_tile) + (size_t)gref.tbase * (kKeyTileBytes / 16),
                              (uint32_t)gref.ntiles, a, wl,
@@ -683,10 +685,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
                              {hf ? live[1] : live[0], hf ? live[3] : live[2], hf ? live[5] : live[4],
                               hf ? live[7] : live[6]},
                              kSample ? P.sample + (size_t)r0 * P.sample_stride : nullptr,
-                             kSample ? nullptr : P.cand + (size_t)r0 * 2 * P.cap + (appended ? 0 : (size_t)segment * seg),
+                             kSample ? nullptr : P.cand + (size_t)r0 * 2 * P.cap,
                              n0, S, kSample && S > 0 ? (float)n0 / (float)S : 0.f, lane, hf, col, col - hf,
-                             (int)gref.pos, r0, seg, cnt,
-                             s_stage[wave], {0, 0, 0, 0, 0, 0, 0, 0}, {0, 0, 0, 0, 0, 0, 0, 0},
+                             (int)gref.pos, r0, !appended && part == 1, s_rcnt,
+                             s_stage[wave], {0, 0, 0, 0, 0, 0, 0, 0},
                              (uint32_t)t0,
                              {kSkip && (live[0] || live[1]), kSkip && (live[2] || live[3]),
                               kSkip && (live[4] || live[5]), kSkip && (live[6] || live[7])},
@@ -723,10 +725,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
             T.flush_all();
         }
     }
-    if (!kSample && lane == 0) {
-#pragma unroll
-        for (int j = 0; j < kRowsPerWave; ++j)
-            if (r0 + j < P.Lb && !appended) P.count[(size_t)(r0 + j) * kSegs + segment] = cnt[j];  // pad rows too (0)
+    // Two key parts: this half's entry count per row, once every wave has reserved its runs
+    // (pad rows too: 0).
+    if (!kSample && !appended) {
+        __syncthreads();
+        if (threadIdx.x < kRowsPerWave && r0 + (int)threadIdx.x < P.Lb)
+            P.count[(size_t)(r0 + threadIdx.x) * kSegs + part] = s_rcnt[threadIdx.x];
     }
 }
 
@@ -1561,14 +1565,14 @@ constexpr int kSelPer = 32;        // candidates per thread (blocks of many rows
 constexpr int kSelPerFew = 16;     // ... blocks of few rows: cap / 16 threads, shorter rows
 constexpr int kSelMaxThreads = 4 * kMaxTopK / kSelPer;  // cap <= 4 * kMaxTopK
 constexpr int kOneLevel = 256;     // a crossing bin this small ends the k-th search
-// Appended candidate lists are put back in key order through a bitmap of the causal keys,
-// when they fit it.
+// Candidate lists hold no key order; the selected keys are put in order through a bitmap of
+// the causal keys, kSelBitmapKeys of them per pass.
 constexpr int kSelBitmapWords = 8192;
 constexpr int kSelBitmapKeys = kSelBitmapWords * 32;  // 262,144 keys
 
 // select's shared memory.  The phases use the union in turn: the k-th search (sel), the
-// band (band), then the output compaction (cmp, bitmap or out).  Small enough (~34 KB) for
-// four rows per compute unit.
+// band (band), then the output bitmap.  Small enough (~34 KB) for four rows per compute
+// unit.
 // Per workgroup, 16 entries x (32 / waves) heads of re-score terms per wave; 512 doubles for
 // any wave count up to 16 (they sit in the union's room beside the bitmap).
 constexpr int kSelTermSlots = 512;
@@ -1588,10 +1592,6 @@ struct SelectLds {
             QHeadStat qs[kIdxHeads];
             double tb[kSelTermSlots];  // head terms on their way to the entries' lanes
         } band;
-        struct {
-            int cnt[kSelPer * 8];  // selected entries per (element, wave): kPer * waves <= 256
-            int pre[kSelPer * 8];
-        } cmp;
         uint32_t bitmap[kSelBitmapWords];
         int out[kMaxTopK];
     };
@@ -1732,12 +1732,12 @@ __device__ __forceinline__ void band_rescore_waves(int nb, const int* band_key, 
     }
 }
 
-// Exact top-k of one row's candidates.  The eight segments written by the scoring waves
-// are each in ascending key order and cover ascending key ranges, so the list's slots in
-// use, in slot order, are sorted by key.  Thread t holds the scores of slots e * blockDim
-// + t (e < 32; a "position" below) in registers (each load instruction reads consecutive
-// slots); keys are read from the list only for band entries and for the output, so a row
-// takes 4 waves and ~35 KB of LDS and every row of a 1,024-row block is resident at once.
+// Exact top-k of one row's candidates.  The row's list holds key half 0's entries in slots
+// [0, c0) and key half 1's in [cap - c1, cap) (more key parts: one list in [0, c0)), in no
+// key order.  Thread t holds the scores of slots e * blockDim + t (e < kPer; a "position"
+// below) in registers (each load instruction reads consecutive slots); keys are read from
+// the list only for band entries and for the output, so a row takes 4 waves and ~35 KB of
+// LDS and every row of a 1,024-row block is resident at once.
 //
 //   1. k-th search: a value-linear histogram over [min, max] of the row's scores, then the
 //      exact range of the bin holding the k-th score; a second or third level narrows it
@@ -1746,8 +1746,9 @@ __device__ __forceinline__ void band_rescore_waves(int nb, const int* band_key, 
 //      over many scales can leave a band too wide for select; the row then goes to the fold.
 //   2. band: the entries between are re-scored in the canonical fp64 order (one wave per
 //      16 entries) and ranked by (score desc, key asc) for the remaining slots.
-//   3. output: a stable compaction of the selected positions (per-element wave ballots and
-//      one block scan); the ascending key order of the list is the output order.
+//   3. output: the selected keys mark a bitmap of the causal keys in LDS (in passes of
+//      kSelBitmapKeys keys), and a block scan of the words' bit counts places each key at
+//      its rank: ascending key order whatever the list order.
 template <int kPer>
 __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerArgs P) {
     static_assert(kPer == 16 || kPer == 32, "per-thread candidates");
@@ -1766,49 +1767,42 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
     }
     __shared__ SelectLds S;
     const int nthr = (int)blockDim.x, tid = (int)threadIdx.x;
-    // Eight key-ordered segments, or (more key parts) one appended list in no key order.
+    // Two key parts: half 0's entries fill the list from slot 0 up, half 1's from slot cap - 1
+    // down.  More key parts: one appended list from slot 0.
     const bool appended = P.parts > 2;
-    const int seg = appended ? P.cap : P.cap / kSegs;
+    const int cap = P.cap;
     // The row's list: scores in words [0, cap), keys in [cap, 2 cap), read through 32-bit byte
     // offsets from a uniform base (one address register per load instead of two).  Thread t's
-    // element e is slot e * blockDim + t of the list: segment w holds slots [w seg, w seg +
-    // cnt[w]), so element e lies in segment e / (kPer / 8) and the slots in use are a mask;
-    // slot order is key order (segments cover ascending key ranges), gaps aside.
-    const char* crow = reinterpret_cast<const char*>(P.cand + (size_t)r * 2 * P.cap);
-    const char* ckey = crow + (size_t)4 * P.cap;
+    // element e is slot e * blockDim + t of the list, so the slots in use are a mask.
+    const char* crow = reinterpret_cast<const char*>(P.cand + (size_t)r * 2 * cap);
+    const char* ckey = crow + (size_t)4 * cap;
     auto word = [](const char* base, uint32_t i) { return *reinterpret_cast<const uint32_t*>(base + 4u * i); };
-    // Loads of every slot first, branch-free (unused slots hold stale words, masked below) and
-    // guarded only by a kernel argument: they are in flight before the count loads are issued,
-    // so waiting for the counts does not wait for them.
-    // With four elements per segment, the fourth (segment offsets 3/4 seg and up) is loaded only
-    // when the segment's count reaches it (after the counts arrive; a wave-uniform test):
-    // segments hold about 0.65 seg on average, so this skips a quarter of the bytes.
-    constexpr int kPerSeg = kPer / kSegs;  // elements per key-ordered segment
-    auto late = [&](int e) { return kPerSeg == 4 && !appended && e % kPerSeg == 3; };
+    // Loads of the slots likely in use first, branch-free (unused slots hold stale words,
+    // masked below) and guarded only by a kernel argument: they are in flight before the
+    // count loads are issued, so waiting for the counts does not wait for them.  The middle
+    // quarter of a two-part list (slots 3/8 cap to 5/8 cap: each half holds about 0.32 cap
+    // on average) is loaded only when a count reaches it (after the counts arrive; a
+    // wave-uniform test), which skips a quarter of the bytes.
+    auto late = [&](int e) { return !appended && (e + 1) * 8 > 3 * kPer && e * 8 < 5 * kPer; };
     float v[kPer];
     if (!P.force_fallback) {
 #pragma unroll
         for (int e = 0; e < kPer; ++e) v[e] = late(e) ? 0.f : __uint_as_float(word(crow, (uint32_t)(e * nthr + tid)));
     }
-    int cnt[kSegs];
-    int total = 0;
-    bool ok = !P.force_fallback;
-#pragma unroll
-    for (int w = 0; w < kSegs; ++w) {
-        const int c_ld = P.count[(size_t)r * kSegs + w];  // (appended lists use word 0 only)
-        const int c = appended && w > 0 ? 0 : c_ld;
-        ok = ok && c <= seg;
-        cnt[w] = c;
-        total += c;
-    }
-    int why = ok ? kDiagFbIncomplete : kDiagFbOverflow;  // the reason if the row falls back
+    const int c0 = P.count[(size_t)r * kSegs];
+    const int c1 = appended ? 0 : P.count[(size_t)r * kSegs + 1];
+    const int total = c0 + c1;
+    bool ok = !P.force_fallback && total <= cap;    int why = ok ? kDiagFbIncomplete : kDiagFbOverflow;  // the reason if the row falls back
     ok = ok && total >= k;
     const float tau_f = P.tau[r];
     const float delta = P.delta[r];
+    // Slot j is in use iff it lies in half 0's run or in half 1's.
+    auto slot_used = [&](int j) { return j < c0 || j >= cap - c1; };
     if (ok) {
 #pragma unroll
         for (int e = 0; e < kPer; ++e)
-            if (late(e) && cnt[e / kPerSeg] > (e % kPerSeg) * nthr) v[e] = __uint_as_float(word(crow, (uint32_t)(e * nthr + tid)));
+            if (late(e) && (e * nthr < c0 || (e + 1) * nthr > cap - c1))
+                v[e] = __uint_as_float(word(crow, (uint32_t)(e * nthr + tid)));
     }
     uint32_t used = 0u;                     // bit e: element e holds a candidate (set below)
     auto in_use = [&](int e) { return ((used >> e) & 1u) != 0u; };
@@ -1819,10 +1813,7 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
     float vmin = INFINITY, vmax = -INFINITY;
     if (ok) {
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            const int lim = appended ? cnt[0] - e * nthr : cnt[e / kPerSeg] - (e % kPerSeg) * nthr;
-            used |= (uint32_t)(tid < lim) << e;
-        }
+        for (int e = 0; e < kPer; ++e) used |= (uint32_t)slot_used(e * nthr + tid) << e;
         asm volatile("" : "+v"(used));  // one register holds the mask (not 32 partial ones)
 #pragma unroll
         for (int e = 0; e < kPer; ++e) {
@@ -1971,67 +1962,39 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
         int key[kPer];
 #pragma unroll
         for (int e = 0; e < kPer; ++e) key[e] = (int)word(ckey, (uint32_t)(selected(e) ? e * nthr + tid : tid));
-        if (!appended) {
-            // Stable compaction: position e * blockDim + t comes after every position of the
-            // earlier elements and of the earlier threads of element e.
-            const int nw = nthr >> 6, wv = tid >> 6;
-#pragma unroll
-            for (int e = 0; e < kPer; ++e) {
-                const uint64_t m = __ballot(selected(e));
-                if ((tid & 63) == 0) S.cmp.cnt[e * nw + wv] = __builtin_popcountll(m);
-            }
-            __syncthreads();
-            const int ce = tid < kPer * nw ? S.cmp.cnt[tid] : 0;
-            const int pre = block_incl_scan(ce, S) - ce;
-            if (tid < kPer * nw) S.cmp.pre[tid] = pre;
-            __syncthreads();
-#pragma unroll
-            for (int e = 0; e < kPer; ++e) {
-                const bool sel = selected(e);
-                const uint64_t m = __ballot(sel);
-                if (sel) {
-                    const int o = S.cmp.pre[e * nw + wv] + mbcnt64(m);
-                    if (o < k) out_row[o] = key[e];
-                }
-            }
-        } else if (nt <= kSelBitmapKeys) {
-            // Appended list (no key order), causal keys within the bitmap: mark the selected
-            // keys, then each thread emits its words' keys at its scanned offset.
-            const int nw = (int)((nt + 31) >> 5);
+        // Keys in [base, base + kSelBitmapKeys) per pass (one pass up to 262,144 causal keys).
+        // Thread t owns the bitmap words [t per, (t + 1) per) and writes their keys from its
+        // scanned offset on, so the output ascends.
+        int written = 0;
+        for (int64_t base = 0; base < nt; base += kSelBitmapKeys) {
+            const int span = (int)(nt - base < kSelBitmapKeys ? nt - base : kSelBitmapKeys);
+            const int nw = (span + 31) >> 5;
             for (int i = tid; i < nw; i += nthr) S.bitmap[i] = 0u;
             __syncthreads();
 #pragma unroll
-            for (int e = 0; e < kPer; ++e)
-                if (selected(e)) atomicOr(&S.bitmap[key[e] >> 5], 1u << (key[e] & 31));
+            for (int e = 0; e < kPer; ++e) {
+                const int64_t d = (int64_t)key[e] - base;
+                if (selected(e) && d >= 0 && d < span) atomicOr(&S.bitmap[d >> 5], 1u << (d & 31));
+            }
             __syncthreads();
             const int per = (nw + nthr - 1) / nthr;
             const int w0 = tid * per, w1 = min(nw, w0 + per);
             int c = 0;
             for (int i = w0; i < w1; ++i) c += __builtin_popcount(S.bitmap[i]);
-            int o = block_incl_scan(c, S) - c;
+            const int incl = block_incl_scan(c, S);
+            int o = written + incl - c;
             for (int i = w0; i < w1; ++i) {
                 uint32_t bits = S.bitmap[i];
                 while (bits) {
                     const int bit = __builtin_ctz(bits);
                     bits &= bits - 1u;
-                    if (o < k) out_row[o] = i * 32 + bit;
+                    if (o < k) out_row[o] = (int)base + i * 32 + bit;
                     ++o;
                 }
             }
-        } else {
-            // Appended list over a larger key range: gather the selection, then sort it.
-            int c = 0;
-#pragma unroll
-            for (int e = 0; e < kPer; ++e) c += selected(e);
-            int o = block_incl_scan(c, S) - c;
-#pragma unroll
-            for (int e = 0; e < kPer; ++e)
-                if (selected(e)) {
-                    if (o < k) S.out[o] = key[e];
-                    ++o;
-                }
+            if (tid == nthr - 1) S.sh[7] = incl;
             __syncthreads();
-            write_sorted_output(S.out, k, out_row);
+            written += S.sh[7];
         }
     }
     if (!ok && tid == 0) {
@@ -2326,23 +2289,23 @@ hipError_t launch_select_fold(const IndexerArgs& a, hipStream_t s) {
 // ------------------------------------------------------------------ score dump (diagnostic)
 
 // One workgroup per block row: the row of `scores` is set to NaN, then every (score, key)
-// entry the filter stored for the row (its kSegs segments of cap / kSegs entries) is written
-// to its key's column.  With tau = -inf the filter stores every causal key.
+// entry the filter stored for the row (key half 0's in slots [0, c0), half 1's in
+// [cap - c1, cap)) is written to its key's column.  With tau = -inf the filter stores every
+// causal key.
 __global__ __launch_bounds__(256) void score_dump_kernel(IndexerArgs P, float* scores, int64_t n_cols,
                                                          float* delta_out) {
     const int r = blockIdx.x;
     float* row = scores + (size_t)r * n_cols;
     for (int64_t c = threadIdx.x; c < n_cols; c += blockDim.x) row[c] = __uint_as_float(0x7fc00000u);
     __syncthreads();
-    const int seg = P.cap / kSegs;
-    for (int w = 0; w < kSegs; ++w) {
-        const int n = min(P.count[(size_t)r * kSegs + w], seg);
-        const uint32_t* e = P.cand + (size_t)r * 2 * P.cap + (size_t)w * seg;
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
-            const uint32_t key = e[P.cap + i];
-            if ((int64_t)key < n_cols) row[key] = __uint_as_float(e[i]);
-        }
-    }
+    const int c0 = P.count[(size_t)r * kSegs], c1 = P.count[(size_t)r * kSegs + 1];
+    const uint32_t* e = P.cand + (size_t)r * 2 * P.cap;
+    if (c0 + c1 <= P.cap)
+        for (int i = threadIdx.x; i < P.cap; i += blockDim.x)
+            if (i < c0 || i >= P.cap - c1) {
+                const uint32_t key = e[P.cap + i];
+                if ((int64_t)key < n_cols) row[key] = __uint_as_float(e[i]);
+            }
     if (threadIdx.x == 0 && delta_out) delta_out[r] = P.delta[r];
 }
 

@@ -74,9 +74,9 @@ def test_c1_gaussian_full_bit_exact(dsa_gpu, oracle_mod):
 # ------------------------------------------------------------------ edge cases
 
 def test_max_topk_key_ordered(dsa_gpu, oracle_mod):
-    """top_k = 4,096 over 1,024 rows (128 groups, key-ordered segments): the candidate
-    capacity is 16,384, so select runs 1,024 threads (16 waves) through its ordered
-    compaction."""
+    """top_k = 4,096 over 1,024 rows (128 groups, two key halves sharing each row's list):
+    the candidate capacity is 16,384, so select runs 512 threads (8 waves) through its
+    bitmap output."""
     wl = di.Workload("maxk", 20000, 1024, 4096, 16, 19, "gauss")
     q, k, w = di.make_indexer_inputs(wl)
     got = run_gpu(dsa_gpu, q, k, w, wl.pos0, wl.top_k)
@@ -86,9 +86,10 @@ def test_max_topk_key_ordered(dsa_gpu, oracle_mod):
 
 
 def test_full_candidate_lists(dsa_gpu, oracle_mod):
-    """1,024 rows in 128 groups (two key halves, key-ordered candidate segments).  With
-    N = 8,184 = capacity - 8 no group samples a threshold: every row keeps all of its 7,161 to
-    8,184 causal keys, so select compacts lists filled almost to its 8,192 positions."""
+    """1,024 rows in 128 groups (two key halves sharing each row's list).  With N = 8,184 =
+    capacity - 8 no group samples a threshold: every row keeps all of its 7,161 to 8,184
+    causal keys, so the halves' runs (one from each end) fill the list almost to its 8,192
+    slots."""
     wl = di.Workload("full", 8184, 1024, 2048, 16, 17, "gauss", q_pos0=8184 - 1024)
     q, k, w = di.make_indexer_inputs(wl)
     got = run_gpu(dsa_gpu, q, k, w, wl.pos0, wl.top_k)

@@ -8,6 +8,10 @@
   narrowest bin's range and ranks that band exactly when it fits its buffer; otherwise the
   row goes to the blocked fold, whose k-th search finishes with the exact radix select.
 
+- Scores that favour recent keys (key norms growing with position): most candidates come
+  from the newest keys, and a row's list must hold them wherever they fall; no row may fall
+  back to the fold for it.
+
 The selection counters (dsa_indexer_topk_stats) show which path each row took.
 """
 import numpy as np
@@ -81,8 +85,8 @@ def test_multiscale_scores_radix_in_fold(dsa_gpu, oracle_mod):
 
 @pytest.mark.parametrize("top_k", [2049, 3000, 3840])
 def test_topk_between_2048_and_4096(dsa_gpu, oracle_mod, top_k):
-    """1,024 rows (128 row groups, key-ordered candidate segments); select runs cap / 16
-    threads = 576 .. 960."""
+    """1,024 rows (128 row groups, two key halves sharing each row's list); select runs
+    cap / 32 threads = 320 .. 512 (5 to 8 waves)."""
     wl = di.Workload("k3000", 60000, 1024, top_k, 16, 23, "gauss")
     q, k, w = di.make_indexer_inputs(wl)
     got, st = run_with_stats(dsa_gpu, q, k, w, wl.pos0, top_k)
@@ -93,3 +97,19 @@ def test_topk_between_2048_and_4096(dsa_gpu, oracle_mod, top_k):
     assert (np.diff(got, axis=1) > 0).all()
     assert st["rows_failed"] == 0
     assert st["rows_fallback"] <= wl.L // 100, "rows should finish on the candidate path"
+
+
+@pytest.mark.parametrize("N,L", [(65536, 1024), (131072, 1024)])
+def test_recency_biased_scores(dsa_gpu, oracle_mod, N, L):
+    """Keys scaled by 1 + s/N (the newest eighth of a row's keys holds about a quarter of its
+    candidates, the newest half about three quarters): indices bit-exact on sampled rows and
+    every row finished in select, none in the fold."""
+    wl = di.Workload("recency", N, L, 2048, 16, 31, "recency")
+    q, k, w = di.make_indexer_inputs(wl)
+    got, st = run_with_stats(dsa_gpu, q, k, w, wl.pos0, wl.top_k)
+    report(f"recency N={N} L={L}: {st}")
+    rows = np.array([0, 1, 7, 8, 255, 511, 512, 777, 1016, 1023], dtype=np.int64)
+    want = oracle_mod.topk(q, k, w, wl.pos0, wl.top_k, rows=rows)
+    assert np.array_equal(got[rows], want)
+    assert (np.diff(got, axis=1) > 0).all()
+    assert st["rows_failed"] == 0 and st["rows_fallback"] == 0
