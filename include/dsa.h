@@ -171,7 +171,7 @@ typedef struct {
     int64_t rows;                /* rows finished from their candidate lists            */
     int64_t rows_all_keys;       /* rows with at most top_k causal keys (no selection)  */
     int64_t rows_fallback;       /* rows finished by the blocked fold, because ...      */
-    int64_t fallback_overflow;   /*   a candidate segment overflowed                    */
+    int64_t fallback_overflow;   /*   the row's candidate list overflowed               */
     int64_t fallback_incomplete; /*   the candidates could miss a top-k key             */
     int64_t fallback_band;       /*   the fp64 band outgrew the selection buffer        */
     int64_t rows_failed;         /* rows no path finished (written as -1): 0 expected   */
