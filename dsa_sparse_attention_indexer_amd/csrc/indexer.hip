@@ -1566,13 +1566,13 @@ constexpr int kSelPerFew = 16;     // ... blocks of few rows: cap / 16 threads, 
 constexpr int kSelMaxThreads = 4 * kMaxTopK / kSelPer;  // cap <= 4 * kMaxTopK
 constexpr int kOneLevel = 256;     // a crossing bin this small ends the k-th search
 // Candidate lists hold no key order; the selected keys are put in order through a bitmap of
-// the causal keys, kSelBitmapKeys of them per pass.
+// the causal keys when there are at most kSelBitmapKeys of them, else by a sort.
 constexpr int kSelBitmapWords = 8192;
 constexpr int kSelBitmapKeys = kSelBitmapWords * 32;  // 262,144 keys
 
 // select's shared memory.  The phases use the union in turn: the k-th search (sel), the
-// band (band), then the output bitmap.  Small enough (~34 KB) for four rows per compute
-// unit.
+// band (band), then the output bitmap (or out, to sort).  Small enough (~34 KB) for four
+// rows per compute unit.
 // Per workgroup, 16 entries x (32 / waves) heads of re-score terms per wave; 512 doubles for
 // any wave count up to 16 (they sit in the union's room beside the bitmap).
 constexpr int kSelTermSlots = 512;
@@ -1746,9 +1746,9 @@ __device__ __forceinline__ void band_rescore_waves(int nb, const int* band_key, 
 //      over many scales can leave a band too wide for select; the row then goes to the fold.
 //   2. band: the entries between are re-scored in the canonical fp64 order (one wave per
 //      16 entries) and ranked by (score desc, key asc) for the remaining slots.
-//   3. output: the selected keys mark a bitmap of the causal keys in LDS (in passes of
-//      kSelBitmapKeys keys), and a block scan of the words' bit counts places each key at
-//      its rank: ascending key order whatever the list order.
+//   3. output: the selected keys mark a bitmap of the causal keys in LDS, and a block scan
+//      of the words' bit counts places each key at its rank: ascending key order whatever
+//      the list order.  Past kSelBitmapKeys causal keys they are sorted instead.
 template <int kPer>
 __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerArgs P) {
     static_assert(kPer == 16 || kPer == 32, "per-thread candidates");
@@ -1962,39 +1962,46 @@ __global__ __launch_bounds__(4 * kMaxTopK / kPer, 4) void select_kernel(IndexerA
         int key[kPer];
 #pragma unroll
         for (int e = 0; e < kPer; ++e) key[e] = (int)word(ckey, (uint32_t)(selected(e) ? e * nthr + tid : tid));
-        // Keys in [base, base + kSelBitmapKeys) per pass (one pass up to 262,144 causal keys).
-        // Thread t owns the bitmap words [t per, (t + 1) per) and writes their keys from its
-        // scanned offset on, so the output ascends.
-        int written = 0;
-        for (int64_t base = 0; base < nt; base += kSelBitmapKeys) {
-            const int span = (int)(nt - base < kSelBitmapKeys ? nt - base : kSelBitmapKeys);
-            const int nw = (span + 31) >> 5;
+        if (nt <= kSelBitmapKeys) {
+            // Causal keys within the bitmap: mark the selected keys, then each thread writes
+            // the keys of its bitmap words [t per, (t + 1) per) from its scanned offset on, so
+            // the output ascends.
+            const int nw = (int)((nt + 31) >> 5);
             for (int i = tid; i < nw; i += nthr) S.bitmap[i] = 0u;
             __syncthreads();
 #pragma unroll
-            for (int e = 0; e < kPer; ++e) {
-                const int64_t d = (int64_t)key[e] - base;
-                if (selected(e) && d >= 0 && d < span) atomicOr(&S.bitmap[d >> 5], 1u << (d & 31));
-            }
+            for (int e = 0; e < kPer; ++e)
+                if (selected(e)) atomicOr(&S.bitmap[key[e] >> 5], 1u << (key[e] & 31));
             __syncthreads();
             const int per = (nw + nthr - 1) / nthr;
             const int w0 = tid * per, w1 = min(nw, w0 + per);
             int c = 0;
             for (int i = w0; i < w1; ++i) c += __builtin_popcount(S.bitmap[i]);
-            const int incl = block_incl_scan(c, S);
-            int o = written + incl - c;
+            int o = block_incl_scan(c, S) - c;
             for (int i = w0; i < w1; ++i) {
                 uint32_t bits = S.bitmap[i];
                 while (bits) {
                     const int bit = __builtin_ctz(bits);
                     bits &= bits - 1u;
-                    if (o < k) out_row[o] = (int)base + i * 32 + bit;
+                    if (o < k) out_row[o] = i * 32 + bit;
                     ++o;
                 }
             }
-            if (tid == nthr - 1) S.sh[7] = incl;
+        } else {
+            // A larger key range: gather the selection, then sort it (a register bitonic
+            // network costs less than several bitmap passes past 262,144 keys).
+            int c = 0;
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) c += selected(e);
+            int o = block_incl_scan(c, S) - c;
+#pragma unroll
+            for (int e = 0; e < kPer; ++e)
+                if (selected(e)) {
+                    if (o < k) S.out[o] = key[e];
+                    ++o;
+                }
             __syncthreads();
-            written += S.sh[7];
+            write_sorted_output(S.out, k, out_row);
         }
     }
     if (!ok && tid == 0) {
