@@ -400,6 +400,8 @@ dsa_status_t indexer_topk_impl(const uint16_t* q_idx, const uint16_t* k_idx, con
     a.fold_bi = reinterpret_cast<int*>(ws + lay.off_fold_bi);
     a.fold_bs = reinterpret_cast<double*>(ws + lay.off_fold_bs);
     a.fold_bf = reinterpret_cast<float*>(ws + lay.off_fold_bf);
+    a.fold_ms = reinterpret_cast<float*>(ws + lay.off_fold_ms);
+    a.fold_mi = reinterpret_cast<int*>(ws + lay.off_fold_mi);
     a.n_ktiles = (n_keys + dsa::kKeyTileKeys - 1) / dsa::kKeyTileKeys;
     if (cached) {
         // The cache's statistics cover every key appended to it (a superset of the keys
@@ -541,7 +543,7 @@ struct ScoreDumpLayout {
         l.off_delta = o; o = al(o + 4 * (size_t)l.rows);
         l.off_mode = o; o = al(o + 4 * (size_t)l.rows);
         l.off_count = o; o = al(o + 4 * (size_t)l.rows * dsa::kCandSegs);
-        l.off_fbctrl = o; o = al(o + 16);
+        l.off_fbctrl = o; o = al(o + 4 * (size_t)dsa::kFbCtrlWords);
         l.off_fblist = o; o = al(o + 4 * (size_t)l.rows);
         l.off_qstat = o; o = al(o + sizeof(dsa::QHeadStat) * 32 * (size_t)l.rows);
         l.off_cand = o; o = al(o + 8 * (size_t)l.rows * (size_t)l.cap);
@@ -885,6 +887,8 @@ dsa_status_t dsa_indexer_topk_varlen(const uint16_t* q_idx, const uint16_t* k_id
     a.fold_bi = reinterpret_cast<int*>(ws + lay.off_fold_bi);
     a.fold_bs = reinterpret_cast<double*>(ws + lay.off_fold_bs);
     a.fold_bf = reinterpret_cast<float*>(ws + lay.off_fold_bf);
+    a.fold_ms = reinterpret_cast<float*>(ws + lay.off_fold_ms);
+    a.fold_mi = reinterpret_cast<int*>(ws + lay.off_fold_mi);
     dsa::RowInfo* rows = reinterpret_cast<dsa::RowInfo*>(ws + lay.off_rowinfo);
     dsa::SeqKeys* seqs = reinterpret_cast<dsa::SeqKeys*>(ws + lay.off_seqkeys);
     uint16_t* k_tile = reinterpret_cast<uint16_t*>(ws + lay.off_ktile);
@@ -1103,6 +1107,8 @@ dsa_status_t dsa_retrieval_topk(const uint16_t* q, const uint16_t* x, int64_t M,
     a.fold_bi = reinterpret_cast<int*>(ws + lay.off_fold_bi);
     a.fold_bs = reinterpret_cast<double*>(ws + lay.off_fold_bs);
     a.fold_bf = reinterpret_cast<float*>(ws + lay.off_fold_bf);
+    a.fold_ms = reinterpret_cast<float*>(ws + lay.off_fold_ms);
+    a.fold_mi = reinterpret_cast<int*>(ws + lay.off_fold_mi);
     a.rows = reinterpret_cast<const dsa::RowInfo*>(ws + lay.off_rowinfo);
     a.n_kstats = dsa::key_stats_blocks(N);
     hipError_t e = dsa::launch_key_stats(x, N, a.kstats, nullptr, a.diag, s);  // statistics only

@@ -78,6 +78,15 @@ inline int key_parts(int groups) {
 
 constexpr int kFallbackSlots = 32;
 constexpr int kFoldKeys = 4096;
+// The first kFoldSplitRows rows of a block that fall back are each folded as up to kFoldParts
+// key ranges by different fold workgroups; the last range to finish merges the ranges' exact
+// top-k lists.  Later rows are folded whole, one per workgroup.
+constexpr int kFoldSplitRows = 16;
+constexpr int kFoldParts = 16;
+// Fold control words: [0] rows handed over, [1] next work item, [4 + j] ranges finished of
+// split row j, [4 + kFoldSplitRows + j] flags of split row j's ranges (1: one failed, 2: one
+// needed the radix select).
+constexpr int kFbCtrlWords = 4 + 2 * kFoldSplitRows;
 constexpr int kCandSegs = 8;  // count words per row; key ranges per row group: 2 key halves x 4 scoring waves
 
 // Indexer keys are re-laid out once per call as 32-key tiles of 8 KB in the order the
@@ -122,7 +131,7 @@ struct IndexerLayout {
     int rows, cap, sample_stride, fold_cap;
     size_t off_diag, off_kstats, off_tau, off_delta, off_mode, off_count, off_fbctrl, off_fblist;
     size_t off_sample, off_cand, off_ktile, off_qstat;
-    size_t off_fold_s, off_fold_i, off_fold_bi, off_fold_bs, off_fold_bf;
+    size_t off_fold_s, off_fold_i, off_fold_bi, off_fold_bs, off_fold_bf, off_fold_ms, off_fold_mi;
     size_t total;
 
     // rows: block rows; N: the most keys a query may see.  A batch of sequences also needs
@@ -144,7 +153,7 @@ struct IndexerLayout {
         l.off_delta = o; o = al(o + 4 * (size_t)l.rows);
         l.off_mode = o; o = al(o + 4 * (size_t)l.rows);
         l.off_count = o; o = al(o + 4 * (size_t)l.rows * kCandSegs);
-        l.off_fbctrl = o; o = al(o + 16);
+        l.off_fbctrl = o; o = al(o + 4 * (size_t)kFbCtrlWords);
         l.off_fblist = o; o = al(o + 4 * (size_t)l.rows);
         l.off_sample = o; o = al(o + 4 * (size_t)l.rows * (size_t)l.sample_stride);
         l.off_cand = o; o = al(o + 8 * (size_t)l.rows * (size_t)l.cap);
@@ -155,6 +164,8 @@ struct IndexerLayout {
         l.off_fold_bi = o; o = al(o + 4 * (size_t)kFallbackSlots * l.fold_cap);
         l.off_fold_bs = o; o = al(o + 8 * (size_t)kFallbackSlots * l.fold_cap);
         l.off_fold_bf = o; o = al(o + 4 * (size_t)kFallbackSlots * l.fold_cap);
+        l.off_fold_ms = o; o = al(o + 4 * (size_t)kFoldSplitRows * kFoldParts * (size_t)top_k);
+        l.off_fold_mi = o; o = al(o + 4 * (size_t)kFoldSplitRows * kFoldParts * (size_t)top_k);
         l.off_rowinfo = o; o = al(o + 40 * (size_t)row_infos);
         l.off_seqkeys = o; o = al(o + 32 * (size_t)n_seqs);
         l.total = o;
@@ -248,6 +259,8 @@ struct IndexerArgs {
     int* fold_bi;           // [slots][fold_cap]
     double* fold_bs;        // [slots][fold_cap]
     float* fold_bf;         // [slots][fold_cap]
+    float* fold_ms;         // [kFoldSplitRows][kFoldParts][top_k]: split rows' range top-k scores
+    int* fold_mi;           // ... and keys
 };
 
 // Optional per-launch event timing (dsa_profile_enable).  A ProfScope records an

@@ -1400,10 +1400,7 @@ __global__ __launch_bounds__(kRowPrepThreads) void row_prep_kernel(IndexerArgs P
     __shared__ int s_eq[kIdxHeads];
     __shared__ float s_delta;
     __shared__ SelectScratch S;
-    if (r == 0 && threadIdx.x == 0) {
-        P.fb_ctrl[0] = 0;
-        P.fb_ctrl[1] = 0;
-    }
+    if (r == 0 && threadIdx.x < kFbCtrlWords) P.fb_ctrl[threadIdx.x] = 0;
     if (P.clear_diag && r == 0 && threadIdx.x < kDiagSlots) P.diag[threadIdx.x] = 0ull;
     if (P.parts > 2 && threadIdx.x == 0) P.count[(size_t)r * kSegs] = 0;  // appended list counter
     if (!ref.valid) {  // padding row of a batched block: nothing to select
@@ -2079,94 +2076,177 @@ __device__ void fold_score_block(const RowRef& R, int64_t k0, int64_t k1, float 
     }
 }
 
-// Persistent: each workgroup takes flagged rows one at a time and runs the exact
-// blocked fold over 4,096-key blocks (the running list is cut back to its exact top-k
-// whenever the next block could overflow it; new keys are admitted only if score >
-// kth(list at the last cut) - 2 delta).
+// The exact blocked fold of one row's keys [k_lo, k_hi) (at least k of them) over 4,096-key
+// blocks: the running list is cut back to its exact top-k whenever the next block could
+// overflow it, and after the last block; new keys are admitted only if score > kth(list at
+// the last cut) - 2 delta.  Leaves the list's top-k in (Rs[cur], Ri[cur]) (n entries) and
+// returns false if a cut failed (never expected).  Every thread of the block calls it.
+struct FoldBufs {
+    float* Rs[2];
+    int* Ri[2];
+    int* band_i;
+    double* band_s;
+    float* band_f;
+};
+__device__ bool fold_range(const IndexerArgs& P, int r, const RowRef& ref, int64_t k_lo, int64_t k_hi,
+                           const FoldBufs& B, SelectScratch& S, int* s_cnt, int& cur, int& n, bool& radix) {
+    const int k = P.top_k;
+    const float delta = P.delta[r];
+    cur = 0;
+    n = 0;
+    float lo = -INFINITY;
+    for (int64_t b0 = k_lo; b0 < k_hi; b0 += kFoldKeys) {
+        const int64_t b1 = b0 + kFoldKeys < k_hi ? b0 + kFoldKeys : k_hi;
+        if (threadIdx.x == 0) *s_cnt = n;
+        __syncthreads();
+        fold_score_block(ref, b0, b1, lo, B.Rs[cur], B.Ri[cur], s_cnt, P.fold_cap);
+        __syncthreads();
+        n = *s_cnt < P.fold_cap ? *s_cnt : P.fold_cap;
+        __syncthreads();
+        // The list is cut back to its exact top-k only when the next block could overflow
+        // it, and after the last block: admitted keys accumulate over many blocks in
+        // between (the admission threshold from the last cut stays a valid lower bound, as
+        // the list's k-th score only rises), so the cut runs a few times per row, not once
+        // per 4,096 keys.
+        if (n > k && (n > P.fold_cap - kFoldKeys || b1 >= k_hi)) {
+            // Keep exactly the top-k of the list; their fp32 scores go to the other buffer.
+            const int nxt = cur ^ 1;
+            CandList L{};
+            L.s[0] = B.Rs[cur];
+            L.i[0] = B.Ri[cur];
+            L.n[0] = n;
+            L.nseg = 1;
+            // The k-th search cannot fail and the band fits (its capacity is the list's), so
+            // select_core succeeds; should it not, the row is emitted as -1 and counted.
+            const bool ok = select_core(L, k, delta, ref.q, ref.w, P.qstat + (size_t)r * kIdxHeads, ref.keys,
+                                        B.band_i, B.band_s, B.band_f, P.fold_cap, B.Ri[nxt], B.Rs[nxt], S,
+                                        &radix);
+            __syncthreads();
+            if (!ok) return false;  // uniform over the block
+            cur = nxt;
+            n = k;
+            CandList R{};
+            R.s[0] = B.Rs[cur];
+            R.i[0] = B.Ri[cur];
+            R.n[0] = n;
+            R.nseg = 1;
+            const float kth = block_kth_binned<true>(ListSrc{R}, k, S, &radix);
+            const double l = (double)kth - 2.0 * (double)delta;
+            float lf = (float)l;
+            if ((double)lf > l) lf = nextafterf(lf, -INFINITY);
+            lo = lf;
+        }
+    }
+    return true;
+}
+
+// Key ranges a split row's fold takes: each holds at least top_k keys (so each range's
+// top-k list is full), at most kFoldParts of them.
+__device__ __forceinline__ int fold_parts(int64_t nt, int k) {
+    const int64_t p = nt / k;
+    return (int)(p < 1 ? 1 : (p > kFoldParts ? kFoldParts : p));
+}
+
+// Persistent: each workgroup takes work items one at a time.  Items [0, n_split *
+// kFoldParts) are (row j, range p) of the first n_split flagged rows: range p of row j's
+// fold_parts(nt) key ranges is folded to its exact top-k, which goes to the row's merge
+// area; the workgroup that finishes the row's last range (a device-scope counter) merges
+// the ranges' lists with one more exact selection (the top-k of the union of the ranges'
+// top-k lists is the row's top-k).  Items past those are the remaining flagged rows, each
+// folded whole.  No workgroup waits for another.
 __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
     __shared__ SelectScratch S;
-    __shared__ int s_row, s_cnt;
+    __shared__ int s_item, s_cnt, s_last;
     const int slot = blockIdx.x;
-    float* Rs[2] = {P.fold_s + (size_t)slot * 2 * P.fold_cap, P.fold_s + (size_t)slot * 2 * P.fold_cap + P.fold_cap};
-    int* Ri[2] = {P.fold_i + (size_t)slot * 2 * P.fold_cap, P.fold_i + (size_t)slot * 2 * P.fold_cap + P.fold_cap};
-    int* band_i = P.fold_bi + (size_t)slot * P.fold_cap;
-    double* band_s = P.fold_bs + (size_t)slot * P.fold_cap;
-    float* band_f = P.fold_bf + (size_t)slot * P.fold_cap;
+    const FoldBufs B{{P.fold_s + (size_t)slot * 2 * P.fold_cap, P.fold_s + (size_t)slot * 2 * P.fold_cap + P.fold_cap},
+                     {P.fold_i + (size_t)slot * 2 * P.fold_cap, P.fold_i + (size_t)slot * 2 * P.fold_cap + P.fold_cap},
+                     P.fold_bi + (size_t)slot * P.fold_cap, P.fold_bs + (size_t)slot * P.fold_cap,
+                     P.fold_bf + (size_t)slot * P.fold_cap};
     const int k = P.top_k;
-    if (P.fb_ctrl[0] == 0) return;  // final here (select has finished): nothing to fold
+    const int n_fb = P.fb_ctrl[0];  // final here (select has finished)
+    if (n_fb == 0) return;          // nothing to fold
+    const int n_split = n_fb < kFoldSplitRows ? n_fb : kFoldSplitRows;
+    const int n_items = n_split * kFoldParts + (n_fb - n_split);
+    int* parts_done = P.fb_ctrl + 4;
+    int* part_flags = P.fb_ctrl + 4 + kFoldSplitRows;  // bit 0: a range failed; bit 1: one needed the radix select
     for (;;) {
-        if (threadIdx.x == 0) {
-            const int i = atomicAdd(&P.fb_ctrl[1], 1);
-            s_row = i < P.fb_ctrl[0] ? P.fb_list[i] : -1;
-        }
+        if (threadIdx.x == 0) s_item = atomicAdd(&P.fb_ctrl[1], 1);
         __syncthreads();
-        const int r = s_row;
+        const int item = s_item;
         __syncthreads();
-        if (r < 0) return;
+        if (item >= n_items) return;
+        const bool split = item < n_split * kFoldParts;
+        const int j = split ? item / kFoldParts : n_split + (item - n_split * kFoldParts);
+        const int part = split ? item % kFoldParts : 0;
+        const int r = P.fb_list[j];
         const RowRef ref = row_ref(P, r);
         const int64_t p = ref.pos;
         const int64_t nt = (p < ref.nkeys - 1 ? p : ref.nkeys - 1) + 1;
-        const float delta = P.delta[r];
-        const uint16_t* q_row = ref.q;
-        const float* w_row = ref.w;
-        int cur = 0, n = 0;
-        float lo = -INFINITY;
-        bool failed = false, radix = false;
-        for (int64_t b0 = 0; b0 < nt && !failed; b0 += kFoldKeys) {
-            const int64_t b1 = b0 + kFoldKeys < nt ? b0 + kFoldKeys : nt;
-            if (threadIdx.x == 0) s_cnt = n;
-            __syncthreads();
-            fold_score_block(ref, b0, b1, lo, Rs[cur], Ri[cur], &s_cnt, P.fold_cap);
-            __syncthreads();
-            n = s_cnt < P.fold_cap ? s_cnt : P.fold_cap;
-            __syncthreads();
-            // The list is cut back to its exact top-k only when the next block could overflow
-            // it, and after the last block: admitted keys accumulate over many blocks in
-            // between (the admission threshold from the last cut stays a valid lower bound, as
-            // the list's k-th score only rises), so the cut runs a few times per row, not once
-            // per 4,096 keys.
-            if (n > k && (n > P.fold_cap - kFoldKeys || b1 >= nt)) {
-                // Keep exactly the top-k of the list; their fp32 scores go to the other buffer.
-                const int nxt = cur ^ 1;
-                CandList L{};
-                L.s[0] = Rs[cur];
-                L.i[0] = Ri[cur];
-                L.n[0] = n;
-                L.nseg = 1;
-                // The k-th search cannot fail and the band fits (its capacity is the list's), so
-                // select_core succeeds; should it not, the row is emitted as -1 and counted.
-                const bool ok = select_core(L, k, delta, q_row, w_row, P.qstat + (size_t)r * kIdxHeads, ref.keys,
-                                            band_i, band_s, band_f,
-                                            P.fold_cap, Ri[nxt], Rs[nxt], S, &radix);
-                __syncthreads();
-                if (!ok) {  // uniform over the block
-                    failed = true;
-                    break;
-                }
-                cur = nxt;
-                n = k;
-                CandList R{};
-                R.s[0] = Rs[cur];
-                R.i[0] = Ri[cur];
-                R.n[0] = n;
-                R.nseg = 1;
-                const float kth = block_kth_binned<true>(ListSrc{R}, k, S, &radix);
-                const double l = (double)kth - 2.0 * (double)delta;
-                float lf = (float)l;
-                if ((double)lf > l) lf = nextafterf(lf, -INFINITY);
-                lo = lf;
-            }
-        }
+        const int np = split ? fold_parts(nt, k) : 1;
+        if (part >= np) continue;  // an unused range slot of a shorter row
+        bool radix = false;
         int32_t* out_row = ref.out;
-        if (radix && threadIdx.x == 0) atomicAdd(&P.diag[kDiagRadix], 1ull);
-        if (failed) {
-            for (int j = threadIdx.x; j < k; j += blockDim.x) out_row[j] = -1;
+        if (np == 1) {  // the row whole
+            int cur, n;
+            const bool ok = fold_range(P, r, ref, 0, nt, B, S, &s_cnt, cur, n, radix);
+            if (radix && threadIdx.x == 0) atomicAdd(&P.diag[kDiagRadix], 1ull);
+            if (!ok) {
+                for (int x = threadIdx.x; x < k; x += blockDim.x) out_row[x] = -1;
+                if (threadIdx.x == 0) atomicAdd(&P.diag[kDiagFailed], 1ull);
+                __syncthreads();
+                continue;
+            }
+            // n == k here (nt > k for every scored row): the list is the exact top-k.
+            for (int x = threadIdx.x; x < k; x += blockDim.x) S.out[x] = x < n ? B.Ri[cur][x] : -1;
+            __syncthreads();
+            write_sorted_output(S.out, k, out_row);
+            __syncthreads();
+            continue;
+        }
+        // Range `part` of np: [part nt / np, (part + 1) nt / np), at least k keys.
+        const int64_t k_lo = nt * part / np, k_hi = nt * (part + 1) / np;
+        int cur, n;
+        const bool ok = fold_range(P, r, ref, k_lo, k_hi, B, S, &s_cnt, cur, n, radix);
+        float* ms = P.fold_ms + ((size_t)j * kFoldParts) * k;
+        int* mi = P.fold_mi + ((size_t)j * kFoldParts) * k;
+        // The range's top-k (exactly k entries: the range holds at least k keys) to its slice.
+        for (int x = threadIdx.x; x < k; x += blockDim.x) {
+            const bool have = ok && x < n;
+            ms[(size_t)part * k + x] = have ? B.Rs[cur][x] : -INFINITY;
+            mi[(size_t)part * k + x] = have ? B.Ri[cur][x] : -1;
+        }
+        // Publish the slice (device-scope release), then count the range; the workgroup that
+        // counts the last range reads every slice after an acquire fence.
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            if (!ok || radix) atomicOr(&part_flags[j], (ok ? 0 : 1) | (radix ? 2 : 0));
+            s_last = atomicAdd(&parts_done[j], 1) == np - 1;
+        }
+        __syncthreads();
+        if (!s_last) continue;
+        __threadfence();
+        const int flags = atomicOr(&part_flags[j], 0);
+        radix = (flags & 2) != 0;
+        bool merged = false;
+        if ((flags & 1) == 0) {
+            CandList L{};
+            L.s[0] = ms;
+            L.i[0] = mi;
+            L.n[0] = np * k;
+            L.nseg = 1;
+            merged = select_core(L, k, P.delta[r], ref.q, ref.w, P.qstat + (size_t)r * kIdxHeads, ref.keys,
+                                 B.band_i, B.band_s, B.band_f, P.fold_cap, B.Ri[0], B.Rs[0], S, &radix);
+            __syncthreads();
+        }
+        if (radix && threadIdx.x == 0) atomicAdd(&P.diag[kDiagRadix], 1ull);  // once per row
+        if (!merged) {
+            for (int x = threadIdx.x; x < k; x += blockDim.x) out_row[x] = -1;
             if (threadIdx.x == 0) atomicAdd(&P.diag[kDiagFailed], 1ull);
             __syncthreads();
             continue;
         }
-        // n == k here (nt > k for every scored row): the list is the exact top-k.
-        for (int j = threadIdx.x; j < k; j += blockDim.x) S.out[j] = j < n ? Ri[cur][j] : -1;
+        for (int x = threadIdx.x; x < k; x += blockDim.x) S.out[x] = B.Ri[0][x];
         __syncthreads();
         write_sorted_output(S.out, k, out_row);
         __syncthreads();

@@ -154,11 +154,15 @@ def _run_forced_fallback(case):
 
 @pytest.mark.parametrize("case", [(30000, 6, 2048, "gauss"), (20000, 4, 512, "concentrated"),
                                   (9000, 5, 256, "int"), (12000, 3, 4096, "gauss"),
-                                  (6000, 4, 100, "concentrated")])
+                                  (6000, 4, 100, "concentrated"), (30000, 24, 2048, "gauss"),
+                                  (5000, 20, 2048, "gauss"), (3000, 6, 2048, "gauss")])
 def test_forced_fallback_fold_gives_same_indices(dsa_gpu, oracle_mod, tmp_path, case):
-    """DSA_DEBUG_FORCE_FALLBACK=1 sends every row through the blocked fold.  The fold sorts its
-    selection on output: with its 512 threads, top_k 512 .. 4,096 take the register form of the
-    sorting network with 1 .. 8 keys per thread, top_k 100 and 256 the LDS form."""
+    """DSA_DEBUG_FORCE_FALLBACK=1 sends every row through the blocked fold.  The first 16 rows of
+    a block are folded as up to 16 key ranges of at least top_k keys each (2 to 16 here) and
+    merged, later rows (of the 24- and 20-row cases) whole; rows of fewer than 2 top_k keys (the
+    3,000-key case) hold a single range and are folded whole.  The fold sorts its selection on output:
+    with its 512 threads, top_k 512 .. 4,096 take the register form of the sorting network with
+    1 .. 8 keys per thread, top_k 100 and 256 the LDS form."""
     wl = di.Workload("fb", case[0], case[1], case[2], 16, 5, case[3])
     q, k, w = di.make_indexer_inputs(wl)
     normal = run_gpu(dsa_gpu, q, k, w, wl.pos0, wl.top_k)
