@@ -2141,15 +2141,19 @@ __device__ bool fold_range(const IndexerArgs& P, int r, const RowRef& ref, int64
 }
 
 // Key ranges a split row's fold takes: each holds at least top_k keys (so each range's
-// top-k list is full), at most kFoldParts of them.
-__device__ __forceinline__ int fold_parts(int64_t nt, int k) {
-    const int64_t p = nt / k;
+// top-k list is full), at most kFoldParts of them, and the merge's ranges x top_k entries
+// fit the fold's band buffer (fold_cap entries): when every score ties, the whole union is
+// the merge's band.
+__device__ __forceinline__ int fold_parts(int64_t nt, int k, int fold_cap) {
+    int64_t p = nt / k;
+    const int64_t fit = fold_cap / k;
+    if (p > fit) p = fit;
     return (int)(p < 1 ? 1 : (p > kFoldParts ? kFoldParts : p));
 }
 
 // Persistent: each workgroup takes work items one at a time.  Items [0, n_split *
 // kFoldParts) are (row j, range p) of the first n_split flagged rows: range p of row j's
-// fold_parts(nt) key ranges is folded to its exact top-k, which goes to the row's merge
+// fold_parts() key ranges is folded to its exact top-k, which goes to the row's merge
 // area; the workgroup that finishes the row's last range (a device-scope counter) merges
 // the ranges' lists with one more exact selection (the top-k of the union of the ranges'
 // top-k lists is the row's top-k).  Items past those are the remaining flagged rows, each
@@ -2182,7 +2186,7 @@ __global__ __launch_bounds__(kSelectThreads) void fold_kernel(IndexerArgs P) {
         const RowRef ref = row_ref(P, r);
         const int64_t p = ref.pos;
         const int64_t nt = (p < ref.nkeys - 1 ? p : ref.nkeys - 1) + 1;
-        const int np = split ? fold_parts(nt, k) : 1;
+        const int np = split ? fold_parts(nt, k, P.fold_cap) : 1;
         if (part >= np) continue;  // an unused range slot of a shorter row
         bool radix = false;
         int32_t* out_row = ref.out;

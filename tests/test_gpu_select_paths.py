@@ -113,3 +113,38 @@ def test_recency_biased_scores(dsa_gpu, oracle_mod, N, L):
     assert np.array_equal(got[rows], want)
     assert (np.diff(got, axis=1) > 0).all()
     assert st["rows_failed"] == 0 and st["rows_fallback"] == 0
+
+
+def test_recency_biased_scores_c4_shape(dsa_gpu, oracle_mod):
+    """C4's shape (786,432 keys, 8,192 queries in 8 blocks) with recency-biased keys: indices
+    bit-exact on sampled rows at every block boundary and no row falls back."""
+    wl = di.Workload("recency-c4", 786432, 8192, 2048, 16, 32, "recency")
+    q, k, w = di.make_indexer_inputs(wl)
+    got, st = run_with_stats(dsa_gpu, q, k, w, wl.pos0, wl.top_k)
+    report(f"recency C4 shape: {st}")
+    rows = np.array([0, 1023, 1024, 4095, 4096, 7167, 8191], dtype=np.int64)
+    want = oracle_mod.topk(q, k, w, wl.pos0, wl.top_k, rows=rows)
+    assert np.array_equal(got[rows], want)
+    assert (np.diff(got, axis=1) > 0).all()
+    assert st["rows_failed"] == 0 and st["rows_fallback"] == 0
+
+
+def test_zero_rows_fold_beside_select(dsa_gpu, oracle_mod):
+    """Three all-zero query rows in a block of 64 at 131,072 keys: every score of those rows is
+    0, so all their keys are candidates and they fall back to the fold, whose split form (key
+    ranges merged) must give keys 0 .. k-1 (the lower index wins every tie); the other rows
+    finish in select in the same launches."""
+    wl = di.Workload("zero-mix", 131072, 64, 2048, 16, 33, "gauss")
+    q, k, w = di.make_indexer_inputs(wl)
+    zero_rows = np.array([3, 17, 40])
+    qf = di.bf16_bits_to_f32(q)
+    qf[zero_rows] = 0.0
+    q = di.f32_to_bf16_bits(qf)
+    got, st = run_with_stats(dsa_gpu, q, k, w, wl.pos0, wl.top_k)
+    report(f"zero rows beside select: {st}")
+    assert st["rows_fallback"] == zero_rows.size and st["rows_failed"] == 0
+    for r in zero_rows:
+        assert np.array_equal(got[r], np.arange(wl.top_k, dtype=np.int32))
+    rows = np.array([0, 2, 4, 18, 39, 41, 63], dtype=np.int64)
+    want = oracle_mod.topk(q, k, w, wl.pos0, wl.top_k, rows=rows)
+    assert np.array_equal(got[rows], want)
