@@ -524,7 +524,7 @@ dsa_status_t dsa_indexer_topk_stats(const void* workspace, dsa_indexer_stats_t* 
 }
 
 // Workspace of dsa_indexer_scores: the indexer sections it uses, with a candidate capacity
-// that holds every key of a row (each of the 8 segments one extra tile wide).
+// that holds every key of a row (its 8 scoring key ranges, one extra tile each).
 struct ScoreDumpLayout {
     int rows, cap;
     size_t off_diag, off_kstats, off_tau, off_delta, off_mode, off_count, off_fbctrl, off_fblist, off_qstat,

@@ -40,9 +40,9 @@ constexpr int kRowsPerGroup = 8;  // indexer query rows scored together (one sam
 // Sample keys expected above the threshold: the threshold is the sample's rank-r score
 // with r about kSampleRank, estimating the 2.5 k-th score of the row.  The true k-th score
 // sits near sample rank kSampleRank / 2.5 (~51, std ~7), so the threshold falls below it
-// with overwhelming probability.  The candidate count (2.5 k, relative std ~1/11) is
-// spread over 8 segments of cap/8 = 1.6 x their mean; a smaller sample (r = 64) was
-// measured to overflow segments and send rows to the fold.
+// with overwhelming probability.  The candidate count (2.5 k, relative std ~1/11) fills a
+// list of cap = 1.56 x its mean (about 6 std); smaller samples (r = 64, 96) were measured
+// to bring the largest rows too close to that capacity.
 constexpr int kSampleRank = 128;
 
 // Keys scored in the threshold sample of a row group whose first row sees n_t keys.
@@ -114,7 +114,7 @@ enum DiagSlot : int {
     kDiagRows = 0,      // rows finished by the candidate path
     kDiagRowsAll,       // rows with at most top_k causal keys (no selection)
     kDiagFallback,      // rows handed to the blocked fold ...
-    kDiagFbOverflow,    // ... because a candidate segment overflowed (or the fold was forced)
+    kDiagFbOverflow,    // ... because the row's candidate list overflowed (or the fold was forced)
     kDiagFbIncomplete,  // ... because the candidates were not provably a superset of the top-k
     kDiagFbBand,        // ... because the band outgrew select's buffer
     kDiagFailed,        // rows no path could finish (emitted as -1; never expected)
@@ -340,8 +340,8 @@ hipError_t launch_causal_mask(int32_t* idx, int64_t L, int top_k, int64_t q_pos0
 // Diagnostic: row_prep and the production filter kernel (two key halves, parts = 2) with every
 // row's threshold at -inf, then each row's stored (score, key) entries scattered into
 // scores[row][key] (NaN elsewhere) and the rows' error bounds into delta_out.  The caller
-// sets a.top_k = 1 and a.cap large enough that no row samples and every segment holds its
-// keys.
+// sets a.top_k = 1 and a.cap large enough that no row samples and every row's list holds
+// all of its keys.
 hipError_t launch_score_dump(const IndexerArgs& a, float* scores, int64_t n_cols, float* delta_out, hipStream_t s);
 
 struct AttentionArgs {

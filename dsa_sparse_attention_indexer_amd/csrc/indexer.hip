@@ -39,7 +39,7 @@
 
 namespace dsa {
 
-constexpr int kSegs = kCandSegs;  // candidate segments per row: (key half, scoring wave)
+constexpr int kSegs = kCandSegs;  // count words per row; key ranges per row group (key half, scoring wave)
 
 // Where block row r's query, weights, output and keys live.
 struct RowRef {
@@ -669,7 +669,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(IndexerArgs P, int
         for (int j = 0; j < kRowsPerWave; ++j)
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+a"(a[j][kk]));  // keep the query fragments in AGPRs
-        // Segment s covers the contiguous tile range [s*tps, (s+1)*tps).
+        // Key range s (part * 4 + wave) covers the contiguous tiles [s*tps, (s+1)*tps).
         const int n_tiles = (int)((n_keys + kKeyTile - 1) / kKeyTile);
         const int tps = (n_tiles + n_segs - 1) / n_segs;
         const int t0 = segment * tps;
